@@ -1,0 +1,154 @@
+"""Reference GEMV, epilogues, MoE index and combine (oracle; test infrastructure).
+
+What the GPU path computes, written as plain definitions in fp64:
+  * GEMV (NInfer article, section 2: the decode matmul over quantised
+    weights, with residual add fused):
+        y[n, m] = r[n, m] + sum_k x[n, k] * W[m, k]
+    x is bf16 (exact in fp64), W the fp32 dequantised weights.
+  * SwiGLU (same section: SwiGLU fused into the matmul): for the fused
+    [2I][K] matrix, gate rows [0, I) and up rows [I, 2I):
+        h[n, i] = silu(g) * u,  silu(g) = g / (1 + exp(-g))
+  * MoE (Decapybara page: a top-8 softmax router; memra page: a 35B-A3B MoE
+    on one card): each token t runs only its top-k experts e_j with weights
+    p_j; per (t, j): h = SwiGLU(x_t W_gu[e]^T) (kept in fp64), o = h W_dn[e]^T,
+    y_t = r_t + sum_j p_j o_j with j in increasing order.
+  * MoE routing index: the (token, slot) pairs grouped by expert, ordered by
+    (expert, token, slot); counts, offsets, the ascending list of active
+    experts and an error flag for ids outside [0, E).
+  * Per-output tolerances for the fp32-accumulating GPU path:
+        GEMV   T = 2e-3 * sum_k |x_k W_k| + 1e-5
+        SwiGLU T_h = 1.1 (|u| + T_u) T_g + |silu(g)| T_u + 1e-6 |h| + 1e-5
+               (max |silu'| < 1.1; the 1e-6 |h| term covers device exp/div)
+        MoE    T_y = sum_j |p_j| (2e-3 sum_c |h_c Wd_c| + sum_c |Wd_c| T_h,c
+                                   + 1e-5) + 1e-5
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from . import encodings as enc
+
+REL = 2e-3
+ABS = 1e-5
+
+
+def x_from_bits(x_bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns [N][K] -> fp64 values."""
+    return enc.f32_from_bf16_bits(x_bits).astype(np.float64)
+
+
+def gemv(x: np.ndarray, W: np.ndarray, residual: np.ndarray | None = None) -> np.ndarray:
+    """y[N][M] = residual + x[N][K] @ W[M][K]^T in fp64."""
+    y = np.asarray(x, dtype=np.float64) @ np.asarray(W, dtype=np.float64).T
+    if residual is not None:
+        y = y + np.asarray(residual, dtype=np.float64)
+    return y
+
+
+def gemv_tolerance(x: np.ndarray, W: np.ndarray) -> np.ndarray:
+    return REL * (np.abs(np.asarray(x, np.float64)) @ np.abs(np.asarray(W, np.float64)).T) + ABS
+
+
+def silu(g: np.ndarray) -> np.ndarray:
+    g = np.asarray(g, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g))
+
+
+def swiglu(x: np.ndarray, W_gu: np.ndarray):
+    """Fused gate/up: returns (h, T_h) for W_gu [2I][K]."""
+    I = W_gu.shape[0] // 2
+    g = gemv(x, W_gu[:I])
+    u = gemv(x, W_gu[I:])
+    Tg = gemv_tolerance(x, W_gu[:I])
+    Tu = gemv_tolerance(x, W_gu[I:])
+    sg = silu(g)
+    h = sg * u
+    Th = 1.1 * (np.abs(u) + Tu) * Tg + np.abs(sg) * Tu + 1e-6 * np.abs(h) + ABS
+    return h, Th
+
+
+def moe_index(ids: np.ndarray, E: int):
+    """Routing index for ids [N][k] (int32).
+
+    Returns counts[E], offsets[E+1], pairs[N*k] (flat entry t*k + j in
+    (expert, token, slot) order, -1 past offsets[E]), active[E] (ascending
+    experts with a nonzero count, -1 after n_active), n_active, err (1 if an
+    id lies outside [0, E)).
+    """
+    ids = np.asarray(ids, dtype=np.int64)
+    N, k = ids.shape
+    flat = ids.reshape(-1)
+    valid = (flat >= 0) & (flat < E)
+    counts = np.zeros(E, dtype=np.int32)
+    for v in flat[valid]:
+        counts[v] += 1
+    offsets = np.zeros(E + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum(counts)
+    pairs = np.full(N * k, -1, dtype=np.int32)
+    pos = offsets[:-1].copy()
+    for idx in range(N * k):            # idx = t*k + j is already (t, j) order
+        if valid[idx]:
+            e = flat[idx]
+            pairs[pos[e]] = idx
+            pos[e] += 1
+    act = np.nonzero(counts)[0].astype(np.int32)
+    active = np.full(E, -1, dtype=np.int32)
+    active[: act.size] = act
+    err = int(not np.all(valid))
+    return counts, offsets, pairs, active, int(act.size), err
+
+
+def moe(x: np.ndarray, ids: np.ndarray, gates: np.ndarray, W_gu: list, W_dn: list,
+        residual: np.ndarray | None = None):
+    """MoE FFN reference. x [N][H] fp64, ids/gates [N][k], W_gu[e] [2I][H],
+    W_dn[e] [H][I] (fp32 dequantised). Returns (y [N][H], T_y [N][H]).
+    Slots whose id is outside [0, E) contribute nothing."""
+    x = np.asarray(x, dtype=np.float64)
+    N, k = ids.shape
+    E = len(W_gu)
+    H = x.shape[1]
+    y = np.zeros((N, H)) if residual is None else np.asarray(residual, np.float64).copy()
+    T = np.full((N, H), ABS)
+    for t in range(N):
+        for j in range(k):
+            e = int(ids[t, j])
+            if not (0 <= e < E):
+                continue
+            p = float(gates[t, j])
+            h, Th = swiglu(x[t: t + 1], W_gu[e])
+            Wd = np.asarray(W_dn[e], np.float64)
+            o = h @ Wd.T
+            y[t] += p * o[0]
+            To = REL * (np.abs(h) @ np.abs(Wd).T) + Th @ np.abs(Wd).T + ABS
+            T[t] += abs(p) * To[0]
+    return y, T
+
+
+def route_topk_softmax(logits: np.ndarray, k: int):
+    """Top-k experts per token (largest logit first, ties to the lower index)
+    and softmax weights over the selected logits (fp64, returned as fp32)."""
+    logits = np.asarray(logits, dtype=np.float64)
+    N, E = logits.shape
+    ids = np.zeros((N, k), dtype=np.int32)
+    gates = np.zeros((N, k), dtype=np.float32)
+    for t in range(N):
+        order = sorted(range(E), key=lambda e: (-logits[t, e], e))[:k]
+        sel = np.array([logits[t, e] for e in order])
+        w = np.exp(sel - sel.max())
+        w = w / w.sum()
+        ids[t] = order
+        gates[t] = w.astype(np.float32)
+    return ids, gates
+
+
+def exact_dot(xs, ws) -> "Fraction":
+    """Exact sum of products of two float sequences (fractions)."""
+    from fractions import Fraction
+    return sum((Fraction(float(a)) * Fraction(float(b)) for a, b in zip(xs, ws)), Fraction(0))
+
+
+def silu_scalar(g: float) -> float:
+    return g / (1.0 + math.exp(-g))

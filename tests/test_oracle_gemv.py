@@ -1,0 +1,176 @@
+"""Pins for the oracle's GEMV, SwiGLU, MoE index/combine and router:
+exact rational brute force, closed forms, special cases and independent
+reformulations."""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import synthetic
+from oracle import encodings as enc
+from oracle import gemv as G
+from oracle import quant
+from oracle.dequant import dequant
+
+
+def _x(rng, N, K, outliers=0.0):
+    return G.x_from_bits(synthetic.activations(rng, N, K, outliers))
+
+
+@pytest.mark.parametrize("N", [1, 3, 8])
+def test_gemv_fp64_against_exact_fractions(N):
+    rng = np.random.default_rng(N)
+    M, K = 64, 64
+    W = dequant(quant.quantize(synthetic.weights(rng, M, K), "int4"))
+    x = _x(rng, N, K)
+    r = synthetic.residual(rng, N, M)
+    y = G.gemv(x, W, r)
+    for n in range(N):
+        for m in range(M):
+            ex = G.exact_dot(x[n], W[m]) + Fraction(float(r[n, m]))
+            bound = K * 2.0 ** -52 * (float(np.abs(x[n]) @ np.abs(W[m])) + abs(float(r[n, m])))
+            assert abs(Fraction(float(y[n, m])) - ex) <= Fraction(bound)
+
+
+def test_gemv_orientation_and_special_cases():
+    rng = np.random.default_rng(7)
+    M, K = 48, 96                      # non-square: a transposed operand fails
+    W = dequant(quant.quantize(synthetic.weights(rng, M, K), "int5"))
+    # one-hot x selects column k of W for every output row
+    for k in (0, 5, 95):
+        x = np.zeros((1, K))
+        x[0, k] = 1.0
+        assert np.array_equal(G.gemv(x, W)[0], W[:, k].astype(np.float64))
+    # all-ones x gives row sums
+    assert np.allclose(G.gemv(np.ones((2, K)), W), W.astype(np.float64).sum(axis=1)[None, :], rtol=0, atol=1e-12)
+    # zero weights: y == residual exactly
+    r = synthetic.residual(rng, 3, M)
+    assert np.array_equal(G.gemv(_x(rng, 3, K), np.zeros((M, K), np.float32), r), r.astype(np.float64))
+    # token n only sees row n of x
+    x = _x(rng, 4, K)
+    y = G.gemv(x, W)
+    for n in range(4):
+        assert np.array_equal(G.gemv(x[n:n + 1], W)[0], y[n])
+
+
+def test_tolerance_covers_fp32_accumulation():
+    rng = np.random.default_rng(8)
+    M, K = 256, 5120
+    W = dequant(quant.quantize(synthetic.weights(rng, M, K), "nvfp4"))
+    x = _x(rng, 4, K, outliers=0.01)
+    y = G.gemv(x, W)
+    T = G.gemv_tolerance(x, W)
+    # sequential fp32 accumulation in the worst (natural) order
+    acc = np.zeros((4, M), np.float32)
+    x32 = x.astype(np.float32)
+    for k in range(K):
+        acc += x32[:, k:k + 1] * W[None, :, k]
+    assert np.all(np.abs(acc - y) <= T)
+    # and the tolerance is not vacuous: scaling one weight row by 1.3 fails it
+    W2 = W.copy()
+    W2[3] *= 1.3
+    assert np.any(np.abs(G.gemv(x, W2) - y) > T)
+
+
+def test_bf16_inputs_decode():
+    bits = synthetic.bf16_bits(np.array([[1.0, -2.5, 3.140625, 1e-3]], np.float32))
+    v = G.x_from_bits(bits)
+    assert v[0, 0] == 1.0 and v[0, 1] == -2.5 and v[0, 2] == 3.140625
+    assert abs(v[0, 3] - 1e-3) <= 1e-3 * 2 ** -8
+    # round to nearest even: 1 + 2^-8 is a tie between 1 and 1 + 2^-7
+    assert synthetic.bf16_bits(np.array([1 + 2 ** -8], np.float32))[0] == 0x3F80
+    assert synthetic.bf16_bits(np.array([1 + 3 * 2 ** -8], np.float32))[0] == 0x3F82
+
+
+def test_silu_closed_forms():
+    assert G.silu(np.array([0.0]))[0] == 0.0
+    assert G.silu(np.array([1.0]))[0] == pytest.approx(1.0 / (1.0 + math.exp(-1.0)), rel=1e-15)
+    assert G.silu(np.array([-1.0]))[0] == pytest.approx(-1.0 / (1.0 + math.e), rel=1e-15)
+    assert G.silu(np.array([40.0]))[0] == pytest.approx(40.0, rel=1e-15)
+    assert abs(G.silu(np.array([-40.0]))[0]) < 1e-15
+    # the derivative bound used by the SwiGLU tolerance
+    g = np.linspace(-20, 20, 200001)
+    ds = np.gradient(G.silu(g), g)
+    assert ds.max() < 1.1 and ds.min() > -0.11
+
+
+def test_swiglu_uses_gate_rows_first():
+    rng = np.random.default_rng(9)
+    I, K = 32, 64
+    W = dequant(quant.quantize(synthetic.weights(rng, 2 * I, K), "int4"))
+    x = _x(rng, 2, K)
+    h, Th = G.swiglu(x, W)
+    g = x @ W[:I].astype(np.float64).T
+    u = x @ W[I:].astype(np.float64).T
+    assert np.allclose(h, g / (1 + np.exp(-g)) * u, rtol=1e-14, atol=0)
+    h_swapped = u / (1 + np.exp(-u)) * g
+    assert not np.allclose(h, h_swapped)
+    assert np.all(Th > 0)
+
+
+def test_moe_index_matches_stable_sort():
+    rng = np.random.default_rng(10)
+    for N, k, E in [(1, 8, 128), (8, 8, 128), (5, 3, 7), (8, 8, 4)]:
+        ids = rng.integers(0, E, size=(N, k)).astype(np.int32)   # duplicates allowed
+        counts, offsets, pairs, active, n_active, err = G.moe_index(ids, E)
+        keys = sorted((int(ids[t, j]), t, j) for t in range(N) for j in range(k))
+        assert [int(p) for p in pairs] == [t * k + j for (_, t, j) in keys]
+        assert counts.sum() == N * k and offsets[-1] == N * k
+        assert list(np.nonzero(counts)[0]) == list(active[:n_active])
+        assert np.all(active[n_active:] == -1) and err == 0
+        for e in range(E):
+            seg = pairs[offsets[e]: offsets[e + 1]]
+            assert all(ids.reshape(-1)[s] == e for s in seg)
+
+
+def test_moe_index_flags_out_of_range_ids():
+    ids = np.array([[0, 5, -1], [9, 2, 2]], np.int32)
+    counts, offsets, pairs, active, n_active, err = G.moe_index(ids, 6)
+    assert err == 1
+    assert counts.sum() == 4 and offsets[-1] == 4
+    assert list(pairs[:4]) == [0, 4, 5, 1] and list(pairs[4:]) == [-1, -1]
+    assert list(active[:n_active]) == [0, 2, 5]
+
+
+def test_moe_reference_equals_dense_expert_formulation():
+    """sum over slots (the oracle) == sum over all experts weighted by a dense
+    token x expert gate matrix (an independent arrangement)."""
+    rng = np.random.default_rng(12)
+    H, I, E, k, N = 64, 32, 6, 3, 4
+    Wgu = [dequant(quant.quantize(synthetic.weights(rng, 2 * I, H), "int4")) for _ in range(E)]
+    Wdn = [dequant(quant.quantize(synthetic.weights(rng, H, I), "int4")) for _ in range(E)]
+    x = _x(rng, N, H)
+    ids = np.array([[0, 2, 2], [5, 1, 0], [3, 3, 3], [4, 0, 9]], np.int32)   # dup + invalid
+    gates = synthetic.random_gates(rng, N, k)
+    r = synthetic.residual(rng, N, H)
+    y, T = G.moe(x, ids, gates, Wgu, Wdn, r)
+    Gm = np.zeros((N, E))
+    for t in range(N):
+        for j in range(k):
+            if 0 <= ids[t, j] < E:
+                Gm[t, ids[t, j]] += gates[t, j]
+    dense = r.astype(np.float64).copy()
+    for e in range(E):
+        g = x @ Wgu[e][:I].astype(np.float64).T
+        u = x @ Wgu[e][I:].astype(np.float64).T
+        o = (g / (1 + np.exp(-g)) * u) @ Wdn[e].astype(np.float64).T
+        dense += Gm[:, e:e + 1] * o
+    assert np.allclose(y, dense, rtol=1e-12, atol=1e-12)
+    assert np.all(T > 0)
+
+
+def test_router_topk_softmax():
+    rng = np.random.default_rng(13)
+    logits = synthetic.router_logits(rng, 8, 128)
+    logits[0, 10] = logits[0, 11] = 9.0            # a tie: lower index first
+    ids, gates = G.route_topk_softmax(logits, 8)
+    assert ids[0, 0] == 10 and ids[0, 1] == 11
+    for t in range(8):
+        order = np.argsort(-logits[t].astype(np.float64), kind="stable")[:8]
+        assert list(ids[t]) == list(order)
+        full = np.exp(logits[t].astype(np.float64) - logits[t].max())
+        full /= full.sum()
+        renorm = full[ids[t]] / full[ids[t]].sum()
+        assert np.allclose(gates[t], renorm, rtol=1e-6)
+        assert abs(float(gates[t].astype(np.float64).sum()) - 1.0) < 1e-6
