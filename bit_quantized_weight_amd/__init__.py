@@ -1,0 +1,183 @@
+"""Python binding for libqgemv (include/qgemv.h): argument marshalling only.
+
+Every computation runs in libqgemv.so (HIP kernels for gfx950, and the C++
+host packer). This module only converts Python arguments into pointers and
+sizes, picks the current torch stream, and turns error codes into
+exceptions. There is no fallback: if the library is not built, importing
+anything that needs it raises.
+
+PyTorch is used for device memory and streams only; torch is imported before
+the library is loaded so that both share torch's HIP runtime.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+FORMATS = {"int4": 1, "int5": 2, "int8": 3, "nvfp4": 4}
+STATUS = {0: "OK", -1: "EINVAL", -2: "EFORMAT", -3: "EALIGN", -4: "ERANGE", -5: "EWORKSPACE",
+          -6: "EHIP", -7: "EUNSUPPORTED"}
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqgemv.so")
+
+_lib = None
+
+
+class QgemvError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {STATUS.get(status, status)} ({strerror(status) if _lib else status})")
+
+
+def _fmt(fmt) -> int:
+    return FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
+
+
+def load(require_torch: bool = True):
+    """Load libqgemv.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if require_torch:
+        import torch  # noqa: F401  (binds the library to torch's HIP runtime)
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m bit_quantized_weight_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    PSZ = ctypes.POINTER(ctypes.c_size_t)
+    sig = {
+        "qgemv_strerror": (ctypes.c_char_p, [I32]),
+        "qgemv_version": (I32, []),
+        "qgemv_packed_bytes": (I32, [I32, I64, I64, PSZ, PSZ]),
+        "qgemv_expert_stride": (I32, [I32, I64, I64, PSZ, PSZ]),
+        "qgemv_pack": (I32, [I32, P, I64, I64, P, P]),
+        "qgemv_pack_codes": (I32, [I32, P, P, P, ctypes.c_float, I64, I64, P, P]),
+        "qgemv": (I32, [I32, P, P, P, P, P, I64, I64, I32, P]),
+        "qgemv_swiglu": (I32, [I32, P, P, P, P, I64, I64, I32, P]),
+        "qgemv_moe_workspace_bytes": (I32, [I32, I64, I64, I32, I32, PSZ]),
+        "qgemv_moe": (I32, [I32, P, P, P, P, I32, I64, I64, P, P, P, I32, P, P, I32, P, SZ, P]),
+        "qgemv_moe_index": (I32, [P, I32, I32, I32, P, P, P, P, P, P]),
+        "qgemv_dequant": (I32, [I32, P, P, I64, I64, P, P]),
+        "qgemv_probe_read": (I32, [P, SZ, P, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def symbols() -> list[str]:
+    """Names of the entry points the binding declares (the C ABI)."""
+    return ["qgemv_strerror", "qgemv_version", "qgemv_packed_bytes", "qgemv_expert_stride", "qgemv_pack",
+            "qgemv_pack_codes", "qgemv", "qgemv_swiglu", "qgemv_moe_workspace_bytes", "qgemv_moe",
+            "qgemv_moe_index", "qgemv_dequant", "qgemv_probe_read"]
+
+
+def strerror(status: int) -> str:
+    return load(False).qgemv_strerror(int(status)).decode()
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise QgemvError(rc, what)
+
+
+def _ptr(t):
+    """Device or host pointer of a torch tensor / numpy array / None."""
+    if t is None:
+        return None
+    if isinstance(t, np.ndarray):
+        return t.ctypes.data
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# ------------------------------------------------------------------ host ---
+
+def packed_bytes(fmt, M: int, K: int) -> tuple[int, int]:
+    a, b = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(load(False).qgemv_packed_bytes(_fmt(fmt), M, K, ctypes.byref(a), ctypes.byref(b)), "qgemv_packed_bytes")
+    return a.value, b.value
+
+
+def expert_stride(fmt, M: int, K: int) -> tuple[int, int]:
+    a, b = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(load(False).qgemv_expert_stride(_fmt(fmt), M, K, ctypes.byref(a), ctypes.byref(b)), "qgemv_expert_stride")
+    return a.value, b.value
+
+
+def pack(fmt, W: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Quantise and pack a host fp32 [M][K] matrix -> (wq, ws) uint8 arrays."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    M, K = W.shape
+    nq, ns = packed_bytes(fmt, M, K)
+    wq = np.empty(nq, np.uint8)
+    ws = np.empty(ns, np.uint8)
+    _check(load(False).qgemv_pack(_fmt(fmt), _ptr(W), M, K, _ptr(wq), _ptr(ws)), "qgemv_pack")
+    return wq, ws
+
+
+def pack_codes(fmt, codes: np.ndarray, scales: np.ndarray, mins: np.ndarray | None = None,
+               tensor_scale: float = 1.0) -> tuple[np.ndarray, np.ndarray]:
+    f = _fmt(fmt)
+    codes = np.ascontiguousarray(codes, dtype=np.int8 if f == 3 else np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8 if f == 4 else np.uint16)
+    mins = None if mins is None else np.ascontiguousarray(mins, dtype=np.uint16)
+    M, K = codes.shape
+    nq, ns = packed_bytes(f, M, K)
+    wq = np.empty(nq, np.uint8)
+    ws = np.empty(ns, np.uint8)
+    _check(load(False).qgemv_pack_codes(f, _ptr(codes), _ptr(scales), _ptr(mins), float(tensor_scale), M, K,
+                                        _ptr(wq), _ptr(ws)), "qgemv_pack_codes")
+    return wq, ws
+
+
+# ---------------------------------------------------------------- device ---
+
+def qgemv(fmt, wq, ws, x, y, M: int, K: int, N: int, residual=None, stream=None) -> None:
+    _check(load().qgemv(_fmt(fmt), _ptr(wq), _ptr(ws), _ptr(x), _ptr(residual), _ptr(y), M, K, N,
+                        _stream(stream)), "qgemv")
+
+
+def qgemv_swiglu(fmt, wq, ws, x, h, I: int, K: int, N: int, stream=None) -> None:
+    _check(load().qgemv_swiglu(_fmt(fmt), _ptr(wq), _ptr(ws), _ptr(x), _ptr(h), I, K, N, _stream(stream)),
+           "qgemv_swiglu")
+
+
+def moe_workspace_bytes(E: int, H: int, I: int, N: int, top_k: int) -> int:
+    b = ctypes.c_size_t()
+    _check(load(False).qgemv_moe_workspace_bytes(E, H, I, N, top_k, ctypes.byref(b)), "qgemv_moe_workspace_bytes")
+    return b.value
+
+
+def qgemv_moe(fmt, wq_gu, ws_gu, wq_dn, ws_dn, E: int, H: int, I: int, x, ids, gates, top_k: int, y, N: int,
+              workspace, workspace_bytes: int, residual=None, stream=None) -> None:
+    _check(load().qgemv_moe(_fmt(fmt), _ptr(wq_gu), _ptr(ws_gu), _ptr(wq_dn), _ptr(ws_dn), E, H, I, _ptr(x),
+                            _ptr(ids), _ptr(gates), top_k, _ptr(residual), _ptr(y), N, _ptr(workspace),
+                            workspace_bytes, _stream(stream)), "qgemv_moe")
+
+
+def qgemv_moe_index(ids, N: int, top_k: int, E: int, counts, offsets, pairs, active, meta, stream=None) -> None:
+    _check(load().qgemv_moe_index(_ptr(ids), N, top_k, E, _ptr(counts), _ptr(offsets), _ptr(pairs), _ptr(active),
+                                  _ptr(meta), _stream(stream)), "qgemv_moe_index")
+
+
+def qgemv_dequant(fmt, wq, ws, M: int, K: int, out, stream=None) -> None:
+    _check(load().qgemv_dequant(_fmt(fmt), _ptr(wq), _ptr(ws), M, K, _ptr(out), _stream(stream)), "qgemv_dequant")
+
+
+def qgemv_probe_read(buf, nbytes: int, sink, stream=None) -> None:
+    _check(load().qgemv_probe_read(_ptr(buf), nbytes, _ptr(sink), _stream(stream)), "qgemv_probe_read")

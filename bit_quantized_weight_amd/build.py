@@ -1,0 +1,77 @@
+"""Build libqgemv.so in-tree for gfx950 with hipcc.
+
+    python -m bit_quantized_weight_amd.build
+
+Compiles the HIP kernels (csrc/*.hip) for gfx950 and the host packer
+(csrc/pack.cpp, no FMA contraction so packed bytes are reproducible), then
+links them into bit_quantized_weight_amd/libqgemv.so. The library links the
+HIP runtime by soname (libamdhip64.so.7); the Python binding imports torch
+first so that torch's copy of the runtime is the one the library uses.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(HERE, "libqgemv.so")
+
+ARCH = "gfx950"
+HIP_SOURCES = ["gemv.hip", "moe.hip"]
+HOST_SOURCES = ["pack.cpp"]
+
+
+def _hipcc() -> str:
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found: the HIP toolchain is required to build libqgemv")
+
+
+def _rocm_include() -> str:
+    return os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "include")
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("build step failed: " + " ".join(cmd))
+
+
+def build(verbose: bool = False) -> str:
+    hipcc = _hipcc()
+    os.makedirs(BUILD, exist_ok=True)
+    objs = []
+    common = ["-O3", "-std=c++17", "-fPIC", "-I" + INCLUDE, "-I" + CSRC]
+    for src in HIP_SOURCES:
+        path = os.path.join(CSRC, src)
+        if not os.path.exists(path):
+            continue
+        obj = os.path.join(BUILD, src + ".o")
+        _run([hipcc, "--offload-arch=" + ARCH, *common,
+              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+              "-c", path, "-o", obj])
+        objs.append(obj)
+    for src in HOST_SOURCES:
+        obj = os.path.join(BUILD, src + ".o")
+        _run([hipcc, "-x", "c++", *common, "-I" + _rocm_include(), "-D__HIP_PLATFORM_AMD__=1",
+              "-ffp-contract=off", "-fno-fast-math",
+              "-c", os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+    tmp = LIB + ".tmp"
+    _run([hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs, "-lpthread"])
+    os.replace(tmp, LIB)
+    if verbose:
+        print("built", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)

@@ -1,0 +1,135 @@
+// Device building blocks for gfx950: buffer loads, the per-format decoders and
+// the MFMA step shared by the GEMV, SwiGLU, MoE and dequant kernels.
+//
+// Decoding follows the formats of the NInfer article (section 2: groupwise
+// 4/5-bit integers, NVFP4), the RustingStrata page (Q8_0-style int8) and the
+// Decapybara page (NVFP4 GEMV). Each decoder turns one lane's 8 codes of one
+// 32-column group into the bf16x8 B operand of v_mfma_f32_16x16x32_bf16:
+//   int4 / int5  bf16(128 + q): the code sits in the low mantissa bits under
+//                the exponent of 128 (bf16 0x4300), exact for q < 128; the
+//                128 * sum(x) bias is removed in the group epilogue
+//   int8         bf16(q), exact (|q| <= 128)
+//   nvfp4        bf16(e2m1), exact, via v_cvt_scalef32_pk_bf16_fp4 with scale 1
+//                (that instruction only applies the exponent of its scale, so
+//                the E4M3 block scale is applied in fp32 afterwards)
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qg {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+// Raw buffer descriptor (gfx9 word 3: 32-bit data format, no swizzle). A load
+// whose offset lies past num_records returns zeros and touches no memory,
+// which is how masked-off lanes get zero operands without branches.
+constexpr int kBufWord3 = 0x00020000;
+constexpr uint32_t kOOB = 0x80000000u;
+constexpr int kNonTemporal = 2;   // cache-policy bit "nt" on gfx94x/gfx950
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kBufWord3);
+}
+
+__device__ __forceinline__ u32x4 ld128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ u32x4 ld128_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNonTemporal);
+}
+__device__ __forceinline__ u32x2 ld64(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t ld32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
+__device__ __forceinline__ float f16_lo(uint32_t v) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xFFFFu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t v) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
+}
+
+// ---- decoders: 8 codes of one lane and group -> bf16x8 (slot e = element e)
+
+// int4 dword: slot e in nibble (e even ? e/2 : 4 + e/2), so the nibble pairs
+// (0,4), (1,5), (2,6), (3,7) are the slot pairs (0,1), (2,3), (4,5), (6,7).
+__device__ __forceinline__ bf16x8 dec_int4(uint32_t v) {
+  u32x4 r;
+  r.x = (v & 0x000F000Fu) | 0x43004300u;
+  r.y = ((v >> 4) & 0x000F000Fu) | 0x43004300u;
+  r.z = ((v >> 8) & 0x000F000Fu) | 0x43004300u;
+  r.w = ((v >> 12) & 0x000F000Fu) | 0x43004300u;
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// hi-bit word of a lane: bit 16*(e&1) + 4*j + (e>>1) is bit 4 of the code of
+// group j, slot e. For slot pair p of group j this moves bits b and 16 + b,
+// b = 4j + p, to bits 4 and 20 and adds the bf16 exponent of 128.
+template <int B>
+__device__ __forceinline__ uint32_t hi_pair(uint32_t H) {
+  const uint32_t t = B >= 4 ? (H >> (B >= 4 ? B - 4 : 0)) : (H << (B < 4 ? 4 - B : 0));
+  return (t & 0x00100010u) | 0x43004300u;
+}
+
+template <int J>
+__device__ __forceinline__ bf16x8 dec_int5(uint32_t v, uint32_t H) {
+  u32x4 r;
+  r.x = (v & 0x000F000Fu) | hi_pair<4 * J + 0>(H);
+  r.y = ((v >> 4) & 0x000F000Fu) | hi_pair<4 * J + 1>(H);
+  r.z = ((v >> 8) & 0x000F000Fu) | hi_pair<4 * J + 2>(H);
+  r.w = ((v >> 12) & 0x000F000Fu) | hi_pair<4 * J + 3>(H);
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+__device__ __forceinline__ uint32_t i8pair_to_bf16x2(uint32_t v, int sh) {
+  f32x2 f;
+  f.x = (float)(int8_t)(v >> sh);
+  f.y = (float)(int8_t)(v >> (sh + 8));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+}
+
+// int8: two dwords, slots 0..3 then 4..7, one byte each (two's complement)
+__device__ __forceinline__ bf16x8 dec_int8(uint32_t a, uint32_t b) {
+  u32x4 r;
+  r.x = i8pair_to_bf16x2(a, 0);
+  r.y = i8pair_to_bf16x2(a, 16);
+  r.z = i8pair_to_bf16x2(b, 0);
+  r.w = i8pair_to_bf16x2(b, 16);
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// nvfp4: byte i holds slots 2i (low nibble) and 2i+1 (high nibble)
+__device__ __forceinline__ bf16x8 dec_nvfp4(uint32_t v) {
+  u32x4 r;
+  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 0));
+  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 1));
+  r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 2));
+  r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 3));
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// OCP E4M3 byte J of v -> fp32 (gfx950 converts OCP FP8)
+template <int J>
+__device__ __forceinline__ float e4m3_byte(uint32_t v) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)v, J);
+}
+
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 bf16x8_splat_128() {
+  const u32x4 r = {0x43004300u, 0x43004300u, 0x43004300u, 0x43004300u};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+__device__ __forceinline__ float bf16_to_f32(__bf16 b) { return (float)b; }
+
+}  // namespace qg

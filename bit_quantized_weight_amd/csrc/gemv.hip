@@ -1,0 +1,382 @@
+// Dequantise-fused skinny GEMV for gfx950 (qgemv, qgemv_swiglu, qgemv_dequant,
+// qgemv_probe_read).
+//
+// What it computes (NInfer article, section 2: the decode matmul over packed
+// low-bit weights with residual add and SwiGLU fused in; "what NInfer is":
+// 1 to 8 decode lanes):  y[n][m] = r[n][m] + sum_k x[n][k] * W[m][k].
+//
+// How it maps to the CDNA4 execution model
+//   * Decode is bound by weight bytes (same section). Each wave streams 16-row
+//     x 128-column tiles of packed codes with one 16-byte non-temporal buffer
+//     load per lane (a contiguous 1 KiB per wave) and feeds them to
+//     v_mfma_f32_16x16x32_bf16 as the B operand: n = weight row, k = 32
+//     columns = one scale group. The A operand holds the activations.
+//   * A rows are (slot, token) = 8*slot + token, 8 tokens max. Int formats
+//     put even groups in slot 0 and odd groups in slot 1, so one accumulator
+//     carries two groups' partial sums apart and the per-group scale step
+//     runs once per two groups. NVFP4 puts its two 16-column blocks of a
+//     group in the two slots. Lanes that must hold zeros load from an
+//     out-of-range buffer offset, which returns zeros.
+//   * Int group epilogue: the B operand is bf16(128 + q); with D = sum x(128+q)
+//     and Db = 128 * sum x (one MFMA against a constant 128 operand, shared by
+//     all tiles of the wave): d*S + m*sum x = d*D + (m/128 - d)*Db.
+//   * Waves of a workgroup split K; their partial sums meet in LDS and are
+//     added in wave order, so results are bitwise reproducible. The sum over
+//     the two slots uses a fixed lane exchange.
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "device.hpp"
+#include "kloop.hpp"
+#include "layout.hpp"
+#include "qgemv.h"
+
+namespace qg {
+
+struct GemvArgs {
+  const uint8_t* wq;
+  const uint8_t* ws;
+  const uint16_t* x;      // bf16 [N][K]
+  const float* res;       // [N][M] or null
+  float* y;               // [N][M]  (swiglu: [N][I])
+  uint32_t wq_bytes, ws_bytes, x_bytes;
+  uint32_t hi_offset, st_offset;
+  int M;                  // output columns (I for swiglu)
+  int K, KS, G;           // G = K / 32 groups that hold data
+  int N;
+  int out_tiles;          // 16-row output tiles (M/16 rounded up)
+  int up_tile0;           // swiglu: tile index of the first "up" row tile
+  int ks_per_wave;
+};
+
+// NT tiles per wave: plain GEMV uses NT output tiles, SwiGLU NT/2 gate tiles
+// followed by NT/2 up tiles.
+template <int FMT, int NT, bool SWIGLU>
+__global__ __launch_bounds__(1024) void k_gemv(GemvArgs a) {
+  extern __shared__ float red[];  // [W][NT][32][4]
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int W = blockDim.x >> 6;
+  const int r = lane & 15, s = lane >> 4;
+  constexpr int TO = SWIGLU ? NT / 2 : NT;
+
+  const __amdgpu_buffer_rsrc_t wq = make_rsrc(a.wq, a.wq_bytes);
+  const __amdgpu_buffer_rsrc_t ws = make_rsrc(a.ws, a.ws_bytes);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, a.x_bytes);
+
+  // row tiles of this wave (clamped: out-of-range tiles compute a copy of the
+  // last tile and are never stored)
+  int tile[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    int ot = blockIdx.x * TO + (SWIGLU ? (t % TO) : t);
+    ot = ot < a.out_tiles ? ot : a.out_tiles - 1;
+    tile[t] = (SWIGLU && t >= TO) ? a.up_tile0 + ot : ot;
+  }
+
+  // activation lane role: A row = 8 * slot + token
+  const int a_tok = r & 7;
+  const bool tok_ok = a_tok < a.N;
+  const uint32_t x_lane = (uint32_t)(a_tok * a.K + 8 * s) * 2u;
+  const int G = a.G;
+  auto aload = [&](int ks, int j, bool use) -> bf16x8 {
+    const int g = ks * 4 + j;
+    const uint32_t off = (use && tok_ok && g < G) ? x_lane + (uint32_t)g * 64u : kOOB;
+    return __builtin_bit_cast(bf16x8, ld128(xr, off));
+  };
+
+  f32x4 acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int ks0 = wave * a.ks_per_wave;
+  const int ks1 = min(a.KS, ks0 + a.ks_per_wave);
+  kloop<FMT, NT>(wq, ws, tile, a.KS, ks0, ks1, a.hi_offset, aload, acc);
+
+  // ---- reduction: the two slots (lanes l and l^32), then the waves via LDS
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float o = __shfl_xor(acc[t][i], 32);
+      acc[t][i] += o;
+    }
+  }
+  if (lane < 32) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      float* p = red + (((size_t)wave * NT + t) * 32 + lane) * 4;
+      p[0] = acc[t][0];
+      p[1] = acc[t][1];
+      p[2] = acc[t][2];
+      p[3] = acc[t][3];
+    }
+  }
+  __syncthreads();
+
+  float st = 1.0f;
+  if constexpr (FMT == NVFP4) st = *(const float*)(a.ws + a.st_offset);
+  const int n_out = TO * 128;
+  for (int o = threadIdx.x; o < n_out; o += blockDim.x) {
+    const int to = o >> 7, rem = o & 127;
+    const int tok = rem >> 4, row = rem & 15;
+    const int ot = blockIdx.x * TO + to;
+    const int col = ot * 16 + row;
+    if (tok >= a.N || ot >= a.out_tiles || col >= a.M) continue;
+    const int l = row + 16 * (tok >> 2), i = tok & 3;
+    float v = 0.f;
+    for (int w = 0; w < W; ++w) v += red[(((size_t)w * NT + to) * 32 + l) * 4 + i];
+    v *= st;
+    if constexpr (SWIGLU) {
+      float u = 0.f;
+      for (int w = 0; w < W; ++w) u += red[(((size_t)w * NT + TO + to) * 32 + l) * 4 + i];
+      u *= st;
+      const float sg = v / (1.0f + expf(-v));
+      a.y[(size_t)tok * a.M + col] = sg * u;
+    } else {
+      if (a.res) v += a.res[(size_t)tok * a.M + col];
+      a.y[(size_t)tok * a.M + col] = v;
+    }
+  }
+}
+
+// ---- debug dump: packed -> fp32 weights, bit-exact definition ---------------
+// One thread per (tile, lane): 4 groups x 8 slots.
+template <int FMT>
+__global__ __launch_bounds__(256) void k_dequant(const uint8_t* wqp, const uint8_t* wsp, uint32_t wq_bytes,
+                                                 uint32_t ws_bytes, uint32_t hi_offset, uint32_t st_offset,
+                                                 int M, int K, int KS, int RT, float* out) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (int64_t)RT * KS * 64) return;
+  const int lane = (int)(gid & 63);
+  const int64_t tau = gid >> 6;
+  const int rt = (int)(tau / KS), ks = (int)(tau % KS);
+  const int r = lane & 15, s = lane >> 4;
+  const int row = rt * 16 + r;
+  if (row >= M) return;
+  const __amdgpu_buffer_rsrc_t wq = make_rsrc(wqp, wq_bytes);
+  const __amdgpu_buffer_rsrc_t ws = make_rsrc(wsp, ws_bytes);
+  const u32x4 cw = ld128(wq, (uint32_t)tau * (FMT == INT8 ? 2048u : 1024u) + (uint32_t)lane * 16u);
+  u32x4 cw2 = {0u, 0u, 0u, 0u};
+  if (FMT == INT8) cw2 = ld128(wq, (uint32_t)tau * 2048u + 1024u + (uint32_t)lane * 16u);
+  uint32_t H = 0;
+  if (FMT == INT5) H = ld32(wq, hi_offset + (uint32_t)tau * 256u + (uint32_t)lane * 4u);
+  float st = 1.0f;
+  if (FMT == NVFP4) st = __builtin_bit_cast(float, ld32(ws, st_offset));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t v = j == 0 ? cw.x : j == 1 ? cw.y : j == 2 ? cw.z : cw.w;
+    bf16x8 B;
+    if (FMT == INT4) B = dec_int4(v);
+    else if (FMT == INT5) B = j == 0 ? dec_int5<0>(v, H) : j == 1 ? dec_int5<1>(v, H) : j == 2 ? dec_int5<2>(v, H) : dec_int5<3>(v, H);
+    else if (FMT == INT8) {
+      const u32x4 q = j < 2 ? cw : cw2;
+      B = (j & 1) ? dec_int8(q.z, q.w) : dec_int8(q.x, q.y);
+    } else B = dec_nvfp4(v);
+    const int pos = 2 * (j & 1) + (j >> 1);
+    float d = 0.f, mn = 0.f, sb = 0.f;
+    if (FMT == INT4 || FMT == INT5) {
+      const uint32_t dm = ld32(ws, (uint32_t)tau * 256u + (uint32_t)r * 16u + 4u * pos);
+      d = f16_lo(dm);
+      mn = f16_hi(dm);
+    } else if (FMT == INT8) {
+      const uint32_t dw = ld32(ws, (uint32_t)tau * 128u + (uint32_t)r * 8u + 4u * (pos >> 1));
+      d = (pos & 1) ? f16_hi(dw) : f16_lo(dw);
+    } else {
+      const uint32_t sw = ld32(ws, (uint32_t)tau * 128u + (uint32_t)r * 8u + 4u * (uint32_t)(s >> 1));
+      sb = j == 0 ? e4m3_byte<0>(sw) : j == 1 ? e4m3_byte<1>(sw) : j == 2 ? e4m3_byte<2>(sw) : e4m3_byte<3>(sw);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int k = ks * 128 + 32 * j + 8 * s + e;
+      if (k >= K) continue;
+      const float b = (float)B[e];
+      float w;
+      if (FMT == INT4 || FMT == INT5) w = fmaf(d, b - 128.0f, mn);  // d*q exact: one rounding
+      else if (FMT == INT8) w = d * b;
+      else w = st * (b * sb);                                        // b*sb exact
+      out[(int64_t)row * K + k] = w;
+    }
+  }
+}
+
+// ---- bandwidth probe -------------------------------------------------------
+__global__ __launch_bounds__(256) void k_probe(const uint8_t* p, uint32_t bytes, uint32_t* sink) {
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(p, bytes);
+  const uint32_t n16 = bytes / 16u;
+  const uint32_t stride = gridDim.x * blockDim.x;
+  uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (; i + 3u * stride < n16; i += 4u * stride) {
+    const u32x4 v0 = ld128_nt(r, i * 16u);
+    const u32x4 v1 = ld128_nt(r, (i + stride) * 16u);
+    const u32x4 v2 = ld128_nt(r, (i + 2u * stride) * 16u);
+    const u32x4 v3 = ld128_nt(r, (i + 3u * stride) * 16u);
+    acc ^= v0 ^ v1 ^ v2 ^ v3;
+  }
+  for (; i < n16; i += stride) acc ^= ld128_nt(r, i * 16u);
+  if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == 0x9E3779B9u) sink[0] = acc.x;
+}
+
+}  // namespace qg
+
+// ============================================================================
+// Host side: validation and dispatch
+// ============================================================================
+using namespace qg;
+
+namespace {
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+int map_hip(hipError_t e) { return e == hipSuccess ? QGEMV_OK : QGEMV_EHIP; }
+
+struct LaunchShape {
+  int nt;       // tiles per wave (including up tiles for SwiGLU)
+  int waves;    // waves per workgroup
+};
+
+// Launch shape: enough waves to cover K in a few k-steps each, two output
+// tiles per wave (x reuse across tiles), workgroups = output tiles / 2.
+LaunchShape pick_shape(int64_t KS, bool swiglu) {
+  LaunchShape ls;
+  ls.nt = swiglu ? 4 : 2;
+  int w = (int)((KS + 4) / 5);  // about five k-steps per wave
+  if (w < 1) w = 1;
+  if (w > 16) w = 16;
+  ls.waves = w;
+  return ls;
+}
+
+template <int FMT>
+hipError_t launch_gemv(const GemvArgs& a, const LaunchShape& ls, bool swiglu, hipStream_t stream) {
+  const int TO = swiglu ? ls.nt / 2 : ls.nt;
+  const dim3 grid((unsigned)((a.out_tiles + TO - 1) / TO));
+  const dim3 block((unsigned)(64 * ls.waves));
+  const size_t lds = (size_t)ls.waves * ls.nt * 32 * 4 * sizeof(float);
+  if (swiglu) {
+    if (ls.nt == 4) hipLaunchKernelGGL((k_gemv<FMT, 4, true>), grid, block, lds, stream, a);
+    else if (ls.nt == 2) hipLaunchKernelGGL((k_gemv<FMT, 2, true>), grid, block, lds, stream, a);
+    else return hipErrorInvalidValue;
+  } else {
+    if (ls.nt == 2) hipLaunchKernelGGL((k_gemv<FMT, 2, false>), grid, block, lds, stream, a);
+    else if (ls.nt == 1) hipLaunchKernelGGL((k_gemv<FMT, 1, false>), grid, block, lds, stream, a);
+    else if (ls.nt == 4) hipLaunchKernelGGL((k_gemv<FMT, 4, false>), grid, block, lds, stream, a);
+    else return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+int validate_common(int fmt, const void* wq, const void* ws, const void* x, const void* y, int64_t M, int64_t K,
+                    int N, Geom* g) {
+  if (fmt < INT4 || fmt > NVFP4) return QGEMV_EFORMAT;
+  if (!wq || !ws || !x || !y) return QGEMV_EINVAL;
+  if (M < 1 || K < 32 || M > (1 << 24)) return QGEMV_EINVAL;
+  if (K % 32) return QGEMV_EALIGN;
+  if (N < 1 || N > 8) return QGEMV_EUNSUPPORTED;
+  if (!aligned16(wq) || !aligned16(ws) || !aligned16(x) || !aligned4(y)) return QGEMV_EALIGN;
+  if (!geom(fmt, M, K, g)) return QGEMV_EINVAL;
+  if (g->wq_bytes >= (1ull << 32) || g->ws_bytes >= (1ull << 32)) return QGEMV_EUNSUPPORTED;
+  if ((uint64_t)N * (uint64_t)K * 2ull >= (1ull << 31)) return QGEMV_EUNSUPPORTED;
+  return QGEMV_OK;
+}
+
+int run_gemv(int fmt, const void* wq, const void* ws, const void* x, const float* res, float* y, int64_t Mout,
+             int64_t Mpacked, int64_t K, int N, bool swiglu, hipStream_t stream) {
+  Geom g;
+  int rc = validate_common(fmt, wq, ws, x, y, Mpacked, K, N, &g);
+  if (rc) return rc;
+  if (res && !aligned4(res)) return QGEMV_EALIGN;
+  GemvArgs a;
+  a.wq = (const uint8_t*)wq;
+  a.ws = (const uint8_t*)ws;
+  a.x = (const uint16_t*)x;
+  a.res = res;
+  a.y = y;
+  a.wq_bytes = (uint32_t)g.wq_bytes;
+  a.ws_bytes = (uint32_t)g.ws_bytes;
+  a.x_bytes = (uint32_t)((int64_t)N * K * 2);
+  a.hi_offset = (uint32_t)g.hi_offset;
+  a.st_offset = (uint32_t)g.st_offset;
+  a.M = (int)Mout;
+  a.K = (int)K;
+  a.KS = (int)g.KS;
+  a.G = (int)(K / 32);
+  a.N = N;
+  a.out_tiles = (int)((Mout + 15) / 16);
+  a.up_tile0 = swiglu ? (int)(Mout / 16) : 0;
+  const LaunchShape ls = pick_shape(g.KS, swiglu);
+  a.ks_per_wave = (int)((g.KS + ls.waves - 1) / ls.waves);
+  hipError_t e;
+  switch (fmt) {
+    case INT4: e = launch_gemv<INT4>(a, ls, swiglu, stream); break;
+    case INT5: e = launch_gemv<INT5>(a, ls, swiglu, stream); break;
+    case INT8: e = launch_gemv<INT8>(a, ls, swiglu, stream); break;
+    default: e = launch_gemv<NVFP4>(a, ls, swiglu, stream); break;
+  }
+  return map_hip(e);
+}
+
+}  // namespace
+
+extern "C" const char* qgemv_strerror(int status) {
+  switch (status) {
+    case QGEMV_OK: return "success";
+    case QGEMV_EINVAL: return "invalid argument (null pointer, bad size or non-finite weights)";
+    case QGEMV_EFORMAT: return "unknown weight format";
+    case QGEMV_EALIGN: return "pointer or shape alignment violated";
+    case QGEMV_ERANGE: return "a scale field overflows its encoding";
+    case QGEMV_EWORKSPACE: return "workspace missing or too small";
+    case QGEMV_EHIP: return "HIP runtime error at launch";
+    case QGEMV_EUNSUPPORTED: return "size outside the supported range";
+    default: return "unknown status";
+  }
+}
+
+extern "C" int qgemv_version(void) { return 100; }
+
+extern "C" int qgemv(int fmt, const void* wq, const void* ws, const void* x, const float* residual, float* y,
+                     int64_t M, int64_t K, int N, hipStream_t stream) {
+  return run_gemv(fmt, wq, ws, x, residual, y, M, M, K, N, false, stream);
+}
+
+extern "C" int qgemv_swiglu(int fmt, const void* wq, const void* ws, const void* x, float* h, int64_t I, int64_t K,
+                            int N, hipStream_t stream) {
+  if (I < 1) return QGEMV_EINVAL;
+  if (I % 16) return QGEMV_EALIGN;
+  return run_gemv(fmt, wq, ws, x, nullptr, h, I, 2 * I, K, N, true, stream);
+}
+
+extern "C" int qgemv_dequant(int fmt, const void* wq, const void* ws, int64_t M, int64_t K, float* w_out,
+                             hipStream_t stream) {
+  if (fmt < INT4 || fmt > NVFP4) return QGEMV_EFORMAT;
+  if (!wq || !ws || !w_out) return QGEMV_EINVAL;
+  if (M < 1 || K < 32) return QGEMV_EINVAL;
+  if (K % 32) return QGEMV_EALIGN;
+  if (!aligned16(wq) || !aligned16(ws) || !aligned4(w_out)) return QGEMV_EALIGN;
+  Geom g;
+  if (!geom(fmt, M, K, &g)) return QGEMV_EINVAL;
+  if (g.wq_bytes >= (1ull << 32) || g.ws_bytes >= (1ull << 32)) return QGEMV_EUNSUPPORTED;
+  const int64_t threads = g.RT * g.KS * 64;
+  const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+  const uint8_t* q = (const uint8_t*)wq;
+  const uint8_t* s = (const uint8_t*)ws;
+  const uint32_t a = (uint32_t)g.wq_bytes, b = (uint32_t)g.ws_bytes;
+  const uint32_t ho = (uint32_t)g.hi_offset, so = (uint32_t)g.st_offset;
+  const int Mi = (int)M, Ki = (int)K, KSi = (int)g.KS, RTi = (int)g.RT;
+  switch (fmt) {
+    case INT4: hipLaunchKernelGGL(k_dequant<INT4>, grid, block, 0, stream, q, s, a, b, ho, so, Mi, Ki, KSi, RTi, w_out); break;
+    case INT5: hipLaunchKernelGGL(k_dequant<INT5>, grid, block, 0, stream, q, s, a, b, ho, so, Mi, Ki, KSi, RTi, w_out); break;
+    case INT8: hipLaunchKernelGGL(k_dequant<INT8>, grid, block, 0, stream, q, s, a, b, ho, so, Mi, Ki, KSi, RTi, w_out); break;
+    default: hipLaunchKernelGGL(k_dequant<NVFP4>, grid, block, 0, stream, q, s, a, b, ho, so, Mi, Ki, KSi, RTi, w_out); break;
+  }
+  return map_hip(hipGetLastError());
+}
+
+extern "C" int qgemv_probe_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream) {
+  if (!buf || !sink || bytes == 0) return QGEMV_EINVAL;
+  if (bytes % 16 || !aligned16(buf) || !aligned4(sink)) return QGEMV_EALIGN;
+  if (bytes >= (1ull << 32)) return QGEMV_EUNSUPPORTED;
+  hipLaunchKernelGGL(k_probe, dim3(8192), dim3(256), 0, stream, (const uint8_t*)buf, (uint32_t)bytes, sink);
+  return map_hip(hipGetLastError());
+}

@@ -1,0 +1,64 @@
+// Packed-weight geometry shared by the host packer and the device kernels.
+//
+// The subject pages only say that engines repack checkpoints into their own
+// layout (memra page, model notes) and pack 4-bit codes as nibbles along K.
+// This layout is built for a 64-lane CDNA wave: one 16-byte load per lane
+// fetches one contiguous 1 KiB tile of 16 rows x 128 columns of 4-bit codes,
+// and the lane's bytes are exactly the B operand of a 16x16x32 bf16 MFMA.
+//
+//   Mp = M rounded up to 16, Kp = K rounded up to 128; padding is weight 0.
+//   RT = Mp/16 row tiles, KS = Kp/128 k-steps, tile index tau = rt*KS + ks.
+//   Lane lam: r = lam % 16 (row 16*rt + r), s = lam / 16; group j in [0,4),
+//   slot e in [0,8): column k = 128*ks + 32*j + 8*s + e.
+//
+//   int4  wq tile 1024 B: lane's 16 B at lam*16, dword j = group j, slot e in
+//         nibble (e even ? e/2 : 4 + e/2).  ws tile 256 B: row r's 16 B at
+//         r*16, group j's dword (d | m<<16, fp16 bits) at position
+//         2*(j&1) + (j>>1).
+//   int5  wq = int4 nibble plane (low code bits) then a hi-bit plane of
+//         256 B tiles: lane's dword at lam*4, bit 16*(e&1) + 4*j + (e>>1).
+//         ws as int4.
+//   int8  wq tile 2048 B: byte (j>>1)*1024 + lam*16 + (j&1)*8 + e.
+//         ws tile 128 B: fp16 d at r*8 + 2*(2*(j&1) + (j>>1)).
+//   nvfp4 wq tile 1024 B: byte lam*16 + 4*j + e/2, low nibble even e.
+//         ws tile 128 B: E4M3 of 16-block 8*ks + 2*j + h at r*8 + 4*h + j;
+//         then the fp32 tensor scale at RT*KS*128, padded to 16 B.
+#pragma once
+#include <stdint.h>
+#include <stddef.h>
+
+namespace qg {
+
+enum Fmt : int { INT4 = 1, INT5 = 2, INT8 = 3, NVFP4 = 4 };
+
+struct Geom {
+  int64_t M, K, Mp, Kp, RT, KS;
+  size_t wq_bytes, ws_bytes;
+  size_t hi_offset;      // int5: byte offset of the hi-bit plane in wq
+  size_t st_offset;      // nvfp4: byte offset of the tensor scale in ws
+};
+
+inline bool geom(int fmt, int64_t M, int64_t K, Geom* g) {
+  if (M < 1 || K < 32 || (K % 32) != 0) return false;
+  g->M = M;
+  g->K = K;
+  g->Mp = (M + 15) / 16 * 16;
+  g->Kp = (K + 127) / 128 * 128;
+  g->RT = g->Mp / 16;
+  g->KS = g->Kp / 128;
+  const size_t tiles = (size_t)g->RT * (size_t)g->KS;
+  g->hi_offset = 0;
+  g->st_offset = 0;
+  switch (fmt) {
+    case INT4: g->wq_bytes = tiles * 1024; g->ws_bytes = tiles * 256; break;
+    case INT5: g->wq_bytes = tiles * 1280; g->ws_bytes = tiles * 256; g->hi_offset = tiles * 1024; break;
+    case INT8: g->wq_bytes = tiles * 2048; g->ws_bytes = tiles * 128; break;
+    case NVFP4: g->wq_bytes = tiles * 1024; g->ws_bytes = tiles * 128 + 16; g->st_offset = tiles * 128; break;
+    default: return false;
+  }
+  return true;
+}
+
+inline int scale_pos(int j) { return 2 * (j & 1) + (j >> 1); }
+
+}  // namespace qg

@@ -1,0 +1,428 @@
+// Mixture-of-experts path (qgemv_moe, qgemv_moe_index, qgemv_moe_workspace_bytes).
+//
+// What it computes (Decapybara page, CUDA kernel list: a top-8 softmax MoE
+// router; memra page: a 35B-A3B MoE served from one card; NInfer article,
+// section 2: SwiGLU fused into the matmul): every token t runs only the
+// experts it selected, y[t] = r[t] + sum_j p[t][j] * down_e(SwiGLU(gate_up_e(x[t]))).
+//
+// Four launches on one stream, no host synchronisation:
+//   1. index: one workgroup turns ids [N][k] into counts, offsets, the
+//      (token, slot) pairs in (expert, token, slot) order and the ascending
+//      list of active experts; exact integer work.
+//   2. gate/up + SwiGLU: grid (row tiles, active-expert slot); a slot past the
+//      number of active experts exits at once. Each workgroup gathers the
+//      rows of x routed to its expert (8 per MFMA pass) and writes h [pair][I]
+//      in fp32.
+//   3. down: same grid shape over H; the fp32 h rows enter the bf16 MFMA as a
+//      hi + lo pair (h = hi + lo + O(2^-16 |h|)), so the A operand holds
+//      4 pairs x {hi, lo} x 2 slots; writes o [pair][H] in fp32.
+//   4. combine: y[t] = r[t] + sum_j p[t][j] o[t*k + j] in increasing j order;
+//      no atomics, so results are bitwise reproducible (RustingStrata page,
+//      known issues: run-to-run reordering changes results).
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include <algorithm>
+
+#include "device.hpp"
+#include "kloop.hpp"
+#include "layout.hpp"
+#include "qgemv.h"
+
+namespace qg {
+
+// int32 index region of the workspace
+struct MoeIndex {
+  int E, NK;
+  __host__ __device__ int counts() const { return 0; }
+  __host__ __device__ int offsets() const { return E; }
+  __host__ __device__ int pairs() const { return 2 * E + 1; }
+  __host__ __device__ int active() const { return 2 * E + 1 + NK; }
+  __host__ __device__ int meta() const { return 3 * E + 1 + NK; }
+  __host__ __device__ int total() const { return 3 * E + 3 + NK; }
+};
+
+__global__ __launch_bounds__(256) void k_moe_index(const int32_t* ids, int NK, int E, int32_t* counts,
+                                                   int32_t* offsets, int32_t* pairs, int32_t* active,
+                                                   int32_t* meta) {
+  __shared__ int sid[64];
+  __shared__ int spos[64];
+  const int tid = threadIdx.x;
+  if (tid < NK) {
+    const int v = ids[tid];
+    sid[tid] = (v >= 0 && v < E) ? v : -1;
+  }
+  __syncthreads();
+  // rank of each valid entry in (expert, flat index) order
+  if (tid < NK) {
+    const int v = sid[tid];
+    int pos = -1;
+    if (v >= 0) {
+      pos = 0;
+      for (int i = 0; i < NK; ++i) {
+        const int u = sid[i];
+        if (u >= 0 && (u < v || (u == v && i < tid))) ++pos;
+      }
+    }
+    spos[tid] = pos;
+  }
+  __syncthreads();
+  int nvalid = 0, bad = 0;
+  for (int i = 0; i < NK; ++i) {
+    nvalid += sid[i] >= 0;
+    bad |= sid[i] < 0;
+  }
+  // pairs
+  for (int p = tid; p < NK; p += blockDim.x) pairs[p] = -1;
+  __syncthreads();
+  if (tid < NK && spos[tid] >= 0) pairs[spos[tid]] = tid;
+  // offsets and counts
+  for (int e = tid; e <= E; e += blockDim.x) {
+    int below = 0;
+    for (int i = 0; i < NK; ++i) below += (sid[i] >= 0 && sid[i] < e);
+    offsets[e] = below;
+  }
+  for (int e = tid; e < E; e += blockDim.x) {
+    int c = 0;
+    for (int i = 0; i < NK; ++i) c += sid[i] == e;
+    counts[e] = c;
+    active[e] = -1;
+  }
+  __syncthreads();
+  // active experts: an entry that is first of its expert in sorted order
+  // (pos == offsets[e]) gets index = number of such firsts with smaller ids
+  int nact = 0;
+  for (int i = 0; i < NK; ++i) {
+    const int v = sid[i];
+    if (v < 0) continue;
+    int first = 1;
+    for (int q = 0; q < i; ++q) first &= (sid[q] != v);
+    nact += first;
+  }
+  if (tid < NK && sid[tid] >= 0) {
+    const int v = sid[tid];
+    int first = 1;
+    for (int q = 0; q < tid; ++q) first &= (sid[q] != v);
+    if (first) {
+      int idx = 0;
+      for (int i = 0; i < NK; ++i) {
+        const int u = sid[i];
+        if (u < 0 || u >= v) continue;
+        int f = 1;
+        for (int q = 0; q < i; ++q) f &= (sid[q] != u);
+        idx += f;
+      }
+      active[idx] = v;
+    }
+  }
+  if (tid == 0) {
+    meta[0] = nact;
+    meta[1] = bad;
+  }
+  (void)nvalid;
+}
+
+struct MoeArgs {
+  const uint8_t* wq;
+  const uint8_t* ws;
+  uint64_t wq_stride, ws_stride;   // bytes between experts
+  uint32_t wq_bytes, ws_bytes;     // one expert's packed sizes
+  uint32_t hi_offset, st_offset;
+  const void* in;                  // gate/up: x bf16 [N][K]; down: h fp32 [NK][K]
+  uint32_t in_bytes;
+  float* out;                      // gate/up: h [NK][Mout]; down: o [NK][Mout]
+  const int32_t* idx;              // workspace index region
+  int E, top_k, NK;
+  int Mout, K, KS, G;
+  int out_tiles, up_tile0;
+  int ks_per_wave;
+};
+
+// hi/lo bf16 split of an fp32 value: hi = bf16(v), lo = bf16(v - hi)
+__device__ __forceinline__ void split_bf16(float v, __bf16& hi, __bf16& lo) {
+  hi = (__bf16)v;
+  lo = (__bf16)(v - (float)hi);
+}
+
+// DOWN = false: gate/up + SwiGLU (NT = 2*TO tiles: gate then up)
+// DOWN = true:  down projection (NT = TO tiles)
+template <int FMT, int NT, bool DOWN>
+__global__ __launch_bounds__(1024) void k_moe_gemv(MoeArgs a) {
+  extern __shared__ float red[];  // [W][NT][32][4]
+  constexpr int TO = DOWN ? NT : NT / 2;
+  constexpr int ROWS = DOWN ? 4 : 8;   // routed rows per MFMA pass
+  const MoeIndex ix{a.E, a.NK};
+  const int32_t* meta = a.idx + ix.meta();
+  const int slot_a = blockIdx.y;
+  if (slot_a >= meta[0]) return;       // uniform: fewer active experts than slots
+  const int e = a.idx[ix.active() + slot_a];
+  const int p0 = a.idx[ix.offsets() + e];
+  const int cnt = a.idx[ix.offsets() + e + 1] - p0;
+  const int32_t* pairs = a.idx + ix.pairs() + p0;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int W = blockDim.x >> 6;
+  const int r = lane & 15, s = lane >> 4;
+
+  const __amdgpu_buffer_rsrc_t wq = make_rsrc(a.wq + (uint64_t)e * a.wq_stride, a.wq_bytes);
+  const __amdgpu_buffer_rsrc_t ws = make_rsrc(a.ws + (uint64_t)e * a.ws_stride, a.ws_bytes);
+  const __amdgpu_buffer_rsrc_t inr = make_rsrc(a.in, a.in_bytes);
+
+  int tile[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    int ot = blockIdx.x * TO + (t % TO);
+    ot = ot < a.out_tiles ? ot : a.out_tiles - 1;
+    tile[t] = (!DOWN && t >= TO) ? a.up_tile0 + ot : ot;
+  }
+  const int ks0 = wave * a.ks_per_wave;
+  const int ks1 = min(a.KS, ks0 + a.ks_per_wave);
+  float st = 1.0f;
+  if constexpr (FMT == NVFP4) st = __builtin_bit_cast(float, ld32(ws, a.st_offset));
+
+  for (int c0 = 0; c0 < cnt; c0 += ROWS) {
+    const int nrows = min(ROWS, cnt - c0);
+    // this lane's routed row (A row r): gate/up token = r & 7; down pair = r & 3
+    const int ar = DOWN ? (r & 3) : (r & 7);
+    const bool row_ok = ar < nrows;
+    const int pflat = row_ok ? pairs[c0 + ar] : 0;
+    f32x4 acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (!DOWN) {
+      const uint32_t base = (uint32_t)((pflat / a.top_k) * a.K + 8 * s) * 2u;
+      auto aload = [&](int ks, int j, bool use) -> bf16x8 {
+        const int g = ks * 4 + j;
+        const uint32_t off = (use && row_ok && g < a.G) ? base + (uint32_t)g * 64u : kOOB;
+        return __builtin_bit_cast(bf16x8, ld128(inr, off));
+      };
+      kloop<FMT, NT>(wq, ws, tile, a.KS, ks0, ks1, a.hi_offset, aload, acc);
+    } else {
+      const bool lo_part = (r >> 2) & 1;
+      const uint32_t base = (uint32_t)(pflat * a.K + 8 * s) * 4u;
+      auto aload = [&](int ks, int j, bool use) -> bf16x8 {
+        const int g = ks * 4 + j;
+        const bool on = use && row_ok && g < a.G;
+        const uint32_t off = on ? base + (uint32_t)g * 128u : kOOB;
+        const u32x4 v0 = ld128(inr, off);
+        const u32x4 v1 = ld128(inr, on ? off + 16u : kOOB);
+        bf16x8 out;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const uint32_t bits = q < 4 ? v0[q] : v1[q - 4];
+          __bf16 hi, lo;
+          split_bf16(__builtin_bit_cast(float, bits), hi, lo);
+          out[q] = lo_part ? lo : hi;
+        }
+        return out;
+      };
+      kloop<FMT, NT>(wq, ws, tile, a.KS, ks0, ks1, a.hi_offset, aload, acc);
+    }
+    // reduce: slots (lane ^ 32); for DOWN also hi/lo parts (lane ^ 16)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[t][i] += __shfl_xor(acc[t][i], 32);
+        if constexpr (DOWN) acc[t][i] += __shfl_xor(acc[t][i], 16);
+      }
+    }
+    constexpr int LANES = DOWN ? 16 : 32;
+    if (lane < LANES) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        float* p = red + (((size_t)wave * NT + t) * 32 + lane) * 4;
+        p[0] = acc[t][0];
+        p[1] = acc[t][1];
+        p[2] = acc[t][2];
+        p[3] = acc[t][3];
+      }
+    }
+    __syncthreads();
+    const int n_out = TO * 16 * ROWS;
+    for (int o = threadIdx.x; o < n_out; o += blockDim.x) {
+      const int to = o / (16 * ROWS), rem = o % (16 * ROWS);
+      const int rr = rem / 16, row = rem % 16;
+      const int ot = blockIdx.x * TO + to;
+      const int col = ot * 16 + row;
+      if (rr >= nrows || ot >= a.out_tiles || col >= a.Mout) continue;
+      const int l = DOWN ? row : row + 16 * (rr >> 2), i = DOWN ? rr : (rr & 3);
+      float v = 0.f;
+      for (int w = 0; w < W; ++w) v += red[(((size_t)w * NT + to) * 32 + l) * 4 + i];
+      v *= st;
+      const int pf = pairs[c0 + rr];
+      if constexpr (DOWN) {
+        a.out[(size_t)pf * a.Mout + col] = v;
+      } else {
+        float u = 0.f;
+        for (int w = 0; w < W; ++w) u += red[(((size_t)w * NT + TO + to) * 32 + l) * 4 + i];
+        u *= st;
+        a.out[(size_t)pf * a.Mout + col] = v / (1.0f + expf(-v)) * u;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(256) void k_moe_combine(const float* o, const int32_t* ids, const float* gates,
+                                                     const float* res, float* y, int N, int H, int top_k,
+                                                     int E) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)N * H) return;
+  const int t = (int)(i / H), col = (int)(i % H);
+  float v = res ? res[i] : 0.0f;
+  for (int j = 0; j < top_k; ++j) {
+    const int e = ids[t * top_k + j];
+    if (e < 0 || e >= E) continue;
+    v = fmaf(gates[t * top_k + j], o[(size_t)(t * top_k + j) * H + col], v);
+  }
+  y[i] = v;
+}
+
+}  // namespace qg
+
+using namespace qg;
+
+namespace {
+
+inline bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline bool al4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+inline size_t up256(size_t v) { return (v + 255) / 256 * 256; }
+
+struct MoeLayout {
+  size_t idx_off, h_off, o_off, total;
+};
+
+MoeLayout moe_layout(int E, int64_t H, int64_t I, int N, int top_k) {
+  const int NK = N * top_k;
+  MoeLayout L;
+  L.idx_off = 0;
+  L.h_off = up256((size_t)MoeIndex{E, NK}.total() * 4);
+  L.o_off = L.h_off + up256((size_t)NK * (size_t)I * 4);
+  L.total = L.o_off + up256((size_t)NK * (size_t)H * 4);
+  return L;
+}
+
+template <int FMT, int NT, bool DOWN>
+void launch_moe(const MoeArgs& a, int waves, int slots, hipStream_t stream) {
+  constexpr int TO = DOWN ? NT : NT / 2;
+  const dim3 grid((unsigned)((a.out_tiles + TO - 1) / TO), (unsigned)slots);
+  const size_t lds = (size_t)waves * NT * 32 * 4 * sizeof(float);
+  hipLaunchKernelGGL((k_moe_gemv<FMT, NT, DOWN>), grid, dim3(64 * waves), lds, stream, a);
+}
+
+template <int FMT>
+void launch_moe_pair(const MoeArgs& gu, const MoeArgs& dn, int wgu, int wdn, int slots, hipStream_t stream) {
+  launch_moe<FMT, 4, false>(gu, wgu, slots, stream);
+  launch_moe<FMT, 2, true>(dn, wdn, slots, stream);
+}
+
+}  // namespace
+
+extern "C" int qgemv_moe_workspace_bytes(int E, int64_t H, int64_t I, int N, int top_k, size_t* bytes) {
+  if (!bytes || E < 1 || H < 1 || I < 1) return QGEMV_EINVAL;
+  if (N < 1 || N > 8 || top_k < 1 || top_k > 8) return QGEMV_EUNSUPPORTED;
+  *bytes = moe_layout(E, H, I, N, top_k).total;
+  return QGEMV_OK;
+}
+
+extern "C" int qgemv_moe_index(const int32_t* ids, int N, int top_k, int E, int32_t* counts, int32_t* offsets,
+                               int32_t* pairs, int32_t* active, int32_t* meta, hipStream_t stream) {
+  if (!ids || !counts || !offsets || !pairs || !active || !meta) return QGEMV_EINVAL;
+  if (E < 1) return QGEMV_EINVAL;
+  if (N < 1 || N > 8 || top_k < 1 || top_k > 8) return QGEMV_EUNSUPPORTED;
+  if (!al4(ids) || !al4(counts) || !al4(offsets) || !al4(pairs) || !al4(active) || !al4(meta)) return QGEMV_EALIGN;
+  hipLaunchKernelGGL(k_moe_index, dim3(1), dim3(256), 0, stream, ids, N * top_k, E, counts, offsets, pairs, active,
+                     meta);
+  return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
+}
+
+extern "C" int qgemv_moe(int fmt, const void* wq_gu, const void* ws_gu, const void* wq_dn, const void* ws_dn, int E,
+                         int64_t H, int64_t I, const void* x, const int32_t* ids, const float* gates, int top_k,
+                         const float* residual, float* y, int N, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  if (fmt < INT4 || fmt > NVFP4) return QGEMV_EFORMAT;
+  if (!wq_gu || !ws_gu || !wq_dn || !ws_dn || !x || !ids || !gates || !y) return QGEMV_EINVAL;
+  if (E < 1 || H < 32 || I < 16) return QGEMV_EINVAL;
+  if (N < 1 || N > 8 || top_k < 1 || top_k > 8) return QGEMV_EUNSUPPORTED;
+  if (H % 32 || I % 32) return QGEMV_EALIGN;
+  if (!al16(wq_gu) || !al16(ws_gu) || !al16(wq_dn) || !al16(ws_dn) || !al16(x) || !al4(ids) || !al4(gates) ||
+      !al4(y) || (residual && !al4(residual)))
+    return QGEMV_EALIGN;
+  if (!workspace) return QGEMV_EWORKSPACE;
+  if (!al16(workspace)) return QGEMV_EALIGN;
+  const MoeLayout L = moe_layout(E, H, I, N, top_k);
+  if (workspace_bytes < L.total) return QGEMV_EWORKSPACE;
+  Geom ggu, gdn;
+  if (!geom(fmt, 2 * I, H, &ggu) || !geom(fmt, H, I, &gdn)) return QGEMV_EINVAL;
+  if ((uint64_t)E * up256(ggu.wq_bytes) >= (1ull << 40)) return QGEMV_EUNSUPPORTED;
+  if (ggu.wq_bytes >= (1ull << 32) || gdn.wq_bytes >= (1ull << 32)) return QGEMV_EUNSUPPORTED;
+  const int NK = N * top_k;
+  uint8_t* wsp = (uint8_t*)workspace;
+  int32_t* idx = (int32_t*)(wsp + L.idx_off);
+  float* h = (float*)(wsp + L.h_off);
+  float* o = (float*)(wsp + L.o_off);
+  const MoeIndex ix{E, NK};
+  hipLaunchKernelGGL(k_moe_index, dim3(1), dim3(256), 0, stream, ids, NK, E, idx + ix.counts(), idx + ix.offsets(),
+                     idx + ix.pairs(), idx + ix.active(), idx + ix.meta());
+
+  MoeArgs gu;
+  gu.wq = (const uint8_t*)wq_gu;
+  gu.ws = (const uint8_t*)ws_gu;
+  gu.wq_stride = up256(ggu.wq_bytes);
+  gu.ws_stride = up256(ggu.ws_bytes);
+  gu.wq_bytes = (uint32_t)ggu.wq_bytes;
+  gu.ws_bytes = (uint32_t)ggu.ws_bytes;
+  gu.hi_offset = (uint32_t)ggu.hi_offset;
+  gu.st_offset = (uint32_t)ggu.st_offset;
+  gu.in = x;
+  gu.in_bytes = (uint32_t)((int64_t)N * H * 2);
+  gu.out = h;
+  gu.idx = idx;
+  gu.E = E;
+  gu.top_k = top_k;
+  gu.NK = NK;
+  gu.Mout = (int)I;
+  gu.K = (int)H;
+  gu.KS = (int)ggu.KS;
+  gu.G = (int)(H / 32);
+  gu.out_tiles = (int)((I + 15) / 16);
+  gu.up_tile0 = (int)(I / 16);
+  const int wgu = (int)std::min<int64_t>(16, std::max<int64_t>(1, (ggu.KS + 3) / 4));
+  gu.ks_per_wave = (int)((ggu.KS + wgu - 1) / wgu);
+
+  MoeArgs dn = gu;
+  dn.wq = (const uint8_t*)wq_dn;
+  dn.ws = (const uint8_t*)ws_dn;
+  dn.wq_stride = up256(gdn.wq_bytes);
+  dn.ws_stride = up256(gdn.ws_bytes);
+  dn.wq_bytes = (uint32_t)gdn.wq_bytes;
+  dn.ws_bytes = (uint32_t)gdn.ws_bytes;
+  dn.hi_offset = (uint32_t)gdn.hi_offset;
+  dn.st_offset = (uint32_t)gdn.st_offset;
+  dn.in = h;
+  dn.in_bytes = (uint32_t)((size_t)NK * I * 4);
+  dn.out = o;
+  dn.Mout = (int)H;
+  dn.K = (int)I;
+  dn.KS = (int)gdn.KS;
+  dn.G = (int)(I / 32);
+  dn.out_tiles = (int)((H + 15) / 16);
+  dn.up_tile0 = 0;
+  const int wdn = (int)std::min<int64_t>(16, std::max<int64_t>(1, (gdn.KS + 2) / 3));
+  dn.ks_per_wave = (int)((gdn.KS + wdn - 1) / wdn);
+
+  if (I % 16) return QGEMV_EALIGN;
+  const int slots = std::min(E, NK);
+  switch (fmt) {
+    case INT4: launch_moe_pair<INT4>(gu, dn, wgu, wdn, slots, stream); break;
+    case INT5: launch_moe_pair<INT5>(gu, dn, wgu, wdn, slots, stream); break;
+    case INT8: launch_moe_pair<INT8>(gu, dn, wgu, wdn, slots, stream); break;
+    default: launch_moe_pair<NVFP4>(gu, dn, wgu, wdn, slots, stream); break;
+  }
+  const int64_t tot = (int64_t)N * H;
+  hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, stream, o, ids, gates,
+                     residual, y, N, (int)H, top_k, E);
+  return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
+}

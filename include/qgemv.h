@@ -1,0 +1,194 @@
+/*
+ * libqgemv — dequantise-fused skinny GEMV / GEMM for MI355X (gfx950).
+ *
+ *   y[N x M] = x[N x K] . dequant(W)[K x M]        N = 1..8 tokens
+ *
+ * over low-bit packed weights, with optional fused residual add and SwiGLU
+ * epilogues and a mixture-of-experts variant that runs only each token's
+ * selected experts.
+ *
+ * The operation follows the subject pages:
+ *   - NInfer article (单卡 LLM 推理引擎 NInfer 完全解析), section 2 (custom
+ *     CUDA operators and mixed quantised weights): decode throughput is bound
+ *     by weight reads, fewer weight bits mean fewer bytes read, and each
+ *     weight format gets its own fused kernel that does the matmul, residual
+ *     add and SwiGLU in one read and one write; the groupwise-int recipe mixes
+ *     4-bit and 5-bit groups, the NVFP4 artefact imports 4-bit weights.
+ *   - Same article, "what NInfer is" and section 3: 1 to 8 concurrent decode
+ *     lanes, and a multi-token-prediction verify pass of several tokens.
+ *   - Decapybara page (GitHub - giveen/Decapybara), CUDA kernel list: a
+ *     blocked NVFP4 matrix-vector multiply, a top-8 softmax MoE router.
+ *   - memra page (avifenesh/memra), model notes: checkpoints are repacked
+ *     into the engine's own layout; unsupported combinations are rejected.
+ *   - RustingStrata page, format list: a Q8_0-style symmetric int8 format;
+ *     known issues: reordering floating-point work between runs changes
+ *     results, so every reduction here has a fixed order.
+ *
+ * Formats (logical definition; 32 weights per group / 16 per NVFP4 block,
+ * both along K):
+ *   QGEMV_INT4   w = d*q + m, q in 0..15, d and m fp16 per group
+ *   QGEMV_INT5   w = d*q + m, q in 0..31, d and m fp16 per group
+ *   QGEMV_INT8   w = d*q,     q in -127..127 (two's complement), fp16 d per group
+ *   QGEMV_NVFP4  w = s_t * e2m1(code) * e4m3(b), OCP FP4 E2M1 codes, one OCP
+ *                FP8 E4M3 scale b per 16 weights, one fp32 tensor scale s_t
+ * The packed device layout is the library's own; qgemv_packed_bytes gives
+ * its size. Weights are logically [K x M] and stored output-row-major.
+ *
+ * Conventions for every entry point:
+ *   - Return value: QGEMV_OK (0) or a negative qgemv_status; never an
+ *     exception, never printed. qgemv_strerror gives the text.
+ *   - All arguments are validated on the host before any launch; an invalid
+ *     call launches nothing and returns an error.
+ *   - Device entry points are asynchronous on `stream` (0 = the null stream),
+ *     never synchronise, and take device pointers owned by the caller. The
+ *     library allocates nothing and keeps no global state: concurrent calls
+ *     on different streams are safe when their output buffers do not overlap.
+ *   - Host entry points (pack) take host pointers and need no GPU.
+ *   - Pointers to packed weights, scales and activations must be 16-byte
+ *     aligned (QGEMV_EALIGN otherwise); float outputs 4-byte aligned.
+ *   - Limits: 1 <= N <= 8 (QGEMV_EUNSUPPORTED otherwise), K % 32 == 0,
+ *     M >= 1, packed matrix under 4 GiB.
+ */
+#ifndef QGEMV_H
+#define QGEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QGEMV_INT4 = 1,
+  QGEMV_INT5 = 2,
+  QGEMV_INT8 = 3,
+  QGEMV_NVFP4 = 4
+} qgemv_format;
+
+typedef enum {
+  QGEMV_OK = 0,
+  QGEMV_EINVAL = -1,       /* null pointer, bad size or non-finite weights */
+  QGEMV_EFORMAT = -2,      /* unknown format value */
+  QGEMV_EALIGN = -3,       /* pointer alignment or shape alignment violated */
+  QGEMV_ERANGE = -4,       /* a scale field overflows its encoding */
+  QGEMV_EWORKSPACE = -5,   /* workspace missing or too small */
+  QGEMV_EHIP = -6,         /* the HIP runtime reported an error at launch */
+  QGEMV_EUNSUPPORTED = -7  /* a size outside the supported range (e.g. N > 8) */
+} qgemv_status;
+
+/* Text for a status code (static storage). */
+const char* qgemv_strerror(int status);
+
+/* Library version: major*10000 + minor*100 + patch. */
+int qgemv_version(void);
+
+/* ---------------------------------------------------------------- host --- */
+
+/* Bytes of the packed weight buffer `wq` and scale buffer `ws` for an
+ * [M][K] matrix in format `fmt`. Rows are padded to 16 and K to 128 inside
+ * the layout (padding holds weight 0). */
+int qgemv_packed_bytes(int fmt, int64_t M, int64_t K, size_t* wq_bytes, size_t* ws_bytes);
+
+/* Quantise and pack a host fp32 matrix W[M][K] (row-major) into host
+ * buffers wq, ws of qgemv_packed_bytes sizes. Quantisation rules (the pages
+ * name the formats only; these are the plainest readings):
+ *   int4/int5: per group of 32, d = fp16((max - min) / (2^b - 1)) (fp32
+ *     arithmetic), m = fp16(min), q = clamp(rint((w - m) / d)) in fp64,
+ *     ties to even, q = 0 when d = 0;
+ *   int8: d = fp16(amax / 127), q = clamp(rint(w / d), -127, 127);
+ *   nvfp4: s_t = amax(W) / 2688 in fp32 (1 if that is 0), block scale
+ *     b = E4M3_rne_saturating(amax_b / (6 * s_t)), codes
+ *     E2M1_rne_saturating(w / (b * s_t)) computed in fp64, +0 when b = 0.
+ * Negative zeros in W count as +0. Errors: EINVAL for null pointers,
+ * non-finite weights or bad sizes, ERANGE when d or m overflows fp16. */
+int qgemv_pack(int fmt, const float* W, int64_t M, int64_t K, void* wq, void* ws);
+
+/* Pack logical codes and scale fields (host) without quantising.
+ *   codes:  [M][K] uint8 (int4 0..15, int5 0..31, nvfp4 4-bit E2M1 codes)
+ *           or int8 (int8 format)
+ *   scales: int formats: uint16 fp16 bits of d, [M][K/32];
+ *           nvfp4: uint8 E4M3 codes, [M][K/16]
+ *   mins:   uint16 fp16 bits of m, [M][K/32] (int4/int5), else NULL
+ *   tensor_scale: s_t (nvfp4), ignored otherwise.
+ * Codes outside the format's range give EINVAL. */
+int qgemv_pack_codes(int fmt, const void* codes, const void* scales, const uint16_t* mins,
+                     float tensor_scale, int64_t M, int64_t K, void* wq, void* ws);
+
+/* -------------------------------------------------------------- device --- */
+
+/* y[n][m] = residual[n][m] + sum_k x[n][k] * W[m][k] for n < N, m < M.
+ *   wq, ws:   packed weights and scales (qgemv_pack layout), device
+ *   x:        bf16 activations [N][K], row-major, device
+ *   residual: fp32 [N][M] or NULL; may be the same buffer as y
+ *   y:        fp32 [N][M] output
+ * Accumulation is fp32 in a fixed order: repeated calls give identical bits. */
+int qgemv(int fmt, const void* wq, const void* ws, const void* x, const float* residual,
+          float* y, int64_t M, int64_t K, int N, hipStream_t stream);
+
+/* Fused gate/up projection with SwiGLU (NInfer article, section 2):
+ *   h[n][i] = silu(g) * u,  g = x . W[i],  u = x . W[I + i],  silu(g) = g / (1 + e^-g)
+ * for the [2I][K] matrix packed as one matrix (rows 0..I-1 gate, I..2I-1
+ * up, one NVFP4 tensor scale for both). h is fp32 [N][I]. I % 16 == 0
+ * (QGEMV_EALIGN otherwise). */
+int qgemv_swiglu(int fmt, const void* wq, const void* ws, const void* x, float* h,
+                 int64_t I, int64_t K, int N, hipStream_t stream);
+
+/* Byte stride between consecutive experts in an expert-stacked weight or
+ * scale buffer: the packed size rounded up to 256. */
+int qgemv_expert_stride(int fmt, int64_t M, int64_t K, size_t* wq_stride, size_t* ws_stride);
+
+/* Workspace bytes qgemv_moe needs for E experts, hidden H, intermediate I,
+ * N tokens and top_k experts per token. */
+int qgemv_moe_workspace_bytes(int E, int64_t H, int64_t I, int N, int top_k, size_t* bytes);
+
+/* Mixture-of-experts FFN for N tokens that each selected top_k experts
+ * (Decapybara page: top-8 softmax router; NInfer article, section 2: fused
+ * SwiGLU):
+ *   for each token t and slot j with e = ids[t][j] in [0, E):
+ *     h = SwiGLU(x[t] . W_gu[e])            (fp32, [I])
+ *     o = h . W_dn[e]                       (fp32, [H])
+ *   y[t] = residual[t] + sum_j gates[t][j] * o_j   (j in increasing order)
+ *   wq_gu, ws_gu: E experts of [2I][H] packed, stacked at qgemv_expert_stride
+ *   wq_dn, ws_dn: E experts of [H][I] packed, stacked likewise
+ *   ids [N][top_k] int32, gates [N][top_k] fp32 (used as given), device
+ *   residual [N][H] fp32 or NULL (may equal y); y [N][H] fp32
+ *   workspace: device scratch of qgemv_moe_workspace_bytes, 16-byte aligned
+ * Only the experts some token selected are read. Ids outside [0, E) add
+ * nothing and set the error flag that qgemv_moe_index reports. Duplicate
+ * ids in a row are processed as separate slots. top_k <= 8, N <= 8,
+ * I % 16 == 0. */
+int qgemv_moe(int fmt, const void* wq_gu, const void* ws_gu, const void* wq_dn, const void* ws_dn,
+              int E, int64_t H, int64_t I, const void* x, const int32_t* ids, const float* gates,
+              int top_k, const float* residual, float* y, int N, void* workspace,
+              size_t workspace_bytes, hipStream_t stream);
+
+/* MoE routing index (the step qgemv_moe runs first), into caller buffers:
+ *   counts [E]      slots routed to each expert
+ *   offsets [E+1]   exclusive prefix sum of counts
+ *   pairs [N*top_k] flat slot t*top_k + j, ordered by (expert, t, j); -1 after
+ *                   offsets[E]
+ *   active [E]      experts with a nonzero count, ascending; -1 after
+ *   meta [2]        {number of active experts, 1 if any id was outside [0, E)}
+ * Exact integer results. */
+int qgemv_moe_index(const int32_t* ids, int N, int top_k, int E, int32_t* counts, int32_t* offsets,
+                    int32_t* pairs, int32_t* active, int32_t* meta, hipStream_t stream);
+
+/* Debug / parity: write the fp32 weights the packed buffers encode,
+ * w_out[m][k] for m < M, k < K. Values are exactly:
+ *   int4/int5: fp32(d*q + m) rounded once; int8: d*q;
+ *   nvfp4: fp32(s_t * (e2m1 * b)) rounded once. */
+int qgemv_dequant(int fmt, const void* wq, const void* ws, int64_t M, int64_t K, float* w_out,
+                  hipStream_t stream);
+
+/* Measurement aid: stream-read `bytes` (multiple of 16) from `buf` with
+ * 128-bit non-temporal loads, folding them into sink[0] (a device uint32).
+ * Gives the achievable read bandwidth that the GEMV kernels approach. */
+int qgemv_probe_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMV_H */

@@ -18,14 +18,16 @@ int4   wq: tile = 1024 B; lane lam's 16 B at lam*16; dword j holds the 8
            codes of group j; code for slot e is nibble i (bits 4i..4i+3 of
            the little-endian dword) with i = e/2 for even e, 4 + (e-1)/2 for
            odd e.
-       ws: tile = 256 B; dword at r*16 + 4*j = fp16(d) | fp16(m) << 16.
+       ws: tile = 256 B; row r's 16 B at r*16 hold the groups in the order
+           j = 0, 2, 1, 3: dword at r*16 + 4*pos(j), pos(j) = 2*(j & 1) + (j >> 1),
+           value fp16(d) | fp16(m) << 16.
 int5   wq: the int4 nibble plane of the low 4 code bits (RT*KS*1024 B), then a
            hi-bit plane of 256 B tiles: lane lam's dword at lam*4 has bit
            16*(e & 1) + 4*j + (e >> 1) = bit 4 of the code.
        ws: as int4.
 int8   wq: tile = 2048 B; byte (j >> 1)*1024 + lam*16 + (j & 1)*8 + e holds the
            code (two's complement).
-       ws: tile = 128 B; fp16(d) at byte r*8 + 2*j.
+       ws: tile = 128 B; fp16(d) at byte r*8 + 2*pos(j) (same group order).
 nvfp4  wq: tile = 1024 B; byte lam*16 + 4*j + (e >> 1), low nibble for even e,
            high nibble for odd e (E2M1 codes).
        ws: tile = 128 B; byte r*8 + 4*h + j holds the E4M3 scale of the 16-block
@@ -85,12 +87,19 @@ def _untile_codes(t: np.ndarray, RT: int, KS: int) -> np.ndarray:
     return c.reshape(RT * 16, KS * KSTEP)
 
 
+# position of group j inside a row's scale record: groups 0, 2, 1, 3
+_SCALE_POS = np.array([0, 2, 1, 3])       # pos(j) = 2*(j & 1) + (j >> 1)
+_SCALE_J = np.argsort(_SCALE_POS)         # j stored at each position
+
+
 def _scales_tiled(f: np.ndarray, RT: int, KS: int) -> np.ndarray:
-    """per-group field [Mp][Kp/32] -> [rt][ks][r][j]."""
-    return f.reshape(RT, 16, KS, 4).transpose(0, 2, 1, 3)
+    """per-group field [Mp][Kp/32] -> [rt][ks][r][pos]."""
+    t = f.reshape(RT, 16, KS, 4).transpose(0, 2, 1, 3)
+    return t[..., _SCALE_J]
 
 
 def _untile_scales(t: np.ndarray, RT: int, KS: int) -> np.ndarray:
+    t = t[..., _SCALE_POS]                # back to j order
     return t.transpose(0, 2, 1, 3).reshape(RT * 16, KS * 4)
 
 

@@ -1,0 +1,170 @@
+"""CPU tests of the C-ABI library: exported symbols, host packer bytes against
+the oracle's packer, and argument validation (no GPU call is ever reached)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import synthetic
+from oracle import layout, quant
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+qg = pytest.importorskip("bit_quantized_weight_amd")
+if not os.path.exists(qg.LIB_PATH):
+    pytest.skip("libqgemv.so not built (run __graft_entry__.build())", allow_module_level=True)
+
+FORMATS = ["int4", "int5", "int8", "nvfp4"]
+
+
+def _header_functions():
+    src = open(os.path.join(ROOT, "include", "qgemv.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(qgemv[a-z_]*)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = qg.load(False)
+    declared = _header_functions()
+    assert len(declared) >= 13
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert sorted(qg.symbols()) == declared
+
+
+def test_version_and_strerror():
+    assert qg.load(False).qgemv_version() >= 100
+    for code in range(0, -8, -1):
+        assert len(qg.strerror(code)) > 3
+    assert qg.strerror(-99) == "unknown status"
+
+
+def _rows(K, rng):
+    rows = [np.zeros(K), np.full(K, 0.125), np.linspace(-1, 1, K), rng.standard_normal(K) * 1e-6,
+            rng.standard_normal(K) * 3, np.where(np.arange(K) % 32 == 3, -5.0, 0.0), -np.zeros(K)]
+    return np.stack(rows).astype(np.float32)
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("M,K", [(16, 128), (23, 160), (1, 32), (40, 640), (7, 96)])
+def test_pack_bytes_equal_oracle(fmt, M, K):
+    rng = np.random.default_rng(M * 131 + K)
+    W = synthetic.weights(rng, M, K)
+    W[: min(M, 7)] = _rows(K, rng)[: min(M, 7)]
+    wq, ws = qg.pack(fmt, W)
+    owq, ows = layout.pack(quant.quantize(W, fmt))
+    assert wq.size == owq.size and ws.size == ows.size
+    assert np.array_equal(wq, owq), np.nonzero(wq != owq)[0][:10]
+    assert np.array_equal(ws, ows), np.nonzero(ws != ows)[0][:10]
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_pack_bytes_equal_oracle_large(fmt):
+    rng = np.random.default_rng(99)
+    W = synthetic.weights(rng, 512, 5120)
+    wq, ws = qg.pack(fmt, W)
+    owq, ows = layout.pack(quant.quantize(W, fmt))
+    assert np.array_equal(wq, owq) and np.array_equal(ws, ows)
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_pack_codes_equal_oracle(fmt):
+    rng = np.random.default_rng(5)
+    M, K = 33, 384
+    hi = {"int4": 16, "int5": 32, "nvfp4": 16}.get(fmt)
+    codes = (rng.integers(-128, 128, (M, K)).astype(np.int8) if fmt == "int8"
+             else rng.integers(0, hi, (M, K)).astype(np.uint8))
+    qz = quant.Quantized(fmt, M, K, codes)
+    if fmt == "nvfp4":
+        qz.sb = rng.integers(0, 256, (M, K // 16)).astype(np.uint8)
+        qz.st = np.float32(0.37)
+        wq, ws = qg.pack_codes(fmt, codes, qz.sb, None, float(qz.st))
+    else:
+        qz.d = rng.integers(0, 65536, (M, K // 32)).astype(np.uint16)
+        qz.m = None if fmt == "int8" else rng.integers(0, 65536, (M, K // 32)).astype(np.uint16)
+        wq, ws = qg.pack_codes(fmt, codes, qz.d, qz.m)
+    owq, ows = layout.pack(qz)
+    assert np.array_equal(wq, owq) and np.array_equal(ws, ows)
+
+
+def test_pack_rejects_bad_input():
+    W = np.zeros((16, 64), np.float32)
+    with pytest.raises(qg.QgemvError) as e:
+        qg.pack(9, W)
+    assert e.value.status == -2
+    Wn = W.copy()
+    Wn[3, 4] = np.nan
+    with pytest.raises(qg.QgemvError) as e:
+        qg.pack("int4", Wn)
+    assert e.value.status == -1
+    big = np.full((16, 64), 1e7, np.float32)
+    big[:, ::2] = -1e7
+    for fmt in ("int4", "int5", "int8"):
+        with pytest.raises(qg.QgemvError) as e:
+            qg.pack(fmt, big)
+        assert e.value.status == -4
+    with pytest.raises(qg.QgemvError) as e:
+        qg.packed_bytes("int4", 16, 48)
+    assert e.value.status == -1
+    codes = np.full((16, 64), 16, np.uint8)
+    with pytest.raises(qg.QgemvError) as e:
+        qg.pack_codes("int4", codes, np.zeros((16, 2), np.uint16), np.zeros((16, 2), np.uint16))
+    assert e.value.status == -1
+
+
+def test_expert_stride_is_256_aligned():
+    a, b = qg.expert_stride("nvfp4", 1536, 2048)
+    pa, pb = qg.packed_bytes("nvfp4", 1536, 2048)
+    assert a % 256 == 0 and b % 256 == 0 and a >= pa and b >= pb and b - pb < 256
+
+
+# Device entry points: every call below fails validation on the host, so no
+# HIP call is made and these run without a GPU.
+FAKE = 0x10000          # 16-byte aligned, never dereferenced
+ODD = 0x10004
+
+
+def _gemv(**kw):
+    a = dict(fmt=1, wq=FAKE, ws=FAKE, x=FAKE, res=None, y=FAKE, M=64, K=128, N=1, stream=None)
+    a.update(kw)
+    return qg.load(False).qgemv(a["fmt"], a["wq"], a["ws"], a["x"], a["res"], a["y"], a["M"], a["K"], a["N"],
+                                a["stream"])
+
+
+def test_qgemv_validation_codes():
+    assert _gemv(fmt=0) == -2 and _gemv(fmt=5) == -2
+    assert _gemv(wq=None) == -1 and _gemv(x=None) == -1 and _gemv(y=None) == -1
+    assert _gemv(N=0) == -7 and _gemv(N=9) == -7
+    assert _gemv(K=48) == -3 and _gemv(K=0) == -1 and _gemv(M=0) == -1
+    assert _gemv(wq=ODD) == -3 and _gemv(x=ODD) == -3 and _gemv(y=FAKE + 2) == -3
+    assert _gemv(res=FAKE + 1, y=FAKE) == -3
+    L = qg.load(False)
+    assert L.qgemv_swiglu(1, FAKE, FAKE, FAKE, FAKE, 24, 128, 1, None) == -3      # I % 16
+    assert L.qgemv_swiglu(1, FAKE, FAKE, FAKE, FAKE, 32, 128, 9, None) == -7
+    assert L.qgemv_dequant(1, FAKE, FAKE, 16, 40, FAKE, None) == -3
+    assert L.qgemv_dequant(7, FAKE, FAKE, 16, 64, FAKE, None) == -2
+    assert L.qgemv_probe_read(FAKE, 100, FAKE, None) == -3
+    assert L.qgemv_probe_read(None, 128, FAKE, None) == -1
+
+
+def test_qgemv_moe_validation_codes():
+    L = qg.load(False)
+    need = qg.moe_workspace_bytes(128, 2048, 768, 8, 8)
+    assert need > 0
+
+    def moe(**kw):
+        a = dict(fmt=1, E=128, H=2048, I=768, top_k=8, N=8, ws=FAKE, wsb=need, ids=FAKE)
+        a.update(kw)
+        return L.qgemv_moe(a["fmt"], FAKE, FAKE, FAKE, FAKE, a["E"], a["H"], a["I"], FAKE, a["ids"], FAKE,
+                           a["top_k"], None, FAKE, a["N"], a["ws"], a["wsb"], None)
+    assert moe(ws=None) == -5
+    assert moe(wsb=need - 1) == -5
+    assert moe(top_k=9) == -7 and moe(N=9) == -7
+    assert moe(H=2047) == -1 or moe(H=2047) == -3
+    assert moe(fmt=0) == -2
+    assert moe(ids=None) == -1
+    assert L.qgemv_moe_index(None, 1, 8, 128, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -1
+    assert L.qgemv_moe_index(FAKE, 9, 8, 128, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -7
+    b = ctypes.c_size_t()
+    assert L.qgemv_moe_workspace_bytes(0, 2048, 768, 1, 8, ctypes.byref(b)) == -1
