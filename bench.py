@@ -1,0 +1,343 @@
+"""Benchmark of the dequantise-fused GEMV path on one MI355X.
+
+A step is one pass of the 27B-class dense layer at N = 1 (one decode token):
+  QKV projection   [7168][5120]        G32 asymmetric int4
+  gate/up + SwiGLU [2 x 17408][5120]   G32 asymmetric int5 (fused SwiGLU)
+  down + residual  [5120][17408]       G32 asymmetric int5 (fused residual)
+Weights and activations are seeded synthetic data of those shapes (no
+checkpoint exists here). Layers are rotated over distinct device copies so
+that the working set (several GB) far exceeds the 256 MB Infinity Cache and
+every step reads its weights from HBM.
+
+value = algorithmic bytes per step / time per step (GB/s): packed weights and
+scales + x (bf16) + outputs (fp32) + residual read.
+
+Also reported on the same JSON line:
+  roofline      the dominant kernel (gate/up + SwiGLU, int5) against 8 TB/s,
+                from HIP events around each of its launches in the timed loop
+  per_format    qgemv on [17408][5120] for each format at N = 1 and N = 8
+  moe           qgemv_moe on the 128-expert, top-8 workload at N = 1 and 8
+  probe         the plain streaming-read kernel on the same rotation
+  cpu_baseline  the CPU oracle on a bounded sample of the layer
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_GBS = 8000.0
+LAYER = [("qkv", 7168, 5120, "int4"), ("gate_up", 2 * 17408, 5120, "int5"), ("down", 5120, 17408, "int5")]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def weight_bytes(qg, fmt, M, K):
+    a, b = qg.packed_bytes(fmt, M, K)
+    return a + b
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "bit_quantized_weight_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def pmc_traffic(name: str, src_hash: str):
+    """HBM traffic per launch from a committed rocprofv3 counter summary, or
+    None when missing or taken on different kernel sources."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(p) as f:
+            t = json.load(f)
+        e = t.get(name)
+        if e and e.get("src_hash") == src_hash:
+            return e.get("bytes_per_launch")
+    except (OSError, ValueError):
+        pass
+    return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--layers", type=int, default=16, help="distinct layer copies rotated on the device")
+    ap.add_argument("--no-extra", action="store_true", help="skip per-format, MoE, probe and CPU baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import bit_quantized_weight_amd as qg
+    import synthetic
+
+    qg.load()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    N = 1
+
+    # ---- weights: a few unique layers packed on the host, replicated on device
+    uniq = 2
+    t0 = time.time()
+    host_layers = []
+    for u in range(uniq):
+        mats = {}
+        for name, M, K, fmt in LAYER:
+            rng = synthetic.rng_for(0, 2, u, M)
+            W = synthetic.weights(rng, M, K)
+            mats[name] = qg.pack(fmt, W)
+            del W
+        host_layers.append(mats)
+    log(f"packed {uniq} unique layers in {time.time() - t0:.1f}s")
+    layers = []
+    for li in range(args.layers):
+        src = host_layers[li % uniq]
+        layers.append({k: (torch.from_numpy(v[0]).to(dev), torch.from_numpy(v[1]).to(dev)) for k, v in src.items()})
+    del host_layers
+    rng = synthetic.rng_for(0, 2, 99)
+    x = torch.from_numpy(synthetic.activations(rng, N, 5120)).to(dev)
+    h = torch.empty((N, 17408), dtype=torch.float32, device=dev)
+    qkv = torch.empty((N, 7168), dtype=torch.float32, device=dev)
+    res = torch.from_numpy(synthetic.residual(rng, N, 5120)).to(dev)
+    y = torch.empty((N, 5120), dtype=torch.float32, device=dev)
+    xd = torch.from_numpy(synthetic.activations(rng, N, 17408)).to(dev)  # bf16 input of the down projection
+
+    layer_w = sum(weight_bytes(qg, f, M, K) for _, M, K, f in LAYER)
+    act = (N * 5120 * 2 + N * 7168 * 4) + (N * 5120 * 2 + N * 17408 * 4) + (N * 17408 * 2 + N * 5120 * 4 * 2)
+    step_bytes = layer_w + act
+    gu_bytes = weight_bytes(qg, "int5", 2 * 17408, 5120) + N * 5120 * 2 + N * 17408 * 4
+    log(f"layer weights {layer_w / 1e6:.1f} MB, rotation {args.layers} layers = {args.layers * layer_w / 1e9:.2f} GB")
+
+    ev = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(args.steps)]
+
+    def step(i, timed=None):
+        L = layers[i % args.layers]
+        qg.qgemv("int4", *L["qkv"], x, qkv, 7168, 5120, N)
+        if timed is not None:
+            timed[0].record(stream)
+        qg.qgemv_swiglu("int5", *L["gate_up"], x, h, 17408, 5120, N)
+        if timed is not None:
+            timed[1].record(stream)
+        qg.qgemv("int5", *L["down"], xd, y, 5120, 17408, N, residual=res)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i, ev[i])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms_step = total_ms / args.steps
+    gu_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    gu_gbs = gu_bytes / (gu_ms * 1e-3) / 1e9
+    log(f"step {ms_step * 1e3:.1f} us -> {value:.0f} GB/s; gate/up launch {gu_ms * 1e3:.1f} us -> {gu_gbs:.0f} GB/s")
+
+    # per-kernel averages (each kernel alone, back to back, rotated)
+    def time_alone(fn, reps):
+        for i in range(min(reps, 8)):
+            fn(i)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(reps):
+            fn(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    kern = {}
+    kern["qkv_int4"] = (time_alone(lambda i: qg.qgemv("int4", *layers[i % args.layers]["qkv"], x, qkv, 7168, 5120, N), 200),
+                        weight_bytes(qg, "int4", 7168, 5120) + N * 5120 * 2 + N * 7168 * 4)
+    kern["gate_up_swiglu_int5"] = (time_alone(lambda i: qg.qgemv_swiglu("int5", *layers[i % args.layers]["gate_up"], x, h, 17408, 5120, N), 100), gu_bytes)
+    kern["down_residual_int5"] = (time_alone(lambda i: qg.qgemv("int5", *layers[i % args.layers]["down"], xd, y, 5120, 17408, N, residual=res), 100),
+                                  weight_bytes(qg, "int5", 5120, 17408) + N * 17408 * 2 + N * 5120 * 8)
+    kernels = {k: {"us": round(ms * 1e3, 2), "GB/s": round(b / (ms * 1e-3) / 1e9, 1)} for k, (ms, b) in kern.items()}
+    log("kernels alone:", kernels)
+
+    src_hash = kernel_source_hash()
+    roofline = {"bound": "hbm", "kernel": "k_gemv<int5, swiglu> (gate/up + SwiGLU)",
+                "achieved": round(gu_gbs, 1), "peak": PEAK_GBS, "unit": "GB/s", "frac": round(gu_gbs / PEAK_GBS, 4),
+                "traffic": pmc_traffic("gate_up_swiglu_int5", src_hash),
+                "algorithmic_bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_ms * 1e3, 2)}
+
+    extra = {}
+    if not args.no_extra:
+        extra = extras(qg, torch, dev, stream, layers, args)
+        del layers
+        torch.cuda.empty_cache()
+        extra["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+
+    out = {
+        "metric": "achieved HBM GB/s (% of MI355X peak) for qgemv at N=1 and N=8, per format",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "27B-class dense layer, N=1: QKV 7168x5120 int4 + gate/up 2x17408x5120 int5 "
+                               "with SwiGLU + down 5120x17408 int5 with residual",
+                   "layers_rotated": args.layers, "rotation_GB": round(args.layers * layer_w / 1e9, 2),
+                   "algorithmic_bytes_per_step": step_bytes, "frac_of_peak": round(value / PEAK_GBS, 4),
+                   "tok_per_s_64_layers": round(1.0 / (64 * ms_step * 1e-3), 1),
+                   "arithmetic": "bf16 MFMA operands (exact codes), fp32 accumulate"},
+        "roofline": roofline,
+        "kernels": kernels,
+        "src_hash": src_hash,
+    }
+    out.update({k: v for k, v in extra.items() if k != "cpu_baseline"})
+    out["cpu_baseline"] = extra.get("cpu_baseline")
+    print(json.dumps(out), flush=True)
+
+
+def extras(qg, torch, dev, stream, layers, args):
+    import synthetic
+    res = {}
+
+    def timeit(fn, reps):
+        for i in range(4):
+            fn(i)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(reps):
+            fn(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    # probe: plain streaming read of each 134 MB gate/up weight buffer
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    pb = [L["gate_up"][0] for L in layers]
+    ms = timeit(lambda i: qg.qgemv_probe_read(pb[i % len(pb)], pb[0].numel() // 16 * 16, sink), 64)
+    res["probe"] = {"bytes": pb[0].numel(), "us": round(ms * 1e3, 2), "GB/s": round(pb[0].numel() / (ms * 1e-3) / 1e9, 1)}
+    log("probe", res["probe"])
+
+    # per format on [17408][5120], N = 1 and 8, rotated over >= 1 GB
+    M, K = 17408, 5120
+    rng = synthetic.rng_for(0, 3, M)
+    W = synthetic.weights(rng, M, K)
+    pf = {}
+    for fmt in ("int4", "int5", "int8", "nvfp4"):
+        wq, ws = qg.pack(fmt, W)
+        nb = wq.size + ws.size
+        copies = max(2, int(np.ceil(1.2e9 / nb)))
+        d = [(torch.from_numpy(wq).to(dev), torch.from_numpy(ws).to(dev)) for _ in range(copies)]
+        pf[fmt] = {}
+        for n in (1, 8):
+            xb = torch.from_numpy(synthetic.activations(rng, n, K, 0.01)).to(dev)
+            yy = torch.empty((n, M), dtype=torch.float32, device=dev)
+            ms = timeit(lambda i: qg.qgemv(fmt, *d[i % copies], xb, yy, M, K, n), 60)
+            b = nb + n * K * 2 + n * M * 4
+            pf[fmt][f"N{n}"] = {"us": round(ms * 1e3, 2), "GB/s": round(b / (ms * 1e-3) / 1e9, 1),
+                                "frac": round(b / (ms * 1e-3) / 1e9 / PEAK_GBS, 4)}
+        del d
+        log("per_format", fmt, pf[fmt])
+    res["per_format"] = {"shape": [M, K], "formats": pf}
+    del W
+
+    # MoE: 128 experts, H 2048, I 768, top-8, int4, N = 1 and 8
+    E, H, I, k = 128, 2048, 768, 8
+    sq, ss = qg.expert_stride("int4", 2 * I, H)
+    dq, ds = qg.expert_stride("int4", H, I)
+    bufs = [np.zeros(E * sq, np.uint8), np.zeros(E * ss, np.uint8), np.zeros(E * dq, np.uint8), np.zeros(E * ds, np.uint8)]
+    rng = synthetic.rng_for(0, 5)
+    for e in range(E):
+        q, s = qg.pack("int4", synthetic.weights(rng, 2 * I, H))
+        bufs[0][e * sq: e * sq + q.size] = q
+        bufs[1][e * ss: e * ss + s.size] = s
+        q, s = qg.pack("int4", synthetic.weights(rng, H, I))
+        bufs[2][e * dq: e * dq + q.size] = q
+        bufs[3][e * ds: e * ds + s.size] = s
+    copies = 32
+    dbufs = [[torch.from_numpy(b).to(dev) for b in bufs] for _ in range(copies)]
+    per_expert = (sq + ss + dq + ds)
+    moe = {}
+    for n in (1, 8):
+        logits = synthetic.router_logits(rng, n, E)
+        ids = np.argsort(-logits.astype(np.float64), axis=1, kind="stable")[:, :k].astype(np.int32)
+        g = np.exp(np.take_along_axis(logits.astype(np.float64), ids, 1))
+        gates = (g / g.sum(1, keepdims=True)).astype(np.float32)
+        uniq = len(set(ids.reshape(-1).tolist()))
+        xb = torch.from_numpy(synthetic.activations(rng, n, H)).to(dev)
+        idt = torch.from_numpy(ids).to(dev)
+        gt = torch.from_numpy(gates).to(dev)
+        nbytes = qg.moe_workspace_bytes(E, H, I, n, k)
+        wsp = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+        yy = torch.empty((n, H), dtype=torch.float32, device=dev)
+        ms = timeit(lambda i: qg.qgemv_moe("int4", *dbufs[i % copies], E, H, I, xb, idt, gt, k, yy, n, wsp, nbytes), 60)
+        b = uniq * per_expert + n * H * 2 + n * H * 4 + n * k * 8
+        moe[f"N{n}"] = {"active_experts": uniq, "us": round(ms * 1e3, 2), "GB/s": round(b / (ms * 1e-3) / 1e9, 1)}
+    res["moe"] = {"workload": "128 experts, H 2048, I 768, top-8, int4, 32 rotated copies", **moe}
+    log("moe", res["moe"])
+    return res
+
+
+def cpu_baseline(seconds: float):
+    """The oracle (dequantise to fp64 + numpy matmul on all host cores) on a
+    sample of the layer: whole row tiles of each matrix, repeated for about
+    `seconds`; reported as GB/s over the same algorithmic bytes."""
+    from oracle import gemv as G
+    from oracle import layout, quant
+    from oracle.dequant import dequant
+    import synthetic
+
+    rng = synthetic.rng_for(0, 6)
+    parts = []
+    for name, M, K, fmt in LAYER:
+        rows = 256
+        W = synthetic.weights(rng, rows, K)
+        wq, ws = layout.pack(quant.quantize(W, fmt))
+        parts.append((fmt, rows, K, wq, ws, sum(layout.packed_bytes(fmt, rows, K)) + K * 2 + rows * 4))
+    x = {K: G.x_from_bits(synthetic.activations(rng, 1, K)) for K in (5120, 17408)}
+    done, nbytes, t0 = 0, 0, time.perf_counter()
+    while True:
+        for fmt, rows, K, wq, ws, b in parts:
+            Wd = dequant(layout.unpack(fmt, rows, K, wq, ws))
+            G.gemv(x[K], Wd)
+            nbytes += b
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    blas = None
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max((p.get("num_threads", 0) for p in threadpool_info() if p.get("user_api") == "blas"), default=None)
+    except Exception:
+        pass
+    return {"value": round(nbytes / el / 1e9, 4), "unit": "GB/s", "cores": blas or cores, "kind": "oracle",
+            "host_cores_visible": cores,
+            "sample": f"{done} passes over 256-row slices of the three layer matrices (unpack + dequantise to fp64 "
+                      f"single-threaded, numpy matmul on {blas} BLAS threads, N=1), {el:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -7,7 +7,8 @@
 // 32-column group into the bf16x8 B operand of v_mfma_f32_16x16x32_bf16:
 //   int4 / int5  bf16(128 + q): the code sits in the low mantissa bits under
 //                the exponent of 128 (bf16 0x4300), exact for q < 128; the
-//                128 * sum(x) bias is removed in the group epilogue
+//                128 * sum(x) bias is removed in the group epilogue (int5's
+//                decoder lives with the k-loop: it decodes a whole k-step)
 //   int8         bf16(q), exact (|q| <= 128)
 //   nvfp4        bf16(e2m1), exact, via v_cvt_scalef32_pk_bf16_fp4 with scale 1
 //                (that instruction only applies the exponent of its scale, so
@@ -48,6 +49,28 @@ __device__ __forceinline__ u32x2 ld64(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 __device__ __forceinline__ uint32_t ld32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
+// voff: per-lane offset, soff: wave-uniform offset (an SGPR). Masked lanes
+// use a voff of 2^31 or more; every soff here stays below 2^31, so the sum
+// cannot wrap back into range.
+__device__ __forceinline__ u32x4 ld128s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+__device__ __forceinline__ u32x4 ld128s_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kNonTemporal);
+}
+__device__ __forceinline__ u32x2 ld64s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+}
+__device__ __forceinline__ uint32_t ld32s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+__device__ __forceinline__ uint32_t ld32s_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kNonTemporal);
+}
+__device__ __forceinline__ uint32_t ld16s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 __device__ __forceinline__ float f16_lo(uint32_t v) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xFFFFu));
@@ -56,35 +79,23 @@ __device__ __forceinline__ float f16_hi(uint32_t v) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
 }
 
+// (a & b) | c in one gfx950 v_bitop3_b32 (truth table 0xEA, S0 the most
+// significant input); VOP3 takes no 32-bit literal here, so plain C becomes
+// an AND and an OR with literals.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t b, uint32_t c) {
+  return __builtin_amdgcn_bitop3_b32(a, b, c, 0xEA);
+}
+
 // ---- decoders: 8 codes of one lane and group -> bf16x8 (slot e = element e)
 
 // int4 dword: slot e in nibble (e even ? e/2 : 4 + e/2), so the nibble pairs
 // (0,4), (1,5), (2,6), (3,7) are the slot pairs (0,1), (2,3), (4,5), (6,7).
 __device__ __forceinline__ bf16x8 dec_int4(uint32_t v) {
   u32x4 r;
-  r.x = (v & 0x000F000Fu) | 0x43004300u;
-  r.y = ((v >> 4) & 0x000F000Fu) | 0x43004300u;
-  r.z = ((v >> 8) & 0x000F000Fu) | 0x43004300u;
-  r.w = ((v >> 12) & 0x000F000Fu) | 0x43004300u;
-  return __builtin_bit_cast(bf16x8, r);
-}
-
-// hi-bit word of a lane: bit 16*(e&1) + 4*j + (e>>1) is bit 4 of the code of
-// group j, slot e. For slot pair p of group j this moves bits b and 16 + b,
-// b = 4j + p, to bits 4 and 20 and adds the bf16 exponent of 128.
-template <int B>
-__device__ __forceinline__ uint32_t hi_pair(uint32_t H) {
-  const uint32_t t = B >= 4 ? (H >> (B >= 4 ? B - 4 : 0)) : (H << (B < 4 ? 4 - B : 0));
-  return (t & 0x00100010u) | 0x43004300u;
-}
-
-template <int J>
-__device__ __forceinline__ bf16x8 dec_int5(uint32_t v, uint32_t H) {
-  u32x4 r;
-  r.x = (v & 0x000F000Fu) | hi_pair<4 * J + 0>(H);
-  r.y = ((v >> 4) & 0x000F000Fu) | hi_pair<4 * J + 1>(H);
-  r.z = ((v >> 8) & 0x000F000Fu) | hi_pair<4 * J + 2>(H);
-  r.w = ((v >> 12) & 0x000F000Fu) | hi_pair<4 * J + 3>(H);
+  r.x = and_or(v, 0x000F000Fu, 0x43004300u);
+  r.y = and_or(v >> 4, 0x000F000Fu, 0x43004300u);
+  r.z = and_or(v >> 8, 0x000F000Fu, 0x43004300u);
+  r.w = and_or(v >> 12, 0x000F000Fu, 0x43004300u);
   return __builtin_bit_cast(bf16x8, r);
 }
 

@@ -49,16 +49,60 @@ struct GemvArgs {
   int ks_per_wave;
 };
 
+// Combine a lane's accumulators into per-(token, row) totals and write them
+// to LDS as red[((wave*NT + t)*8 + token)*16 + row]; fixed order throughout.
+template <int S, int NT>
+__device__ __forceinline__ void reduce_to_lds(f32x4 (&acc)[NT], float* red, int wave, int lane) {
+  const int r = lane & 15, s = lane >> 4;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    float* p = red + (size_t)(wave * NT + t) * 128;
+    if constexpr (S == 16) {          // every register a different slot, token 0
+      float v = (acc[t][0] + acc[t][1]) + (acc[t][2] + acc[t][3]);
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      if (lane < 16) p[r] = v;
+    } else if constexpr (S == 8) {    // tokens 0, 1 in registers (0, 2) and (1, 3)
+      float v0 = acc[t][0] + acc[t][2], v1 = acc[t][1] + acc[t][3];
+      v0 += __shfl_xor(v0, 16);
+      v1 += __shfl_xor(v1, 16);
+      v0 += __shfl_xor(v0, 32);
+      v1 += __shfl_xor(v1, 32);
+      if (lane < 16) {
+        p[r] = v0;
+        p[16 + r] = v1;
+      }
+    } else if constexpr (S == 4) {    // register i = token i, slot = s
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v = acc[t][i];
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+        if (lane < 16) p[i * 16 + r] = v;
+      }
+    } else {                          // S = 2: token 4*(s&1) + i, slot = s >> 1
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v = acc[t][i];
+        v += __shfl_xor(v, 32);
+        if (lane < 32) p[(4 * s + i) * 16 + r] = v;
+      }
+    }
+  }
+}
+
 // NT tiles per wave: plain GEMV uses NT output tiles, SwiGLU NT/2 gate tiles
-// followed by NT/2 up tiles.
-template <int FMT, int NT, bool SWIGLU>
-__global__ __launch_bounds__(1024) void k_gemv(GemvArgs a) {
-  extern __shared__ float red[];  // [W][NT][32][4]
+// followed by NT/2 up tiles. S: slots (16 / S tokens per slot >= N). KPS:
+// k-steps per weight prefetch buffer.
+template <int FMT, int NT, int S, int KPS, bool SWIGLU>
+__global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
+  extern __shared__ float red[];  // [W][NT][8][16]
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = uniform(threadIdx.x >> 6);
   const int W = blockDim.x >> 6;
   const int r = lane & 15, s = lane >> 4;
   constexpr int TO = SWIGLU ? NT / 2 : NT;
+  constexpr int T = 16 / S;
 
   const __amdgpu_buffer_rsrc_t wq = make_rsrc(a.wq, a.wq_bytes);
   const __amdgpu_buffer_rsrc_t ws = make_rsrc(a.ws, a.ws_bytes);
@@ -74,15 +118,12 @@ __global__ __launch_bounds__(1024) void k_gemv(GemvArgs a) {
     tile[t] = (SWIGLU && t >= TO) ? a.up_tile0 + ot : ot;
   }
 
-  // activation lane role: A row = 8 * slot + token
-  const int a_tok = r & 7;
-  const bool tok_ok = a_tok < a.N;
-  const uint32_t x_lane = (uint32_t)(a_tok * a.K + 8 * s) * 2u;
-  const int G = a.G;
-  auto aload = [&](int ks, int j, bool use) -> bf16x8 {
-    const int g = ks * 4 + j;
-    const uint32_t off = (use && tok_ok && g < G) ? x_lane + (uint32_t)g * 64u : kOOB;
-    return __builtin_bit_cast(bf16x8, ld128(xr, off));
+  // activation lane role: A row r = slot * T + token; the lane's base offset
+  // carries its slot term, tokens >= N start past the buffer
+  const int a_tok = r % T;
+  const uint32_t xbase = (a_tok < a.N ? (uint32_t)(a_tok * a.K + 8 * s) * 2u : kAbsentRow) + lane_slot_term<FMT, S>(lane);
+  auto aload = [&](int g, uint32_t adj) -> bf16x8 {
+    return __builtin_bit_cast(bf16x8, ld128s(xr, xbase + adj, (uint32_t)g * 64u));
   };
 
   f32x4 acc[NT];
@@ -90,31 +131,13 @@ __global__ __launch_bounds__(1024) void k_gemv(GemvArgs a) {
   for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int ks0 = wave * a.ks_per_wave;
   const int ks1 = min(a.KS, ks0 + a.ks_per_wave);
-  kloop<FMT, NT>(wq, ws, tile, a.KS, ks0, ks1, a.hi_offset, aload, acc);
+  kloop<FMT, NT, S, KPS>(wq, ws, tile, a.KS, a.G, ks0, ks1, a.hi_offset, aload, acc);
 
-  // ---- reduction: the two slots (lanes l and l^32), then the waves via LDS
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float o = __shfl_xor(acc[t][i], 32);
-      acc[t][i] += o;
-    }
-  }
-  if (lane < 32) {
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      float* p = red + (((size_t)wave * NT + t) * 32 + lane) * 4;
-      p[0] = acc[t][0];
-      p[1] = acc[t][1];
-      p[2] = acc[t][2];
-      p[3] = acc[t][3];
-    }
-  }
+  reduce_to_lds<S, NT>(acc, red, wave, lane);
   __syncthreads();
 
   float st = 1.0f;
-  if constexpr (FMT == NVFP4) st = *(const float*)(a.ws + a.st_offset);
+  if constexpr (FMT == NVFP4) st = __builtin_bit_cast(float, ld32(ws, a.st_offset));
   const int n_out = TO * 128;
   for (int o = threadIdx.x; o < n_out; o += blockDim.x) {
     const int to = o >> 7, rem = o & 127;
@@ -122,13 +145,12 @@ __global__ __launch_bounds__(1024) void k_gemv(GemvArgs a) {
     const int ot = blockIdx.x * TO + to;
     const int col = ot * 16 + row;
     if (tok >= a.N || ot >= a.out_tiles || col >= a.M) continue;
-    const int l = row + 16 * (tok >> 2), i = tok & 3;
     float v = 0.f;
-    for (int w = 0; w < W; ++w) v += red[(((size_t)w * NT + to) * 32 + l) * 4 + i];
+    for (int w = 0; w < W; ++w) v += red[((size_t)(w * NT + to) * 8 + tok) * 16 + row];
     v *= st;
     if constexpr (SWIGLU) {
       float u = 0.f;
-      for (int w = 0; w < W; ++w) u += red[(((size_t)w * NT + TO + to) * 32 + l) * 4 + i];
+      for (int w = 0; w < W; ++w) u += red[((size_t)(w * NT + TO + to) * 8 + tok) * 16 + row];
       u *= st;
       const float sg = v / (1.0f + expf(-v));
       a.y[(size_t)tok * a.M + col] = sg * u;
@@ -167,7 +189,11 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* wqp, const uint8
     const uint32_t v = j == 0 ? cw.x : j == 1 ? cw.y : j == 2 ? cw.z : cw.w;
     bf16x8 B;
     if (FMT == INT4) B = dec_int4(v);
-    else if (FMT == INT5) B = j == 0 ? dec_int5<0>(v, H) : j == 1 ? dec_int5<1>(v, H) : j == 2 ? dec_int5<2>(v, H) : dec_int5<3>(v, H);
+    else if (FMT == INT5) {
+      bf16x8 B4[4];
+      dec_int5_step(cw, H, B4);
+      B = B4[j];
+    }
     else if (FMT == INT8) {
       const u32x4 q = j < 2 ? cw : cw2;
       B = (j & 1) ? dec_int8(q.z, q.w) : dec_int8(q.x, q.y);
@@ -233,38 +259,69 @@ int map_hip(hipError_t e) { return e == hipSuccess ? QGEMV_OK : QGEMV_EHIP; }
 
 struct LaunchShape {
   int nt;       // tiles per wave (including up tiles for SwiGLU)
-  int waves;    // waves per workgroup
+  int waves;    // waves per workgroup (<= kMaxWaves)
+  int slots;    // S
+  int kpw;      // k-steps per wave (a multiple of the cycle)
+  int kps;      // k-steps per weight prefetch buffer
 };
 
-// Launch shape: enough waves to cover K in a few k-steps each, two output
-// tiles per wave (x reuse across tiles), workgroups = output tiles / 2.
-LaunchShape pick_shape(int64_t KS, bool swiglu) {
+int slots_for(int N) { return N == 1 ? 16 : N == 2 ? 8 : N <= 4 ? 4 : 2; }
+
+// k-steps per cycle for (format, slots): wave ranges are multiples of it
+int cycle_ksteps(int fmt, int S) {
+  const int groups = fmt == NVFP4 ? S / 2 : S;
+  return groups >= 4 ? groups / 4 : 1;
+}
+
+// Launch shape: two 16-row tiles per wave, S slots from N, and K split
+// over W waves so that the grid holds about kTargetWaves waves (measured on
+// MI355X: long-running waves that stream many k-steps beat short ones; small
+// matrices need the K split to fill 256 CUs). Each wave's range is a whole
+// number of cycles.
+constexpr int kMaxWaves = 8;
+constexpr int64_t kTargetWaves = 1100;
+
+LaunchShape pick_shape(int fmt, int64_t KS, int64_t out_tiles, int N, bool swiglu) {
   LaunchShape ls;
-  ls.nt = swiglu ? 4 : 2;
-  int w = (int)((KS + 4) / 5);  // about five k-steps per wave
-  if (w < 1) w = 1;
-  if (w > 16) w = 16;
-  ls.waves = w;
+  ls.nt = 2;
+  ls.kps = 2;
+  ls.slots = slots_for(N);
+  const int cyc = cycle_ksteps(fmt, ls.slots);
+  const int64_t wgs = (out_tiles + (swiglu ? 0 : 1)) / (swiglu ? 1 : 2);
+  int64_t w = (kTargetWaves + wgs / 2) / wgs;
+  w = w < 1 ? 1 : (w > kMaxWaves ? kMaxWaves : w);
+  int64_t kpw = (KS + w - 1) / w;
+  kpw = (kpw + cyc - 1) / cyc * cyc;
+  ls.waves = (int)((KS + kpw - 1) / kpw);
+  ls.kpw = (int)kpw;
   return ls;
+}
+
+template <int FMT, int NT, int S, int KPS>
+hipError_t launch_s(const GemvArgs& a, const LaunchShape& ls, bool swiglu, hipStream_t stream) {
+  const int TO = swiglu ? NT / 2 : NT;
+  const dim3 grid((unsigned)((a.out_tiles + TO - 1) / TO));
+  const dim3 block((unsigned)(64 * ls.waves));
+  const size_t lds = (size_t)ls.waves * NT * 128 * sizeof(float);
+  if (swiglu) hipLaunchKernelGGL((k_gemv<FMT, NT, S, KPS, true>), grid, block, lds, stream, a);
+  else hipLaunchKernelGGL((k_gemv<FMT, NT, S, KPS, false>), grid, block, lds, stream, a);
+  return hipGetLastError();
+}
+
+template <int FMT, int NT, int KPS>
+hipError_t launch_k(const GemvArgs& a, const LaunchShape& ls, bool swiglu, hipStream_t stream) {
+  switch (ls.slots) {
+    case 16: return launch_s<FMT, NT, 16, KPS>(a, ls, swiglu, stream);
+    case 8: return launch_s<FMT, NT, 8, KPS>(a, ls, swiglu, stream);
+    case 4: return launch_s<FMT, NT, 4, KPS>(a, ls, swiglu, stream);
+    default: return launch_s<FMT, NT, 2, KPS>(a, ls, swiglu, stream);
+  }
 }
 
 template <int FMT>
 hipError_t launch_gemv(const GemvArgs& a, const LaunchShape& ls, bool swiglu, hipStream_t stream) {
-  const int TO = swiglu ? ls.nt / 2 : ls.nt;
-  const dim3 grid((unsigned)((a.out_tiles + TO - 1) / TO));
-  const dim3 block((unsigned)(64 * ls.waves));
-  const size_t lds = (size_t)ls.waves * ls.nt * 32 * 4 * sizeof(float);
-  if (swiglu) {
-    if (ls.nt == 4) hipLaunchKernelGGL((k_gemv<FMT, 4, true>), grid, block, lds, stream, a);
-    else if (ls.nt == 2) hipLaunchKernelGGL((k_gemv<FMT, 2, true>), grid, block, lds, stream, a);
-    else return hipErrorInvalidValue;
-  } else {
-    if (ls.nt == 2) hipLaunchKernelGGL((k_gemv<FMT, 2, false>), grid, block, lds, stream, a);
-    else if (ls.nt == 1) hipLaunchKernelGGL((k_gemv<FMT, 1, false>), grid, block, lds, stream, a);
-    else if (ls.nt == 4) hipLaunchKernelGGL((k_gemv<FMT, 4, false>), grid, block, lds, stream, a);
-    else return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  if (ls.kps == 4) return launch_k<FMT, 2, 4>(a, ls, swiglu, stream);
+  return launch_k<FMT, 2, 2>(a, ls, swiglu, stream);
 }
 
 int validate_common(int fmt, const void* wq, const void* ws, const void* x, const void* y, int64_t M, int64_t K,
@@ -277,7 +334,8 @@ int validate_common(int fmt, const void* wq, const void* ws, const void* x, cons
   if (!aligned16(wq) || !aligned16(ws) || !aligned16(x) || !aligned4(y)) return QGEMV_EALIGN;
   if (!geom(fmt, M, K, g)) return QGEMV_EINVAL;
   if (g->wq_bytes >= (1ull << 32) || g->ws_bytes >= (1ull << 32)) return QGEMV_EUNSUPPORTED;
-  if ((uint64_t)N * (uint64_t)K * 2ull >= (1ull << 31)) return QGEMV_EUNSUPPORTED;
+  if ((uint64_t)N * (uint64_t)K * 2ull >= (1ull << 25)) return QGEMV_EUNSUPPORTED;  // activation bytes < 2^25
+  if (g->wq_bytes >= (1ull << 31) || g->ws_bytes >= (1ull << 31)) return QGEMV_EUNSUPPORTED;
   return QGEMV_OK;
 }
 
@@ -305,8 +363,8 @@ int run_gemv(int fmt, const void* wq, const void* ws, const void* x, const float
   a.N = N;
   a.out_tiles = (int)((Mout + 15) / 16);
   a.up_tile0 = swiglu ? (int)(Mout / 16) : 0;
-  const LaunchShape ls = pick_shape(g.KS, swiglu);
-  a.ks_per_wave = (int)((g.KS + ls.waves - 1) / ls.waves);
+  const LaunchShape ls = pick_shape(fmt, g.KS, a.out_tiles, N, swiglu);
+  a.ks_per_wave = ls.kpw;
   hipError_t e;
   switch (fmt) {
     case INT4: e = launch_gemv<INT4>(a, ls, swiglu, stream); break;

@@ -1,134 +1,327 @@
 // The weight-streaming inner loop shared by the dense and MoE kernels.
 //
 // One wave owns NT row tiles (16 weight rows each) and a range of k-steps
-// (128 columns = 4 scale groups). Per k-step and tile it issues one 16-byte
-// non-temporal load per lane for the codes (int8: two), plus the scale
-// record (and the int5 hi-bit word), decodes each group into the B operand of
-// a 16x16x32 bf16 MFMA and accumulates in fp32 per tile.
+// (128 columns = 4 groups of 32). Per k-step and tile it issues one 16-byte
+// non-temporal buffer load per lane for the codes (int8: two, int5: plus one
+// dword), decodes each 32-column group into the B operand of a 16x16x32 bf16
+// MFMA and accumulates in fp32. Loads for later k-steps are issued before the
+// decode and MFMAs of k-step i: weights in two buffers of KPS k-steps, so a
+// wave keeps KPS k-steps of weights in flight while it computes, and
+// activations one k-step ahead. Wave-uniform offsets travel in SGPRs (buffer
+// soffset); the per-lane offsets are loop constants.
 //
-// A operand rows are (slot, token) = 8 * slot + token. The caller's ALoad
-// functor returns this lane's 8 activations of a group (bf16x8) and must
-// return zeros when `use` is false; the slot roles are:
-//   int formats: group j of a k-step lives in slot j & 1, so one accumulator
-//     holds two groups apart and the scale step runs per pair of groups;
-//   nvfp4: the two 16-column blocks of a group live in slots 0 and 1
-//     (lanes with s = lane/16 in {0,1} hold block 0, {2,3} block 1).
+// Slots. A operand row m (0..15) = slot * T + token with T = 16 / S tokens per
+// slot. Consecutive scale units (int: 32-column groups; nvfp4: 16-column
+// blocks) go to consecutive slots, so one accumulator keeps S units apart and
+// the per-unit scale step runs once per S units ("cycle") instead of once per
+// unit. S = 16 at N = 1, 8 at N = 2, 4 at N <= 4, 2 at N <= 8. A lane whose
+// row is not in a unit's slot gets its offset moved by the slot difference
+// times 2^25 (activations stay below 2^25 bytes), so the buffer range check
+// returns zeros without a memory access. Rows of absent tokens start at
+// 2^30, and k-steps past the range or groups past K add 2^31: in every case
+// the offset lands at least 2^25 away from [0, 2^25).
+//
+// Int group scale: B = bf16(128 + q); with D = sum x (128 + q) and
+// Db = 128 sum x (an MFMA against a constant-128 operand shared by all
+// tiles), d * sum(x q) + m * sum(x) = d * D + (m / 128 - d) * Db.
+//
 // After the loop, lane l's acc[t][i] is the partial sum of A row 4*(l/16) + i
-// for weight row 16*tile + (l % 16) (NVFP4 without the tensor scale).
+// for weight row 16*tile[t] + (l % 16) (nvfp4: without the tensor scale).
 #pragma once
 #include "device.hpp"
 #include "layout.hpp"
 
 namespace qg {
 
-template <int FMT>
-__device__ __forceinline__ void group_pair_scale(f32x4& acc, const f32x4& D, const f32x4& Db, uint32_t sc) {
-  if constexpr (FMT == INT8) {
-    const float d = f16_lo(sc);
+constexpr uint32_t kSlotStride = 1u << 25;   // offset step per slot mismatch
+constexpr uint32_t kAbsentRow = 1u << 30;    // lane base of an A row with no token
+
+// ---- compile-time geometry of a (format, slots) pair
+template <int FMT, int S>
+struct Cyc {
+  static constexpr int T = 16 / S;                          // tokens per slot
+  static constexpr int UNITS_PER_GROUP = FMT == NVFP4 ? 2 : 1;
+  static constexpr int GROUPS = S / UNITS_PER_GROUP;        // groups per cycle (>= 1)
+  static constexpr int KSTEPS = GROUPS >= 4 ? GROUPS / 4 : 1;   // k-steps per cycle
+  static constexpr int UNROLL = KSTEPS >= 2 ? KSTEPS : 2;   // k-steps per loop trip (even)
+};
+
+// Slot of A rows that group j of k-step kk (counted from the cycle start)
+// feeds; for nvfp4 the lane's block half is folded into the lane base.
+template <int FMT, int S>
+__host__ __device__ constexpr int slot_pos(int kk, int j) {
+  return FMT == NVFP4 ? (8 * kk + 2 * j) % S : (4 * kk + j) % S;
+}
+
+// Per-lane A base offset term: (slot of this lane's row, nvfp4 minus its
+// block half) * 2^25; the loader adds the row offset and subtracts
+// slot_pos * 2^25, so only lanes of the unit's slot stay in range.
+template <int FMT, int S>
+__device__ __forceinline__ uint32_t lane_slot_term(int lane) {
+  const int r = lane & 15, s = lane >> 4;
+  const int sigma = r / Cyc<FMT, S>::T - (FMT == NVFP4 ? (s >> 1) : 0);
+  return (uint32_t)sigma * kSlotStride;
+}
+
+// ---- packed weights of KPS consecutive k-steps (all tiles)
+template <int FMT, int NT, int KPS>
+struct Step {
+  u32x4 q[KPS][NT];      // codes: int4/nvfp4 dword j = group j; int5 dwords D0..D3; int8 groups 0,1
+  u32x4 q2[KPS][NT];     // int8 groups 2,3
+  uint32_t h[KPS][NT];   // int5 dword D4
+  u32x4 sc[KPS][NT];     // scale words (cycles of at most one k-step)
+};
+
+// Scale words of one tile for the cycle whose first k-step is tile record
+// tau0 (int formats: 16 B (int4/5) or 8 B (int8) records per row and k-step;
+// nvfp4: 8 B of E4M3 block scales per row and k-step). krem: k-steps of the
+// wave's range left from the cycle start; records past it read as zero.
+// tau0 stays below 2^31 / 256 (validated), so offsets never wrap.
+template <int FMT, int S>
+__device__ __forceinline__ u32x4 load_scales(__amdgpu_buffer_rsrc_t ws, uint32_t tau0, int lane, int krem) {
+  const int r = lane & 15, s = lane >> 4;
+  u32x4 v = {0u, 0u, 0u, 0u};
+  constexpr bool REC_S = FMT != NVFP4 && S == 16;                                   // record k-step s
+  constexpr bool REC_S2 = (FMT != NVFP4 && S == 8) || (FMT == NVFP4 && S == 16);     // record k-step s >> 1
+  const int rec = REC_S ? s : (REC_S2 ? (s >> 1) : 0);
+  const uint32_t mask = rec < krem ? 0u : 0x80000000u;
+  if constexpr (FMT == INT4 || FMT == INT5) {
+    const uint32_t so = tau0 * 256u;
+    const uint32_t row = (uint32_t)r * 16u | mask;
+    if constexpr (S == 16) {          // groups 16c + 4s + i: record of k-step 4c + s, all four
+      v = ld128s(ws, row + (uint32_t)s * 256u, so);
+    } else if constexpr (S == 8) {    // groups 8c + 2s + (i>>1): record 2c + (s>>1), j = 2(s&1) + (i>>1)
+      const uint32_t b = row + (uint32_t)(s >> 1) * 256u;
+      v.x = ld32s(ws, b + 4u * (uint32_t)(s & 1), so);          // pos(j) = s & 1 for i < 2
+      v.y = ld32s(ws, b + 4u * (uint32_t)(2 + (s & 1)), so);    // pos(j) = 2 + (s & 1)
+    } else if constexpr (S == 4) {    // group 4c + s: j = s
+      v.x = ld32s(ws, row + 4u * (uint32_t)(2 * (s & 1) + (s >> 1)), so);
+    } else {                          // S = 2: groups 2c + (s>>1), c = 0, 1: positions 2(s>>1) + c
+      const u32x2 t = ld64s(ws, row + 8u * (uint32_t)(s >> 1), so);
+      v.x = t.x;
+      v.y = t.y;
+    }
+  } else if constexpr (FMT == INT8) {
+    const uint32_t so = tau0 * 128u;
+    const uint32_t row = (uint32_t)r * 8u | mask;
+    if constexpr (S == 16) {
+      const u32x2 t = ld64s(ws, row + (uint32_t)s * 128u, so);
+      v.x = t.x;
+      v.y = t.y;
+    } else if constexpr (S == 8) {
+      const u32x2 t = ld64s(ws, row + (uint32_t)(s >> 1) * 128u, so);
+      const uint32_t sh = 16u * (uint32_t)(s & 1);
+      v.x = t.x >> sh;   // pos s&1      -> low half
+      v.y = t.y >> sh;   // pos 2 + s&1  -> low half
+    } else if constexpr (S == 4) {
+      v.x = ld16s(ws, row + 2u * (uint32_t)(2 * (s & 1) + (s >> 1)), so);
+    } else {
+      v.x = ld32s(ws, row + 4u * (uint32_t)(s >> 1), so);
+    }
+  } else {  // NVFP4: byte 4h + j of the row record holds block 8ks + 2j + h
+    const uint32_t so = tau0 * 128u;
+    const uint32_t row = (uint32_t)r * 8u | mask;
+    if constexpr (S == 16) {          // blocks 16c + 4s + i: record 2c + (s>>1)
+      const u32x2 t = ld64s(ws, row + (uint32_t)(s >> 1) * 128u, so);
+      const uint32_t sh = 16u * (uint32_t)(s & 1);
+      v.x = t.x >> sh;   // i = 0: byte 0, i = 2: byte 1 (h = 0)
+      v.y = t.y >> sh;   // i = 1: byte 0, i = 3: byte 1 (h = 1)
+    } else if constexpr (S == 8) {    // block 2s + (i>>1) of the k-step: j = s, h = i >> 1
+      const u32x2 t = ld64s(ws, row, so);
+      const uint32_t sh = 8u * (uint32_t)s;
+      v.x = t.x >> sh;
+      v.y = t.y >> sh;
+    } else if constexpr (S == 4) {    // block 4c + s: j = 2c + (s>>1), h = s & 1
+      v.x = ld32s(ws, row + 4u * (uint32_t)(s & 1), so) >> (8u * (uint32_t)(s >> 1));
+    } else {                          // S = 2: block 2j + (s>>1)
+      v.x = ld32s(ws, row + 4u * (uint32_t)(s >> 1), so);
+    }
+  }
+  return v;
+}
+
+// ---- int5: 16 pair-words (bf16x2 of 128 + q) from the lane's five dwords
+__device__ __forceinline__ void dec_int5_step(const u32x4& q, uint32_t d4, bf16x8 (&B)[4]) {
+  const uint32_t D[5] = {q.x, q.y, q.z, q.w, d4};
+  uint32_t P[16];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = fmaf(d, D[i], acc[i]);
-  } else {
-    // D = sum x (128 + q), Db = 128 sum x:  d*sum(x q) + m*sum(x) = d*D + (m/128 - d)*Db
-    const float d = f16_lo(sc), m = f16_hi(sc);
-    const float c = fmaf(m, 0.0078125f, -d);
+  for (int i = 0; i < 5; ++i) {
+    P[3 * i + 0] = and_or(D[i], 0x001F001Fu, 0x43004300u);
+    P[3 * i + 1] = and_or(D[i] >> 5, 0x001F001Fu, 0x43004300u);
+    P[3 * i + 2] = and_or(D[i] >> 10, 0x001F001Fu, 0x43004300u);
+  }
+  uint32_t p15 = 0x43004300u;
+#pragma unroll
+  for (int b = 0; b < 5; ++b) p15 = and_or(D[b] >> (15 - b), 0x00010001u << b, p15);
+  P[15] = p15;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const u32x4 v = {P[4 * j], P[4 * j + 1], P[4 * j + 2], P[4 * j + 3]};
+    B[j] = __builtin_bit_cast(bf16x8, v);
+  }
+}
+
+// ---- scale step at the end of a cycle ------------------------------------
+// c: cycle index inside the k-step when a k-step holds several cycles.
+template <int FMT, int S>
+__device__ __forceinline__ void flush(f32x4& acc, const f32x4& D, const f32x4& Db, const u32x4& sc, int c) {
+  if constexpr (FMT == INT4 || FMT == INT5) {
+    uint32_t w[4];
+    if constexpr (S == 16) { w[0] = sc.x; w[1] = sc.z; w[2] = sc.y; w[3] = sc.w; }      // pos(i)
+    else if constexpr (S == 8) { w[0] = w[1] = sc.x; w[2] = w[3] = sc.y; }
+    else if constexpr (S == 4) { w[0] = w[1] = w[2] = w[3] = sc.x; }
+    else { w[0] = w[1] = w[2] = w[3] = (c == 0 ? sc.x : sc.y); }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      const float d = f16_lo(w[i]), m = f16_hi(w[i]);
+      const float cc = fmaf(m, 0.0078125f, -d);
       acc[i] = fmaf(d, D[i], acc[i]);
-      acc[i] = fmaf(c, Db[i], acc[i]);
+      acc[i] = fmaf(cc, Db[i], acc[i]);
+    }
+  } else if constexpr (FMT == INT8) {
+    float d[4];
+    if constexpr (S == 16) { d[0] = f16_lo(sc.x); d[1] = f16_lo(sc.y); d[2] = f16_hi(sc.x); d[3] = f16_hi(sc.y); }
+    else if constexpr (S == 8) { d[0] = d[1] = f16_lo(sc.x); d[2] = d[3] = f16_lo(sc.y); }
+    else if constexpr (S == 4) { d[0] = d[1] = d[2] = d[3] = f16_lo(sc.x); }
+    else { d[0] = d[1] = d[2] = d[3] = (c == 0 ? f16_lo(sc.x) : f16_hi(sc.x)); }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = fmaf(d[i], D[i], acc[i]);
+  } else {
+    float b[4];
+    if constexpr (S == 16) {
+      b[0] = e4m3_byte<0>(sc.x); b[1] = e4m3_byte<0>(sc.y); b[2] = e4m3_byte<1>(sc.x); b[3] = e4m3_byte<1>(sc.y);
+    } else if constexpr (S == 8) {
+      b[0] = b[1] = e4m3_byte<0>(sc.x); b[2] = b[3] = e4m3_byte<0>(sc.y);
+    } else if constexpr (S == 4) {
+      b[0] = b[1] = b[2] = b[3] = (c == 0 ? e4m3_byte<0>(sc.x) : e4m3_byte<2>(sc.x));
+    } else {
+      const float v = c == 0 ? e4m3_byte<0>(sc.x) : c == 1 ? e4m3_byte<1>(sc.x) : c == 2 ? e4m3_byte<2>(sc.x)
+                                                                                         : e4m3_byte<3>(sc.x);
+      b[0] = b[1] = b[2] = b[3] = v;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = fmaf(b[i], D[i], acc[i]);
+  }
+}
+
+// Loads the packed weights of KPS k-steps starting at ks (wave-uniform) into
+// st. K-steps at or past ks1 read as zeros (out-of-range offsets, no memory
+// traffic).
+template <int FMT, int NT, int S, int KPS>
+__device__ __forceinline__ void load_weights(Step<FMT, NT, KPS>& st, __amdgpu_buffer_rsrc_t wq,
+                                             __amdgpu_buffer_rsrc_t ws, const int (&tile)[NT], int KS, int ks,
+                                             int ks1, uint32_t hi_offset) {
+  const int lane = threadIdx.x & 63;
+  constexpr int TB = FMT == INT8 ? 2048 : 1024;
+#pragma unroll
+  for (int i = 0; i < KPS; ++i) {
+    const int k = ks + i;
+    const bool ok = k < ks1;
+    const uint32_t bad = ok ? 0u : 0x80000000u;
+    const uint32_t lo = (uint32_t)lane * 16u | bad;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const uint32_t tau = (uint32_t)tile[t] * (uint32_t)KS + (uint32_t)k;
+      st.q[i][t] = ld128s_nt(wq, lo, tau * TB);
+      if constexpr (FMT == INT8) st.q2[i][t] = ld128s_nt(wq, lo, tau * TB + 1024u);
+      if constexpr (FMT == INT5) st.h[i][t] = ld32s_nt(wq, (uint32_t)lane * 4u | bad, hi_offset + tau * 256u);
+      if constexpr (Cyc<FMT, S>::KSTEPS == 1) st.sc[i][t] = load_scales<FMT, S>(ws, tau, lane, ok ? 1 : 0);
     }
   }
 }
 
-// true when this lane's A row takes part in group j (see header comment)
-template <int FMT>
-__device__ __forceinline__ bool a_slot_uses(int a_slot, int s, int j) {
-  return FMT == NVFP4 ? (a_slot == (s >> 1)) : (a_slot == (j & 1));
+// Activations of the 4 groups of k-step k (zeros past ks1 or past G).
+// aload(g, adj): this lane's 8 activations of group g with the uniform offset
+// adjustment adj added to its lane base. ckk: k-step position in its cycle.
+template <int FMT, int S, class ALoad>
+__device__ __forceinline__ void load_acts(bf16x8 (&A)[4], int k, int ks1, int G, int ckk, const ALoad& aload) {
+  const bool ok = k < ks1;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int g = k * 4 + j;
+    const uint32_t adj = 0u - (uint32_t)slot_pos<FMT, S>(ckk, j) * kSlotStride + ((ok && g < G) ? 0u : 0x80000000u);
+    A[j] = aload(g, adj);
+  }
 }
 
-template <int FMT, int NT, class ALoad>
+// KPS: k-steps per weight buffer; weights run one buffer ahead of the
+// compute, activations one k-step ahead.
+template <int FMT, int NT, int S, int KPS, class ALoad>
 __device__ __forceinline__ void kloop(__amdgpu_buffer_rsrc_t wq, __amdgpu_buffer_rsrc_t ws, const int (&tile)[NT],
-                                      int KS, int ks0, int ks1, uint32_t hi_offset, const ALoad& aload,
+                                      int KS, int G, int ks0, int ks1, uint32_t hi_offset, const ALoad& aload,
                                       f32x4 (&acc)[NT]) {
-  const int lane = threadIdx.x & 63;
-  const int r = lane & 15, s = lane >> 4;
-  const int a_slot = r >> 3;
+  using C = Cyc<FMT, S>;
+  constexpr int U = 2 * KPS;                     // k-steps per loop trip (a multiple of C::KSTEPS)
+  static_assert(U % C::KSTEPS == 0, "cycle must divide the trip");
   const bf16x8 b128 = bf16x8_splat_128();
+  Step<FMT, NT, KPS> buf[2];
+  bf16x8 xa[2][4];
+  u32x4 csc[NT];                                 // scale words of the current cycle (KSTEPS > 1)
+  f32x4 D[NT];
+  f32x4 Db = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    D[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    csc[t] = u32x4{0u, 0u, 0u, 0u};
+  }
+  if (ks0 >= ks1) return;
 
-  for (int ks = ks0; ks < ks1; ++ks) {
-    u32x4 cw[NT], cw2[NT];
-    uint32_t hw[NT], sc32[NT];
-    u32x2 sc64[NT];
+  load_weights<FMT, NT, S, KPS>(buf[0], wq, ws, tile, KS, ks0, ks1, hi_offset);
+  load_acts<FMT, S>(xa[0], ks0, ks1, G, 0, aload);
+  for (int base = ks0; base < ks1; base += U) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const uint32_t tau = (uint32_t)tile[t] * (uint32_t)KS + (uint32_t)ks;
-      if constexpr (FMT == INT8) {
-        cw[t] = ld128_nt(wq, tau * 2048u + (uint32_t)lane * 16u);
-        cw2[t] = ld128_nt(wq, tau * 2048u + 1024u + (uint32_t)lane * 16u);
-        sc32[t] = ld32(ws, tau * 128u + (uint32_t)r * 8u + 4u * (uint32_t)(s >> 1));
-      } else if constexpr (FMT == NVFP4) {
-        cw[t] = ld128_nt(wq, tau * 1024u + (uint32_t)lane * 16u);
-        sc32[t] = ld32(ws, tau * 128u + (uint32_t)r * 8u + 4u * (uint32_t)(s >> 1));
-      } else {
-        cw[t] = ld128_nt(wq, tau * 1024u + (uint32_t)lane * 16u);
-        if constexpr (FMT == INT5)
-          hw[t] = __builtin_amdgcn_raw_buffer_load_b32(wq, hi_offset + tau * 256u + (uint32_t)lane * 4u, 0,
-                                                       kNonTemporal);
-        sc64[t] = ld64(ws, tau * 256u + (uint32_t)r * 16u + 8u * (uint32_t)(s >> 1));
-      }
-    }
-    bf16x8 A[4];
+    for (int b = 0; b < 2; ++b) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) A[j] = aload(ks, j, a_slot_uses<FMT>(a_slot, s, j));
-
-    if constexpr (FMT == NVFP4) {
+      for (int i = 0; i < KPS; ++i) {
+        const int kk = b * KPS + i;                // k-step index in the trip
+        const int ks = base + kk;
+        const int ckk = kk % C::KSTEPS;            // k-step position inside its cycle
+        if (i == 0)                                // next weight buffer
+          load_weights<FMT, NT, S, KPS>(buf[b ^ 1], wq, ws, tile, KS, base + (b + 1) * KPS, ks1, hi_offset);
+        load_acts<FMT, S>(xa[(kk + 1) & 1], ks + 1, ks1, G, (kk + 1) % C::KSTEPS, aload);
+        if constexpr (C::KSTEPS > 1) {
+          if (ckk == 0) {                          // cycle start: its scale words, used KSTEPS k-steps later
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
+            for (int t = 0; t < NT; ++t)
+              csc[t] = load_scales<FMT, S>(ws, (uint32_t)tile[t] * (uint32_t)KS + (uint32_t)ks, threadIdx.x & 63,
+                                           ks1 - ks);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        const Step<FMT, NT, KPS>& cur = buf[b];
+        bf16x8 B5[NT][4];
+        if constexpr (FMT == INT5) {
+#pragma unroll
+          for (int t = 0; t < NT; ++t) dec_int5_step(cur.q[i][t], cur.h[i][t], B5[t]);
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const uint32_t v = j == 0 ? cw[t].x : j == 1 ? cw[t].y : j == 2 ? cw[t].z : cw[t].w;
-          const f32x4 D = mfma(A[j], dec_nvfp4(v), f32x4{0.f, 0.f, 0.f, 0.f});
-          float sc;
-          if (j == 0) sc = e4m3_byte<0>(sc32[t]);
-          else if (j == 1) sc = e4m3_byte<1>(sc32[t]);
-          else if (j == 2) sc = e4m3_byte<2>(sc32[t]);
-          else sc = e4m3_byte<3>(sc32[t]);
+          const int gpos = 4 * ckk + j;            // group position in the cycle
+          const bool first = (gpos % C::GROUPS) == 0;
+          const bool last = ((gpos + 1) % C::GROUPS) == 0;
+          const int cidx = gpos / C::GROUPS;       // cycle index inside the k-step
+          const bf16x8 A = xa[kk & 1][j];
+          if constexpr (FMT == INT4 || FMT == INT5) Db = mfma(A, b128, first ? f32x4{0.f, 0.f, 0.f, 0.f} : Db);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[t][i] = fmaf(sc, D[i], acc[t][i]);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        f32x4 Db = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (FMT != INT8) {
-          Db = mfma(A[2 * c], b128, Db);
-          Db = mfma(A[2 * c + 1], b128, Db);
-        }
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          bf16x8 B0, B1;
-          if constexpr (FMT == INT4) {
-            B0 = dec_int4(c == 0 ? cw[t].x : cw[t].z);
-            B1 = dec_int4(c == 0 ? cw[t].y : cw[t].w);
-          } else if constexpr (FMT == INT5) {
-            if (c == 0) {
-              B0 = dec_int5<0>(cw[t].x, hw[t]);
-              B1 = dec_int5<1>(cw[t].y, hw[t]);
+          for (int t = 0; t < NT; ++t) {
+            bf16x8 B;
+            const u32x4 q = cur.q[i][t];
+            if constexpr (FMT == INT4) {
+              B = dec_int4(j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w);
+            } else if constexpr (FMT == INT5) {
+              B = B5[t][j];
+            } else if constexpr (FMT == INT8) {
+              const u32x4 qq = j < 2 ? q : cur.q2[i][t];
+              B = (j & 1) ? dec_int8(qq.z, qq.w) : dec_int8(qq.x, qq.y);
             } else {
-              B0 = dec_int5<2>(cw[t].z, hw[t]);
-              B1 = dec_int5<3>(cw[t].w, hw[t]);
+              B = dec_nvfp4(j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w);
             }
-          } else {  // INT8: groups 0,1 in the first 1 KiB, 2,3 in the second
-            const u32x4 q = c == 0 ? cw[t] : cw2[t];
-            B0 = dec_int8(q.x, q.y);
-            B1 = dec_int8(q.z, q.w);
+            D[t] = mfma(A, B, first ? f32x4{0.f, 0.f, 0.f, 0.f} : D[t]);
+            if (last) {
+              if constexpr (C::KSTEPS > 1) flush<FMT, S>(acc[t], D[t], Db, csc[t], cidx);
+              else flush<FMT, S>(acc[t], D[t], Db, cur.sc[i][t], cidx);
+            }
           }
-          f32x4 D = mfma(A[2 * c], B0, f32x4{0.f, 0.f, 0.f, 0.f});
-          D = mfma(A[2 * c + 1], B1, D);
-          uint32_t sc;
-          if constexpr (FMT == INT8) sc = c == 0 ? (sc32[t] & 0xFFFFu) : (sc32[t] >> 16);
-          else sc = c == 0 ? sc64[t].x : sc64[t].y;
-          group_pair_scale<FMT>(acc[t], D, Db, sc);
         }
       }
     }

@@ -13,9 +13,10 @@
 //      number of active experts exits at once. Each workgroup gathers the
 //      rows of x routed to its expert (8 per MFMA pass) and writes h [pair][I]
 //      in fp32.
-//   3. down: same grid shape over H; the fp32 h rows enter the bf16 MFMA as a
-//      hi + lo pair (h = hi + lo + O(2^-16 |h|)), so the A operand holds
-//      4 pairs x {hi, lo} x 2 slots; writes o [pair][H] in fp32.
+//   3. down: same grid shape over H. h leaves step 2 as a pair of bf16 planes
+//      hi = bf16(h), lo = bf16(h - hi) (h = hi + lo + O(2^-16 |h|), the same
+//      bytes as fp32), so the A operand holds 4 pairs x {hi, lo} x 2 slots;
+//      writes o [pair][H] in fp32.
 //   4. combine: y[t] = r[t] + sum_j p[t][j] o[t*k + j] in increasing j order;
 //      no atomics, so results are bitwise reproducible (RustingStrata page,
 //      known issues: run-to-run reordering changes results).
@@ -128,9 +129,9 @@ struct MoeArgs {
   uint64_t wq_stride, ws_stride;   // bytes between experts
   uint32_t wq_bytes, ws_bytes;     // one expert's packed sizes
   uint32_t hi_offset, st_offset;
-  const void* in;                  // gate/up: x bf16 [N][K]; down: h fp32 [NK][K]
+  const void* in;                  // gate/up: x bf16 [N][K]; down: h as bf16 hi and lo planes [2][NK][K]
   uint32_t in_bytes;
-  float* out;                      // gate/up: h [NK][Mout]; down: o [NK][Mout]
+  float* out;                      // gate/up: h planes (bf16) [2][NK][Mout]; down: o fp32 [NK][Mout]
   const int32_t* idx;              // workspace index region
   int E, top_k, NK;
   int Mout, K, KS, G;
@@ -147,7 +148,7 @@ __device__ __forceinline__ void split_bf16(float v, __bf16& hi, __bf16& lo) {
 // DOWN = false: gate/up + SwiGLU (NT = 2*TO tiles: gate then up)
 // DOWN = true:  down projection (NT = TO tiles)
 template <int FMT, int NT, bool DOWN>
-__global__ __launch_bounds__(1024) void k_moe_gemv(MoeArgs a) {
+__global__ __launch_bounds__(512) void k_moe_gemv(MoeArgs a) {
   extern __shared__ float red[];  // [W][NT][32][4]
   constexpr int TO = DOWN ? NT : NT / 2;
   constexpr int ROWS = DOWN ? 4 : 8;   // routed rows per MFMA pass
@@ -161,7 +162,7 @@ __global__ __launch_bounds__(1024) void k_moe_gemv(MoeArgs a) {
   const int32_t* pairs = a.idx + ix.pairs() + p0;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = uniform(threadIdx.x >> 6);
   const int W = blockDim.x >> 6;
   const int r = lane & 15, s = lane >> 4;
 
@@ -190,34 +191,21 @@ __global__ __launch_bounds__(1024) void k_moe_gemv(MoeArgs a) {
     f32x4 acc[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const uint32_t slot_term = lane_slot_term<FMT, 2>(lane);
     if constexpr (!DOWN) {
-      const uint32_t base = (uint32_t)((pflat / a.top_k) * a.K + 8 * s) * 2u;
-      auto aload = [&](int ks, int j, bool use) -> bf16x8 {
-        const int g = ks * 4 + j;
-        const uint32_t off = (use && row_ok && g < a.G) ? base + (uint32_t)g * 64u : kOOB;
-        return __builtin_bit_cast(bf16x8, ld128(inr, off));
+      const uint32_t base = (row_ok ? (uint32_t)((pflat / a.top_k) * a.K + 8 * s) * 2u : kAbsentRow) + slot_term;
+      auto aload = [&](int g, uint32_t adj) -> bf16x8 {
+        return __builtin_bit_cast(bf16x8, ld128s(inr, base + adj, (uint32_t)g * 64u));
       };
-      kloop<FMT, NT>(wq, ws, tile, a.KS, ks0, ks1, a.hi_offset, aload, acc);
+      kloop<FMT, NT, 2, 2>(wq, ws, tile, a.KS, a.G, ks0, ks1, a.hi_offset, aload, acc);
     } else {
-      const bool lo_part = (r >> 2) & 1;
-      const uint32_t base = (uint32_t)(pflat * a.K + 8 * s) * 4u;
-      auto aload = [&](int ks, int j, bool use) -> bf16x8 {
-        const int g = ks * 4 + j;
-        const bool on = use && row_ok && g < a.G;
-        const uint32_t off = on ? base + (uint32_t)g * 128u : kOOB;
-        const u32x4 v0 = ld128(inr, off);
-        const u32x4 v1 = ld128(inr, on ? off + 16u : kOOB);
-        bf16x8 out;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const uint32_t bits = q < 4 ? v0[q] : v1[q - 4];
-          __bf16 hi, lo;
-          split_bf16(__builtin_bit_cast(float, bits), hi, lo);
-          out[q] = lo_part ? lo : hi;
-        }
-        return out;
+      // A rows 8*slot + 4*part + pair: part 0 reads the hi plane of h, part 1 the lo plane
+      const int part = (r >> 2) & 1;
+      const uint32_t base = (row_ok ? (uint32_t)((part * a.NK + pflat) * a.K + 8 * s) * 2u : kAbsentRow) + slot_term;
+      auto aload = [&](int g, uint32_t adj) -> bf16x8 {
+        return __builtin_bit_cast(bf16x8, ld128s(inr, base + adj, (uint32_t)g * 64u));
       };
-      kloop<FMT, NT>(wq, ws, tile, a.KS, ks0, ks1, a.hi_offset, aload, acc);
+      kloop<FMT, NT, 2, 2>(wq, ws, tile, a.KS, a.G, ks0, ks1, a.hi_offset, aload, acc);
     }
     // reduce: slots (lane ^ 32); for DOWN also hi/lo parts (lane ^ 16)
 #pragma unroll
@@ -258,7 +246,12 @@ __global__ __launch_bounds__(1024) void k_moe_gemv(MoeArgs a) {
         float u = 0.f;
         for (int w = 0; w < W; ++w) u += red[(((size_t)w * NT + TO + to) * 32 + l) * 4 + i];
         u *= st;
-        a.out[(size_t)pf * a.Mout + col] = v / (1.0f + expf(-v)) * u;
+        const float hv = v / (1.0f + expf(-v)) * u;
+        __bf16 hi, lo;
+        split_bf16(hv, hi, lo);
+        __bf16* hs = (__bf16*)a.out;             // hi plane [NK][I], then lo plane
+        hs[(size_t)pf * a.Mout + col] = hi;
+        hs[((size_t)a.NK + pf) * a.Mout + col] = lo;
       }
     }
     __syncthreads();
@@ -314,7 +307,7 @@ void launch_moe(const MoeArgs& a, int waves, int slots, hipStream_t stream) {
 
 template <int FMT>
 void launch_moe_pair(const MoeArgs& gu, const MoeArgs& dn, int wgu, int wdn, int slots, hipStream_t stream) {
-  launch_moe<FMT, 4, false>(gu, wgu, slots, stream);
+  launch_moe<FMT, 2, false>(gu, wgu, slots, stream);
   launch_moe<FMT, 2, true>(dn, wdn, slots, stream);
 }
 
@@ -357,6 +350,9 @@ extern "C" int qgemv_moe(int fmt, const void* wq_gu, const void* ws_gu, const vo
   Geom ggu, gdn;
   if (!geom(fmt, 2 * I, H, &ggu) || !geom(fmt, H, I, &gdn)) return QGEMV_EINVAL;
   if ((uint64_t)E * up256(ggu.wq_bytes) >= (1ull << 40)) return QGEMV_EUNSUPPORTED;
+  // activation bytes stay below 2^25 (x: N*H bf16; h: N*top_k*I fp32)
+  if ((uint64_t)N * H * 2 >= (1ull << 25) || (uint64_t)N * top_k * I * 4 >= (1ull << 25)) return QGEMV_EUNSUPPORTED;
+  if (ggu.wq_bytes >= (1ull << 31) || gdn.wq_bytes >= (1ull << 31)) return QGEMV_EUNSUPPORTED;
   if (ggu.wq_bytes >= (1ull << 32) || gdn.wq_bytes >= (1ull << 32)) return QGEMV_EUNSUPPORTED;
   const int NK = N * top_k;
   uint8_t* wsp = (uint8_t*)workspace;
@@ -389,7 +385,7 @@ extern "C" int qgemv_moe(int fmt, const void* wq_gu, const void* ws_gu, const vo
   gu.G = (int)(H / 32);
   gu.out_tiles = (int)((I + 15) / 16);
   gu.up_tile0 = (int)(I / 16);
-  const int wgu = (int)std::min<int64_t>(16, std::max<int64_t>(1, (ggu.KS + 3) / 4));
+  const int wgu = (int)std::min<int64_t>(8, std::max<int64_t>(1, (ggu.KS + 3) / 4));  // ~4 k-steps per wave
   gu.ks_per_wave = (int)((ggu.KS + wgu - 1) / wgu);
 
   MoeArgs dn = gu;
@@ -402,7 +398,7 @@ extern "C" int qgemv_moe(int fmt, const void* wq_gu, const void* ws_gu, const vo
   dn.hi_offset = (uint32_t)gdn.hi_offset;
   dn.st_offset = (uint32_t)gdn.st_offset;
   dn.in = h;
-  dn.in_bytes = (uint32_t)((size_t)NK * I * 4);
+  dn.in_bytes = (uint32_t)((size_t)NK * I * 4);   // two bf16 planes
   dn.out = o;
   dn.Mout = (int)H;
   dn.K = (int)I;
@@ -410,7 +406,7 @@ extern "C" int qgemv_moe(int fmt, const void* wq_gu, const void* ws_gu, const vo
   dn.G = (int)(I / 32);
   dn.out_tiles = (int)((H + 15) / 16);
   dn.up_tile0 = 0;
-  const int wdn = (int)std::min<int64_t>(16, std::max<int64_t>(1, (gdn.KS + 2) / 3));
+  const int wdn = (int)std::min<int64_t>(8, std::max<int64_t>(1, (gdn.KS + 3) / 4));
   dn.ks_per_wave = (int)((gdn.KS + wdn - 1) / wdn);
 
   if (I % 16) return QGEMV_EALIGN;

@@ -115,6 +115,16 @@ struct Dest {
       wq[tau * 2048 + (j >> 1) * 1024 + lane * 16 + (j & 1) * 8 + e] = (uint8_t)(int8_t)c;
       return;
     }
+    if (fmt == qg::INT5) {  // 5-bit fields, three pairs per dword; pair 15 spread over bit 15/31
+      const int64_t P = 4 * j + (e >> 1), h = e & 1;
+      if (P < 15) {
+        or_dword(int5_dword(tau, lane, (int)(P / 3)), (uint32_t)(c & 31) << (16 * h + 5 * (P % 3)));
+      } else {
+        for (int b = 0; b < 5; ++b)
+          if ((c >> b) & 1) or_dword(int5_dword(tau, lane, b), 1u << (16 * h + 15));
+      }
+      return;
+    }
     int64_t byte, shift;
     if (fmt == qg::NVFP4) {
       byte = tau * 1024 + lane * 16 + 4 * j + (e >> 1);
@@ -125,11 +135,13 @@ struct Dest {
       shift = 4 * (i & 1);
     }
     wq[byte] = (uint8_t)(wq[byte] | ((c & 15) << shift));
-    if (fmt == qg::INT5 && (c & 16)) {
-      const int64_t bit = 16 * (e & 1) + 4 * j + (e >> 1);
-      uint8_t* hw = wq + g->hi_offset + tau * 256 + lane * 4;
-      hw[bit >> 3] = (uint8_t)(hw[bit >> 3] | (1u << (bit & 7)));
-    }
+  }
+  // int5: dwords 0..3 of a lane in plane A, dword 4 in plane B
+  inline uint8_t* int5_dword(int64_t tau, int64_t lane, int i) const {
+    return i < 4 ? wq + tau * 1024 + lane * 16 + 4 * i : wq + g->hi_offset + tau * 256 + lane * 4;
+  }
+  static inline void or_dword(uint8_t* p, uint32_t v) {
+    for (int b = 0; b < 4; ++b) p[b] = (uint8_t)(p[b] | (v >> (8 * b)));
   }
   // per-group scale fields (int formats), group index gi along K
   inline void group(int64_t m, int64_t gi, uint16_t d, uint16_t mn) const {

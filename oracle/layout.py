@@ -21,9 +21,12 @@ int4   wq: tile = 1024 B; lane lam's 16 B at lam*16; dword j holds the 8
        ws: tile = 256 B; row r's 16 B at r*16 hold the groups in the order
            j = 0, 2, 1, 3: dword at r*16 + 4*pos(j), pos(j) = 2*(j & 1) + (j >> 1),
            value fp16(d) | fp16(m) << 16.
-int5   wq: the int4 nibble plane of the low 4 code bits (RT*KS*1024 B), then a
-           hi-bit plane of 256 B tiles: lane lam's dword at lam*4 has bit
-           16*(e & 1) + 4*j + (e >> 1) = bit 4 of the code.
+int5   wq: plane A (RT*KS*1024 B: lane lam's 16 B at tau*1024 + lam*16 = dwords
+           D0..D3), then plane B (RT*KS*256 B: lane lam's dword D4 at
+           RT*KS*1024 + tau*256 + lam*4). The lane's 32 codes form 16 pairs
+           P = 4*j + (e >> 1), half h = e & 1. For P < 15 the 5-bit code sits at
+           bits 16*h + 5*c .. +4 of dword D(P // 3), c = P % 3. For P = 15, bit b
+           of the code (b = 0..4) is bit 16*h + 15 of dword D(b).
        ws: as int4.
 int8   wq: tile = 2048 B; byte (j >> 1)*1024 + lam*16 + (j & 1)*8 + e holds the
            code (two's complement).
@@ -114,6 +117,45 @@ def _dword_nibbles(w: np.ndarray, order: np.ndarray) -> np.ndarray:
     return ((w[..., None] >> sh) & np.uint32(0xF)).astype(np.uint8)
 
 
+def _int5_place(j: int, e: int):
+    """(dword, shift) of a whole 5-bit code, or None for pair 15."""
+    P, h = 4 * j + (e >> 1), e & 1
+    if P < 15:
+        return P // 3, 16 * h + 5 * (P % 3)
+    return None
+
+
+def _int5_dwords(t: np.ndarray) -> np.ndarray:
+    """codes [..., 4 (j), 8 (e)] (< 32) -> the lane's five dwords [..., 5]."""
+    D = np.zeros(t.shape[:-2] + (5,), dtype=np.uint32)
+    for j in range(4):
+        for e in range(8):
+            c = t[..., j, e].astype(np.uint32) & np.uint32(31)
+            pl = _int5_place(j, e)
+            if pl is not None:
+                D[..., pl[0]] |= c << np.uint32(pl[1])
+            else:
+                for b in range(5):
+                    D[..., b] |= ((c >> np.uint32(b)) & np.uint32(1)) << np.uint32(16 * (e & 1) + 15)
+    return D
+
+
+def _int5_codes(D: np.ndarray) -> np.ndarray:
+    """the lane's five dwords [..., 5] -> codes [..., 4, 8]."""
+    t = np.zeros(D.shape[:-1] + (4, 8), dtype=np.uint8)
+    for j in range(4):
+        for e in range(8):
+            pl = _int5_place(j, e)
+            if pl is not None:
+                c = (D[..., pl[0]] >> np.uint32(pl[1])) & np.uint32(31)
+            else:
+                c = np.zeros(D.shape[:-1], dtype=np.uint32)
+                for b in range(5):
+                    c |= ((D[..., b] >> np.uint32(16 * (e & 1) + 15)) & np.uint32(1)) << np.uint32(b)
+            t[..., j, e] = c.astype(np.uint8)
+    return t
+
+
 def pack(qz: Quantized) -> tuple[np.ndarray, np.ndarray]:
     """Logical fields -> (wq, ws) byte arrays in the device layout."""
     fmt, M, K = qz.fmt, qz.M, qz.K
@@ -124,14 +166,11 @@ def pack(qz: Quantized) -> tuple[np.ndarray, np.ndarray]:
         t = _codes_tiled(codes, RT, KS)                              # rt ks lane j e
         order = _INT4_NIB if fmt != "nvfp4" else np.arange(8)
         nib = _nibble_dwords(t & np.uint8(0xF), order)               # rt ks lane j
-        wq = [nib.astype("<u4").tobytes()]
         if fmt == "int5":
-            hb = ((t >> np.uint8(4)) & np.uint8(1)).astype(np.uint32)  # rt ks lane j e
-            j = np.arange(4).reshape(4, 1)
-            e = np.arange(8).reshape(1, 8)
-            pos = (16 * (e & 1) + 4 * j + (e >> 1)).astype(np.uint32)
-            hw = np.bitwise_or.reduce(np.bitwise_or.reduce(hb << pos, axis=-1), axis=-1)
-            wq.append(hw.astype("<u4").tobytes())
+            D = _int5_dwords(t)                                       # rt ks lane 5
+            wq = [D[..., :4].astype("<u4").tobytes(), D[..., 4].astype("<u4").tobytes()]
+        else:
+            wq = [nib.astype("<u4").tobytes()]
         wq = np.frombuffer(b"".join(wq), dtype=np.uint8).copy()
         if fmt == "nvfp4":
             sb = _pad(qz.sb.astype(np.uint8), Mp, Kp // 16)           # [Mp][8*KS]
@@ -168,15 +207,12 @@ def unpack(fmt: str, M: int, K: int, wq: np.ndarray, ws: np.ndarray) -> Quantize
     tiles = RT * KS
     if fmt in ("int4", "int5", "nvfp4"):
         nib = wq[: tiles * 1024].view("<u4").reshape(RT, KS, 64, 4)
-        order = _INT4_NIB if fmt != "nvfp4" else np.arange(8)
-        t = _dword_nibbles(nib, order)                               # rt ks lane j e
         if fmt == "int5":
-            hw = wq[tiles * 1024:].view("<u4").reshape(RT, KS, 64, 1, 1)
-            j = np.arange(4).reshape(4, 1)
-            e = np.arange(8).reshape(1, 8)
-            pos = (16 * (e & 1) + 4 * j + (e >> 1)).astype(np.uint32)
-            hb = ((hw >> pos) & np.uint32(1)).astype(np.uint8)
-            t = t | (hb << np.uint8(4))
+            D = np.concatenate([nib, wq[tiles * 1024:].view("<u4").reshape(RT, KS, 64, 1)], axis=-1)
+            t = _int5_codes(D)                                        # rt ks lane j e
+        else:
+            order = _INT4_NIB if fmt != "nvfp4" else np.arange(8)
+            t = _dword_nibbles(nib, order)                            # rt ks lane j e
         codes = _untile_codes(t, RT, KS)[:M, :K]
         if fmt == "nvfp4":
             s5 = ws[: tiles * 128].reshape(RT, KS, 16, 2, 4)              # rt ks r h j
