@@ -13,8 +13,9 @@ value = algorithmic bytes per step / time per step (GB/s): packed weights and
 scales + x (bf16) + outputs (fp32) + residual read.
 
 Also reported on the same JSON line:
-  roofline      the dominant kernel (gate/up + SwiGLU, int5) against 8 TB/s,
-                from HIP events around each of its launches in the timed loop
+  roofline      the dominant kernel (gate/up + SwiGLU, int5) against 8 TB/s:
+                its average launch duration from HIP events on the launch
+                stream around batches of back-to-back launches (median batch)
   per_format    qgemv on [17408][5120] for each format at N = 1 and N = 8
   moe           qgemv_moe on the 128-expert, top-8 workload at N = 1 and 8
   probe         the plain streaming-read kernel on the same rotation
@@ -125,16 +126,10 @@ def main():
     gu_bytes = weight_bytes(qg, "int5", 2 * 17408, 5120) + N * 5120 * 2 + N * 17408 * 4
     log(f"layer weights {layer_w / 1e6:.1f} MB, rotation {args.layers} layers = {args.layers * layer_w / 1e9:.2f} GB")
 
-    ev = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(args.steps)]
-
-    def step(i, timed=None):
+    def step(i):
         L = layers[i % args.layers]
         qg.qgemv("int4", *L["qkv"], x, qkv, 7168, 5120, N)
-        if timed is not None:
-            timed[0].record(stream)
         qg.qgemv_swiglu("int5", *L["gate_up"], x, h, 17408, 5120, N)
-        if timed is not None:
-            timed[1].record(stream)
         qg.qgemv("int5", *L["down"], xd, y, 5120, 17408, N, residual=res)
 
     for i in range(args.warmup):
@@ -143,37 +138,43 @@ def main():
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for i in range(args.steps):
-        step(args.warmup + i, ev[i])
+        step(args.warmup + i)
     stop.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
     ms_step = total_ms / args.steps
-    gu_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     value = step_bytes / (ms_step * 1e-3) / 1e9
-    gu_gbs = gu_bytes / (gu_ms * 1e-3) / 1e9
-    log(f"step {ms_step * 1e3:.1f} us -> {value:.0f} GB/s; gate/up launch {gu_ms * 1e3:.1f} us -> {gu_gbs:.0f} GB/s")
+    log(f"step {ms_step * 1e3:.1f} us -> {value:.0f} GB/s")
 
-    # per-kernel averages (each kernel alone, back to back, rotated)
-    def time_alone(fn, reps):
+    # Per-kernel average launch duration: batches of back-to-back launches of
+    # one kernel over the rotated layers, events on the launch stream; the
+    # median over batches.
+    def time_alone(fn, reps, batches=5):
         for i in range(min(reps, 8)):
             fn(i)
         torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for i in range(reps):
-            fn(i)
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / reps
+        out = []
+        for bi in range(batches):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for i in range(reps):
+                fn(bi * reps + i)
+            b.record(stream)
+            torch.cuda.synchronize()
+            out.append(a.elapsed_time(b) / reps)
+        return float(np.median(out)), float(min(out)), float(max(out))
 
     kern = {}
-    kern["qkv_int4"] = (time_alone(lambda i: qg.qgemv("int4", *layers[i % args.layers]["qkv"], x, qkv, 7168, 5120, N), 200),
+    kern["qkv_int4"] = (time_alone(lambda i: qg.qgemv("int4", *layers[i % args.layers]["qkv"], x, qkv, 7168, 5120, N), 100),
                         weight_bytes(qg, "int4", 7168, 5120) + N * 5120 * 2 + N * 7168 * 4)
-    kern["gate_up_swiglu_int5"] = (time_alone(lambda i: qg.qgemv_swiglu("int5", *layers[i % args.layers]["gate_up"], x, h, 17408, 5120, N), 100), gu_bytes)
-    kern["down_residual_int5"] = (time_alone(lambda i: qg.qgemv("int5", *layers[i % args.layers]["down"], xd, y, 5120, 17408, N, residual=res), 100),
+    kern["gate_up_swiglu_int5"] = (time_alone(lambda i: qg.qgemv_swiglu("int5", *layers[i % args.layers]["gate_up"], x, h, 17408, 5120, N), 50), gu_bytes)
+    kern["down_residual_int5"] = (time_alone(lambda i: qg.qgemv("int5", *layers[i % args.layers]["down"], xd, y, 5120, 17408, N, residual=res), 50),
                                   weight_bytes(qg, "int5", 5120, 17408) + N * 17408 * 2 + N * 5120 * 8)
-    kernels = {k: {"us": round(ms * 1e3, 2), "GB/s": round(b / (ms * 1e-3) / 1e9, 1)} for k, (ms, b) in kern.items()}
+    kernels = {k: {"us": round(t[0] * 1e3, 2), "us_min": round(t[1] * 1e3, 2), "us_max": round(t[2] * 1e3, 2),
+                   "GB/s": round(b / (t[0] * 1e-3) / 1e9, 1)} for k, (t, b) in kern.items()}
     log("kernels alone:", kernels)
+    gu_ms = kern["gate_up_swiglu_int5"][0][0]
+    gu_gbs = gu_bytes / (gu_ms * 1e-3) / 1e9
 
     src_hash = kernel_source_hash()
     roofline = {"bound": "hbm", "kernel": "k_gemv<int5, swiglu> (gate/up + SwiGLU)",
@@ -250,13 +251,18 @@ def extras(qg, torch, dev, stream, layers, args):
         copies = max(2, int(np.ceil(1.2e9 / nb)))
         d = [(torch.from_numpy(wq).to(dev), torch.from_numpy(ws).to(dev)) for _ in range(copies)]
         pf[fmt] = {}
-        for n in (1, 8):
+        # plain streaming read of the same code buffers: the ceiling at this size
+        ms = timeit(lambda i: qg.qgemv_probe_read(d[i % copies][0], wq.size // 16 * 16, sink), 60)
+        probe_gbs = (wq.size // 16 * 16) / (ms * 1e-3) / 1e9
+        pf[fmt]["probe_GB/s"] = round(probe_gbs, 1)
+        for n in (1, 2, 4, 8):
             xb = torch.from_numpy(synthetic.activations(rng, n, K, 0.01)).to(dev)
             yy = torch.empty((n, M), dtype=torch.float32, device=dev)
             ms = timeit(lambda i: qg.qgemv(fmt, *d[i % copies], xb, yy, M, K, n), 60)
             b = nb + n * K * 2 + n * M * 4
-            pf[fmt][f"N{n}"] = {"us": round(ms * 1e3, 2), "GB/s": round(b / (ms * 1e-3) / 1e9, 1),
-                                "frac": round(b / (ms * 1e-3) / 1e9 / PEAK_GBS, 4)}
+            gbs = b / (ms * 1e-3) / 1e9
+            pf[fmt][f"N{n}"] = {"us": round(ms * 1e3, 2), "GB/s": round(gbs, 1), "frac": round(gbs / PEAK_GBS, 4),
+                                "of_probe": round(gbs / probe_gbs, 4)}
         del d
         log("per_format", fmt, pf[fmt])
     res["per_format"] = {"shape": [M, K], "formats": pf}

@@ -47,6 +47,7 @@ struct GemvArgs {
   int out_tiles;          // 16-row output tiles (M/16 rounded up)
   int up_tile0;           // swiglu: tile index of the first "up" row tile
   int ks_per_wave;
+  int x_nks;              // LDS activation records per wave (XL kernels)
 };
 
 // Combine a lane's accumulators into per-(token, row) totals and write them
@@ -91,18 +92,48 @@ __device__ __forceinline__ void reduce_to_lds(f32x4 (&acc)[NT], float* red, int 
   }
 }
 
+// Activations in LDS: this wave's k-steps [ks0, ks0 + nks) as nks records
+// of xs = 256 N + 16 bytes (token t's 128 bf16 at 256 t, then 16 zero bytes
+// that A lanes outside the unit's slot read). Columns at or past K and
+// k-steps at or past ks1 hold zeros, so the k-loop needs no masking.
+__device__ __forceinline__ void stage_x(uint8_t* xl, __amdgpu_buffer_rsrc_t xr, int N, int K, int ks0, int ks1,
+                                        int nks, int lane) {
+  const int per = N * 16 + 1;   // 16-byte chunks per record
+  const int xs = per * 16;
+  const int total = nks * per;
+  constexpr int B = 8;          // loads in flight per lane
+  for (int i0 = 0; i0 < total; i0 += 64 * B) {
+    u32x4 v[B];
+    int dst[B];
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const int i = i0 + 64 * u + lane;
+      const int kk = i / per, c = i - kk * per;
+      const int t = c >> 4, col = (ks0 + kk) * 128 + (c & 15) * 8;
+      const bool data = i < total && c < N * 16 && ks0 + kk < ks1 && col < K;
+      v[u] = ld128(xr, data ? (uint32_t)(t * K + col) * 2u : kOOB);
+      dst[u] = i < total ? kk * xs + c * 16 : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < B; ++u)
+      if (dst[u] >= 0) *reinterpret_cast<u32x4*>(xl + dst[u]) = v[u];
+  }
+}
+
 // NT tiles per wave: plain GEMV uses NT output tiles, SwiGLU NT/2 gate tiles
 // followed by NT/2 up tiles. S: slots (16 / S tokens per slot >= N). KPS:
-// k-steps per weight prefetch buffer.
-template <int FMT, int NT, int S, int KPS, bool SWIGLU>
+// k-steps per weight prefetch buffer. XL: activations staged in LDS (else
+// buffer loads that land out of range for lanes outside the unit's slot).
+template <int FMT, int NT, int S, int KPS, bool SWIGLU, bool XL>
 __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
-  extern __shared__ float red[];  // [W][NT][8][16]
+  extern __shared__ __attribute__((aligned(16))) float red[];  // [W][NT][8][16], then the LDS activations
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
   const int W = blockDim.x >> 6;
   const int r = lane & 15, s = lane >> 4;
   constexpr int TO = SWIGLU ? NT / 2 : NT;
   constexpr int T = 16 / S;
+  using C = Cyc<FMT, S>;
 
   const __amdgpu_buffer_rsrc_t wq = make_rsrc(a.wq, a.wq_bytes);
   const __amdgpu_buffer_rsrc_t ws = make_rsrc(a.ws, a.ws_bytes);
@@ -118,20 +149,43 @@ __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
     tile[t] = (SWIGLU && t >= TO) ? a.up_tile0 + ot : ot;
   }
 
-  // activation lane role: A row r = slot * T + token; the lane's base offset
-  // carries its slot term, tokens >= N start past the buffer
-  const int a_tok = r % T;
-  const uint32_t xbase = (a_tok < a.N ? (uint32_t)(a_tok * a.K + 8 * s) * 2u : kAbsentRow) + lane_slot_term<FMT, S>(lane);
-  auto aload = [&](int g, uint32_t adj) -> bf16x8 {
-    return __builtin_bit_cast(bf16x8, ld128s(xr, xbase + adj, (uint32_t)g * 64u));
-  };
-
   f32x4 acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int ks0 = wave * a.ks_per_wave;
   const int ks1 = min(a.KS, ks0 + a.ks_per_wave);
-  kloop<FMT, NT, S, KPS>(wq, ws, tile, a.KS, a.G, ks0, ks1, a.hi_offset, aload, acc);
+
+  // activation lane role: A row r = slot * T + token
+  const int a_tok = r % T;
+  if constexpr (XL) {
+    const int xs = a.N * 256 + 16;
+    uint8_t* xl = reinterpret_cast<uint8_t*>(red) + (size_t)W * NT * 512 + (size_t)wave * a.x_nks * xs;
+    // per (cycle position, group): this lane's data or the record's zero block
+    uint32_t off[C::KSTEPS][4];
+    const int sigma = r / T - (FMT == NVFP4 ? (s >> 1) : 0);
+#pragma unroll
+    for (int c = 0; c < C::KSTEPS; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        off[c][j] = (sigma == slot_pos<FMT, S>(c, j) && a_tok < a.N) ? (uint32_t)(a_tok * 256 + j * 64 + s * 16)
+                                                                      : (uint32_t)(a.N * 256);
+    auto acts = [&](bf16x8 (&A)[4], int k, int ckk) {
+      const uint8_t* rec = xl + (k - ks0) * xs;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) A[j] = *reinterpret_cast<const bf16x8*>(rec + off[ckk][j]);
+    };
+    // staged after the first weight loads are issued, so the two overlap
+    auto pre = [&]() { stage_x(xl, xr, a.N, a.K, ks0, ks1, a.x_nks, lane); };
+    kloop<FMT, NT, S, KPS>(wq, ws, tile, a.KS, ks0, ks1, a.hi_offset, acts, acc, pre);
+  } else {
+    // the lane's base offset carries its slot term; tokens >= N start past the buffer
+    const uint32_t xbase = (a_tok < a.N ? (uint32_t)(a_tok * a.K + 8 * s) * 2u : kAbsentRow) + lane_slot_term<FMT, S>(lane);
+    auto aload = [&](int g, uint32_t adj) -> bf16x8 {
+      return __builtin_bit_cast(bf16x8, ld128s(xr, xbase + adj, (uint32_t)g * 64u));
+    };
+    auto acts = [&](bf16x8 (&A)[4], int k, int ckk) { load_acts<FMT, S>(A, k, ks1, a.G, ckk, aload); };
+    kloop<FMT, NT, S, KPS>(wq, ws, tile, a.KS, ks0, ks1, a.hi_offset, acts, acc);
+  }
 
   reduce_to_lds<S, NT>(acc, red, wave, lane);
   __syncthreads();
@@ -297,14 +351,28 @@ LaunchShape pick_shape(int fmt, int64_t KS, int64_t out_tiles, int N, bool swigl
   return ls;
 }
 
+// Activations go to LDS when a workgroup's share stays within this budget
+// (N = 1 and small N * K); larger ones use buffer loads.
+constexpr size_t kMaxLdsActs = 48 * 1024;
+
 template <int FMT, int NT, int S, int KPS>
-hipError_t launch_s(const GemvArgs& a, const LaunchShape& ls, bool swiglu, hipStream_t stream) {
+hipError_t launch_s(const GemvArgs& a0, const LaunchShape& ls, bool swiglu, hipStream_t stream) {
   const int TO = swiglu ? NT / 2 : NT;
-  const dim3 grid((unsigned)((a.out_tiles + TO - 1) / TO));
+  const dim3 grid((unsigned)((a0.out_tiles + TO - 1) / TO));
   const dim3 block((unsigned)(64 * ls.waves));
-  const size_t lds = (size_t)ls.waves * NT * 128 * sizeof(float);
-  if (swiglu) hipLaunchKernelGGL((k_gemv<FMT, NT, S, KPS, true>), grid, block, lds, stream, a);
-  else hipLaunchKernelGGL((k_gemv<FMT, NT, S, KPS, false>), grid, block, lds, stream, a);
+  GemvArgs a = a0;
+  const int U = 2 * KPS;   // k-steps per trip of the k-loop
+  a.x_nks = (ls.kpw + U - 1) / U * U + 1;
+  const size_t xlds = (size_t)ls.waves * a.x_nks * (a.N * 256 + 16);
+  const bool xl = xlds <= kMaxLdsActs;
+  const size_t lds = (size_t)ls.waves * NT * 128 * sizeof(float) + (xl ? xlds : 0);
+  if (swiglu) {
+    if (xl) hipLaunchKernelGGL((k_gemv<FMT, NT, S, KPS, true, true>), grid, block, lds, stream, a);
+    else hipLaunchKernelGGL((k_gemv<FMT, NT, S, KPS, true, false>), grid, block, lds, stream, a);
+  } else {
+    if (xl) hipLaunchKernelGGL((k_gemv<FMT, NT, S, KPS, false, true>), grid, block, lds, stream, a);
+    else hipLaunchKernelGGL((k_gemv<FMT, NT, S, KPS, false, false>), grid, block, lds, stream, a);
+  }
   return hipGetLastError();
 }
 
@@ -320,7 +388,6 @@ hipError_t launch_k(const GemvArgs& a, const LaunchShape& ls, bool swiglu, hipSt
 
 template <int FMT>
 hipError_t launch_gemv(const GemvArgs& a, const LaunchShape& ls, bool swiglu, hipStream_t stream) {
-  if (ls.kps == 4) return launch_k<FMT, 2, 4>(a, ls, swiglu, stream);
   return launch_k<FMT, 2, 2>(a, ls, swiglu, stream);
 }
 

@@ -244,12 +244,18 @@ __device__ __forceinline__ void load_acts(bf16x8 (&A)[4], int k, int ks1, int G,
   }
 }
 
+struct NoPrologue {
+  __device__ void operator()() const {}
+};
+
 // KPS: k-steps per weight buffer; weights run one buffer ahead of the
-// compute, activations one k-step ahead.
-template <int FMT, int NT, int S, int KPS, class ALoad>
+// compute, activations one k-step ahead. acts(A, k, ckk) fetches the four A
+// operands of k-step k at cycle position ckk (zeros past ks1 or past G);
+// pre() runs once after the first weight loads are issued.
+template <int FMT, int NT, int S, int KPS, class Acts, class Pre = NoPrologue>
 __device__ __forceinline__ void kloop(__amdgpu_buffer_rsrc_t wq, __amdgpu_buffer_rsrc_t ws, const int (&tile)[NT],
-                                      int KS, int G, int ks0, int ks1, uint32_t hi_offset, const ALoad& aload,
-                                      f32x4 (&acc)[NT]) {
+                                      int KS, int ks0, int ks1, uint32_t hi_offset, const Acts& acts,
+                                      f32x4 (&acc)[NT], const Pre& pre = Pre()) {
   using C = Cyc<FMT, S>;
   constexpr int U = 2 * KPS;                     // k-steps per loop trip (a multiple of C::KSTEPS)
   static_assert(U % C::KSTEPS == 0, "cycle must divide the trip");
@@ -267,7 +273,8 @@ __device__ __forceinline__ void kloop(__amdgpu_buffer_rsrc_t wq, __amdgpu_buffer
   if (ks0 >= ks1) return;
 
   load_weights<FMT, NT, S, KPS>(buf[0], wq, ws, tile, KS, ks0, ks1, hi_offset);
-  load_acts<FMT, S>(xa[0], ks0, ks1, G, 0, aload);
+  pre();
+  acts(xa[0], ks0, 0);
   for (int base = ks0; base < ks1; base += U) {
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
@@ -278,7 +285,7 @@ __device__ __forceinline__ void kloop(__amdgpu_buffer_rsrc_t wq, __amdgpu_buffer
         const int ckk = kk % C::KSTEPS;            // k-step position inside its cycle
         if (i == 0)                                // next weight buffer
           load_weights<FMT, NT, S, KPS>(buf[b ^ 1], wq, ws, tile, KS, base + (b + 1) * KPS, ks1, hi_offset);
-        load_acts<FMT, S>(xa[(kk + 1) & 1], ks + 1, ks1, G, (kk + 1) % C::KSTEPS, aload);
+        acts(xa[(kk + 1) & 1], ks + 1, (kk + 1) % C::KSTEPS);
         if constexpr (C::KSTEPS > 1) {
           if (ckk == 0) {                          // cycle start: its scale words, used KSTEPS k-steps later
 #pragma unroll
