@@ -58,17 +58,22 @@ def kernel_source_hash() -> str:
 
 
 def pmc_traffic(name: str, src_hash: str):
-    """HBM traffic per launch from a committed rocprofv3 counter summary, or
-    None when missing or taken on different kernel sources."""
-    p = os.path.join(ROOT, "profiles", "traffic.json")
+    """HBM bytes per launch of kernel `name` from the committed rocprofv3
+    counter summary (FETCH_SIZE + WRITE_SIZE, each scaled by what the same
+    counter reads for a 1 GiB device copy), or None when the summary is
+    missing or was taken on other kernel sources."""
+    p = os.path.join(ROOT, "profiles", "dense_layer_n1_hbm_traffic.txt")
     try:
         with open(p) as f:
-            t = json.load(f)
-        e = t.get(name)
-        if e and e.get("src_hash") == src_hash:
-            return e.get("bytes_per_launch")
-    except (OSError, ValueError):
-        pass
+            lines = [ln.strip() for ln in f]
+    except OSError:
+        return None
+    if f"src_hash: {src_hash}" not in lines:
+        return None
+    key = f"traffic {name}:"
+    for ln in lines:
+        if ln.startswith(key):
+            return int(ln[len(key):].strip())
     return None
 
 
@@ -80,6 +85,9 @@ def main():
     ap.add_argument("--layers", type=int, default=16, help="distinct layer copies rotated on the device")
     ap.add_argument("--no-extra", action="store_true", help="skip per-format, MoE, probe and CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="first run a plain device-to-device copy of this many MiB three times "
+                         "(the known-size reference that scales rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
@@ -93,6 +101,14 @@ def main():
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
     N = 1
+    if args.calib_copy_mib > 0:
+        src = torch.ones(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"calibration copy: 3 x {args.calib_copy_mib} MiB")
 
     # ---- weights: a few unique layers packed on the host, replicated on device
     uniq = 2
