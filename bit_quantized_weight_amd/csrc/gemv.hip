@@ -327,13 +327,16 @@ int cycle_ksteps(int fmt, int S) {
   return groups >= 4 ? groups / 4 : 1;
 }
 
-// Launch shape: two 16-row tiles per wave, S slots from N, and K split
-// over W waves so that the grid holds about kTargetWaves waves (measured on
-// MI355X: long-running waves that stream many k-steps beat short ones; small
-// matrices need the K split to fill 256 CUs). Each wave's range is a whole
+// Launch shape: two 16-row tiles per wave, S slots from N, and K split over
+// the W waves of a workgroup. Measured on MI355X (sweeps of W over the dense
+// layer and the [17408][5120] shapes at N = 1..8): a wave streams best with
+// about 20 k-steps of its row tiles (NVFP4 at N <= 2: 10; int8 at N = 1: the
+// whole K, its k-steps being twice as long), and the grid should hold at least
+// ~900 waves so that the chip's 1024 SIMDs have work; below that the k-range
+// per wave shrinks (never under one scale cycle). Each wave's range is a whole
 // number of cycles.
 constexpr int kMaxWaves = 8;
-constexpr int64_t kTargetWaves = 1100;
+constexpr int64_t kMinGridWaves = 900;
 
 LaunchShape pick_shape(int fmt, int64_t KS, int64_t out_tiles, int N, bool swiglu) {
   LaunchShape ls;
@@ -342,11 +345,16 @@ LaunchShape pick_shape(int fmt, int64_t KS, int64_t out_tiles, int N, bool swigl
   ls.slots = slots_for(N);
   const int cyc = cycle_ksteps(fmt, ls.slots);
   const int64_t wgs = (out_tiles + (swiglu ? 0 : 1)) / (swiglu ? 1 : 2);
-  int64_t w = (kTargetWaves + wgs / 2) / wgs;
-  w = w < 1 ? 1 : (w > kMaxWaves ? kMaxWaves : w);
-  int64_t kpw = (KS + w - 1) / w;
-  kpw = (kpw + cyc - 1) / cyc * cyc;
-  ls.waves = (int)((KS + kpw - 1) / kpw);
+  const bool whole_k = fmt == INT8 && N == 1;
+  int64_t target = whole_k ? KS : (fmt == NVFP4 && N <= 2 ? 10 : 20);
+  auto waves_for = [&](int64_t kpw) { return (KS + kpw - 1) / kpw; };
+  auto round_cyc = [&](int64_t kpw) { return (kpw + cyc - 1) / cyc * cyc; };
+  int64_t kpw = round_cyc(target < 1 ? 1 : target);
+  if (!whole_k) {
+    while (kpw > cyc && wgs * waves_for(kpw) < kMinGridWaves) kpw = round_cyc(kpw - cyc > cyc ? kpw - cyc : cyc);
+  }
+  while (waves_for(kpw) > kMaxWaves) kpw += cyc;
+  ls.waves = (int)waves_for(kpw);
   ls.kpw = (int)kpw;
   return ls;
 }
