@@ -5,19 +5,19 @@
 // section 2: SwiGLU fused into the matmul): every token t runs only the
 // experts it selected, y[t] = r[t] + sum_j p[t][j] * down_e(SwiGLU(gate_up_e(x[t]))).
 //
-// Four launches on one stream, no host synchronisation:
-//   1. index: one workgroup turns ids [N][k] into counts, offsets, the
-//      (token, slot) pairs in (expert, token, slot) order and the ascending
-//      list of active experts; exact integer work.
-//   2. gate/up + SwiGLU: grid (row tiles, active-expert slot); a slot past the
-//      number of active experts exits at once. Each workgroup gathers the
-//      rows of x routed to its expert (8 per MFMA pass) and writes h [pair][I]
-//      in fp32.
-//   3. down: same grid shape over H. h leaves step 2 as a pair of bf16 planes
+// Three launches on one stream, no host synchronisation:
+//   1. gate/up + SwiGLU: grid (row tiles, expert). Each workgroup first
+//      routes in LDS (one wave, a ballot over the <= 64 selected ids): the
+//      (token, slot) pairs routed to its expert in (token, slot) order; an
+//      expert nobody selected exits at once. It then gathers the rows of x
+//      routed to its expert (8 per MFMA pass) and writes h [pair][I].
+//   2. down: same grid shape over H and the same routing. h leaves step 1 as a pair of bf16 planes
 //      hi = bf16(h), lo = bf16(h - hi) (h = hi + lo + O(2^-16 |h|), the same
 //      bytes as fp32), so the A operand holds 4 pairs x {hi, lo} x 2 slots;
 //      writes o [pair][H] in fp32.
-//   4. combine: y[t] = r[t] + sum_j p[t][j] o[t*k + j] in increasing j order;
+// The routing index itself (counts, offsets, pairs in (expert, token, slot)
+// order, active experts, error flag) is qgemv_moe_index, one workgroup.
+//   3. combine: y[t] = r[t] + sum_j p[t][j] o[t*k + j] in increasing j order;
 //      no atomics, so results are bitwise reproducible (RustingStrata page,
 //      known issues: run-to-run reordering changes results).
 #include <hip/hip_runtime.h>
@@ -32,95 +32,86 @@
 
 namespace qg {
 
-// int32 index region of the workspace
-struct MoeIndex {
-  int E, NK;
-  __host__ __device__ int counts() const { return 0; }
-  __host__ __device__ int offsets() const { return E; }
-  __host__ __device__ int pairs() const { return 2 * E + 1; }
-  __host__ __device__ int active() const { return 2 * E + 1 + NK; }
-  __host__ __device__ int meta() const { return 3 * E + 1 + NK; }
-  __host__ __device__ int total() const { return 3 * E + 3 + NK; }
+// ---- routing (exact integer work on the N * top_k <= 64 selected ids) -----
+// Wave-level: lane i holds entry i (flat index t * top_k + j) for i < NK.
+struct Route {
+  int v;          // this lane's expert id, -1 if outside [0, E), -2 past NK
+  bool first;     // first occurrence of its expert among valid entries
+  int rank;       // first occurrences: rank of its expert among active experts
+  uint64_t act;   // lanes that are first occurrences
 };
 
+__device__ __forceinline__ Route route_lanes(const int32_t* ids, int NK, int E, int* s_v) {
+  const int lane = threadIdx.x & 63;
+  Route R;
+  int v = -2;
+  if (lane < NK) {
+    const int id = ids[lane];
+    v = (id >= 0 && id < E) ? id : -1;
+  }
+  R.v = v;
+  s_v[lane] = v;   // one wave: its LDS accesses complete in order
+  bool first = v >= 0;
+  for (int j = 0; j < NK; ++j) first &= !(j < lane && s_v[j] == v);
+  R.first = first;
+  R.act = __ballot(first);
+  int rank = 0;
+  for (uint64_t m = R.act; m; m &= m - 1) {
+    const int j = __builtin_ctzll(m);
+    rank += s_v[j] < v;
+  }
+  R.rank = rank;
+  return R;
+}
+
+// Pairs routed to expert e, in LDS: s_route[0] = count, s_route[1..] = flat
+// entries t * top_k + j with ids == e, ascending. Called by one whole wave.
+__device__ __forceinline__ void route_expert(const int32_t* ids, int NK, int e, int* s_route) {
+  const int lane = threadIdx.x & 63;
+  const bool hit = lane < NK && ids[lane] == e;
+  const uint64_t mine = __ballot(hit);
+  if (hit) s_route[1 + __builtin_popcountll(mine & ((1ull << lane) - 1ull))] = lane;
+  if (lane == 0) s_route[0] = __builtin_popcountll(mine);
+}
+
+// qgemv_moe_index: one workgroup of 256 threads; wave 0 ranks the entries.
 __global__ __launch_bounds__(256) void k_moe_index(const int32_t* ids, int NK, int E, int32_t* counts,
                                                    int32_t* offsets, int32_t* pairs, int32_t* active,
                                                    int32_t* meta) {
-  __shared__ int sid[64];
-  __shared__ int spos[64];
+  __shared__ int s_v[64];
+  __shared__ int s_meta[2];
   const int tid = threadIdx.x;
-  if (tid < NK) {
-    const int v = ids[tid];
-    sid[tid] = (v >= 0 && v < E) ? v : -1;
-  }
-  __syncthreads();
-  // rank of each valid entry in (expert, flat index) order
-  if (tid < NK) {
-    const int v = sid[tid];
-    int pos = -1;
-    if (v >= 0) {
-      pos = 0;
-      for (int i = 0; i < NK; ++i) {
-        const int u = sid[i];
-        if (u >= 0 && (u < v || (u == v && i < tid))) ++pos;
-      }
+  if (tid < 64) {
+    const Route R = route_lanes(ids, NK, E, s_v);
+    // pairs: position = (# valid entries with a smaller id) + (# equal ids before)
+    if (R.v >= 0) {
+      int pos = 0;
+      for (int j = 0; j < NK; ++j) pos += (s_v[j] >= 0 && s_v[j] < R.v) || (s_v[j] == R.v && j < tid);
+      pairs[pos] = tid;
     }
-    spos[tid] = pos;
+    if (R.first) active[R.rank] = R.v;
+    const uint64_t valid = __ballot(R.v >= 0);
+    const uint64_t bad = __ballot(R.v == -1);
+    if (tid == 0) {
+      s_meta[0] = __builtin_popcountll(R.act);
+      s_meta[1] = __builtin_popcountll(valid);
+      meta[0] = s_meta[0];
+      meta[1] = bad ? 1 : 0;
+    }
   }
   __syncthreads();
-  int nvalid = 0, bad = 0;
-  for (int i = 0; i < NK; ++i) {
-    nvalid += sid[i] >= 0;
-    bad |= sid[i] < 0;
-  }
-  // pairs
-  for (int p = tid; p < NK; p += blockDim.x) pairs[p] = -1;
-  __syncthreads();
-  if (tid < NK && spos[tid] >= 0) pairs[spos[tid]] = tid;
-  // offsets and counts
-  for (int e = tid; e <= E; e += blockDim.x) {
-    int below = 0;
-    for (int i = 0; i < NK; ++i) below += (sid[i] >= 0 && sid[i] < e);
-    offsets[e] = below;
-  }
+  for (int p = s_meta[1] + tid; p < NK; p += blockDim.x) pairs[p] = -1;
   for (int e = tid; e < E; e += blockDim.x) {
-    int c = 0;
-    for (int i = 0; i < NK; ++i) c += sid[i] == e;
-    counts[e] = c;
-    active[e] = -1;
-  }
-  __syncthreads();
-  // active experts: an entry that is first of its expert in sorted order
-  // (pos == offsets[e]) gets index = number of such firsts with smaller ids
-  int nact = 0;
-  for (int i = 0; i < NK; ++i) {
-    const int v = sid[i];
-    if (v < 0) continue;
-    int first = 1;
-    for (int q = 0; q < i; ++q) first &= (sid[q] != v);
-    nact += first;
-  }
-  if (tid < NK && sid[tid] >= 0) {
-    const int v = sid[tid];
-    int first = 1;
-    for (int q = 0; q < tid; ++q) first &= (sid[q] != v);
-    if (first) {
-      int idx = 0;
-      for (int i = 0; i < NK; ++i) {
-        const int u = sid[i];
-        if (u < 0 || u >= v) continue;
-        int f = 1;
-        for (int q = 0; q < i; ++q) f &= (sid[q] != u);
-        idx += f;
-      }
-      active[idx] = v;
+    int c = 0, below = 0;
+    for (int j = 0; j < NK; ++j) {
+      c += s_v[j] == e;
+      below += s_v[j] >= 0 && s_v[j] < e;
     }
+    counts[e] = c;
+    offsets[e] = below;
+    if (e >= s_meta[0]) active[e] = -1;
   }
-  if (tid == 0) {
-    meta[0] = nact;
-    meta[1] = bad;
-  }
-  (void)nvalid;
+  if (tid == 0) offsets[E] = s_meta[1];
 }
 
 struct MoeArgs {
@@ -132,7 +123,7 @@ struct MoeArgs {
   const void* in;                  // gate/up: x bf16 [N][K]; down: h as bf16 hi and lo planes [2][NK][K]
   uint32_t in_bytes;
   float* out;                      // gate/up: h planes (bf16) [2][NK][Mout]; down: o fp32 [NK][Mout]
-  const int32_t* idx;              // workspace index region
+  const int32_t* ids;              // [N][top_k] selected experts
   int E, top_k, NK;
   int Mout, K, KS, G;
   int out_tiles, up_tile0;
@@ -150,16 +141,15 @@ __device__ __forceinline__ void split_bf16(float v, __bf16& hi, __bf16& lo) {
 template <int FMT, int NT, bool DOWN>
 __global__ __launch_bounds__(512) void k_moe_gemv(MoeArgs a) {
   extern __shared__ float red[];  // [W][NT][32][4]
+  __shared__ int s_route[1 + 64];
   constexpr int TO = DOWN ? NT : NT / 2;
   constexpr int ROWS = DOWN ? 4 : 8;   // routed rows per MFMA pass
-  const MoeIndex ix{a.E, a.NK};
-  const int32_t* meta = a.idx + ix.meta();
-  const int slot_a = blockIdx.y;
-  if (slot_a >= meta[0]) return;       // uniform: fewer active experts than slots
-  const int e = a.idx[ix.active() + slot_a];
-  const int p0 = a.idx[ix.offsets() + e];
-  const int cnt = a.idx[ix.offsets() + e + 1] - p0;
-  const int32_t* pairs = a.idx + ix.pairs() + p0;
+  const int e = blockIdx.y;            // one grid row per expert
+  if (threadIdx.x < 64) route_expert(a.ids, a.NK, e, s_route);
+  __syncthreads();
+  const int cnt = s_route[0];
+  if (cnt == 0) return;                // uniform: no token selected this expert
+  const int* pairs = s_route + 1;
 
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
@@ -266,12 +256,21 @@ __global__ __launch_bounds__(256) void k_moe_combine(const float* o, const int32
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= (int64_t)N * H) return;
   const int t = (int)(i / H), col = (int)(i % H);
-  float v = res ? res[i] : 0.0f;
-  for (int j = 0; j < top_k; ++j) {
-    const int e = ids[t * top_k + j];
-    if (e < 0 || e >= E) continue;
-    v = fmaf(gates[t * top_k + j], o[(size_t)(t * top_k + j) * H + col], v);
+  // every load first (independent), then the fixed-order sum
+  float ov[8], pv[8];
+  int ev[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j < top_k) {
+      ev[j] = ids[t * top_k + j];
+      pv[j] = gates[t * top_k + j];
+      ov[j] = o[(size_t)(t * top_k + j) * H + col];
+    }
   }
+  float v = res ? res[i] : 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (j < top_k && ev[j] >= 0 && ev[j] < E) v = fmaf(pv[j], ov[j], v);
   y[i] = v;
 }
 
@@ -293,7 +292,7 @@ MoeLayout moe_layout(int E, int64_t H, int64_t I, int N, int top_k) {
   const int NK = N * top_k;
   MoeLayout L;
   L.idx_off = 0;
-  L.h_off = up256((size_t)MoeIndex{E, NK}.total() * 4);
+  L.h_off = 0;
   L.o_off = L.h_off + up256((size_t)NK * (size_t)I * 4);
   L.total = L.o_off + up256((size_t)NK * (size_t)H * 4);
   return L;
@@ -358,12 +357,8 @@ extern "C" int qgemv_moe(int fmt, const void* wq_gu, const void* ws_gu, const vo
   if (ggu.wq_bytes >= (1ull << 32) || gdn.wq_bytes >= (1ull << 32)) return QGEMV_EUNSUPPORTED;
   const int NK = N * top_k;
   uint8_t* wsp = (uint8_t*)workspace;
-  int32_t* idx = (int32_t*)(wsp + L.idx_off);
   float* h = (float*)(wsp + L.h_off);
   float* o = (float*)(wsp + L.o_off);
-  const MoeIndex ix{E, NK};
-  hipLaunchKernelGGL(k_moe_index, dim3(1), dim3(256), 0, stream, ids, NK, E, idx + ix.counts(), idx + ix.offsets(),
-                     idx + ix.pairs(), idx + ix.active(), idx + ix.meta());
 
   MoeArgs gu;
   gu.wq = (const uint8_t*)wq_gu;
@@ -377,7 +372,7 @@ extern "C" int qgemv_moe(int fmt, const void* wq_gu, const void* ws_gu, const vo
   gu.in = x;
   gu.in_bytes = (uint32_t)((int64_t)N * H * 2);
   gu.out = h;
-  gu.idx = idx;
+  gu.ids = ids;
   gu.E = E;
   gu.top_k = top_k;
   gu.NK = NK;
@@ -412,7 +407,7 @@ extern "C" int qgemv_moe(int fmt, const void* wq_gu, const void* ws_gu, const vo
   dn.ks_per_wave = (int)((gdn.KS + wdn - 1) / wdn);
 
   if (I % 16) return QGEMV_EALIGN;
-  const int slots = std::min(E, NK);
+  const int slots = E;
   switch (fmt) {
     case INT4: launch_moe_pair<INT4>(gu, dn, wgu, wdn, slots, stream); break;
     case INT5: launch_moe_pair<INT5>(gu, dn, wgu, wdn, slots, stream); break;
