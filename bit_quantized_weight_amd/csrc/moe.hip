@@ -6,11 +6,12 @@
 // experts it selected, y[t] = r[t] + sum_j p[t][j] * down_e(SwiGLU(gate_up_e(x[t]))).
 //
 // Three launches on one stream, no host synchronisation:
-//   1. gate/up + SwiGLU: grid (row tiles, expert). Each workgroup first
-//      routes in LDS (one wave, a ballot over the <= 64 selected ids): the
-//      (token, slot) pairs routed to its expert in (token, slot) order; an
-//      expert nobody selected exits at once. It then gathers the rows of x
-//      routed to its expert (8 per MFMA pass) and writes h [pair][I].
+//   1. gate/up + SwiGLU: grid (row tiles, active-expert slot). Each
+//      workgroup first routes in LDS (one wave, exact integer work on the
+//      <= 64 selected ids): the a-th smallest selected expert and the (token,
+//      slot) pairs routed to it in (token, slot) order; a slot past the number
+//      of selected experts exits at once. It then gathers the rows of x routed
+//      to its expert (8 per MFMA pass) and writes h [pair][I].
 //   2. down: same grid shape over H and the same routing. h leaves step 1 as a pair of bf16 planes
 //      hi = bf16(h), lo = bf16(h - hi) (h = hi + lo + O(2^-16 |h|), the same
 //      bytes as fp32), so the A operand holds 4 pairs x {hi, lo} x 2 slots;
@@ -64,14 +65,66 @@ __device__ __forceinline__ Route route_lanes(const int32_t* ids, int NK, int E, 
   return R;
 }
 
-// Pairs routed to expert e, in LDS: s_route[0] = count, s_route[1..] = flat
-// entries t * top_k + j with ids == e, ascending. Called by one whole wave.
-__device__ __forceinline__ void route_expert(const int32_t* ids, int NK, int e, int* s_route) {
+// Largest expert count qgemv_moe accepts: the routing bitmap lives in LDS.
+constexpr int kMaxExperts = 16384;
+
+// Active slot a -> expert, in LDS, for one whole wave: s_route[0] = the a-th
+// smallest selected expert id (-1 if fewer than a + 1 experts are selected),
+// s_route[1] = the number of pairs routed to it, s_route[2..] = those flat
+// entries t * top_k + j, ascending. A bitmap of selected experts (OR is
+// order-independent) is scanned with one prefix sum over the lanes' chunks.
+__device__ __forceinline__ void route_slot(const int32_t* ids, int NK, int E, int a, uint32_t* s_bits,
+                                           int* s_route) {
   const int lane = threadIdx.x & 63;
-  const bool hit = lane < NK && ids[lane] == e;
-  const uint64_t mine = __ballot(hit);
-  if (hit) s_route[1 + __builtin_popcountll(mine & ((1ull << lane) - 1ull))] = lane;
-  if (lane == 0) s_route[0] = __builtin_popcountll(mine);
+  const int W = (E + 31) >> 5, c = (W + 63) >> 6;   // bitmap words, words per lane
+  for (int i = 0; i < c; ++i) {
+    const int w = lane * c + i;
+    if (w < W) s_bits[w] = 0u;
+  }
+  int v = -1;
+  if (lane < NK) {
+    const int id = ids[lane];
+    v = (id >= 0 && id < E) ? id : -1;
+  }
+  // one wave: its LDS operations complete in issue order (clears, ORs, reads)
+  __builtin_amdgcn_wave_barrier();
+  if (v >= 0) atomicOr(s_bits + (v >> 5), 1u << (v & 31));
+  __builtin_amdgcn_wave_barrier();
+  int cnt = 0;
+  for (int i = 0; i < c; ++i) {
+    const int w = lane * c + i;
+    if (w < W) cnt += __builtin_popcount(s_bits[w]);
+  }
+  int incl = cnt;                 // inclusive prefix sum over lanes
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int t = __shfl_up(incl, d);
+    if (lane >= d) incl += t;
+  }
+  const int n_active = __shfl(incl, 63);
+  int e = -1;
+  if (a < n_active && incl - cnt <= a && a < incl) {
+    int rem = a - (incl - cnt);
+    for (int i = 0; i < c && e < 0; ++i) {
+      const int w = lane * c + i;
+      uint32_t bits = w < W ? s_bits[w] : 0u;
+      const int pc = __builtin_popcount(bits);
+      if (rem < pc) {
+        for (int r = 0; r < rem; ++r) bits &= bits - 1u;   // drop the lowest rem set bits
+        e = 32 * w + __builtin_ctz(bits);
+      } else {
+        rem -= pc;
+      }
+    }
+  }
+  const uint64_t owner = __ballot(e >= 0);
+  e = owner ? __shfl(e, __builtin_ctzll(owner)) : -1;
+  const uint64_t mine = __ballot(e >= 0 && v == e);
+  if (e >= 0 && v == e) s_route[2 + __builtin_popcountll(mine & ((1ull << lane) - 1ull))] = lane;
+  if (lane == 0) {
+    s_route[0] = e;
+    s_route[1] = __builtin_popcountll(mine);
+  }
 }
 
 // qgemv_moe_index: one workgroup of 256 threads; wave 0 ranks the entries.
@@ -141,15 +194,16 @@ __device__ __forceinline__ void split_bf16(float v, __bf16& hi, __bf16& lo) {
 template <int FMT, int NT, bool DOWN>
 __global__ __launch_bounds__(512) void k_moe_gemv(MoeArgs a) {
   extern __shared__ float red[];  // [W][NT][32][4]
-  __shared__ int s_route[1 + 64];
+  __shared__ uint32_t s_bits[kMaxExperts / 32];
+  __shared__ int s_route[2 + 64];
   constexpr int TO = DOWN ? NT : NT / 2;
   constexpr int ROWS = DOWN ? 4 : 8;   // routed rows per MFMA pass
-  const int e = blockIdx.y;            // one grid row per expert
-  if (threadIdx.x < 64) route_expert(a.ids, a.NK, e, s_route);
+  if (threadIdx.x < 64) route_slot(a.ids, a.NK, a.E, blockIdx.y, s_bits, s_route);
   __syncthreads();
-  const int cnt = s_route[0];
-  if (cnt == 0) return;                // uniform: no token selected this expert
-  const int* pairs = s_route + 1;
+  const int e = s_route[0];
+  if (e < 0) return;                   // uniform: fewer selected experts than slots
+  const int cnt = s_route[1];
+  const int* pairs = s_route + 2;
 
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
@@ -339,6 +393,7 @@ extern "C" int qgemv_moe(int fmt, const void* wq_gu, const void* ws_gu, const vo
   if (fmt < INT4 || fmt > NVFP4) return QGEMV_EFORMAT;
   if (!wq_gu || !ws_gu || !wq_dn || !ws_dn || !x || !ids || !gates || !y) return QGEMV_EINVAL;
   if (E < 1 || H < 32 || I < 16) return QGEMV_EINVAL;
+  if (E > kMaxExperts) return QGEMV_EUNSUPPORTED;
   if (N < 1 || N > 8 || top_k < 1 || top_k > 8) return QGEMV_EUNSUPPORTED;
   if (H % 32 || I % 32) return QGEMV_EALIGN;
   if (!al16(wq_gu) || !al16(ws_gu) || !al16(wq_dn) || !al16(ws_dn) || !al16(x) || !al4(ids) || !al4(gates) ||
@@ -407,7 +462,7 @@ extern "C" int qgemv_moe(int fmt, const void* wq_gu, const void* ws_gu, const vo
   dn.ks_per_wave = (int)((gdn.KS + wdn - 1) / wdn);
 
   if (I % 16) return QGEMV_EALIGN;
-  const int slots = E;
+  const int slots = std::min(E, NK);   // one grid row per active-expert slot
   switch (fmt) {
     case INT4: launch_moe_pair<INT4>(gu, dn, wgu, wdn, slots, stream); break;
     case INT5: launch_moe_pair<INT5>(gu, dn, wgu, wdn, slots, stream); break;
