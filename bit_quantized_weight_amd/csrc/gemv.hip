@@ -328,13 +328,21 @@ int cycle_ksteps(int fmt, int S) {
 }
 
 // Launch shape: two 16-row tiles per wave, S slots from N, and K split over
-// the W waves of a workgroup. Measured on MI355X (sweeps of W over the dense
-// layer and the [17408][5120] shapes at N = 1..8): a wave streams best with
-// about 20 k-steps of its row tiles (NVFP4 at N <= 2: 10; int8 at N = 1: the
-// whole K, its k-steps being twice as long), and the grid should hold at least
-// ~900 waves so that the chip's 1024 SIMDs have work; below that the k-range
-// per wave shrinks (never under one scale cycle). Each wave's range is a whole
-// number of cycles.
+// the W waves of a workgroup. The k-steps per wave come from sweeps on MI355X
+// (the dense layer and [17408][5120] in every format at N = 1, 2, 4, 8): a
+// wave streams best with about 20 k-steps of its row tiles, fewer where a
+// k-step is cheap to decode for many tokens (N = 2; int8 and NVFP4 at N = 4;
+// NVFP4 at N = 1: 10), and int8 at N = 1 keeps the whole K (its k-steps carry
+// twice the bytes). The grid should hold at least ~900 waves so the chip's
+// 1024 SIMDs have work; below that the k-range per wave shrinks (never under
+// one scale cycle). Each wave's range is a whole number of cycles.
+int ksteps_per_wave(int fmt, int N) {
+  if (N == 1) return fmt == INT8 ? 0 : (fmt == NVFP4 ? 10 : 20);   // 0: whole K
+  if (N == 2) return 12;
+  if (N <= 4) return (fmt == INT8 || fmt == NVFP4) ? 12 : 20;
+  return 20;
+}
+
 constexpr int kMaxWaves = 8;
 constexpr int64_t kMinGridWaves = 900;
 
@@ -345,8 +353,9 @@ LaunchShape pick_shape(int fmt, int64_t KS, int64_t out_tiles, int N, bool swigl
   ls.slots = slots_for(N);
   const int cyc = cycle_ksteps(fmt, ls.slots);
   const int64_t wgs = (out_tiles + (swiglu ? 0 : 1)) / (swiglu ? 1 : 2);
-  const bool whole_k = fmt == INT8 && N == 1;
-  int64_t target = whole_k ? KS : (fmt == NVFP4 && N <= 2 ? 10 : 20);
+  const int per = ksteps_per_wave(fmt, N);
+  const bool whole_k = per == 0;
+  int64_t target = whole_k ? KS : per;
   auto waves_for = [&](int64_t kpw) { return (KS + kpw - 1) / kpw; };
   auto round_cyc = [&](int64_t kpw) { return (kpw + cyc - 1) / cyc * cyc; };
   int64_t kpw = round_cyc(target < 1 ? 1 : target);
