@@ -176,7 +176,7 @@ __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
     };
     // staged after the first weight loads are issued, so the two overlap
     auto pre = [&]() { stage_x(xl, xr, a.N, a.K, ks0, ks1, a.x_nks, lane); };
-    kloop<FMT, NT, S, KPS>(wq, ws, tile, a.KS, ks0, ks1, a.hi_offset, acts, acc, pre);
+    kloop<FMT, NT, S, KPS, 1>(wq, ws, tile, a.KS, ks0, ks1, a.hi_offset, acts, acc, pre);
   } else {
     // the lane's base offset carries its slot term; tokens >= N start past the buffer
     const uint32_t xbase = (a_tok < a.N ? (uint32_t)(a_tok * a.K + 8 * s) * 2u : kAbsentRow) + lane_slot_term<FMT, S>(lane);
@@ -184,7 +184,7 @@ __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
       return __builtin_bit_cast(bf16x8, ld128s(xr, xbase + adj, (uint32_t)g * 64u));
     };
     auto acts = [&](bf16x8 (&A)[4], int k, int ckk) { load_acts<FMT, S>(A, k, ks1, a.G, ckk, aload); };
-    kloop<FMT, NT, S, KPS>(wq, ws, tile, a.KS, ks0, ks1, a.hi_offset, acts, acc);
+    kloop<FMT, NT, S, KPS, 1>(wq, ws, tile, a.KS, ks0, ks1, a.hi_offset, acts, acc);
   }
 
   reduce_to_lds<S, NT>(acc, red, wave, lane);

@@ -249,19 +249,23 @@ struct NoPrologue {
 };
 
 // KPS: k-steps per weight buffer; weights run one buffer ahead of the
-// compute, activations one k-step ahead. acts(A, k, ckk) fetches the four A
+// compute, activations AD k-steps ahead (1 everywhere: a deeper activation
+// ring measured slower on MI355X, its registers cost more than the latency
+// they hide). acts(A, k, ckk) fetches the four A
 // operands of k-step k at cycle position ckk (zeros past ks1 or past G);
 // pre() runs once after the first weight loads are issued.
-template <int FMT, int NT, int S, int KPS, class Acts, class Pre = NoPrologue>
+template <int FMT, int NT, int S, int KPS, int AD, class Acts, class Pre = NoPrologue>
 __device__ __forceinline__ void kloop(__amdgpu_buffer_rsrc_t wq, __amdgpu_buffer_rsrc_t ws, const int (&tile)[NT],
                                       int KS, int ks0, int ks1, uint32_t hi_offset, const Acts& acts,
                                       f32x4 (&acc)[NT], const Pre& pre = Pre()) {
   using C = Cyc<FMT, S>;
   constexpr int U = 2 * KPS;                     // k-steps per loop trip (a multiple of C::KSTEPS)
+  constexpr int R = AD + 1;                      // activation ring
   static_assert(U % C::KSTEPS == 0, "cycle must divide the trip");
+  static_assert(U % R == 0, "the activation ring must divide the trip");
   const bf16x8 b128 = bf16x8_splat_128();
   Step<FMT, NT, KPS> buf[2];
-  bf16x8 xa[2][4];
+  bf16x8 xa[R][4];
   u32x4 csc[NT];                                 // scale words of the current cycle (KSTEPS > 1)
   f32x4 D[NT];
   f32x4 Db = {0.f, 0.f, 0.f, 0.f};
@@ -274,7 +278,8 @@ __device__ __forceinline__ void kloop(__amdgpu_buffer_rsrc_t wq, __amdgpu_buffer
 
   load_weights<FMT, NT, S, KPS>(buf[0], wq, ws, tile, KS, ks0, ks1, hi_offset);
   pre();
-  acts(xa[0], ks0, 0);
+#pragma unroll
+  for (int d = 0; d < AD; ++d) acts(xa[d], ks0 + d, d % C::KSTEPS);
   for (int base = ks0; base < ks1; base += U) {
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
@@ -285,7 +290,7 @@ __device__ __forceinline__ void kloop(__amdgpu_buffer_rsrc_t wq, __amdgpu_buffer
         const int ckk = kk % C::KSTEPS;            // k-step position inside its cycle
         if (i == 0)                                // next weight buffer
           load_weights<FMT, NT, S, KPS>(buf[b ^ 1], wq, ws, tile, KS, base + (b + 1) * KPS, ks1, hi_offset);
-        acts(xa[(kk + 1) & 1], ks + 1, (kk + 1) % C::KSTEPS);
+        acts(xa[(kk + AD) % R], ks + AD, (kk + AD) % C::KSTEPS);
         if constexpr (C::KSTEPS > 1) {
           if (ckk == 0) {                          // cycle start: its scale words, used KSTEPS k-steps later
 #pragma unroll
@@ -307,7 +312,7 @@ __device__ __forceinline__ void kloop(__amdgpu_buffer_rsrc_t wq, __amdgpu_buffer
           const bool first = (gpos % C::GROUPS) == 0;
           const bool last = ((gpos + 1) % C::GROUPS) == 0;
           const int cidx = gpos / C::GROUPS;       // cycle index inside the k-step
-          const bf16x8 A = xa[kk & 1][j];
+          const bf16x8 A = xa[kk % R][j];
           if constexpr (FMT == INT4 || FMT == INT5) Db = mfma(A, b128, first ? f32x4{0.f, 0.f, 0.f, 0.f} : Db);
 #pragma unroll
           for (int t = 0; t < NT; ++t) {

@@ -242,7 +242,7 @@ __global__ __launch_bounds__(512) void k_moe_gemv(MoeArgs a) {
         return __builtin_bit_cast(bf16x8, ld128s(inr, base + adj, (uint32_t)g * 64u));
       };
       auto acts = [&](bf16x8 (&A)[4], int k, int ckk) { load_acts<FMT, 2>(A, k, ks1, a.G, ckk, aload); };
-      kloop<FMT, NT, 2, 2>(wq, ws, tile, a.KS, ks0, ks1, a.hi_offset, acts, acc);
+      kloop<FMT, NT, 2, 2, 1>(wq, ws, tile, a.KS, ks0, ks1, a.hi_offset, acts, acc);
     } else {
       // A rows 8*slot + 4*part + pair: part 0 reads the hi plane of h, part 1 the lo plane
       const int part = (r >> 2) & 1;
@@ -251,7 +251,7 @@ __global__ __launch_bounds__(512) void k_moe_gemv(MoeArgs a) {
         return __builtin_bit_cast(bf16x8, ld128s(inr, base + adj, (uint32_t)g * 64u));
       };
       auto acts = [&](bf16x8 (&A)[4], int k, int ckk) { load_acts<FMT, 2>(A, k, ks1, a.G, ckk, aload); };
-      kloop<FMT, NT, 2, 2>(wq, ws, tile, a.KS, ks0, ks1, a.hi_offset, acts, acc);
+      kloop<FMT, NT, 2, 2, 1>(wq, ws, tile, a.KS, ks0, ks1, a.hi_offset, acts, acc);
     }
     // reduce: slots (lane ^ 32); for DOWN also hi/lo parts (lane ^ 16)
 #pragma unroll
