@@ -287,7 +287,27 @@ def test_moe_duplicates_and_bad_ids():
     check_tol(y.cpu().numpy(), y_ref, T, "moe dup/bad")
 
 
-@pytest.mark.parametrize("N,k,E", [(1, 8, 128), (8, 8, 128), (5, 3, 7), (8, 8, 4), (4, 3, 6)])
+@pytest.mark.parametrize("E,ids", [(3000, None),
+                                   (5000, [[4999, 0, 2048, 4999], [2047, 2049, 4095, 4096], [1, 4998, 3, 2], [4999, 7, 4096, 0]])])
+def test_moe_many_experts(E, ids):
+    """Expert counts past one bitmap word per lane (E > 2048), with ids at the
+    word edges and the last expert, so every slot's expert lookup is exercised."""
+    H, I, k, N = 128, 32, 4, 4
+    log("moe many experts", E)
+    ids = None if ids is None else np.array(ids, np.int32)
+    bufs, Wgu, Wdn, xb, ids, gates, r = _moe_case("int4", E, H, I, N, k, seed=E, ids=ids)
+    y_ref, T = G.moe(G.x_from_bits(xb), ids, gates, Wgu, Wdn, r)
+    nbytes = qg().moe_workspace_bytes(E, H, I, N, k)
+    wsp = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    y = torch.empty((N, H), dtype=torch.float32, device="cuda")
+    d = [dev(b, torch) for b in bufs]
+    qg().qgemv_moe("int4", *d, E, H, I, dev(xb, torch), dev(ids, torch), dev(gates, torch), k, y, N, wsp, nbytes,
+                   residual=dev(r, torch))
+    torch.cuda.synchronize()
+    check_tol(y.cpu().numpy(), y_ref, T, f"moe E={E}")
+
+
+@pytest.mark.parametrize("N,k,E", [(1, 8, 128), (8, 8, 128), (5, 3, 7), (8, 8, 4), (4, 3, 6), (8, 8, 3000), (3, 5, 1)])
 def test_moe_index_bit_exact(N, k, E):
     rng = np.random.default_rng(N * 100 + k)
     ids = rng.integers(0, E, size=(N, k)).astype(np.int32)

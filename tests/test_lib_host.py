@@ -164,6 +164,7 @@ def test_qgemv_moe_validation_codes():
     assert moe(H=2047) == -1 or moe(H=2047) == -3
     assert moe(fmt=0) == -2
     assert moe(ids=None) == -1
+    assert moe(E=16385) == -7          # routing bitmap limit: 16384 experts
     assert L.qgemv_moe_index(None, 1, 8, 128, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -1
     assert L.qgemv_moe_index(FAKE, 9, 8, 128, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -7
     b = ctypes.c_size_t()
