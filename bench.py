@@ -16,7 +16,8 @@ Also reported on the same JSON line:
   roofline      the dominant kernel (gate/up + SwiGLU, int5) against 8 TB/s:
                 its average launch duration from HIP events on the launch
                 stream around batches of back-to-back launches (median batch)
-  per_format    qgemv on [17408][5120] for each format at N = 1 and N = 8
+  nvfp4_layer   the same layer in NVFP4 at N = 1, 2, 4, 8
+  per_format    qgemv on [17408][5120] for each format at N = 1, 2, 4, 8
   moe           qgemv_moe on the 128-expert, top-8 workload at N = 1 and 8
   probe         the plain streaming-read kernel on the same rotation
   cpu_baseline  the CPU oracle on a bounded sample of the layer
@@ -256,7 +257,41 @@ def extras(qg, torch, dev, stream, layers, args):
     res["probe"] = {"bytes": pb[0].numel(), "us": round(ms * 1e3, 2), "GB/s": round(pb[0].numel() / (ms * 1e-3) / 1e9, 1)}
     log("probe", res["probe"])
 
-    # per format on [17408][5120], N = 1 and 8, rotated over >= 1 GB
+    # the same layer in NVFP4 at N = 1, 2, 4, 8 (1-8 decode lanes), 8 rotated layer copies
+    nv = {}
+    nv_host = {}
+    for name, M_, K_, _ in LAYER:
+        rng_l = synthetic.rng_for(0, 3, 1, M_)
+        nv_host[name] = qg.pack("nvfp4", synthetic.weights(rng_l, M_, K_))
+    nv_layers = [{k: (torch.from_numpy(v[0]).to(dev), torch.from_numpy(v[1]).to(dev)) for k, v in nv_host.items()}
+                 for _ in range(8)]
+    nv_w = sum(v[0].size + v[1].size for v in nv_host.values())
+    del nv_host
+    for n in (1, 2, 4, 8):
+        rng_x = synthetic.rng_for(0, 3, 2, n)
+        xn = torch.from_numpy(synthetic.activations(rng_x, n, 5120)).to(dev)
+        xdn = torch.from_numpy(synthetic.activations(rng_x, n, 17408)).to(dev)
+        qn = torch.empty((n, 7168), dtype=torch.float32, device=dev)
+        hn = torch.empty((n, 17408), dtype=torch.float32, device=dev)
+        rn = torch.from_numpy(synthetic.residual(rng_x, n, 5120)).to(dev)
+        yn = torch.empty((n, 5120), dtype=torch.float32, device=dev)
+
+        def nv_step(i):
+            L = nv_layers[i % len(nv_layers)]
+            qg.qgemv("nvfp4", *L["qkv"], xn, qn, 7168, 5120, n)
+            qg.qgemv_swiglu("nvfp4", *L["gate_up"], xn, hn, 17408, 5120, n)
+            qg.qgemv("nvfp4", *L["down"], xdn, yn, 5120, 17408, n, residual=rn)
+        ms = timeit(nv_step, 40)
+        b = nv_w + n * (5120 * 2 + 7168 * 4 + 5120 * 2 + 17408 * 4 + 17408 * 2 + 5120 * 8)
+        nv[f"N{n}"] = {"us": round(ms * 1e3, 2), "GB/s": round(b / (ms * 1e-3) / 1e9, 1),
+                       "frac": round(b / (ms * 1e-3) / 1e9 / PEAK_GBS, 4),
+                       "tok_per_s_64_layers": round(n / (64 * ms * 1e-3), 1)}
+    del nv_layers
+    res["nvfp4_layer"] = {"workload": "27B-class dense layer in NVFP4 (QKV, gate/up + SwiGLU, down + residual), "
+                                      "8 rotated copies", "weight_bytes": nv_w, **nv}
+    log("nvfp4_layer", res["nvfp4_layer"])
+
+    # per format on [17408][5120], N = 1, 2, 4, 8, rotated over >= 1 GB
     M, K = 17408, 5120
     rng = synthetic.rng_for(0, 3, M)
     W = synthetic.weights(rng, M, K)

@@ -70,6 +70,7 @@ struct Step {
   u32x4 q2[KPS][NT];     // int8 groups 2,3
   uint32_t h[KPS][NT];   // int5 dword D4
   u32x4 sc[KPS][NT];     // scale words (cycles of at most one k-step)
+  u32x4 cyc[NT];         // scale words of the cycle starting at this buffer (cycles of several k-steps)
 };
 
 // Scale words of one tile for the cycle whose first k-step is tile record
@@ -207,7 +208,10 @@ __device__ __forceinline__ void flush(f32x4& acc, const f32x4& D, const f32x4& D
 // Loads the packed weights of KPS k-steps starting at ks (wave-uniform) into
 // st. K-steps at or past ks1 read as zeros (out-of-range offsets, no memory
 // traffic).
-template <int FMT, int NT, int S, int KPS>
+// CYC: this buffer's first k-step starts a scale cycle of several k-steps;
+// that cycle's scale words travel with the buffer, so they are in flight as
+// long as the weights (a cycle's flush comes KSTEPS k-steps after its start).
+template <int FMT, int NT, int S, int KPS, bool CYC>
 __device__ __forceinline__ void load_weights(Step<FMT, NT, KPS>& st, __amdgpu_buffer_rsrc_t wq,
                                              __amdgpu_buffer_rsrc_t ws, const int (&tile)[NT], int KS, int ks,
                                              int ks1, uint32_t hi_offset) {
@@ -226,6 +230,9 @@ __device__ __forceinline__ void load_weights(Step<FMT, NT, KPS>& st, __amdgpu_bu
       if constexpr (FMT == INT8) st.q2[i][t] = ld128s_nt(wq, lo, tau * TB + 1024u);
       if constexpr (FMT == INT5) st.h[i][t] = ld32s_nt(wq, (uint32_t)lane * 4u | bad, hi_offset + tau * 256u);
       if constexpr (Cyc<FMT, S>::KSTEPS == 1) st.sc[i][t] = load_scales<FMT, S>(ws, tau, lane, ok ? 1 : 0);
+      if constexpr (Cyc<FMT, S>::KSTEPS > 1 && CYC) {
+        if (i == 0) st.cyc[t] = load_scales<FMT, S>(ws, tau, lane, ks1 - k);
+      }
     }
   }
 }
@@ -276,7 +283,7 @@ __device__ __forceinline__ void kloop(__amdgpu_buffer_rsrc_t wq, __amdgpu_buffer
   }
   if (ks0 >= ks1) return;
 
-  load_weights<FMT, NT, S, KPS>(buf[0], wq, ws, tile, KS, ks0, ks1, hi_offset);
+  load_weights<FMT, NT, S, KPS, true>(buf[0], wq, ws, tile, KS, ks0, ks1, hi_offset);
   pre();
 #pragma unroll
   for (int d = 0; d < AD; ++d) acts(xa[d], ks0 + d, d % C::KSTEPS);
@@ -288,15 +295,17 @@ __device__ __forceinline__ void kloop(__amdgpu_buffer_rsrc_t wq, __amdgpu_buffer
         const int kk = b * KPS + i;                // k-step index in the trip
         const int ks = base + kk;
         const int ckk = kk % C::KSTEPS;            // k-step position inside its cycle
-        if (i == 0)                                // next weight buffer
-          load_weights<FMT, NT, S, KPS>(buf[b ^ 1], wq, ws, tile, KS, base + (b + 1) * KPS, ks1, hi_offset);
+        if (i == 0) {                              // next weight buffer (and its cycle's scales)
+          constexpr bool cyc1 = KPS % C::KSTEPS == 0;        // buffer base + KPS starts a cycle
+          constexpr bool cyc2 = (2 * KPS) % C::KSTEPS == 0;  // buffer base + 2 KPS does
+          if (b == 0) load_weights<FMT, NT, S, KPS, cyc1>(buf[1], wq, ws, tile, KS, base + KPS, ks1, hi_offset);
+          else load_weights<FMT, NT, S, KPS, cyc2>(buf[0], wq, ws, tile, KS, base + 2 * KPS, ks1, hi_offset);
+        }
         acts(xa[(kk + AD) % R], ks + AD, (kk + AD) % C::KSTEPS);
         if constexpr (C::KSTEPS > 1) {
-          if (ckk == 0) {                          // cycle start: its scale words, used KSTEPS k-steps later
+          if (ckk == 0) {                          // cycle start: its scale words came with this buffer
 #pragma unroll
-            for (int t = 0; t < NT; ++t)
-              csc[t] = load_scales<FMT, S>(ws, (uint32_t)tile[t] * (uint32_t)KS + (uint32_t)ks, threadIdx.x & 63,
-                                           ks1 - ks);
+            for (int t = 0; t < NT; ++t) csc[t] = buf[b].cyc[t];
           }
         }
         __builtin_amdgcn_sched_barrier(0);
