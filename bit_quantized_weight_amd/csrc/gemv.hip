@@ -343,17 +343,28 @@ int ksteps_per_wave(int fmt, int N) {
   return 20;
 }
 
+// One row tile per wave instead of two where that measured faster: NVFP4 at
+// N <= 2 (12 k-steps per wave) and int8 at N = 2 (20); the plain GEMV only
+// (SwiGLU keeps a gate tile and its up tile together).
+bool single_tile(int fmt, int N, bool swiglu, int* kpw) {
+  if (swiglu) return false;
+  if (fmt == NVFP4 && N <= 2) { *kpw = 12; return true; }
+  if (fmt == INT8 && N == 2) { *kpw = 20; return true; }
+  return false;
+}
+
 constexpr int kMaxWaves = 8;
 constexpr int64_t kMinGridWaves = 900;
 
 LaunchShape pick_shape(int fmt, int64_t KS, int64_t out_tiles, int N, bool swiglu) {
   LaunchShape ls;
-  ls.nt = 2;
   ls.kps = 2;
   ls.slots = slots_for(N);
   const int cyc = cycle_ksteps(fmt, ls.slots);
-  const int64_t wgs = (out_tiles + (swiglu ? 0 : 1)) / (swiglu ? 1 : 2);
-  const int per = ksteps_per_wave(fmt, N);
+  int per = ksteps_per_wave(fmt, N);
+  ls.nt = single_tile(fmt, N, swiglu, &per) ? 1 : 2;
+  const int64_t to = swiglu ? ls.nt / 2 : ls.nt;     // output tiles per workgroup
+  const int64_t wgs = (out_tiles + to - 1) / to;
   const bool whole_k = per == 0;
   int64_t target = whole_k ? KS : per;
   auto waves_for = [&](int64_t kpw) { return (KS + kpw - 1) / kpw; };
@@ -383,10 +394,14 @@ hipError_t launch_s(const GemvArgs& a0, const LaunchShape& ls, bool swiglu, hipS
   const size_t xlds = (size_t)ls.waves * a.x_nks * (a.N * 256 + 16);
   const bool xl = xlds <= kMaxLdsActs;
   const size_t lds = (size_t)ls.waves * NT * 128 * sizeof(float) + (xl ? xlds : 0);
-  if (swiglu) {
-    if (xl) hipLaunchKernelGGL((k_gemv<FMT, NT, S, KPS, true, true>), grid, block, lds, stream, a);
-    else hipLaunchKernelGGL((k_gemv<FMT, NT, S, KPS, true, false>), grid, block, lds, stream, a);
-  } else {
+  if constexpr (NT >= 2) {
+    if (swiglu) {
+      if (xl) hipLaunchKernelGGL((k_gemv<FMT, NT, S, KPS, true, true>), grid, block, lds, stream, a);
+      else hipLaunchKernelGGL((k_gemv<FMT, NT, S, KPS, true, false>), grid, block, lds, stream, a);
+      return hipGetLastError();
+    }
+  }
+  {
     if (xl) hipLaunchKernelGGL((k_gemv<FMT, NT, S, KPS, false, true>), grid, block, lds, stream, a);
     else hipLaunchKernelGGL((k_gemv<FMT, NT, S, KPS, false, false>), grid, block, lds, stream, a);
   }
@@ -405,6 +420,12 @@ hipError_t launch_k(const GemvArgs& a, const LaunchShape& ls, bool swiglu, hipSt
 
 template <int FMT>
 hipError_t launch_gemv(const GemvArgs& a, const LaunchShape& ls, bool swiglu, hipStream_t stream) {
+  if constexpr (FMT == NVFP4 || FMT == INT8) {
+    if (ls.nt == 1) {   // N <= 2 only (single_tile)
+      if (ls.slots == 16) return launch_s<FMT, 1, 16, 2>(a, ls, false, stream);
+      return launch_s<FMT, 1, 8, 2>(a, ls, false, stream);
+    }
+  }
   return launch_k<FMT, 2, 2>(a, ls, swiglu, stream);
 }
 

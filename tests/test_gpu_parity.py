@@ -327,7 +327,8 @@ def test_moe_index_bit_exact(N, k, E):
 # --------------------------------------------------- full sizes, sampled rows
 
 FULL = [("int4", 7168, 5120, 1), ("int5", 17408, 5120, 8), ("int5", 5120, 17408, 1), ("int8", 17408, 5120, 8),
-        ("nvfp4", 17408, 5120, 8), ("nvfp4", 5120, 17408, 4)]
+        ("nvfp4", 17408, 5120, 8), ("nvfp4", 5120, 17408, 4), ("nvfp4", 17408, 5120, 1), ("nvfp4", 17408, 5120, 2),
+        ("int8", 17408, 5120, 2), ("int8", 17408, 5120, 1), ("int4", 17408, 5120, 2)]
 
 
 @pytest.mark.parametrize("fmt,M,K,N", FULL)
