@@ -437,7 +437,10 @@ extern "C" int qgemv_moe(int fmt, const void* wq_gu, const void* ws_gu, const vo
   gu.G = (int)(H / 32);
   gu.out_tiles = (int)((I + 15) / 16);
   gu.up_tile0 = (int)(I / 16);
-  const int wgu = (int)std::min<int64_t>(8, std::max<int64_t>(1, (ggu.KS + 3) / 4));  // ~4 k-steps per wave
+  // waves per workgroup (measured on the 128-expert workload): ~4 k-steps per
+  // wave while few rows are routed (N * top_k < 32), whole K per wave beyond
+  const bool many = NK >= 32;
+  const int wgu = many ? 1 : (int)std::min<int64_t>(8, std::max<int64_t>(1, (ggu.KS + 3) / 4));
   gu.ks_per_wave = (int)((ggu.KS + wgu - 1) / wgu);
 
   MoeArgs dn = gu;
@@ -458,7 +461,7 @@ extern "C" int qgemv_moe(int fmt, const void* wq_gu, const void* ws_gu, const vo
   dn.G = (int)(I / 32);
   dn.out_tiles = (int)((H + 15) / 16);
   dn.up_tile0 = 0;
-  const int wdn = (int)std::min<int64_t>(8, std::max<int64_t>(1, (gdn.KS + 3) / 4));
+  const int wdn = many ? 1 : (int)std::min<int64_t>(8, std::max<int64_t>(1, (gdn.KS + 3) / 4));
   dn.ks_per_wave = (int)((gdn.KS + wdn - 1) / wdn);
 
   if (I % 16) return QGEMV_EALIGN;
