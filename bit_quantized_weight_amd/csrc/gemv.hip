@@ -329,18 +329,25 @@ int cycle_ksteps(int fmt, int S) {
 
 // Launch shape: two 16-row tiles per wave, S slots from N, and K split over
 // the W waves of a workgroup. The k-steps per wave come from sweeps on MI355X
-// (the dense layer and [17408][5120] in every format at N = 1, 2, 4, 8): a
-// wave streams best with about 20 k-steps of its row tiles, fewer where a
-// k-step is cheap to decode for many tokens (N = 2; int8 and NVFP4 at N = 4;
-// NVFP4 at N = 1: 10), and int8 at N = 1 keeps the whole K (its k-steps carry
-// twice the bytes). The grid should hold at least ~900 waves so the chip's
-// 1024 SIMDs have work; below that the k-range per wave shrinks (never under
-// one scale cycle). Each wave's range is a whole number of cycles.
-int ksteps_per_wave(int fmt, int N) {
-  if (N == 1) return fmt == INT8 ? 0 : (fmt == NVFP4 ? 10 : 20);   // 0: whole K
+// (the dense layer's three shapes and [17408][5120], every format, N = 1, 2,
+// 4, 8): a wave streams best with about 20 k-steps of its row tiles, fewer
+// where a k-step is cheap to decode for several tokens (N = 2..4), more where
+// many tokens make each k-step long (SwiGLU and long K at N > 4), and int8 at
+// N = 1 keeps the whole K (its k-steps carry twice the bytes). The grid
+// should hold at least ~900 waves so the chip's 1024 SIMDs have work; below
+// that the k-range per wave shrinks (never under one scale cycle). Each
+// wave's range is a whole number of cycles.
+int ksteps_per_wave(int fmt, int N, bool swiglu, int64_t KS) {
+  if (swiglu) {                          // gate/up pairs: [2 x 17408][5120] sweeps
+    if (N == 1) return 20;
+    if (N == 2) return fmt == NVFP4 ? 20 : 12;
+    if (N <= 4) return 12;
+    return 40;
+  }
+  if (N == 1) return fmt == INT8 ? 0 : 20;   // 0: whole K
   if (N == 2) return 12;
   if (N <= 4) return (fmt == INT8 || fmt == NVFP4) ? 12 : 20;
-  return 20;
+  return KS >= 64 ? (int)((KS + 4) / 5) : 20;   // long K at N > 4: five waves per workgroup
 }
 
 // One row tile per wave instead of two where that measured faster: NVFP4 at
@@ -361,7 +368,7 @@ LaunchShape pick_shape(int fmt, int64_t KS, int64_t out_tiles, int N, bool swigl
   ls.kps = 2;
   ls.slots = slots_for(N);
   const int cyc = cycle_ksteps(fmt, ls.slots);
-  int per = ksteps_per_wave(fmt, N);
+  int per = ksteps_per_wave(fmt, N, swiglu, KS);
   ls.nt = single_tile(fmt, N, swiglu, &per) ? 1 : 2;
   const int64_t to = swiglu ? ls.nt / 2 : ls.nt;     // output tiles per workgroup
   const int64_t wgs = (out_tiles + to - 1) / to;
