@@ -47,7 +47,7 @@ struct GemvArgs {
   int out_tiles;          // 16-row output tiles (M/16 rounded up)
   int up_tile0;           // swiglu: tile index of the first "up" row tile
   int ks_per_wave;
-  int x_nks;              // LDS activation records per wave (XL kernels)
+  int x_nks;              // LDS activation records per wave (XM_LDS kernels)
 };
 
 // Combine a lane's accumulators into per-(token, row) totals and write them
@@ -120,11 +120,20 @@ __device__ __forceinline__ void stage_x(uint8_t* xl, __amdgpu_buffer_rsrc_t xr, 
   }
 }
 
+// Activation paths (A operands of the MFMAs):
+//   XM_LDS   the wave's whole k-range of x staged in LDS up front;
+//   XM_RING  a ring of kRing k-step records in LDS, refilled kRing - 1
+//            k-steps ahead through registers (when the whole range does not
+//            fit the LDS budget, e.g. 8 tokens over K = 5120);
+//   XM_LOAD  buffer loads one k-step ahead that land out of range for lanes
+//            outside the unit's slot.
+constexpr int XM_LOAD = 0, XM_LDS = 1, XM_RING = 2;
+constexpr int kRing = 4;
+
 // NT tiles per wave: plain GEMV uses NT output tiles, SwiGLU NT/2 gate tiles
 // followed by NT/2 up tiles. S: slots (16 / S tokens per slot >= N). KPS:
-// k-steps per weight prefetch buffer. XL: activations staged in LDS (else
-// buffer loads that land out of range for lanes outside the unit's slot).
-template <int FMT, int NT, int S, int KPS, bool SWIGLU, bool XL>
+// k-steps per weight prefetch buffer. XM: activation path.
+template <int FMT, int NT, int S, int KPS, bool SWIGLU, int XM>
 __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
   extern __shared__ __attribute__((aligned(16))) float red[];  // [W][NT][8][16], then the LDS activations
   const int lane = threadIdx.x & 63;
@@ -157,9 +166,10 @@ __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
 
   // activation lane role: A row r = slot * T + token
   const int a_tok = r % T;
-  if constexpr (XL) {
-    const int xs = a.N * 256 + 16;
-    uint8_t* xl = reinterpret_cast<uint8_t*>(red) + (size_t)W * NT * 512 + (size_t)wave * a.x_nks * xs;
+  if constexpr (XM == XM_LDS || XM == XM_RING) {
+    const int xs = a.N * 256 + 16;   // one k-step record: token t's 128 bf16 at 256 t, then 16 zero bytes
+    const int nrec = XM == XM_LDS ? a.x_nks : kRing;
+    uint8_t* xl = reinterpret_cast<uint8_t*>(red) + (size_t)W * NT * 512 + (size_t)wave * nrec * xs;
     // per (cycle position, group): this lane's data or the record's zero block
     uint32_t off[C::KSTEPS][4];
     const int sigma = r / T - (FMT == NVFP4 ? (s >> 1) : 0);
@@ -169,21 +179,68 @@ __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
       for (int j = 0; j < 4; ++j)
         off[c][j] = (sigma == slot_pos<FMT, S>(c, j) && a_tok < a.N) ? (uint32_t)(a_tok * 256 + j * 64 + s * 16)
                                                                       : (uint32_t)(a.N * 256);
-    auto acts = [&](bf16x8 (&A)[4], int k, int ckk) {
-      const uint8_t* rec = xl + (k - ks0) * xs;
+    if constexpr (XM == XM_LDS) {
+      auto acts = [&](bf16x8 (&A)[4], int k, int pos) {
+        const uint8_t* rec = xl + (k - ks0) * xs;
+        const int ckk = pos % C::KSTEPS;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) A[j] = *reinterpret_cast<const bf16x8*>(rec + off[ckk][j]);
-    };
-    // staged after the first weight loads are issued, so the two overlap
-    auto pre = [&]() { stage_x(xl, xr, a.N, a.K, ks0, ks1, a.x_nks, lane); };
-    kloop<FMT, NT, S, KPS, 1>(wq, ws, tile, a.KS, ks0, ks1, a.hi_offset, acts, acc, pre);
+        for (int j = 0; j < 4; ++j) A[j] = *reinterpret_cast<const bf16x8*>(rec + off[ckk][j]);
+      };
+      // staged after the first weight loads are issued, so the two overlap
+      auto pre = [&]() { stage_x(xl, xr, a.N, a.K, ks0, ks1, a.x_nks, lane); };
+      kloop<FMT, NT, S, KPS, 1>(wq, ws, tile, a.KS, ks0, ks1, a.hi_offset, acts, acc, pre);
+    } else {
+      // Ring slot of k-step k: (k - ks0) % kRing, which equals its trip
+      // position modulo kRing (trips start at ks0 + a multiple of 2 * KPS).
+      // Each lane moves two 16-byte chunks of a record (N <= 8: 16 N chunks).
+      // The call that fetches A for k-step k loads record k + 3 into
+      // registers; two calls later that record is written to its slot (the
+      // slot last read three calls before), and one call after that it is read.
+      static_assert((2 * KPS) % kRing == 0, "the ring must divide the trip");
+      const int nch = a.N * 16;
+      auto ring_load = [&](u32x4 (&v)[2], int k) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int c = lane + 64 * h;
+          const int t = c >> 4, col = k * 128 + (c & 15) * 8;
+          const bool data = c < nch && k < ks1 && col < a.K;
+          v[h] = ld128(xr, data ? (uint32_t)(t * a.K + col) * 2u : kOOB);
+        }
+      };
+      auto ring_store = [&](const u32x4 (&v)[2], int slot) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int c = lane + 64 * h;
+          if (c < nch) *reinterpret_cast<u32x4*>(xl + slot * xs + c * 16) = v[h];
+        }
+      };
+      u32x4 stg[2][2];                 // records loaded, not yet written
+      auto acts = [&](bf16x8 (&A)[4], int k, int pos) {
+        ring_store(stg[pos & 1], (pos + 1) % kRing);   // record k + 1 (loaded two calls ago)
+        ring_load(stg[pos & 1], k + 3);
+        const uint8_t* rec = xl + (pos % kRing) * xs;
+        const int ckk = pos % C::KSTEPS;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) A[j] = *reinterpret_cast<const bf16x8*>(rec + off[ckk][j]);
+      };
+      auto pre = [&]() {
+        // zero blocks; record ks0 written now, ks0 + 1 and ks0 + 2 staged
+        if (lane < kRing) *reinterpret_cast<u32x4*>(xl + lane * xs + a.N * 256) = u32x4{0u, 0u, 0u, 0u};
+        u32x4 v0[2];
+        ring_load(v0, ks0);
+        ring_load(stg[0], ks0 + 1);
+        ring_load(stg[1], ks0 + 2);
+        ring_store(v0, 0);
+      };
+      kloop<FMT, NT, S, KPS, 1>(wq, ws, tile, a.KS, ks0, ks1, a.hi_offset, acts, acc, pre);
+    }
   } else {
     // the lane's base offset carries its slot term; tokens >= N start past the buffer
     const uint32_t xbase = (a_tok < a.N ? (uint32_t)(a_tok * a.K + 8 * s) * 2u : kAbsentRow) + lane_slot_term<FMT, S>(lane);
     auto aload = [&](int g, uint32_t adj) -> bf16x8 {
       return __builtin_bit_cast(bf16x8, ld128s(xr, xbase + adj, (uint32_t)g * 64u));
     };
-    auto acts = [&](bf16x8 (&A)[4], int k, int ckk) { load_acts<FMT, S>(A, k, ks1, a.G, ckk, aload); };
+    auto acts = [&](bf16x8 (&A)[4], int k, int pos) { load_acts<FMT, S>(A, k, ks1, a.G, pos % C::KSTEPS, aload); };
     kloop<FMT, NT, S, KPS, 1>(wq, ws, tile, a.KS, ks0, ks1, a.hi_offset, acts, acc);
   }
 
@@ -398,20 +455,22 @@ hipError_t launch_s(const GemvArgs& a0, const LaunchShape& ls, bool swiglu, hipS
   GemvArgs a = a0;
   const int U = 2 * KPS;   // k-steps per trip of the k-loop
   a.x_nks = (ls.kpw + U - 1) / U * U + 1;
-  const size_t xlds = (size_t)ls.waves * a.x_nks * (a.N * 256 + 16);
-  const bool xl = xlds <= kMaxLdsActs;
-  const size_t lds = (size_t)ls.waves * NT * 128 * sizeof(float) + (xl ? xlds : 0);
+  const size_t rec = (size_t)a.N * 256 + 16;
+  const size_t red = (size_t)ls.waves * NT * 128 * sizeof(float);
+  const size_t whole = (size_t)ls.waves * a.x_nks * rec, ring = (size_t)ls.waves * kRing * rec;
+  const int xm = whole <= kMaxLdsActs ? XM_LDS : (ring <= kMaxLdsActs ? XM_RING : XM_LOAD);
+  const size_t lds = red + (xm == XM_LDS ? whole : (xm == XM_RING ? ring : 0));
   if constexpr (NT >= 2) {
     if (swiglu) {
-      if (xl) hipLaunchKernelGGL((k_gemv<FMT, NT, S, KPS, true, true>), grid, block, lds, stream, a);
-      else hipLaunchKernelGGL((k_gemv<FMT, NT, S, KPS, true, false>), grid, block, lds, stream, a);
+      if (xm == XM_LDS) hipLaunchKernelGGL((k_gemv<FMT, NT, S, KPS, true, XM_LDS>), grid, block, lds, stream, a);
+      else if (xm == XM_RING) hipLaunchKernelGGL((k_gemv<FMT, NT, S, KPS, true, XM_RING>), grid, block, lds, stream, a);
+      else hipLaunchKernelGGL((k_gemv<FMT, NT, S, KPS, true, XM_LOAD>), grid, block, lds, stream, a);
       return hipGetLastError();
     }
   }
-  {
-    if (xl) hipLaunchKernelGGL((k_gemv<FMT, NT, S, KPS, false, true>), grid, block, lds, stream, a);
-    else hipLaunchKernelGGL((k_gemv<FMT, NT, S, KPS, false, false>), grid, block, lds, stream, a);
-  }
+  if (xm == XM_LDS) hipLaunchKernelGGL((k_gemv<FMT, NT, S, KPS, false, XM_LDS>), grid, block, lds, stream, a);
+  else if (xm == XM_RING) hipLaunchKernelGGL((k_gemv<FMT, NT, S, KPS, false, XM_RING>), grid, block, lds, stream, a);
+  else hipLaunchKernelGGL((k_gemv<FMT, NT, S, KPS, false, XM_LOAD>), grid, block, lds, stream, a);
   return hipGetLastError();
 }
 

@@ -258,8 +258,9 @@ struct NoPrologue {
 // KPS: k-steps per weight buffer; weights run one buffer ahead of the
 // compute, activations AD k-steps ahead (1 everywhere: a deeper activation
 // ring measured slower on MI355X, its registers cost more than the latency
-// they hide). acts(A, k, ckk) fetches the four A
-// operands of k-step k at cycle position ckk (zeros past ks1 or past G);
+// they hide). acts(A, k, pos) fetches the four A operands of k-step k,
+// which sits at position pos of its loop trip (a compile-time constant at
+// each call; its cycle position is pos % KSTEPS) — zeros past ks1 or past G;
 // pre() runs once after the first weight loads are issued.
 template <int FMT, int NT, int S, int KPS, int AD, class Acts, class Pre = NoPrologue>
 __device__ __forceinline__ void kloop(__amdgpu_buffer_rsrc_t wq, __amdgpu_buffer_rsrc_t ws, const int (&tile)[NT],
@@ -286,7 +287,7 @@ __device__ __forceinline__ void kloop(__amdgpu_buffer_rsrc_t wq, __amdgpu_buffer
   load_weights<FMT, NT, S, KPS, true>(buf[0], wq, ws, tile, KS, ks0, ks1, hi_offset);
   pre();
 #pragma unroll
-  for (int d = 0; d < AD; ++d) acts(xa[d], ks0 + d, d % C::KSTEPS);
+  for (int d = 0; d < AD; ++d) acts(xa[d], ks0 + d, d);
   for (int base = ks0; base < ks1; base += U) {
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
@@ -301,7 +302,7 @@ __device__ __forceinline__ void kloop(__amdgpu_buffer_rsrc_t wq, __amdgpu_buffer
           if (b == 0) load_weights<FMT, NT, S, KPS, cyc1>(buf[1], wq, ws, tile, KS, base + KPS, ks1, hi_offset);
           else load_weights<FMT, NT, S, KPS, cyc2>(buf[0], wq, ws, tile, KS, base + 2 * KPS, ks1, hi_offset);
         }
-        acts(xa[(kk + AD) % R], ks + AD, (kk + AD) % C::KSTEPS);
+        acts(xa[(kk + AD) % R], ks + AD, (kk + AD) % U);
         if constexpr (C::KSTEPS > 1) {
           if (ckk == 0) {                          // cycle start: its scale words came with this buffer
 #pragma unroll

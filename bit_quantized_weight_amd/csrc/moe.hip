@@ -241,7 +241,9 @@ __global__ __launch_bounds__(512) void k_moe_gemv(MoeArgs a) {
       auto aload = [&](int g, uint32_t adj) -> bf16x8 {
         return __builtin_bit_cast(bf16x8, ld128s(inr, base + adj, (uint32_t)g * 64u));
       };
-      auto acts = [&](bf16x8 (&A)[4], int k, int ckk) { load_acts<FMT, 2>(A, k, ks1, a.G, ckk, aload); };
+      auto acts = [&](bf16x8 (&A)[4], int k, int pos) {
+        load_acts<FMT, 2>(A, k, ks1, a.G, pos % Cyc<FMT, 2>::KSTEPS, aload);
+      };
       kloop<FMT, NT, 2, 2, 1>(wq, ws, tile, a.KS, ks0, ks1, a.hi_offset, acts, acc);
     } else {
       // A rows 8*slot + 4*part + pair: part 0 reads the hi plane of h, part 1 the lo plane
@@ -250,7 +252,9 @@ __global__ __launch_bounds__(512) void k_moe_gemv(MoeArgs a) {
       auto aload = [&](int g, uint32_t adj) -> bf16x8 {
         return __builtin_bit_cast(bf16x8, ld128s(inr, base + adj, (uint32_t)g * 64u));
       };
-      auto acts = [&](bf16x8 (&A)[4], int k, int ckk) { load_acts<FMT, 2>(A, k, ks1, a.G, ckk, aload); };
+      auto acts = [&](bf16x8 (&A)[4], int k, int pos) {
+        load_acts<FMT, 2>(A, k, ks1, a.G, pos % Cyc<FMT, 2>::KSTEPS, aload);
+      };
       kloop<FMT, NT, 2, 2, 1>(wq, ws, tile, a.KS, ks0, ks1, a.hi_offset, acts, acc);
     }
     // reduce: slots (lane ^ 32); for DOWN also hi/lo parts (lane ^ 16)
