@@ -129,6 +129,9 @@ __device__ __forceinline__ void stage_x(uint8_t* xl, __amdgpu_buffer_rsrc_t xr, 
 //            outside the unit's slot.
 constexpr int XM_LOAD = 0, XM_LDS = 1, XM_RING = 2;
 constexpr int kRing = 4;
+// ring record stride for S slots: room for 16 / S tokens (>= N) and the zero block
+template <int S>
+__host__ __device__ constexpr int ring_stride() { return (16 / S) * 256 + 16; }
 
 // NT tiles per wave: plain GEMV uses NT output tiles, SwiGLU NT/2 gate tiles
 // followed by NT/2 up tiles. S: slots (16 / S tokens per slot >= N). KPS:
@@ -167,7 +170,10 @@ __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
   // activation lane role: A row r = slot * T + token
   const int a_tok = r % T;
   if constexpr (XM == XM_LDS || XM == XM_RING) {
-    const int xs = a.N * 256 + 16;   // one k-step record: token t's 128 bf16 at 256 t, then 16 zero bytes
+    // one k-step record: token t's 128 bf16 at 256 t, then 16 zero bytes at
+    // 256 N; ring records take the stride of T tokens, a compile-time
+    // constant, so slot addresses fold into the LDS instructions' offsets
+    const int xs = XM == XM_RING ? ring_stride<S>() : a.N * 256 + 16;
     const int nrec = XM == XM_LDS ? a.x_nks : kRing;
     uint8_t* xl = reinterpret_cast<uint8_t*>(red) + (size_t)W * NT * 512 + (size_t)wave * nrec * xs;
     // per (cycle position, group): this lane's data or the record's zero block
@@ -198,34 +204,39 @@ __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
       // slot last read three calls before), and one call after that it is read.
       static_assert((2 * KPS) % kRing == 0, "the ring must divide the trip");
       const int nch = a.N * 16;
+      // Chunks past the record (c >= 16 N) load as zeros and are written
+      // onto the record's zero block, so neither side branches per lane; the
+      // second chunk is skipped (uniformly) when N <= 4.
+      const bool two = nch > 64;
+      const uint32_t sdst0 = (uint32_t)lane * 16u;
+      const uint32_t sdst1 = (uint32_t)min(lane + 64, nch) * 16u;
       auto ring_load = [&](u32x4 (&v)[2], int k) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
+          if (h == 1 && !two) { v[1] = u32x4{0u, 0u, 0u, 0u}; continue; }
           const int c = lane + 64 * h;
           const int t = c >> 4, col = k * 128 + (c & 15) * 8;
-          const bool data = c < nch && k < ks1 && col < a.K;
+          const bool data = (c < nch) & (k < ks1) & (col < a.K);
           v[h] = ld128(xr, data ? (uint32_t)(t * a.K + col) * 2u : kOOB);
         }
       };
       auto ring_store = [&](const u32x4 (&v)[2], int slot) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int c = lane + 64 * h;
-          if (c < nch) *reinterpret_cast<u32x4*>(xl + slot * xs + c * 16) = v[h];
-        }
+        uint8_t* rec = xl + slot * ring_stride<S>();
+        *reinterpret_cast<u32x4*>(rec + sdst0) = v[0];
+        if (two) *reinterpret_cast<u32x4*>(rec + sdst1) = v[1];
       };
       u32x4 stg[2][2];                 // records loaded, not yet written
       auto acts = [&](bf16x8 (&A)[4], int k, int pos) {
         ring_store(stg[pos & 1], (pos + 1) % kRing);   // record k + 1 (loaded two calls ago)
         ring_load(stg[pos & 1], k + 3);
-        const uint8_t* rec = xl + (pos % kRing) * xs;
+        const uint8_t* rec = xl + (pos % kRing) * ring_stride<S>();
         const int ckk = pos % C::KSTEPS;
 #pragma unroll
         for (int j = 0; j < 4; ++j) A[j] = *reinterpret_cast<const bf16x8*>(rec + off[ckk][j]);
       };
       auto pre = [&]() {
         // zero blocks; record ks0 written now, ks0 + 1 and ks0 + 2 staged
-        if (lane < kRing) *reinterpret_cast<u32x4*>(xl + lane * xs + a.N * 256) = u32x4{0u, 0u, 0u, 0u};
+        if (lane < kRing) *reinterpret_cast<u32x4*>(xl + lane * ring_stride<S>() + a.N * 256) = u32x4{0u, 0u, 0u, 0u};
         u32x4 v0[2];
         ring_load(v0, ks0);
         ring_load(stg[0], ks0 + 1);
@@ -457,7 +468,7 @@ hipError_t launch_s(const GemvArgs& a0, const LaunchShape& ls, bool swiglu, hipS
   a.x_nks = (ls.kpw + U - 1) / U * U + 1;
   const size_t rec = (size_t)a.N * 256 + 16;
   const size_t red = (size_t)ls.waves * NT * 128 * sizeof(float);
-  const size_t whole = (size_t)ls.waves * a.x_nks * rec, ring = (size_t)ls.waves * kRing * rec;
+  const size_t whole = (size_t)ls.waves * a.x_nks * rec, ring = (size_t)ls.waves * kRing * ring_stride<S>();
   const int xm = whole <= kMaxLdsActs ? XM_LDS : (ring <= kMaxLdsActs ? XM_RING : XM_LOAD);
   const size_t lds = red + (xm == XM_LDS ? whole : (xm == XM_RING ? ring : 0));
   if constexpr (NT >= 2) {
