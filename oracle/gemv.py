@@ -102,10 +102,12 @@ def moe_index(ids: np.ndarray, E: int):
 
 
 def moe(x: np.ndarray, ids: np.ndarray, gates: np.ndarray, W_gu: list, W_dn: list,
-        residual: np.ndarray | None = None):
+        residual: np.ndarray | None = None, gate_tol: np.ndarray | None = None):
     """MoE FFN reference. x [N][H] fp64, ids/gates [N][k], W_gu[e] [2I][H],
     W_dn[e] [H][I] (fp32 dequantised). Returns (y [N][H], T_y [N][H]).
-    Slots whose id is outside [0, E) contribute nothing."""
+    Slots whose id is outside [0, E) contribute nothing. gate_tol [N][k]:
+    a bound on how far the GPU's own mixing weights may be from `gates`
+    (device routing); it adds gate_tol * |o| per slot."""
     x = np.asarray(x, dtype=np.float64)
     N, k = ids.shape
     E = len(W_gu)
@@ -124,24 +126,51 @@ def moe(x: np.ndarray, ids: np.ndarray, gates: np.ndarray, W_gu: list, W_dn: lis
             y[t] += p * o[0]
             To = REL * (np.abs(h) @ np.abs(Wd).T) + Th @ np.abs(Wd).T + ABS
             T[t] += abs(p) * To[0]
+            if gate_tol is not None:
+                T[t] += float(gate_tol[t, j]) * (np.abs(o[0]) + To[0])
     return y, T
 
 
 def route_topk_softmax(logits: np.ndarray, k: int):
-    """Top-k experts per token (largest logit first, ties to the lower index)
-    and softmax weights over the selected logits (fp64, returned as fp32)."""
+    """Top-k experts per token and their mixing weights (Decapybara page,
+    CUDA kernel list: a top-8 softmax router).
+
+    Selection: largest logit first; equal logits (-0 equals +0) in increasing
+    expert order; a NaN logit ranks below every number, NaNs among
+    themselves in increasing order. Weights: softmax over the selected
+    logits, exp(l_j - l_0) / sum_i exp(l_i - l_0), in fp64, returned as fp32.
+    """
     logits = np.asarray(logits, dtype=np.float64)
     N, E = logits.shape
     ids = np.zeros((N, k), dtype=np.int32)
     gates = np.zeros((N, k), dtype=np.float32)
     for t in range(N):
-        order = sorted(range(E), key=lambda e: (-logits[t, e], e))[:k]
+        def key(e):
+            v = float(logits[t, e])
+            return (1, 0.0, e) if math.isnan(v) else (0, -v, e)
+        order = sorted(range(E), key=key)[:k]
         sel = np.array([logits[t, e] for e in order])
-        w = np.exp(sel - sel.max())
-        w = w / w.sum()
+        with np.errstate(invalid="ignore", over="ignore"):
+            w = np.exp(sel - sel[0])
+            w = w / w.sum()
         ids[t] = order
         gates[t] = w.astype(np.float32)
     return ids, gates
+
+
+def route_tolerance(logits: np.ndarray, ids: np.ndarray, gates_ref: np.ndarray) -> np.ndarray:
+    """Per-weight bound for an fp32 evaluation of the selected softmax
+    (d_j = l_j - l_0, e_j = exp(d_j), S = sum e_j, p_j = e_j / S, each step
+    rounded once, exp within 2 ulp): the relative error of p_j stays below
+    2^-24 (|d_j| + 4) for e_j, 2^-24 (max|d| + 4 + k) for S and 2^-24 for the
+    quotient; doubled for margin:
+        T_j = p_j * 2^-23 * (|d_j| + max_i |d_i| + 9 + k) + 2^-40
+    """
+    logits = np.asarray(logits, np.float64)
+    sel = np.take_along_axis(logits, np.asarray(ids, np.int64), 1)
+    d = np.abs(sel - sel[:, :1])
+    k = ids.shape[1]
+    return np.asarray(gates_ref, np.float64) * 2.0 ** -23 * (d + d.max(1, keepdims=True) + 9 + k) + 2.0 ** -40
 
 
 def exact_dot(xs, ws) -> "Fraction":

@@ -174,3 +174,57 @@ def test_router_topk_softmax():
         renorm = full[ids[t]] / full[ids[t]].sum()
         assert np.allclose(gates[t], renorm, rtol=1e-6)
         assert abs(float(gates[t].astype(np.float64).sum()) - 1.0) < 1e-6
+
+
+def _beats(a, ia, b, ib):
+    """True if logit a at index ia ranks above logit b at index ib: larger
+    number first, equal numbers by lower index, NaN below every number."""
+    na, nb = np.isnan(a), np.isnan(b)
+    if na or nb:
+        return (not na and nb) or (na and nb and ia < ib)
+    return a > b or (a == b and ia < ib)
+
+
+def test_router_selection_by_pairwise_rank():
+    """The router's selection equals the experts whose pairwise rank (number
+    of experts that beat them) is below k, in rank order; covers ties,
+    -0/+0, infinities and NaNs."""
+    rng = np.random.default_rng(17)
+    rows = [
+        np.array([1.0, np.nan, 3.0, -np.inf, 3.0, -0.0, 0.0, np.inf, np.nan, -2.0], np.float32),
+        np.zeros(10, np.float32),
+        np.full(10, np.nan, np.float32),
+        rng.integers(-2, 3, 10).astype(np.float32),
+    ]
+    for row in rows:
+        E = row.size
+        for k in (1, 3, E):
+            ids, _ = G.route_topk_softmax(row[None, :], k)
+            rank = [sum(_beats(row[f], f, row[e], e) for f in range(E)) for e in range(E)]
+            want = sorted((e for e in range(E) if rank[e] < k), key=lambda e: rank[e])
+            assert list(ids[0]) == want, (row, k)
+    ids, _ = G.route_topk_softmax(rows[0][None, :], 10)
+    assert list(ids[0]) == [7, 2, 4, 0, 5, 6, 9, 3, 1, 8]
+
+
+def test_router_tolerance_covers_fp32_and_rejects_larger_errors():
+    rng = np.random.default_rng(19)
+    logits = (rng.standard_normal((64, 128)) * 3).astype(np.float32)
+    ids, g = G.route_topk_softmax(logits, 8)
+    sel = np.take_along_axis(logits, ids.astype(np.int64), 1)
+    # an fp32 evaluation in the stated order
+    d = (sel - sel[:, :1]).astype(np.float32)
+    e = np.exp(d).astype(np.float32)
+    S = np.zeros(64, np.float32)
+    for j in range(8):
+        S = (S + e[:, j]).astype(np.float32)
+    p32 = (e / S[:, None]).astype(np.float32)
+    sel64 = sel.astype(np.float64)
+    ref = np.exp(sel64 - sel64[:, :1])
+    ref /= ref.sum(1, keepdims=True)
+    T = G.route_tolerance(logits, ids, ref)
+    assert np.all(np.abs(p32 - ref) <= T)
+    assert np.all(np.abs(g - ref) <= T)            # the oracle's own fp32 rounding
+    assert np.all(T < 1e-4 * ref + 1e-10)          # and the bound stays tight
+    bad = p32 * np.float32(1 + 2e-4)
+    assert np.any(np.abs(bad - ref) > T)
