@@ -353,6 +353,32 @@ def extras(qg, torch, dev, stream, layers, args):
         moe[f"N{n}"] = {"active_experts": uniq, "us": round(ms * 1e3, 2), "GB/s": round(b / (ms * 1e-3) / 1e9, 1)}
     res["moe"] = {"workload": "128 experts, H 2048, I 768, top-8, int4, 32 rotated copies", **moe}
     log("moe", res["moe"])
+
+    # the same MoE routed on the device in one launch (qgemv_moe_fused), with
+    # 16 seeded logit sets in rotation so the routing changes every call;
+    # algorithmic bytes: the selected experts' weights + x + logits + r + y
+    fused = {}
+    for n in (1, 2, 8):
+        sets = [synthetic.router_logits(rng, n, E) for _ in range(16)]
+        uniq = [len({int(e) for e in np.argsort(-lg.astype(np.float64), axis=1, kind="stable")[:, :k].reshape(-1)})
+                for lg in sets]
+        lt = [torch.from_numpy(lg).to(dev) for lg in sets]
+        xb = torch.from_numpy(synthetic.activations(rng, n, H)).to(dev)
+        rr = torch.from_numpy(synthetic.residual(rng, n, H)).to(dev)
+        nbytes = qg.moe_fused_workspace_bytes(E, H, I, n, k)
+        wsp = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+        yy = torch.empty((n, H), dtype=torch.float32, device=dev)
+        ms = timeit(lambda i: qg.qgemv_moe_fused("int4", *dbufs[i % copies], E, H, I, xb, lt[i % 16], k, yy, n, wsp,
+                                                 nbytes, residual=rr), 64)
+        b = float(np.mean(uniq)) * per_expert + n * H * 2 + n * E * 4 + n * H * 8
+        fused[f"N{n}"] = {"mean_active_experts": round(float(np.mean(uniq)), 2), "us": round(ms * 1e3, 2),
+                          "GB/s": round(b / (ms * 1e-3) / 1e9, 1), "frac": round(b / (ms * 1e-3) / 1e9 / PEAK_GBS, 4)}
+        err = int(wsp[12:16].cpu().view(torch.int32).item())
+        if err:
+            raise RuntimeError("qgemv_moe_fused reported a timed-out dependency wait")
+    res["moe_fused"] = {"workload": "128 experts, H 2048, I 768, top-8 routed on the device from fresh logits, int4, "
+                                    "one launch, 32 rotated copies", **fused}
+    log("moe_fused", res["moe_fused"])
     return res
 
 

@@ -58,6 +58,9 @@ def load(require_torch: bool = True):
         "qgemv_moe_workspace_bytes": (I32, [I32, I64, I64, I32, I32, PSZ]),
         "qgemv_moe": (I32, [I32, P, P, P, P, I32, I64, I64, P, P, P, I32, P, P, I32, P, SZ, P]),
         "qgemv_moe_index": (I32, [P, I32, I32, I32, P, P, P, P, P, P]),
+        "qgemv_moe_route": (I32, [P, I32, I32, I32, P, P, P]),
+        "qgemv_moe_fused_workspace_bytes": (I32, [I32, I64, I64, I32, I32, PSZ]),
+        "qgemv_moe_fused": (I32, [I32, P, P, P, P, I32, I64, I64, P, P, I32, P, P, I32, P, P, P, SZ, P]),
         "qgemv_dequant": (I32, [I32, P, P, I64, I64, P, P]),
         "qgemv_probe_read": (I32, [P, SZ, P, P]),
     }
@@ -73,7 +76,8 @@ def symbols() -> list[str]:
     """Names of the entry points the binding declares (the C ABI)."""
     return ["qgemv_strerror", "qgemv_version", "qgemv_packed_bytes", "qgemv_expert_stride", "qgemv_pack",
             "qgemv_pack_codes", "qgemv", "qgemv_swiglu", "qgemv_moe_workspace_bytes", "qgemv_moe",
-            "qgemv_moe_index", "qgemv_dequant", "qgemv_probe_read"]
+            "qgemv_moe_index", "qgemv_moe_route", "qgemv_moe_fused_workspace_bytes", "qgemv_moe_fused",
+            "qgemv_dequant", "qgemv_probe_read"]
 
 
 def strerror(status: int) -> str:
@@ -173,6 +177,26 @@ def qgemv_moe(fmt, wq_gu, ws_gu, wq_dn, ws_dn, E: int, H: int, I: int, x, ids, g
 def qgemv_moe_index(ids, N: int, top_k: int, E: int, counts, offsets, pairs, active, meta, stream=None) -> None:
     _check(load().qgemv_moe_index(_ptr(ids), N, top_k, E, _ptr(counts), _ptr(offsets), _ptr(pairs), _ptr(active),
                                   _ptr(meta), _stream(stream)), "qgemv_moe_index")
+
+
+def qgemv_moe_route(logits, N: int, E: int, top_k: int, ids, gates, stream=None) -> None:
+    _check(load().qgemv_moe_route(_ptr(logits), N, E, top_k, _ptr(ids), _ptr(gates), _stream(stream)),
+           "qgemv_moe_route")
+
+
+def moe_fused_workspace_bytes(E: int, H: int, I: int, N: int, top_k: int) -> int:
+    b = ctypes.c_size_t()
+    _check(load(False).qgemv_moe_fused_workspace_bytes(E, H, I, N, top_k, ctypes.byref(b)),
+           "qgemv_moe_fused_workspace_bytes")
+    return b.value
+
+
+def qgemv_moe_fused(fmt, wq_gu, ws_gu, wq_dn, ws_dn, E: int, H: int, I: int, x, logits, top_k: int, y, N: int,
+                    workspace, workspace_bytes: int, residual=None, ids_out=None, gates_out=None,
+                    stream=None) -> None:
+    _check(load().qgemv_moe_fused(_fmt(fmt), _ptr(wq_gu), _ptr(ws_gu), _ptr(wq_dn), _ptr(ws_dn), E, H, I, _ptr(x),
+                                  _ptr(logits), top_k, _ptr(residual), _ptr(y), N, _ptr(ids_out), _ptr(gates_out),
+                                  _ptr(workspace), workspace_bytes, _stream(stream)), "qgemv_moe_fused")
 
 
 def qgemv_dequant(fmt, wq, ws, M: int, K: int, out, stream=None) -> None:

@@ -24,6 +24,10 @@ LIB = os.path.join(HERE, "libqgemv.so")
 
 ARCH = "gfx950"
 HIP_SOURCES = ["gemv.hip", "moe.hip"]
+# moe.hip: keep single-lane atomics as written (the atomic optimizer would
+# wave-aggregate the work-ticket claim and wait for its result at once,
+# instead of when the ticket is first needed)
+EXTRA_FLAGS = {"moe.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
 HOST_SOURCES = ["pack.cpp"]
 
 
@@ -56,7 +60,7 @@ def build(verbose: bool = False) -> str:
             continue
         obj = os.path.join(BUILD, src + ".o")
         _run([hipcc, "--offload-arch=" + ARCH, *common,
-              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", *EXTRA_FLAGS.get(src, []),
               "-c", path, "-o", obj])
         objs.append(obj)
     for src in HOST_SOURCES:

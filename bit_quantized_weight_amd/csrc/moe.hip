@@ -30,6 +30,7 @@
 #include "kloop.hpp"
 #include "layout.hpp"
 #include "qgemv.h"
+#include "route.hpp"
 
 namespace qg {
 
@@ -176,6 +177,7 @@ struct MoeArgs {
   const void* in;                  // gate/up: x bf16 [N][K]; down: h as bf16 hi and lo planes [2][NK][K]
   uint32_t in_bytes;
   float* out;                      // gate/up: h planes (bf16) [2][NK][Mout]; down: o fp32 [NK][Mout]
+  uint32_t out_bytes;
   const int32_t* ids;              // [N][top_k] selected experts
   int E, top_k, NK;
   int Mout, K, KS, G;
@@ -189,22 +191,36 @@ __device__ __forceinline__ void split_bf16(float v, __bf16& hi, __bf16& lo) {
   lo = (__bf16)(v - (float)hi);
 }
 
+// Buffer accesses at device scope (cache policy sc1): they bypass the
+// per-XCD caches that are not coherent with each other, so data one
+// workgroup writes this way is seen by a workgroup on another XCD once the
+// writer's stores have completed (s_waitcnt) before it bumps a counter.
+constexpr int kDeviceScope = 16;
+__device__ __forceinline__ u32x4 ld128s_dev(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kDeviceScope);
+}
+__device__ __forceinline__ float ld_f32_dev(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kDeviceScope));
+}
+
+struct NoWait {
+  __device__ void operator()() const {}
+};
+
+// One work item of the expert GEMVs: output row block rb of expert e for
+// the cnt routed entries pairs[0..cnt) (flat t * top_k + j, ascending).
 // DOWN = false: gate/up + SwiGLU (NT = 2*TO tiles: gate then up)
 // DOWN = true:  down projection (NT = TO tiles)
-template <int FMT, int NT, bool DOWN>
-__global__ __launch_bounds__(512) void k_moe_gemv(MoeArgs a) {
-  extern __shared__ float red[];  // [W][NT][32][4]
-  __shared__ uint32_t s_bits[kMaxExperts / 32];
-  __shared__ int s_route[2 + 64];
+// COH: the item runs inside the single-launch MoE kernel, where another
+// workgroup consumes its output: outputs are stored at device scope, and the
+// down projection reads h at device scope after wait() (run by every wave
+// once its first weight loads are in flight) has seen h complete.
+// red: LDS of W * NT * 32 * 4 floats. Ends with a workgroup barrier.
+template <int FMT, int NT, bool DOWN, bool COH, class Wait = NoWait>
+__device__ __forceinline__ void moe_item(const MoeArgs& a, int e, int cnt, const int* pairs, int rb, float* red,
+                                         const Wait& wait = Wait()) {
   constexpr int TO = DOWN ? NT : NT / 2;
   constexpr int ROWS = DOWN ? 4 : 8;   // routed rows per MFMA pass
-  if (threadIdx.x < 64) route_slot(a.ids, a.NK, a.E, blockIdx.y, s_bits, s_route);
-  __syncthreads();
-  const int e = s_route[0];
-  if (e < 0) return;                   // uniform: fewer selected experts than slots
-  const int cnt = s_route[1];
-  const int* pairs = s_route + 2;
-
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
   const int W = blockDim.x >> 6;
@@ -213,11 +229,12 @@ __global__ __launch_bounds__(512) void k_moe_gemv(MoeArgs a) {
   const __amdgpu_buffer_rsrc_t wq = make_rsrc(a.wq + (uint64_t)e * a.wq_stride, a.wq_bytes);
   const __amdgpu_buffer_rsrc_t ws = make_rsrc(a.ws + (uint64_t)e * a.ws_stride, a.ws_bytes);
   const __amdgpu_buffer_rsrc_t inr = make_rsrc(a.in, a.in_bytes);
+  const __amdgpu_buffer_rsrc_t outr = make_rsrc(a.out, a.out_bytes);
 
   int tile[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    int ot = blockIdx.x * TO + (t % TO);
+    int ot = rb * TO + (t % TO);
     ot = ot < a.out_tiles ? ot : a.out_tiles - 1;
     tile[t] = (!DOWN && t >= TO) ? a.up_tile0 + ot : ot;
   }
@@ -250,12 +267,15 @@ __global__ __launch_bounds__(512) void k_moe_gemv(MoeArgs a) {
       const int part = (r >> 2) & 1;
       const uint32_t base = (row_ok ? (uint32_t)((part * a.NK + pflat) * a.K + 8 * s) * 2u : kAbsentRow) + slot_term;
       auto aload = [&](int g, uint32_t adj) -> bf16x8 {
+        if constexpr (COH) return __builtin_bit_cast(bf16x8, ld128s_dev(inr, base + adj, (uint32_t)g * 64u));
         return __builtin_bit_cast(bf16x8, ld128s(inr, base + adj, (uint32_t)g * 64u));
       };
       auto acts = [&](bf16x8 (&A)[4], int k, int pos) {
         load_acts<FMT, 2>(A, k, ks1, a.G, pos % Cyc<FMT, 2>::KSTEPS, aload);
       };
-      kloop<FMT, NT, 2, 2, 1>(wq, ws, tile, a.KS, ks0, ks1, a.hi_offset, acts, acc);
+      // the wait runs once per item, before the first pass reads h
+      if (c0 == 0) kloop<FMT, NT, 2, 2, 1>(wq, ws, tile, a.KS, ks0, ks1, a.hi_offset, acts, acc, wait);
+      else kloop<FMT, NT, 2, 2, 1>(wq, ws, tile, a.KS, ks0, ks1, a.hi_offset, acts, acc);
     }
     // reduce: slots (lane ^ 32); for DOWN also hi/lo parts (lane ^ 16)
 #pragma unroll
@@ -282,7 +302,7 @@ __global__ __launch_bounds__(512) void k_moe_gemv(MoeArgs a) {
     for (int o = threadIdx.x; o < n_out; o += blockDim.x) {
       const int to = o / (16 * ROWS), rem = o % (16 * ROWS);
       const int rr = rem / 16, row = rem % 16;
-      const int ot = blockIdx.x * TO + to;
+      const int ot = rb * TO + to;
       const int col = ot * 16 + row;
       if (rr >= nrows || ot >= a.out_tiles || col >= a.Mout) continue;
       const int l = DOWN ? row : row + 16 * (rr >> 2), i = DOWN ? rr : (rr & 3);
@@ -291,7 +311,12 @@ __global__ __launch_bounds__(512) void k_moe_gemv(MoeArgs a) {
       v *= st;
       const int pf = pairs[c0 + rr];
       if constexpr (DOWN) {
-        a.out[(size_t)pf * a.Mout + col] = v;
+        if constexpr (COH) {
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), outr,
+                                                (uint32_t)(pf * a.Mout + col) * 4u, 0, kDeviceScope);
+        } else {
+          a.out[(size_t)pf * a.Mout + col] = v;
+        }
       } else {
         float u = 0.f;
         for (int w = 0; w < W; ++w) u += red[(((size_t)w * NT + TO + to) * 32 + l) * 4 + i];
@@ -299,13 +324,32 @@ __global__ __launch_bounds__(512) void k_moe_gemv(MoeArgs a) {
         const float hv = v / (1.0f + expf(-v)) * u;
         __bf16 hi, lo;
         split_bf16(hv, hi, lo);
-        __bf16* hs = (__bf16*)a.out;             // hi plane [NK][I], then lo plane
-        hs[(size_t)pf * a.Mout + col] = hi;
-        hs[((size_t)a.NK + pf) * a.Mout + col] = lo;
+        if constexpr (COH) {
+          const uint32_t o0 = (uint32_t)(pf * a.Mout + col) * 2u, o1 = (uint32_t)((a.NK + pf) * a.Mout + col) * 2u;
+          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, hi), outr, o0, 0, kDeviceScope);
+          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, lo), outr, o1, 0, kDeviceScope);
+        } else {
+          __bf16* hs = (__bf16*)a.out;             // hi plane [NK][I], then lo plane
+          hs[(size_t)pf * a.Mout + col] = hi;
+          hs[((size_t)a.NK + pf) * a.Mout + col] = lo;
+        }
       }
     }
     __syncthreads();
   }
+}
+
+// Grid (row blocks, active-expert slot): routes in LDS, then one item.
+template <int FMT, int NT, bool DOWN>
+__global__ __launch_bounds__(512) void k_moe_gemv(MoeArgs a) {
+  extern __shared__ float red[];  // [W][NT][32][4]
+  __shared__ uint32_t s_bits[kMaxExperts / 32];
+  __shared__ int s_route[2 + 64];
+  if (threadIdx.x < 64) route_slot(a.ids, a.NK, a.E, blockIdx.y, s_bits, s_route);
+  __syncthreads();
+  const int e = s_route[0];
+  if (e < 0) return;                   // uniform: fewer selected experts than slots
+  moe_item<FMT, NT, DOWN, false>(a, e, s_route[1], s_route + 2, blockIdx.x, red);
 }
 
 __global__ __launch_bounds__(256) void k_moe_combine(const float* o, const int32_t* ids, const float* gates,
@@ -330,6 +374,212 @@ __global__ __launch_bounds__(256) void k_moe_combine(const float* o, const int32
   for (int j = 0; j < 8; ++j)
     if (j < top_k && ev[j] >= 0 && ev[j] < E) v = fmaf(pv[j], ov[j], v);
   y[i] = v;
+}
+
+// qgemv_moe_route: one wave per token, 4 tokens per workgroup.
+__global__ __launch_bounds__(256) void k_moe_route(const float* logits, int N, int E, int top_k, int32_t* ids,
+                                                   float* gates) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= N) return;                 // uniform per wave
+  const int lane = threadIdx.x & 63;
+  int id;
+  float g;
+  route_token_any(logits + (size_t)t * E, E, top_k, &id, &g);
+  if (lane < top_k) {
+    ids[t * top_k + lane] = id;
+    gates[t * top_k + lane] = g;
+  }
+}
+
+// ---- single-launch MoE FFN (few routed rows) ---------------------------------
+// One workgroup of four waves per work item, launched in item order: first
+// one item per (slot, gate/up row block), then one per 16-column block of the
+// output y.
+//   gate/up item: writes its rows of h at device scope, then counts itself in
+//     h_done[slot]; the item that completes the slot clears h_done[slot] and
+//     raises one ready flag per output block (each flag in its own 64-byte
+//     line, so no two waiting waves poll the same address).
+//   output item: wave w computes o = h . W_dn[e] for slots w, w + 4, ... over
+//     the whole K, its weight loads issued before it polls (bounded) and clears
+//     its (slot, block) flag and reads h at device scope; the o values meet in
+//     LDS and the workgroup sums y = r + sum_j p_j o_j in fixed j order.
+// Deadlock-free without co-residency: workgroups are dispatched in increasing
+// order on every XCD, gate/up workgroups precede every output workgroup and
+// never wait, so a waiting wave only waits for workgroups already running or
+// done. A time-out sets the sticky error word and lets the kernel finish.
+// Every counter and flag is cleared by its last user, so the workspace is
+// zero again after each call.
+struct MoeFusedArgs {
+  MoeArgs gu, dn;
+  const float* logits;     // [N][E]
+  const float* res;        // [N][H] or null
+  float* y;                // [N][H]
+  int32_t* ids_out;        // [N][top_k] or null
+  float* gates_out;        // [N][top_k] or null
+  uint32_t* ctr;           // workspace counters (see kCtr*)
+  int N, H, E, top_k, NK, slots;
+  int nA, nB;              // gate/up row blocks per slot; 16-column output blocks
+};
+constexpr int kFusedMaxRows = 16;           // N * top_k handled by the single launch
+constexpr int kFusedWaves = 4;              // waves per workgroup of the single launch
+// counter words: [3] sticky error, [4, 4 + 16) h_done per slot, then ready
+// flags [slot][output block] at kReadyStride-word spacing from word 32
+constexpr int kCtrError = 3, kCtrH = 4, kReadyWord = 32;
+constexpr int kReadyStride = 16;            // 64 bytes per flag
+constexpr uint32_t kSpinLimit = 1u << 20;   // polls before a wait gives up
+
+__device__ __forceinline__ uint32_t ctr_load(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ctr_add(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void ctr_store(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// o of one expert for one 16-row tile of the down projection, computed by one
+// wave over the whole K: o_lds[pair][row] for the expert's cnt pairs.
+template <int FMT, class Wait>
+__device__ __forceinline__ void down_tile_wave(const MoeArgs& a, int e, int cnt, const int* pairs, int rt,
+                                               float* o_lds, const Wait& wait) {
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15, s = lane >> 4;
+  const __amdgpu_buffer_rsrc_t wq = make_rsrc(a.wq + (uint64_t)e * a.wq_stride, a.wq_bytes);
+  const __amdgpu_buffer_rsrc_t ws = make_rsrc(a.ws + (uint64_t)e * a.ws_stride, a.ws_bytes);
+  const __amdgpu_buffer_rsrc_t inr = make_rsrc(a.in, a.in_bytes);
+  const int tile[1] = {rt};
+  float st = 1.0f;
+  if constexpr (FMT == NVFP4) st = __builtin_bit_cast(float, ld32(ws, a.st_offset));
+  const uint32_t slot_term = lane_slot_term<FMT, 2>(lane);
+  for (int c0 = 0; c0 < cnt; c0 += 4) {
+    const int nrows = min(4, cnt - c0);
+    const int ar = r & 3;
+    const bool row_ok = ar < nrows;
+    const int pflat = row_ok ? pairs[c0 + ar] : 0;
+    const int part = (r >> 2) & 1;   // A rows 8*slot + 4*part + pair: hi / lo plane of h
+    const uint32_t base = (row_ok ? (uint32_t)((part * a.NK + pflat) * a.K + 8 * s) * 2u : kAbsentRow) + slot_term;
+    auto aload = [&](int g, uint32_t adj) -> bf16x8 {
+      return __builtin_bit_cast(bf16x8, ld128s_dev(inr, base + adj, (uint32_t)g * 64u));
+    };
+    auto acts = [&](bf16x8 (&A)[4], int k, int pos) {
+      load_acts<FMT, 2>(A, k, a.KS, a.G, pos % Cyc<FMT, 2>::KSTEPS, aload);
+    };
+    f32x4 acc[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
+    if (c0 == 0) kloop<FMT, 1, 2, 3, 1>(wq, ws, tile, a.KS, 0, a.KS, a.hi_offset, acts, acc, wait);
+    else kloop<FMT, 1, 2, 3, 1>(wq, ws, tile, a.KS, 0, a.KS, a.hi_offset, acts, acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[0][i] += __shfl_xor(acc[0][i], 32);   // slots
+      acc[0][i] += __shfl_xor(acc[0][i], 16);   // hi + lo parts
+    }
+    if (lane < 16 && rt * 16 + lane < a.Mout) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (i < nrows) o_lds[pairs[c0 + i] * 16 + lane] = acc[0][i] * st;
+    }
+  }
+}
+
+template <int FMT>
+__global__ __launch_bounds__(64 * kFusedWaves) void k_moe_fused(MoeFusedArgs f) {
+  extern __shared__ float red[];          // [4][2][32][4] (gate/up), then o [16][16]
+  __shared__ int32_t s_ids[64];
+  __shared__ float s_gates[64];
+  __shared__ int s_v[64];
+  __shared__ int s_pairs[64];
+  __shared__ int s_slot_e[64], s_slot_off[64], s_slot_cnt[64];
+  __shared__ int s_meta[4];               // n_active, last-of-slot flag
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int W = blockDim.x >> 6;
+  uint32_t* ctr = f.ctr;
+  uint32_t* ready = ctr + kReadyWord;
+
+  // router: every workgroup routes every token itself (no launch, no wait),
+  // one wave per token
+  for (int t = wave; t < f.N; t += W) {
+    int id;
+    float g;
+    route_token_any(f.logits + (size_t)t * f.E, f.E, f.top_k, &id, &g);
+    if (lane < f.top_k) {
+      s_ids[t * f.top_k + lane] = id;
+      s_gates[t * f.top_k + lane] = g;
+    }
+  }
+  __syncthreads();
+  // routing index: slot a = a-th smallest active expert, its entries in (t, j) order
+  if (wave == 0) {
+    const Route R = route_lanes(s_ids, f.NK, f.E, s_v);
+    if (R.v >= 0) {
+      int below = 0, same_before = 0, same = 0;
+      for (int j = 0; j < f.NK; ++j) {
+        const int u = s_v[j];
+        below += u >= 0 && u < R.v;
+        same_before += u == R.v && j < lane;
+        same += u == R.v;
+      }
+      s_pairs[below + same_before] = lane;
+      if (R.first) {
+        s_slot_e[R.rank] = R.v;
+        s_slot_off[R.rank] = below;
+        s_slot_cnt[R.rank] = same;
+      }
+    }
+    if (lane == 0) s_meta[0] = __builtin_popcountll(R.act);
+  }
+  if (blockIdx.x == 0 && threadIdx.x < f.NK) {
+    if (f.ids_out) f.ids_out[threadIdx.x] = s_ids[threadIdx.x];
+    if (f.gates_out) f.gates_out[threadIdx.x] = s_gates[threadIdx.x];
+  }
+  __syncthreads();
+  const int n_active = s_meta[0];
+  const int nA_all = f.slots * f.nA;
+  const int tk = blockIdx.x;
+
+  if (tk < nA_all) {
+    const int a = tk / f.nA, rb = tk - a * f.nA;
+    if (a >= n_active) return;            // uniform
+    moe_item<FMT, 2, false, true>(f.gu, s_slot_e[a], s_slot_cnt[a], s_pairs + s_slot_off[a], rb, red);
+    __builtin_amdgcn_s_waitcnt(0);        // this thread's h stores have completed
+    __syncthreads();
+    if (threadIdx.x == 0) s_meta[1] = ctr_add(ctr + kCtrH + a, 1u) == (uint32_t)(f.nA - 1);
+    __syncthreads();
+    if (s_meta[1]) {                      // h of this slot is complete: release the output blocks
+      if (threadIdx.x == 0) ctr_store(ctr + kCtrH + a, 0u);
+      for (int b = threadIdx.x; b < f.nB; b += blockDim.x) ctr_store(ready + ((size_t)a * f.nB + b) * kReadyStride, 1u);
+    }
+    return;
+  }
+
+  // output block rt: 16 columns of y for every token
+  const int rt = tk - nA_all;
+  float* o_lds = red + kFusedWaves * 2 * 32 * 4;   // [NK][16]
+  for (int a = wave; a < n_active; a += W) {
+    uint32_t* flag = ready + ((size_t)a * f.nB + rt) * kReadyStride;
+    auto wait = [&]() {
+      uint32_t it = 0;
+      while (ctr_load(flag) == 0u) {
+        if (++it >= kSpinLimit) {
+          if (lane == 0) atomicOr(ctr + kCtrError, 1u);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+      ctr_store(flag, 0u);                // this wave is the flag's only reader
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    };
+    down_tile_wave<FMT>(f.dn, s_slot_e[a], s_slot_cnt[a], s_pairs + s_slot_off[a], rt, o_lds, wait);
+  }
+  __syncthreads();
+  for (int o = threadIdx.x; o < f.N * 16; o += blockDim.x) {
+    const int t = o >> 4, c = o & 15;
+    const int col = rt * 16 + c;
+    if (col >= f.H) continue;
+    float v = f.res ? f.res[(size_t)t * f.H + col] : 0.0f;
+    for (int j = 0; j < f.top_k; ++j) v = fmaf(s_gates[t * f.top_k + j], o_lds[(t * f.top_k + j) * 16 + c], v);
+    f.y[(size_t)t * f.H + col] = v;
+  }
 }
 
 }  // namespace qg
@@ -390,34 +640,35 @@ extern "C" int qgemv_moe_index(const int32_t* ids, int N, int top_k, int E, int3
   return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
 }
 
-extern "C" int qgemv_moe(int fmt, const void* wq_gu, const void* ws_gu, const void* wq_dn, const void* ws_dn, int E,
-                         int64_t H, int64_t I, const void* x, const int32_t* ids, const float* gates, int top_k,
-                         const float* residual, float* y, int N, void* workspace, size_t workspace_bytes,
-                         hipStream_t stream) {
+namespace {
+
+void launch_route(const float* logits, int N, int E, int top_k, int32_t* ids, float* gates, hipStream_t stream) {
+  hipLaunchKernelGGL(k_moe_route, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, stream, logits, N, E, top_k, ids, gates);
+}
+
+// Shared validation and argument set-up of both MoE entry points (ids and
+// gates are checked by the callers). h: two bf16 planes [2][NK][I]; o: fp32
+// [NK][H].
+int moe_setup(int fmt, const void* wq_gu, const void* ws_gu, const void* wq_dn, const void* ws_dn, int E, int64_t H,
+              int64_t I, const void* x, int top_k, const float* residual, const float* y, int N, void* h, float* o,
+              MoeArgs* gu_out, MoeArgs* dn_out, int* wgu_out, int* wdn_out) {
   if (fmt < INT4 || fmt > NVFP4) return QGEMV_EFORMAT;
-  if (!wq_gu || !ws_gu || !wq_dn || !ws_dn || !x || !ids || !gates || !y) return QGEMV_EINVAL;
+  if (!wq_gu || !ws_gu || !wq_dn || !ws_dn || !x || !y) return QGEMV_EINVAL;
   if (E < 1 || H < 32 || I < 16) return QGEMV_EINVAL;
   if (E > kMaxExperts) return QGEMV_EUNSUPPORTED;
   if (N < 1 || N > 8 || top_k < 1 || top_k > 8) return QGEMV_EUNSUPPORTED;
   if (H % 32 || I % 32) return QGEMV_EALIGN;
-  if (!al16(wq_gu) || !al16(ws_gu) || !al16(wq_dn) || !al16(ws_dn) || !al16(x) || !al4(ids) || !al4(gates) ||
-      !al4(y) || (residual && !al4(residual)))
+  if (!al16(wq_gu) || !al16(ws_gu) || !al16(wq_dn) || !al16(ws_dn) || !al16(x) || !al4(y) ||
+      (residual && !al4(residual)))
     return QGEMV_EALIGN;
-  if (!workspace) return QGEMV_EWORKSPACE;
-  if (!al16(workspace)) return QGEMV_EALIGN;
-  const MoeLayout L = moe_layout(E, H, I, N, top_k);
-  if (workspace_bytes < L.total) return QGEMV_EWORKSPACE;
   Geom ggu, gdn;
   if (!geom(fmt, 2 * I, H, &ggu) || !geom(fmt, H, I, &gdn)) return QGEMV_EINVAL;
   if ((uint64_t)E * up256(ggu.wq_bytes) >= (1ull << 40)) return QGEMV_EUNSUPPORTED;
   // activation bytes stay below 2^25 (x: N*H bf16; h: N*top_k*I fp32)
   if ((uint64_t)N * H * 2 >= (1ull << 25) || (uint64_t)N * top_k * I * 4 >= (1ull << 25)) return QGEMV_EUNSUPPORTED;
+  if ((uint64_t)N * top_k * H * 4 >= (1ull << 31)) return QGEMV_EUNSUPPORTED;
   if (ggu.wq_bytes >= (1ull << 31) || gdn.wq_bytes >= (1ull << 31)) return QGEMV_EUNSUPPORTED;
-  if (ggu.wq_bytes >= (1ull << 32) || gdn.wq_bytes >= (1ull << 32)) return QGEMV_EUNSUPPORTED;
   const int NK = N * top_k;
-  uint8_t* wsp = (uint8_t*)workspace;
-  float* h = (float*)(wsp + L.h_off);
-  float* o = (float*)(wsp + L.o_off);
 
   MoeArgs gu;
   gu.wq = (const uint8_t*)wq_gu;
@@ -430,8 +681,9 @@ extern "C" int qgemv_moe(int fmt, const void* wq_gu, const void* ws_gu, const vo
   gu.st_offset = (uint32_t)ggu.st_offset;
   gu.in = x;
   gu.in_bytes = (uint32_t)((int64_t)N * H * 2);
-  gu.out = h;
-  gu.ids = ids;
+  gu.out = (float*)h;
+  gu.out_bytes = (uint32_t)((size_t)NK * I * 4);   // two bf16 planes
+  gu.ids = nullptr;
   gu.E = E;
   gu.top_k = top_k;
   gu.NK = NK;
@@ -459,6 +711,7 @@ extern "C" int qgemv_moe(int fmt, const void* wq_gu, const void* ws_gu, const vo
   dn.in = h;
   dn.in_bytes = (uint32_t)((size_t)NK * I * 4);   // two bf16 planes
   dn.out = o;
+  dn.out_bytes = (uint32_t)((size_t)NK * H * 4);
   dn.Mout = (int)H;
   dn.K = (int)I;
   dn.KS = (int)gdn.KS;
@@ -467,9 +720,36 @@ extern "C" int qgemv_moe(int fmt, const void* wq_gu, const void* ws_gu, const vo
   dn.up_tile0 = 0;
   const int wdn = many ? 1 : (int)std::min<int64_t>(8, std::max<int64_t>(1, (gdn.KS + 3) / 4));
   dn.ks_per_wave = (int)((gdn.KS + wdn - 1) / wdn);
+  *gu_out = gu;
+  *dn_out = dn;
+  *wgu_out = wgu;
+  *wdn_out = wdn;
+  return QGEMV_OK;
+}
 
-  if (I % 16) return QGEMV_EALIGN;
-  const int slots = std::min(E, NK);   // one grid row per active-expert slot
+}  // namespace
+
+extern "C" int qgemv_moe(int fmt, const void* wq_gu, const void* ws_gu, const void* wq_dn, const void* ws_dn, int E,
+                         int64_t H, int64_t I, const void* x, const int32_t* ids, const float* gates, int top_k,
+                         const float* residual, float* y, int N, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  if (!ids || !gates) return QGEMV_EINVAL;
+  if (!al4(ids) || !al4(gates)) return QGEMV_EALIGN;
+  if (!workspace) return QGEMV_EWORKSPACE;
+  if (!al16(workspace)) return QGEMV_EALIGN;
+  if (E >= 1 && H >= 1 && I >= 1 && N >= 1 && N <= 8 && top_k >= 1 && top_k <= 8 &&
+      workspace_bytes < moe_layout(E, H, I, N, top_k).total)
+    return QGEMV_EWORKSPACE;
+  const MoeLayout L = moe_layout(E, H, I, N, top_k);
+  uint8_t* wsp = (uint8_t*)workspace;
+  MoeArgs gu, dn;
+  int wgu, wdn;
+  const int rc = moe_setup(fmt, wq_gu, ws_gu, wq_dn, ws_dn, E, H, I, x, top_k, residual, y, N, wsp + L.h_off,
+                           (float*)(wsp + L.o_off), &gu, &dn, &wgu, &wdn);
+  if (rc) return rc;
+  gu.ids = ids;
+  dn.ids = ids;
+  const int slots = std::min(E, gu.NK);   // one grid row per active-expert slot
   switch (fmt) {
     case INT4: launch_moe_pair<INT4>(gu, dn, wgu, wdn, slots, stream); break;
     case INT5: launch_moe_pair<INT5>(gu, dn, wgu, wdn, slots, stream); break;
@@ -477,7 +757,119 @@ extern "C" int qgemv_moe(int fmt, const void* wq_gu, const void* ws_gu, const vo
     default: launch_moe_pair<NVFP4>(gu, dn, wgu, wdn, slots, stream); break;
   }
   const int64_t tot = (int64_t)N * H;
-  hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, stream, o, ids, gates,
-                     residual, y, N, (int)H, top_k, E);
+  hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, stream,
+                     (const float*)(wsp + L.o_off), ids, gates, residual, y, N, (int)H, top_k, E);
   return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
+}
+
+extern "C" int qgemv_moe_route(const float* logits, int N, int E, int top_k, int32_t* ids, float* gates,
+                               hipStream_t stream) {
+  if (!logits || !ids || !gates) return QGEMV_EINVAL;
+  if (N < 1 || E < 1 || top_k < 1) return QGEMV_EINVAL;
+  if (top_k > 64 || top_k > E || E > kMaxExperts || (int64_t)N * E >= (1ll << 31)) return QGEMV_EUNSUPPORTED;
+  if (!al4(logits) || !al4(ids) || !al4(gates)) return QGEMV_EALIGN;
+  launch_route(logits, N, E, top_k, ids, gates, stream);
+  return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
+}
+
+namespace {
+
+struct FusedLayout {
+  size_t ctr_bytes, route_off, h_off, o_off, total;
+};
+
+// Counters and flags first (their size depends on H only, so calls with the
+// same H may share a workspace whatever their N, E, I), then ids and weights
+// of the routing (when the caller passes no buffers for them), h and o.
+FusedLayout fused_layout(int64_t H, int64_t I, int N, int top_k) {
+  const size_t NK = (size_t)N * top_k;
+  const size_t nB = (size_t)((H + 15) / 16);
+  FusedLayout L;
+  L.ctr_bytes = up256(((size_t)kReadyWord + (size_t)kFusedMaxRows * nB * kReadyStride) * 4);
+  L.route_off = L.ctr_bytes;
+  L.h_off = L.route_off + 512;            // 64 ids + 64 weights
+  L.o_off = L.h_off + up256(NK * (size_t)I * 4);
+  L.total = L.o_off + up256(NK * (size_t)H * 4);
+  return L;
+}
+
+template <int FMT>
+hipError_t launch_fused(const MoeFusedArgs& f, hipStream_t stream) {
+  const size_t lds = (size_t)(kFusedWaves * 2 * 32 * 4 + kFusedMaxRows * 16) * sizeof(float);
+  const unsigned grid = (unsigned)(f.slots * f.nA + f.nB);
+  hipLaunchKernelGGL(k_moe_fused<FMT>, dim3(grid), dim3(64 * kFusedWaves), lds, stream, f);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+extern "C" int qgemv_moe_fused_workspace_bytes(int E, int64_t H, int64_t I, int N, int top_k, size_t* bytes) {
+  if (!bytes || E < 1 || H < 1 || I < 1) return QGEMV_EINVAL;
+  if (N < 1 || N > 8 || top_k < 1 || top_k > 8) return QGEMV_EUNSUPPORTED;
+  *bytes = fused_layout(H, I, N, top_k).total;
+  return QGEMV_OK;
+}
+
+extern "C" int qgemv_moe_fused(int fmt, const void* wq_gu, const void* ws_gu, const void* wq_dn, const void* ws_dn,
+                               int E, int64_t H, int64_t I, const void* x, const float* logits, int top_k,
+                               const float* residual, float* y, int N, int32_t* ids_out, float* gates_out,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!logits) return QGEMV_EINVAL;
+  if (!al4(logits) || (ids_out && !al4(ids_out)) || (gates_out && !al4(gates_out))) return QGEMV_EALIGN;
+  if (!workspace) return QGEMV_EWORKSPACE;
+  if (!al16(workspace)) return QGEMV_EALIGN;
+  if (E >= 1 && top_k > E) return QGEMV_EUNSUPPORTED;
+  if (E >= 1 && H >= 1 && I >= 1 && N >= 1 && N <= 8 && top_k >= 1 && top_k <= 8 &&
+      workspace_bytes < fused_layout(H, I, N, top_k).total)
+    return QGEMV_EWORKSPACE;
+  const FusedLayout L = fused_layout(H, I, N, top_k);
+  uint8_t* wsp = (uint8_t*)workspace;
+  MoeFusedArgs f;
+  int wgu, wdn;
+  const int rc = moe_setup(fmt, wq_gu, ws_gu, wq_dn, ws_dn, E, H, I, x, top_k, residual, y, N, wsp + L.h_off,
+                           (float*)(wsp + L.o_off), &f.gu, &f.dn, &wgu, &wdn);
+  if (rc) return rc;
+  f.logits = logits;
+  f.res = residual;
+  f.y = y;
+  f.ctr = (uint32_t*)wsp;
+  f.N = N;
+  f.H = (int)H;
+  f.E = E;
+  f.top_k = top_k;
+  f.NK = N * top_k;
+  f.slots = std::min(E, f.NK);
+  if (f.NK > kFusedMaxRows) {
+    // many routed rows: bandwidth-bound; the router in its own launch, then
+    // the three launches of qgemv_moe on its ids and weights
+    int32_t* ids = ids_out ? ids_out : (int32_t*)(wsp + L.route_off);
+    float* gates = gates_out ? gates_out : (float*)(wsp + L.route_off + 256);
+    launch_route(logits, N, E, top_k, ids, gates, stream);
+    f.gu.ids = ids;
+    f.dn.ids = ids;
+    switch (fmt) {
+      case INT4: launch_moe_pair<INT4>(f.gu, f.dn, wgu, wdn, f.slots, stream); break;
+      case INT5: launch_moe_pair<INT5>(f.gu, f.dn, wgu, wdn, f.slots, stream); break;
+      case INT8: launch_moe_pair<INT8>(f.gu, f.dn, wgu, wdn, f.slots, stream); break;
+      default: launch_moe_pair<NVFP4>(f.gu, f.dn, wgu, wdn, f.slots, stream); break;
+    }
+    const int64_t tot = (int64_t)N * H;
+    hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, stream,
+                       (const float*)(wsp + L.o_off), ids, gates, residual, y, N, (int)H, top_k, E);
+    return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
+  }
+  // few routed rows: one launch; gate/up items split K over its waves
+  f.gu.ks_per_wave = (f.gu.KS + kFusedWaves - 1) / kFusedWaves;
+  f.ids_out = ids_out;
+  f.gates_out = gates_out;
+  f.nA = f.gu.out_tiles;                    // one gate tile and its up tile per item
+  f.nB = f.dn.out_tiles;                    // 16 output columns per item
+  hipError_t e;
+  switch (fmt) {
+    case INT4: e = launch_fused<INT4>(f, stream); break;
+    case INT5: e = launch_fused<INT5>(f, stream); break;
+    case INT8: e = launch_fused<INT8>(f, stream); break;
+    default: e = launch_fused<NVFP4>(f, stream); break;
+  }
+  return e == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
 }

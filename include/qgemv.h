@@ -164,6 +164,50 @@ int qgemv_moe(int fmt, const void* wq_gu, const void* ws_gu, const void* wq_dn, 
               int top_k, const float* residual, float* y, int N, void* workspace,
               size_t workspace_bytes, hipStream_t stream);
 
+/* Top-k softmax router (Decapybara page, CUDA kernel list: a top-8 softmax
+ * router in front of the experts). For each token t < N:
+ *   ids[t][j]   the j-th largest of logits[t][0..E) (j < top_k); equal
+ *               logits go in increasing expert order; -0 equals +0; a NaN
+ *               ranks below every number
+ *   gates[t][j] exp(l_j - l_0) / sum_{i<top_k} exp(l_i - l_0) in fp32,
+ *               summed in increasing i (the softmax over the selected
+ *               logits, which equals the full softmax renormalised)
+ *   logits [N][E] fp32, ids [N][top_k] int32, gates [N][top_k] fp32, device.
+ * The ids are exact; the gates are meaningful for finite logits.
+ * 1 <= top_k <= min(E, 64), E <= 16384 (QGEMV_EUNSUPPORTED otherwise). */
+int qgemv_moe_route(const float* logits, int N, int E, int top_k, int32_t* ids, float* gates,
+                    hipStream_t stream);
+
+/* Workspace bytes of qgemv_moe_fused. */
+int qgemv_moe_fused_workspace_bytes(int E, int64_t H, int64_t I, int N, int top_k, size_t* bytes);
+
+/* The MoE FFN of qgemv_moe in a single launch, routed on the device from
+ * router logits (the router of qgemv_moe_route, run by every workgroup):
+ *   ids, gates = route(logits [N][E], top_k)
+ *   y[t] = residual[t] + sum_j gates[t][j] * down_e(SwiGLU(gate_up_e(x[t])))
+ * with the arithmetic of qgemv_moe, so given the same ids and gates the two
+ * produce identical bits. Work items are taken in order from a counter in the
+ * workspace; a down-projection item waits (bounded) until the gate/up items
+ * of its expert are complete; the item that completes a 32-column block of
+ * the expert outputs sums that block of y.
+ *   ids_out [N][top_k], gates_out [N][top_k]: receive the routing (device),
+ *   or NULL.
+ *   workspace: device memory of qgemv_moe_fused_workspace_bytes, 16-byte
+ *   aligned, ZERO-FILLED BEFORE ITS FIRST USE. It starts with counters and
+ *   flags that every call returns to zero when it completes, so one fill
+ *   serves every later call in stream order with the same H (the counter
+ *   region's size depends on H only; N, E, I and top_k may change if the
+ *   workspace is large enough). Calls that may overlap in time need separate
+ *   workspaces. Byte offset 12 holds a sticky 32-bit flag that becomes
+ *   nonzero if a dependency wait ever timed out (the results of that call are
+ *   then invalid). The launch is cooperative: every workgroup is resident at
+ *   once, which the dependency waits rely on.
+ * Other arguments and limits as qgemv_moe; 1 <= top_k <= min(E, 8). */
+int qgemv_moe_fused(int fmt, const void* wq_gu, const void* ws_gu, const void* wq_dn, const void* ws_dn,
+                    int E, int64_t H, int64_t I, const void* x, const float* logits, int top_k,
+                    const float* residual, float* y, int N, int32_t* ids_out, float* gates_out,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* MoE routing index (the step qgemv_moe runs first), into caller buffers:
  *   counts [E]      slots routed to each expert
  *   offsets [E+1]   exclusive prefix sum of counts

@@ -64,3 +64,39 @@ def ref_gemv(fmt, wq, ws, xb, M, K, residual=None):
     W = oracle_weights(fmt, wq, ws, M, K)
     x = G.x_from_bits(xb)
     return G.gemv(x, W, residual), G.gemv_tolerance(x, W)
+
+
+def moe_case(fmt, E, H, I, N, k, seed, ids=None, logits=None):
+    """Expert-stacked packed weights of E experts ([2I][H] gate/up, [H][I]
+    down), x, ids and gates (oracle router over seeded logits unless ids are
+    given), residual, and the oracle weights of the experts in use."""
+    import bit_quantized_weight_amd as qg
+    rng = np.random.default_rng(seed)
+    gu = [synthetic.weights(rng, 2 * I, H) for _ in range(E)]
+    dn = [synthetic.weights(rng, H, I) for _ in range(E)]
+    sq, ss = qg.expert_stride(fmt, 2 * I, H)
+    dq, ds = qg.expert_stride(fmt, H, I)
+    bufs = [np.zeros(E * sq, np.uint8), np.zeros(E * ss, np.uint8), np.zeros(E * dq, np.uint8),
+            np.zeros(E * ds, np.uint8)]
+    xb = synthetic.activations(rng, N, H)
+    if ids is None:
+        if logits is None:
+            logits = synthetic.router_logits(rng, N, E)
+        ids, gates = G.route_topk_softmax(logits, k)
+    else:
+        gates = synthetic.random_gates(rng, N, k)
+    r = synthetic.residual(rng, N, H)
+    used = {int(e) for e in ids.reshape(-1) if 0 <= e < E}
+    Wgu, Wdn = [None] * E, [None] * E          # oracle weights of the used experts only
+    for e in range(E):
+        q, s = qg.pack(fmt, gu[e])
+        bufs[0][e * sq: e * sq + q.size] = q
+        bufs[1][e * ss: e * ss + s.size] = s
+        if e in used:
+            Wgu[e] = oracle_weights(fmt, q, s, 2 * I, H)
+        q, s = qg.pack(fmt, dn[e])
+        bufs[2][e * dq: e * dq + q.size] = q
+        bufs[3][e * ds: e * ds + s.size] = s
+        if e in used:
+            Wdn[e] = oracle_weights(fmt, q, s, H, I)
+    return bufs, Wgu, Wdn, xb, ids.astype(np.int32), gates, r

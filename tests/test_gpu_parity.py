@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 import synthetic
-from gpu_helpers import FORMATS, check_tol, dev, make_case, oracle_weights, ref_gemv, tile_rows
+from gpu_helpers import FORMATS, check_tol, dev, make_case, moe_case, oracle_weights, ref_gemv, tile_rows
 from oracle import gemv as G
 
 torch = pytest.importorskip("torch")
@@ -207,43 +207,12 @@ def test_swiglu_parity(fmt, I, K, N):
 
 # -------------------------------------------------------------------- MoE
 
-def _moe_case(fmt, E, H, I, N, k, seed, ids=None):
-    rng = np.random.default_rng(seed)
-    gu = [synthetic.weights(rng, 2 * I, H) for _ in range(E)]
-    dn = [synthetic.weights(rng, H, I) for _ in range(E)]
-    sq, ss = qg().expert_stride(fmt, 2 * I, H)
-    dq, ds = qg().expert_stride(fmt, H, I)
-    bufs = [np.zeros(E * sq, np.uint8), np.zeros(E * ss, np.uint8), np.zeros(E * dq, np.uint8),
-            np.zeros(E * ds, np.uint8)]
-    xb = synthetic.activations(rng, N, H)
-    if ids is None:
-        logits = synthetic.router_logits(rng, N, E)
-        ids, gates = G.route_topk_softmax(logits, k)
-    else:
-        gates = synthetic.random_gates(rng, N, k)
-    r = synthetic.residual(rng, N, H)
-    used = {int(e) for e in ids.reshape(-1) if 0 <= e < E}
-    Wgu, Wdn = [None] * E, [None] * E          # oracle weights of the used experts only
-    for e in range(E):
-        q, s = qg().pack(fmt, gu[e])
-        bufs[0][e * sq: e * sq + q.size] = q
-        bufs[1][e * ss: e * ss + s.size] = s
-        if e in used:
-            Wgu[e] = oracle_weights(fmt, q, s, 2 * I, H)
-        q, s = qg().pack(fmt, dn[e])
-        bufs[2][e * dq: e * dq + q.size] = q
-        bufs[3][e * ds: e * ds + s.size] = s
-        if e in used:
-            Wdn[e] = oracle_weights(fmt, q, s, H, I)
-    return bufs, Wgu, Wdn, xb, ids.astype(np.int32), gates, r
-
-
 @pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("N", [1, 3, 8])
 def test_moe_parity(fmt, N):
     E, H, I, k = 16, 256, 64, 4
     log("moe", fmt, N)
-    bufs, Wgu, Wdn, xb, ids, gates, r = _moe_case(fmt, E, H, I, N, k, seed=N)
+    bufs, Wgu, Wdn, xb, ids, gates, r = moe_case(fmt, E, H, I, N, k, seed=N)
     y_ref, T = G.moe(G.x_from_bits(xb), ids, gates, Wgu, Wdn, r)
     nbytes = qg().moe_workspace_bytes(E, H, I, N, k)
     wsp = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
@@ -259,7 +228,7 @@ def test_moe_full_shape_int4():
     """The MoE workload's shapes: H = 2048, 128 experts, I = 768, top-8 of
     seeded softmax logits, N = 8, int4 experts."""
     E, H, I, k, N = 128, 2048, 768, 8, 8
-    bufs, Wgu, Wdn, xb, ids, gates, r = _moe_case("int4", E, H, I, N, k, seed=77)
+    bufs, Wgu, Wdn, xb, ids, gates, r = moe_case("int4", E, H, I, N, k, seed=77)
     y_ref, T = G.moe(G.x_from_bits(xb), ids, gates, Wgu, Wdn, r)
     nbytes = qg().moe_workspace_bytes(E, H, I, N, k)
     wsp = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
@@ -275,7 +244,7 @@ def test_moe_full_shape_int4():
 def test_moe_duplicates_and_bad_ids():
     E, H, I, k, N = 6, 128, 32, 3, 4
     ids = np.array([[0, 2, 2], [5, 1, 0], [3, 3, 3], [4, 0, 9]], np.int32)
-    bufs, Wgu, Wdn, xb, ids, gates, r = _moe_case("int5", E, H, I, N, k, seed=3, ids=ids)
+    bufs, Wgu, Wdn, xb, ids, gates, r = moe_case("int5", E, H, I, N, k, seed=3, ids=ids)
     y_ref, T = G.moe(G.x_from_bits(xb), ids, gates, Wgu, Wdn, r)
     nbytes = qg().moe_workspace_bytes(E, H, I, N, k)
     wsp = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
@@ -295,7 +264,7 @@ def test_moe_many_experts(E, ids):
     H, I, k, N = 128, 32, 4, 4
     log("moe many experts", E)
     ids = None if ids is None else np.array(ids, np.int32)
-    bufs, Wgu, Wdn, xb, ids, gates, r = _moe_case("int4", E, H, I, N, k, seed=E, ids=ids)
+    bufs, Wgu, Wdn, xb, ids, gates, r = moe_case("int4", E, H, I, N, k, seed=E, ids=ids)
     y_ref, T = G.moe(G.x_from_bits(xb), ids, gates, Wgu, Wdn, r)
     nbytes = qg().moe_workspace_bytes(E, H, I, N, k)
     wsp = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")

@@ -169,3 +169,28 @@ def test_qgemv_moe_validation_codes():
     assert L.qgemv_moe_index(FAKE, 9, 8, 128, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -7
     b = ctypes.c_size_t()
     assert L.qgemv_moe_workspace_bytes(0, 2048, 768, 1, 8, ctypes.byref(b)) == -1
+
+
+def test_router_and_fused_moe_validation_codes():
+    """Argument checks of qgemv_moe_route and qgemv_moe_fused return before
+    any launch (no GPU needed)."""
+    L = qg.load(False)
+    assert L.qgemv_moe_route(None, 2, 8, 2, FAKE, FAKE, None) == -1
+    assert L.qgemv_moe_route(FAKE, 2, 8, 9, FAKE, FAKE, None) == -7           # top_k > E
+    assert L.qgemv_moe_route(FAKE, 2, 100, 65, FAKE, FAKE, None) == -7        # top_k > 64
+    assert L.qgemv_moe_route(FAKE, 2, 16385, 8, FAKE, FAKE, None) == -7       # E limit
+    assert L.qgemv_moe_route(FAKE + 2, 2, 8, 2, FAKE, FAKE, None) == -3
+    need = qg.moe_fused_workspace_bytes(128, 2048, 768, 8, 8)
+    assert need > qg.moe_workspace_bytes(128, 2048, 768, 8, 8)
+
+    def fused(**kw):
+        a = dict(fmt=1, E=128, H=2048, I=768, top_k=8, N=8, ws=FAKE, wsb=need, logits=FAKE)
+        a.update(kw)
+        return L.qgemv_moe_fused(a["fmt"], FAKE, FAKE, FAKE, FAKE, a["E"], a["H"], a["I"], FAKE, a["logits"],
+                                 a["top_k"], None, FAKE, a["N"], None, None, a["ws"], a["wsb"], None)
+    assert fused(ws=None) == -5 and fused(wsb=need - 1) == -5
+    assert fused(logits=None) == -1 and fused(logits=FAKE + 2) == -3
+    assert fused(top_k=9) == -7 and fused(N=9) == -7 and fused(E=4, top_k=5) == -7
+    assert fused(fmt=9) == -2 and fused(H=2047) in (-1, -3)
+    b = ctypes.c_size_t()
+    assert L.qgemv_moe_fused_workspace_bytes(128, 2048, 768, 0, 8, ctypes.byref(b)) == -7
