@@ -354,8 +354,8 @@ def extras(qg, torch, dev, stream, layers, args):
     res["moe"] = {"workload": "128 experts, H 2048, I 768, top-8, int4, 32 rotated copies", **moe}
     log("moe", res["moe"])
 
-    # the same MoE routed on the device in one launch (qgemv_moe_fused), with
-    # 16 seeded logit sets in rotation so the routing changes every call;
+    # the same MoE routed on the device (qgemv_moe_fused), with 16 seeded
+    # logit sets in rotation so the routing changes every call;
     # algorithmic bytes: the selected experts' weights + x + logits + r + y
     fused = {}
     for n in (1, 2, 8):
@@ -376,8 +376,9 @@ def extras(qg, torch, dev, stream, layers, args):
         err = int(wsp[12:16].cpu().view(torch.int32).item())
         if err:
             raise RuntimeError("qgemv_moe_fused reported a timed-out dependency wait")
-    res["moe_fused"] = {"workload": "128 experts, H 2048, I 768, top-8 routed on the device from fresh logits, int4, "
-                                    "one launch, 32 rotated copies", **fused}
+    res["moe_fused"] = {"workload": "128 experts, H 2048, I 768, top-8 routed on the device from fresh logits, int4 "
+                                    "(qgemv_moe_fused: one launch at N = 1, router + 3 launches above), "
+                                    "32 rotated copies", **fused}
     log("moe_fused", res["moe_fused"])
     return res
 

@@ -395,37 +395,48 @@ int cycle_ksteps(int fmt, int S) {
   return groups >= 4 ? groups / 4 : 1;
 }
 
-// Launch shape: two 16-row tiles per wave, S slots from N, and K split over
-// the W waves of a workgroup. The k-steps per wave come from sweeps on MI355X
-// (the dense layer's three shapes and [17408][5120], every format, N = 1, 2,
-// 4, 8): a wave streams best with about 20 k-steps of its row tiles, fewer
-// where a k-step is cheap to decode for several tokens (N = 2..4), more where
-// many tokens make each k-step long (SwiGLU and long K at N > 4), and int8 at
-// N = 1 keeps the whole K (its k-steps carry twice the bytes). The grid
-// should hold at least ~900 waves so the chip's 1024 SIMDs have work; below
-// that the k-range per wave shrinks (never under one scale cycle). Each
-// wave's range is a whole number of cycles.
-int ksteps_per_wave(int fmt, int N, bool swiglu, int64_t KS) {
+// Launch shape: S slots from N, NT row tiles per workgroup and K split over
+// its W waves. The choices come from sweeps on MI355X (the dense layer's
+// three shapes and [17408][5120], every format, N = 1, 2, 4, 8):
+//   * The plain GEMV takes one row tile per workgroup once the matrix has
+//     enough tiles: the chip's 256 compute units then see twice as many
+//     workgroups, so the share of units that get one workgroup more than the
+//     others (and finish last) costs half as much. Measured 5-20% faster from
+//     768 tiles at every N, and from 384 tiles at N >= 2; smaller matrices
+//     (the down projection's 320 tiles) stay faster with two, except NVFP4
+//     at N <= 2 and int8 at N = 2, which take one tile on every shape.
+//     SwiGLU always keeps a gate tile and its up tile together.
+//   * A wave streams best with 12-20 k-steps of its tiles: 20 at N = 1 and
+//     N > 4, 12 at N = 2 and for int5/int8 at N = 4, 16 for int4/NVFP4 at
+//     N = 4; NVFP4 at N = 1 with 12; SwiGLU and long K at N > 4 take longer
+//     ranges (five waves per workgroup); int8 at N = 1 on two-tile
+//     workgroups keeps the whole K.
+// The grid should hold at least ~900 waves so the chip's 1024 SIMDs have
+// work; below that the k-range per wave shrinks (never under one scale
+// cycle). Each wave's range is a whole number of cycles.
+bool single_tile(int fmt, int N, bool swiglu, int64_t out_tiles) {
+  if (swiglu) return false;
+  if ((fmt == NVFP4 && N <= 2) || (fmt == INT8 && N == 2)) return true;   // every shape
+  return out_tiles >= 768 || (N >= 2 && out_tiles >= 384);
+}
+
+int ksteps_per_wave(int fmt, int N, bool swiglu, bool one_tile, int64_t KS) {
   if (swiglu) {                          // gate/up pairs: [2 x 17408][5120] sweeps
     if (N == 1) return 20;
     if (N == 2) return fmt == NVFP4 ? 20 : 12;
     if (N <= 4) return 12;
     return 40;
   }
+  if (one_tile) {
+    if (N == 1) return fmt == NVFP4 ? 12 : 20;
+    if (N == 2) return fmt == INT8 ? 20 : 12;
+    if (N <= 4) return (fmt == INT4 || fmt == NVFP4) ? 16 : 12;
+    return 20;
+  }
   if (N == 1) return fmt == INT8 ? 0 : 20;   // 0: whole K
   if (N == 2) return 12;
   if (N <= 4) return (fmt == INT8 || fmt == NVFP4) ? 12 : 20;
   return KS >= 64 ? (int)((KS + 4) / 5) : 20;   // long K at N > 4: five waves per workgroup
-}
-
-// One row tile per wave instead of two where that measured faster: NVFP4 at
-// N <= 2 (12 k-steps per wave) and int8 at N = 2 (20); the plain GEMV only
-// (SwiGLU keeps a gate tile and its up tile together).
-bool single_tile(int fmt, int N, bool swiglu, int* kpw) {
-  if (swiglu) return false;
-  if (fmt == NVFP4 && N <= 2) { *kpw = 12; return true; }
-  if (fmt == INT8 && N == 2) { *kpw = 20; return true; }
-  return false;
 }
 
 constexpr int kMaxWaves = 8;
@@ -436,8 +447,9 @@ LaunchShape pick_shape(int fmt, int64_t KS, int64_t out_tiles, int N, bool swigl
   ls.kps = 2;
   ls.slots = slots_for(N);
   const int cyc = cycle_ksteps(fmt, ls.slots);
-  int per = ksteps_per_wave(fmt, N, swiglu, KS);
-  ls.nt = single_tile(fmt, N, swiglu, &per) ? 1 : 2;
+  const bool one = single_tile(fmt, N, swiglu, out_tiles);
+  ls.nt = one ? 1 : 2;
+  const int per = ksteps_per_wave(fmt, N, swiglu, one, KS);
   const int64_t to = swiglu ? ls.nt / 2 : ls.nt;     // output tiles per workgroup
   const int64_t wgs = (out_tiles + to - 1) / to;
   const bool whole_k = per == 0;
@@ -497,12 +509,7 @@ hipError_t launch_k(const GemvArgs& a, const LaunchShape& ls, bool swiglu, hipSt
 
 template <int FMT>
 hipError_t launch_gemv(const GemvArgs& a, const LaunchShape& ls, bool swiglu, hipStream_t stream) {
-  if constexpr (FMT == NVFP4 || FMT == INT8) {
-    if (ls.nt == 1) {   // N <= 2 only (single_tile)
-      if (ls.slots == 16) return launch_s<FMT, 1, 16, 2>(a, ls, false, stream);
-      return launch_s<FMT, 1, 8, 2>(a, ls, false, stream);
-    }
-  }
+  if (ls.nt == 1) return launch_k<FMT, 1, 2>(a, ls, false, stream);   // plain GEMV only
   return launch_k<FMT, 2, 2>(a, ls, swiglu, stream);
 }
 

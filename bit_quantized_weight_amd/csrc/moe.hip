@@ -420,7 +420,7 @@ struct MoeFusedArgs {
   int N, H, E, top_k, NK, slots;
   int nA, nB;              // gate/up row blocks per slot; 16-column output blocks
 };
-constexpr int kFusedMaxRows = 16;           // N * top_k handled by the single launch
+constexpr int kFusedMaxRows = 8;            // N * top_k handled by the single launch
 constexpr int kFusedWaves = 4;              // waves per workgroup of the single launch
 // counter words: [3] sticky error, [4, 4 + 16) h_done per slot, then ready
 // flags [slot][output block] at kReadyStride-word spacing from word 32
@@ -840,8 +840,10 @@ extern "C" int qgemv_moe_fused(int fmt, const void* wq_gu, const void* ws_gu, co
   f.NK = N * top_k;
   f.slots = std::min(E, f.NK);
   if (f.NK > kFusedMaxRows) {
-    // many routed rows: bandwidth-bound; the router in its own launch, then
-    // the three launches of qgemv_moe on its ids and weights
+    // more routed rows: the router in its own launch, then the three launches
+    // of qgemv_moe on its ids and weights (measured faster from 16 rows: the
+    // single launch's chain of dependent memory round trips outweighs the
+    // launches it saves)
     int32_t* ids = ids_out ? ids_out : (int32_t*)(wsp + L.route_off);
     float* gates = gates_out ? gates_out : (float*)(wsp + L.route_off + 256);
     launch_route(logits, N, E, top_k, ids, gates, stream);

@@ -185,11 +185,13 @@ int qgemv_moe_fused_workspace_bytes(int E, int64_t H, int64_t I, int N, int top_
  * router logits (the router of qgemv_moe_route, run by every workgroup):
  *   ids, gates = route(logits [N][E], top_k)
  *   y[t] = residual[t] + sum_j gates[t][j] * down_e(SwiGLU(gate_up_e(x[t])))
- * with the arithmetic of qgemv_moe, so given the same ids and gates the two
- * produce identical bits. Work items are taken in order from a counter in the
- * workspace; a down-projection item waits (bounded) until the gate/up items
- * of its expert are complete; the item that completes a 32-column block of
- * the expert outputs sums that block of y.
+ * With N * top_k <= 8 routed rows (batch-1 decode at top-8) it is one
+ * launch: gate/up work items publish h and raise ready flags in the
+ * workspace; each output item waits (bounded) for its experts' flags, computes
+ * every expert's output for 16 columns of y and sums them in fixed order in
+ * LDS. With more rows it runs qgemv_moe_route and then the launches of
+ * qgemv_moe, whose bits it then reproduces for the same ids and gates.
+ * Either way results are bitwise reproducible from call to call.
  *   ids_out [N][top_k], gates_out [N][top_k]: receive the routing (device),
  *   or NULL.
  *   workspace: device memory of qgemv_moe_fused_workspace_bytes, 16-byte

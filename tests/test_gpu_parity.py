@@ -295,9 +295,12 @@ def test_moe_index_bit_exact(N, k, E):
 
 # --------------------------------------------------- full sizes, sampled rows
 
-FULL = [("int4", 7168, 5120, 1), ("int5", 17408, 5120, 8), ("int5", 5120, 17408, 1), ("int8", 17408, 5120, 8),
-        ("nvfp4", 17408, 5120, 8), ("nvfp4", 5120, 17408, 4), ("nvfp4", 17408, 5120, 1), ("nvfp4", 17408, 5120, 2),
-        ("int8", 17408, 5120, 2), ("int8", 17408, 5120, 1), ("int4", 17408, 5120, 2)]
+# every launch shape the benchmark times: [17408][5120] (one tile per
+# workgroup) at N = 1, 2, 4, 8 in each format, the QKV shape (one tile from
+# N = 2, two at N = 1) and the down projection (two tiles)
+FULL = [("int4", 7168, 5120, 1), ("int4", 7168, 5120, 8), ("int4", 7168, 5120, 4), ("int5", 5120, 17408, 1),
+        ("int5", 5120, 17408, 8), ("nvfp4", 5120, 17408, 4), ("nvfp4", 7168, 5120, 2)] + \
+       [(f, 17408, 5120, n) for f in ("int4", "int5", "int8", "nvfp4") for n in (1, 2, 4, 8)]
 
 
 @pytest.mark.parametrize("fmt,M,K,N", FULL)

@@ -4,10 +4,10 @@ MoE (qgemv_moe_fused) against the oracle, through the C ABI.
 Bit-exact: the selected expert ids (the oracle's top-k order: larger logit
 first, ties to the lower index, NaN last). Tolerance: the mixing weights
 within oracle.gemv.route_tolerance; the MoE output within the oracle's MoE
-bound widened by the weights' tolerance. With more than 16 routed rows the fused
+bound widened by the weights' tolerance. With more than 8 routed rows the fused
 call runs the router and then qgemv_moe's launches, so the two give identical
-bits on the same ids and weights; with 16 or fewer it is one launch of its
-own, checked against the oracle and for run-to-run determinism.
+bits on the same ids and weights; with 8 or fewer it is one launch of its own,
+checked against the oracle and for run-to-run determinism.
 """
 import numpy as np
 import pytest
@@ -154,7 +154,7 @@ def _check_fused(fmt, E, H, I, N, k, seed, calls=2):
     for y in ys[1:]:
         assert np.array_equal(y.view(np.uint32), ys[0].view(np.uint32)), "repeat call differs"
     # the three-launch path on the same ids and weights: the same bits when the
-    # fused call takes that path (N * top_k > 16), within tolerance otherwise
+    # fused call takes that path (N * top_k > 8), within tolerance otherwise
     nb = qg().moe_workspace_bytes(E, H, I, N, k)
     wsp2 = torch.zeros(nb, dtype=torch.uint8, device="cuda")
     y2 = torch.empty((N, H), dtype=torch.float32, device="cuda")
@@ -162,14 +162,14 @@ def _check_fused(fmt, E, H, I, N, k, seed, calls=2):
                    residual=None if r is None else dev(r, torch))
     torch.cuda.synchronize()
     y2 = y2.cpu().numpy()
-    if N * k > 16:
+    if N * k > 8:
         assert np.array_equal(y2.view(np.uint32), ys[0].view(np.uint32)), np.argwhere(y2 != ys[0])[:5]
     else:
         check_tol(y2, y_ref, T, "three-launch path")
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
-@pytest.mark.parametrize("N", [1, 3, 8])
+@pytest.mark.parametrize("N", [1, 2, 3, 8])
 def test_fused_moe_parity(fmt, N):
     log("fused moe", fmt, N)
     _check_fused(fmt, 16, 256, 64, N, 4, seed=N)
@@ -184,7 +184,7 @@ def test_fused_moe_full_shape_int4(N):
 
 
 @pytest.mark.parametrize("E,H,I,N,k", [(4, 96, 32, 2, 4), (8, 160, 96, 5, 1), (3, 64, 96, 1, 3), (40, 128, 32, 8, 8),
-                                       (300, 128, 32, 2, 8), (300, 96, 64, 4, 8)])
+                                       (300, 128, 32, 1, 8), (300, 96, 64, 4, 8)])
 def test_fused_moe_odd_shapes(E, H, I, N, k):
     """Odd numbers of row blocks (H = 96, 160; I = 96), top_k = E (every
     expert active), top_k = 1, more selected slots than experts, and E > 256
