@@ -12,6 +12,10 @@ What the GPU path computes, written as plain definitions in fp64:
     on one card): each token t runs only its top-k experts e_j with weights
     p_j; per (t, j): h = SwiGLU(x_t W_gu[e]^T) (kept in fp64), o = h W_dn[e]^T,
     y_t = r_t + sum_j p_j o_j with j in increasing order.
+  * RMSNorm prologue (same section: normalisation fused into the matmul
+    that consumes it):
+        x[n, k] = h[n, k] * gamma[k] / sqrt(mean_k h[n, k]^2 + eps)
+    then the GEMV / SwiGLU on x.
   * MoE routing index: the (token, slot) pairs grouped by expert, ordered by
     (expert, token, slot); counts, offsets, the ascending list of active
     experts and an error flag for ids outside [0, E).
@@ -49,6 +53,39 @@ def gemv(x: np.ndarray, W: np.ndarray, residual: np.ndarray | None = None) -> np
 
 def gemv_tolerance(x: np.ndarray, W: np.ndarray) -> np.ndarray:
     return REL * (np.abs(np.asarray(x, np.float64)) @ np.abs(np.asarray(W, np.float64)).T) + ABS
+
+
+def rmsnorm(h: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
+    """x[n, k] = h[n, k] * gamma[k] / sqrt(mean_k h[n, k]^2 + eps), in fp64."""
+    h = np.asarray(h, dtype=np.float64)
+    g = np.asarray(gamma, dtype=np.float64)
+    ms = np.mean(h * h, axis=1, keepdims=True)
+    return h * g[None, :] / np.sqrt(ms + float(eps))
+
+
+def norm_rel(K: int) -> float:
+    """Relative bound (on sum_k |x_k W_k|) that a normalised GEMV adds to the
+    GEMV's own 2e-3: the GPU rounds each gamma*h to bf16 once (2^-9) and
+    multiplies the dot product by an fp32 norm scale (K squares summed in
+    fp32, a square root and a division: under K * 2^-24 + 2^-22)."""
+    return 2.0 ** -9 + K * 2.0 ** -24 + 2.0 ** -22
+
+
+def norm_gemv_tolerance(x: np.ndarray, W: np.ndarray) -> np.ndarray:
+    """Per-output bound for y = x W^T with x = rmsnorm(...) evaluated as above."""
+    K = np.asarray(x).shape[1]
+    return (REL + norm_rel(K)) * (np.abs(np.asarray(x, np.float64)) @ np.abs(np.asarray(W, np.float64)).T) + ABS
+
+
+def swiglu_from(g, u, Tg, Tu):
+    """h = silu(g) * u and its bound, from gate/up values and their bounds."""
+    sg = silu(g)
+    h = sg * u
+    Th = 1.1 * (np.abs(u) + Tu) * Tg + np.abs(sg) * Tu + 1e-6 * np.abs(h) + ABS
+    return h, Th
+
+
+BF16_REL = 2.0 ** -9    # round-to-nearest-even to bfloat16
 
 
 def silu(g: np.ndarray) -> np.ndarray:

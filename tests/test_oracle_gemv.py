@@ -228,3 +228,50 @@ def test_router_tolerance_covers_fp32_and_rejects_larger_errors():
     assert np.all(T < 1e-4 * ref + 1e-10)          # and the bound stays tight
     bad = p32 * np.float32(1 + 2e-4)
     assert np.any(np.abs(bad - ref) > T)
+
+
+def test_rmsnorm_closed_forms():
+    # h = [3, 4]: mean square 12.5, so x = h / sqrt(12.5) (hand-worked)
+    x = G.rmsnorm(np.array([[3.0, 4.0]]), np.ones(2), 0.0)
+    assert np.allclose(x, [[3 / math.sqrt(12.5), 4 / math.sqrt(12.5)]], rtol=1e-15)
+    assert abs(float(np.mean(x * x)) - 1.0) < 1e-15          # unit mean square
+    # a constant row normalises to sign(c) * gamma (eps = 0), gamma applied per column
+    g = np.linspace(-2, 3, 16)
+    assert np.allclose(G.rmsnorm(np.full((1, 16), -7.5), g, 0.0), -g[None, :], rtol=1e-15)
+    # scale invariance (eps = 0) and rows independent
+    rng = np.random.default_rng(31)
+    h = rng.standard_normal((3, 64))
+    assert np.allclose(G.rmsnorm(h * 1e3, g.repeat(4), 0.0), G.rmsnorm(h, g.repeat(4), 0.0), rtol=1e-13)
+    assert np.allclose(G.rmsnorm(h[1:2], g.repeat(4), 1e-5), G.rmsnorm(h, g.repeat(4), 1e-5)[1:2], rtol=0)
+    # eps enters under the square root of the mean square
+    x = G.rmsnorm(np.array([[1.0, 1.0]]), np.ones(2), 3.0)
+    assert np.allclose(x, [[0.5, 0.5]], rtol=1e-15)
+
+
+def test_norm_tolerance_covers_the_gpu_evaluation():
+    """An fp32 emulation of the normalised GEMV the GPU runs (bf16(gamma*h)
+    operands, fp32 dot, fp32 norm scale applied after) stays within the
+    bound; planted mistakes (sum instead of mean, gamma applied twice, no
+    scale) do not."""
+    rng = np.random.default_rng(33)
+    N, K, M = 4, 5120, 96
+    W = dequant(quant.quantize(synthetic.weights(rng, M, K), "int5"))
+    h = rng.standard_normal((N, K)).astype(np.float32) * np.float32(3)
+    gamma = (1 + 0.1 * rng.standard_normal(K)).astype(np.float32)
+    x = G.rmsnorm(h, gamma, 1e-6)
+    y_ref = G.gemv(x, W)
+    T = G.norm_gemv_tolerance(x, W)
+
+    def emul(scale_fn, gmul=1):
+        a = enc.f32_from_bf16_bits(synthetic.bf16_bits((h * (gamma * np.float32(gmul))).astype(np.float32)))
+        dot = (a.astype(np.float32) @ W.astype(np.float32).T).astype(np.float32)
+        ss = np.sum(h * h, axis=1, dtype=np.float32)
+        return (dot * scale_fn(ss)[:, None]).astype(np.float64)
+    good = emul(lambda ss: (np.float32(1) / np.sqrt(ss / np.float32(K) + np.float32(1e-6))).astype(np.float32))
+    assert np.all(np.abs(good - y_ref) <= T)
+    bad_sum = emul(lambda ss: (np.float32(1) / np.sqrt(ss + np.float32(1e-6))).astype(np.float32))
+    bad_gamma = emul(lambda ss: (np.float32(1) / np.sqrt(ss / np.float32(K) + np.float32(1e-6))).astype(np.float32),
+                     gmul=gamma)
+    no_scale = emul(lambda ss: np.ones_like(ss))
+    for bad in (bad_sum, bad_gamma, no_scale):
+        assert np.any(np.abs(bad - y_ref) > T)
