@@ -24,6 +24,12 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqgemv.so
 _lib = None
 
 
+class Fusion(ctypes.Structure):
+    """qgemv_fusion (include/qgemv.h): RMSNorm prologue and bf16 output."""
+    _fields_ = [("norm_src", ctypes.c_void_p), ("norm_gamma", ctypes.c_void_p), ("norm_eps", ctypes.c_float),
+                ("out_bf16", ctypes.c_void_p)]
+
+
 class QgemvError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
@@ -55,6 +61,8 @@ def load(require_torch: bool = True):
         "qgemv_pack_codes": (I32, [I32, P, P, P, ctypes.c_float, I64, I64, P, P]),
         "qgemv": (I32, [I32, P, P, P, P, P, I64, I64, I32, P]),
         "qgemv_swiglu": (I32, [I32, P, P, P, P, I64, I64, I32, P]),
+        "qgemv_ex": (I32, [I32, P, P, P, P, P, I64, I64, I32, ctypes.POINTER(Fusion), P]),
+        "qgemv_swiglu_ex": (I32, [I32, P, P, P, P, I64, I64, I32, ctypes.POINTER(Fusion), P]),
         "qgemv_moe_workspace_bytes": (I32, [I32, I64, I64, I32, I32, PSZ]),
         "qgemv_moe": (I32, [I32, P, P, P, P, I32, I64, I64, P, P, P, I32, P, P, I32, P, SZ, P]),
         "qgemv_moe_index": (I32, [P, I32, I32, I32, P, P, P, P, P, P]),
@@ -75,7 +83,8 @@ def load(require_torch: bool = True):
 def symbols() -> list[str]:
     """Names of the entry points the binding declares (the C ABI)."""
     return ["qgemv_strerror", "qgemv_version", "qgemv_packed_bytes", "qgemv_expert_stride", "qgemv_pack",
-            "qgemv_pack_codes", "qgemv", "qgemv_swiglu", "qgemv_moe_workspace_bytes", "qgemv_moe",
+            "qgemv_pack_codes", "qgemv", "qgemv_swiglu", "qgemv_ex", "qgemv_swiglu_ex",
+            "qgemv_moe_workspace_bytes", "qgemv_moe",
             "qgemv_moe_index", "qgemv_moe_route", "qgemv_moe_fused_workspace_bytes", "qgemv_moe_fused",
             "qgemv_dequant", "qgemv_probe_read"]
 
@@ -159,6 +168,28 @@ def qgemv(fmt, wq, ws, x, y, M: int, K: int, N: int, residual=None, stream=None)
 def qgemv_swiglu(fmt, wq, ws, x, h, I: int, K: int, N: int, stream=None) -> None:
     _check(load().qgemv_swiglu(_fmt(fmt), _ptr(wq), _ptr(ws), _ptr(x), _ptr(h), I, K, N, _stream(stream)),
            "qgemv_swiglu")
+
+
+def _fusion(norm_src, norm_gamma, norm_eps, out_bf16):
+    if norm_src is None and out_bf16 is None:
+        return None
+    return ctypes.byref(Fusion(_ptr(norm_src), _ptr(norm_gamma), float(norm_eps), _ptr(out_bf16)))
+
+
+def qgemv_ex(fmt, wq, ws, x, y, M: int, K: int, N: int, residual=None, norm_src=None, norm_gamma=None,
+             norm_eps: float = 1e-6, out_bf16=None, stream=None) -> None:
+    """qgemv with the optional RMSNorm prologue (norm_src, norm_gamma,
+    norm_eps; x may be None then) and bf16 output copy (out_bf16; y may be
+    None then)."""
+    _check(load().qgemv_ex(_fmt(fmt), _ptr(wq), _ptr(ws), _ptr(x), _ptr(residual), _ptr(y), M, K, N,
+                           _fusion(norm_src, norm_gamma, norm_eps, out_bf16), _stream(stream)), "qgemv_ex")
+
+
+def qgemv_swiglu_ex(fmt, wq, ws, x, h, I: int, K: int, N: int, norm_src=None, norm_gamma=None,
+                    norm_eps: float = 1e-6, out_bf16=None, stream=None) -> None:
+    _check(load().qgemv_swiglu_ex(_fmt(fmt), _ptr(wq), _ptr(ws), _ptr(x), _ptr(h), I, K, N,
+                                  _fusion(norm_src, norm_gamma, norm_eps, out_bf16), _stream(stream)),
+           "qgemv_swiglu_ex")
 
 
 def moe_workspace_bytes(E: int, H: int, I: int, N: int, top_k: int) -> int:

@@ -48,7 +48,51 @@ struct GemvArgs {
   int up_tile0;           // swiglu: tile index of the first "up" row tile
   int ks_per_wave;
   int x_nks;              // LDS activation records per wave (XM_LDS kernels)
+  // RMSNorm prologue (nsrc != null): activations are bf16(gamma * nsrc), and
+  // the per-token scale 1 / sqrt(mean(nsrc^2) + eps) multiplies the dot
+  // products in the epilogue
+  const float* nsrc;      // [N][K] fp32
+  const float* gamma;     // [K] fp32
+  float eps;
+  uint32_t nsrc_bytes, gamma_bytes;
+  uint16_t* ybf;          // bf16 copy of the output [N][M], or null
+  bool ystore;            // write the fp32 output y
 };
+
+// bf16 round to nearest even of a finite or infinite fp32 (NaN stays NaN)
+__device__ __forceinline__ uint32_t bf16_bits(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// 8 activations bf16(gamma * h) of token row t, columns col..col+7 (zeros
+// when !data), and their sum of squares of h added to ss
+__device__ __forceinline__ u32x4 norm_chunk(__amdgpu_buffer_rsrc_t hr, __amdgpu_buffer_rsrc_t gr, int K, int t,
+                                            int col, bool data, float& ss) {
+  const uint32_t ho = data ? (uint32_t)(t * K + col) * 4u : kOOB;
+  const uint32_t go = data ? (uint32_t)col * 4u : kOOB;
+  const u32x4 h0 = ld128(hr, ho), h1 = ld128(hr, ho + 16u);
+  const u32x4 g0 = ld128(gr, go), g1 = ld128(gr, go + 16u);
+  // whole-vector casts: a bit cast of one element of an ext vector would
+  // read the vector's first element instead
+  const f32x4 ha = __builtin_bit_cast(f32x4, h0), hb = __builtin_bit_cast(f32x4, h1);
+  const f32x4 ga = __builtin_bit_cast(f32x4, g0), gb = __builtin_bit_cast(f32x4, g1);
+  const float hv[8] = {ha[0], ha[1], ha[2], ha[3], hb[0], hb[1], hb[2], hb[3]};
+  const float gv[8] = {ga[0], ga[1], ga[2], ga[3], gb[0], gb[1], gb[2], gb[3]};
+  uint32_t b[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    ss = fmaf(hv[e], hv[e], ss);
+    b[e] = bf16_bits(gv[e] * hv[e]);
+  }
+  return u32x4{b[0] | b[1] << 16, b[2] | b[3] << 16, b[4] | b[5] << 16, b[6] | b[7] << 16};
+}
+
+// Sum over the 64 lanes in a fixed order (xor butterfly)
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
+  return v;
+}
 
 // Combine a lane's accumulators into per-(token, row) totals and write them
 // to LDS as red[((wave*NT + t)*8 + token)*16 + row]; fixed order throughout.
@@ -120,6 +164,38 @@ __device__ __forceinline__ void stage_x(uint8_t* xl, __amdgpu_buffer_rsrc_t xr, 
   }
 }
 
+// stage_x for the RMSNorm prologue: token t's records come from
+// bf16(gamma * nsrc[t]); the wave's sum of squares of nsrc over its k-range,
+// per token, lands in ssw[t] (t < N; fixed summation order).
+__device__ __forceinline__ void stage_x_norm(uint8_t* xl, __amdgpu_buffer_rsrc_t hr, __amdgpu_buffer_rsrc_t gr, int N,
+                                             int K, int ks0, int ks1, int nks, int lane, float* ssw) {
+  const int xs = (N * 16 + 1) * 16;       // record stride (as stage_x)
+  const int per_tok = nks * 16;           // 16-byte chunks of one token over the wave's records
+  for (int t = 0; t < N; ++t) {
+    float ss = 0.0f;
+    for (int i0 = 0; i0 < per_tok; i0 += 64 * 4) {
+      u32x4 v[4];
+      int dst[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + 64 * u + lane;
+        const int kk = i >> 4, c = i & 15;
+        const int col = (ks0 + kk) * 128 + c * 8;
+        const bool data = i < per_tok && ks0 + kk < ks1 && col < K;
+        v[u] = norm_chunk(hr, gr, K, t, col, data, ss);
+        dst[u] = i < per_tok ? kk * xs + (t * 16 + c) * 16 : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (dst[u] >= 0) *reinterpret_cast<u32x4*>(xl + dst[u]) = v[u];
+    }
+    ss = wave_sum(ss);
+    if (lane == 0) ssw[t] = ss;
+  }
+  // the zero block of every record
+  for (int kk = lane; kk < nks; kk += 64) *reinterpret_cast<u32x4*>(xl + kk * xs + N * 256) = u32x4{0u, 0u, 0u, 0u};
+}
+
 // Activation paths (A operands of the MFMAs):
 //   XM_LDS   the wave's whole k-range of x staged in LDS up front;
 //   XM_RING  a ring of kRing k-step records in LDS, refilled kRing - 1
@@ -139,6 +215,7 @@ __host__ __device__ constexpr int ring_stride() { return (16 / S) * 256 + 16; }
 template <int FMT, int NT, int S, int KPS, bool SWIGLU, int XM>
 __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
   extern __shared__ __attribute__((aligned(16))) float red[];  // [W][NT][8][16], then the LDS activations
+  __shared__ float s_ss[8][8];                                  // RMSNorm: [wave][token] sums of squares
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
   const int W = blockDim.x >> 6;
@@ -166,6 +243,10 @@ __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
   for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int ks0 = wave * a.ks_per_wave;
   const int ks1 = min(a.KS, ks0 + a.ks_per_wave);
+  const bool norm = a.nsrc != nullptr;   // uniform
+  const __amdgpu_buffer_rsrc_t hr = make_rsrc(a.nsrc, a.nsrc_bytes);
+  const __amdgpu_buffer_rsrc_t gr = make_rsrc(a.gamma, a.gamma_bytes);
+  if (lane < 8) s_ss[wave][lane] = 0.0f;  // waves with an empty k-range add nothing
 
   // activation lane role: A row r = slot * T + token
   const int a_tok = r % T;
@@ -193,7 +274,10 @@ __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
         for (int j = 0; j < 4; ++j) A[j] = *reinterpret_cast<const bf16x8*>(rec + off[ckk][j]);
       };
       // staged after the first weight loads are issued, so the two overlap
-      auto pre = [&]() { stage_x(xl, xr, a.N, a.K, ks0, ks1, a.x_nks, lane); };
+      auto pre = [&]() {
+        if (norm) stage_x_norm(xl, hr, gr, a.N, a.K, ks0, ks1, a.x_nks, lane, s_ss[wave]);
+        else stage_x(xl, xr, a.N, a.K, ks0, ks1, a.x_nks, lane);
+      };
       kloop<FMT, NT, S, KPS, 1>(wq, ws, tile, a.KS, ks0, ks1, a.hi_offset, acts, acc, pre);
     } else {
       // Ring slot of k-step k: (k - ks0) % kRing, which equals its trip
@@ -210,6 +294,9 @@ __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
       const bool two = nch > 64;
       const uint32_t sdst0 = (uint32_t)lane * 16u;
       const uint32_t sdst1 = (uint32_t)min(lane + 64, nch) * 16u;
+      // RMSNorm: lane chunk c always belongs to token c >> 4, so each lane sums
+      // the squares of its two chunks' tokens over the k-range in ssr
+      float ssr[2] = {0.0f, 0.0f};
       auto ring_load = [&](u32x4 (&v)[2], int k) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -217,7 +304,8 @@ __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
           const int c = lane + 64 * h;
           const int t = c >> 4, col = k * 128 + (c & 15) * 8;
           const bool data = (c < nch) & (k < ks1) & (col < a.K);
-          v[h] = ld128(xr, data ? (uint32_t)(t * a.K + col) * 2u : kOOB);
+          if (norm) v[h] = norm_chunk(hr, gr, a.K, t, col, data, ssr[h]);
+          else v[h] = ld128(xr, data ? (uint32_t)(t * a.K + col) * 2u : kOOB);
         }
       };
       auto ring_store = [&](const u32x4 (&v)[2], int slot) {
@@ -244,6 +332,18 @@ __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
         ring_store(v0, 0);
       };
       kloop<FMT, NT, S, KPS, 1>(wq, ws, tile, a.KS, ks0, ks1, a.hi_offset, acts, acc, pre);
+      if (norm && ks0 < ks1) {
+        // tokens (lane >> 4) and 4 + (lane >> 4): sum the 16 lanes of each row
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int d = 8; d >= 1; d >>= 1) ssr[h] += __shfl_xor(ssr[h], d);
+        if ((lane & 15) == 0) {
+          const int t = lane >> 4;
+          if (t < a.N) s_ss[wave][t] = ssr[0];
+          if (4 + t < a.N) s_ss[wave][4 + t] = ssr[1];
+        }
+      }
     }
   } else {
     // the lane's base offset carries its slot term; tokens >= N start past the buffer
@@ -267,19 +367,26 @@ __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
     const int ot = blockIdx.x * TO + to;
     const int col = ot * 16 + row;
     if (tok >= a.N || ot >= a.out_tiles || col >= a.M) continue;
+    float sc = st;                        // NVFP4 tensor scale, times the RMSNorm scale
+    if (norm) {
+      float ss = 0.f;
+      for (int w = 0; w < W; ++w) ss += s_ss[w][tok];
+      sc = sc * (1.0f / sqrtf(ss / (float)a.K + a.eps));
+    }
     float v = 0.f;
     for (int w = 0; w < W; ++w) v += red[((size_t)(w * NT + to) * 8 + tok) * 16 + row];
-    v *= st;
+    v *= sc;
+    const size_t at = (size_t)tok * a.M + col;
     if constexpr (SWIGLU) {
       float u = 0.f;
       for (int w = 0; w < W; ++w) u += red[((size_t)(w * NT + TO + to) * 8 + tok) * 16 + row];
-      u *= st;
-      const float sg = v / (1.0f + expf(-v));
-      a.y[(size_t)tok * a.M + col] = sg * u;
+      u *= sc;
+      v = v / (1.0f + expf(-v)) * u;
     } else {
-      if (a.res) v += a.res[(size_t)tok * a.M + col];
-      a.y[(size_t)tok * a.M + col] = v;
+      if (a.res) v += a.res[at];
     }
+    if (a.ystore) a.y[at] = v;
+    if (a.ybf) a.ybf[at] = (uint16_t)bf16_bits(v);
   }
 }
 
@@ -439,10 +546,12 @@ int ksteps_per_wave(int fmt, int N, bool swiglu, bool one_tile, int64_t KS) {
   return KS >= 64 ? (int)((KS + 4) / 5) : 20;   // long K at N > 4: five waves per workgroup
 }
 
+constexpr size_t kMaxLdsActs = 48 * 1024;
+constexpr size_t kMaxLdsNorm = 64 * 1024;   // RMSNorm prologue: the ring may use up to this
 constexpr int kMaxWaves = 8;
 constexpr int64_t kMinGridWaves = 900;
 
-LaunchShape pick_shape(int fmt, int64_t KS, int64_t out_tiles, int N, bool swiglu) {
+LaunchShape pick_shape(int fmt, int64_t KS, int64_t out_tiles, int N, bool swiglu, bool norm) {
   LaunchShape ls;
   ls.kps = 2;
   ls.slots = slots_for(N);
@@ -461,6 +570,11 @@ LaunchShape pick_shape(int fmt, int64_t KS, int64_t out_tiles, int N, bool swigl
     while (kpw > cyc && wgs * waves_for(kpw) < kMinGridWaves) kpw = round_cyc(kpw - cyc > cyc ? kpw - cyc : cyc);
   }
   while (waves_for(kpw) > kMaxWaves) kpw += cyc;
+  if (norm) {
+    // the RMSNorm prologue stages activations in LDS: keep the ring within budget
+    const int64_t ring = 4 * ((16 / ls.slots) * 256 + 16) + ls.nt * 512;
+    while (waves_for(kpw) * ring > (int64_t)kMaxLdsNorm && kpw < KS) kpw += cyc;
+  }
   ls.waves = (int)waves_for(kpw);
   ls.kpw = (int)kpw;
   return ls;
@@ -468,7 +582,7 @@ LaunchShape pick_shape(int fmt, int64_t KS, int64_t out_tiles, int N, bool swigl
 
 // Activations go to LDS when a workgroup's share stays within this budget
 // (N = 1 and small N * K); larger ones use buffer loads.
-constexpr size_t kMaxLdsActs = 48 * 1024;
+
 
 template <int FMT, int NT, int S, int KPS>
 hipError_t launch_s(const GemvArgs& a0, const LaunchShape& ls, bool swiglu, hipStream_t stream) {
@@ -481,7 +595,11 @@ hipError_t launch_s(const GemvArgs& a0, const LaunchShape& ls, bool swiglu, hipS
   const size_t rec = (size_t)a.N * 256 + 16;
   const size_t red = (size_t)ls.waves * NT * 128 * sizeof(float);
   const size_t whole = (size_t)ls.waves * a.x_nks * rec, ring = (size_t)ls.waves * kRing * ring_stride<S>();
-  const int xm = whole <= kMaxLdsActs ? XM_LDS : (ring <= kMaxLdsActs ? XM_RING : XM_LOAD);
+  int xm = whole <= kMaxLdsActs ? XM_LDS : (ring <= kMaxLdsActs ? XM_RING : XM_LOAD);
+  if (a.nsrc && xm == XM_LOAD) {         // the RMSNorm prologue stages its activations in LDS
+    if (red + ring > kMaxLdsNorm) return hipErrorNotSupported;
+    xm = XM_RING;
+  }
   const size_t lds = red + (xm == XM_LDS ? whole : (xm == XM_RING ? ring : 0));
   if constexpr (NT >= 2) {
     if (swiglu) {
@@ -513,14 +631,13 @@ hipError_t launch_gemv(const GemvArgs& a, const LaunchShape& ls, bool swiglu, hi
   return launch_k<FMT, 2, 2>(a, ls, swiglu, stream);
 }
 
-int validate_common(int fmt, const void* wq, const void* ws, const void* x, const void* y, int64_t M, int64_t K,
-                    int N, Geom* g) {
+int validate_common(int fmt, const void* wq, const void* ws, int64_t M, int64_t K, int N, Geom* g) {
   if (fmt < INT4 || fmt > NVFP4) return QGEMV_EFORMAT;
-  if (!wq || !ws || !x || !y) return QGEMV_EINVAL;
+  if (!wq || !ws) return QGEMV_EINVAL;
   if (M < 1 || K < 32 || M > (1 << 24)) return QGEMV_EINVAL;
   if (K % 32) return QGEMV_EALIGN;
   if (N < 1 || N > 8) return QGEMV_EUNSUPPORTED;
-  if (!aligned16(wq) || !aligned16(ws) || !aligned16(x) || !aligned4(y)) return QGEMV_EALIGN;
+  if (!aligned16(wq) || !aligned16(ws)) return QGEMV_EALIGN;
   if (!geom(fmt, M, K, g)) return QGEMV_EINVAL;
   if (g->wq_bytes >= (1ull << 32) || g->ws_bytes >= (1ull << 32)) return QGEMV_EUNSUPPORTED;
   if ((uint64_t)N * (uint64_t)K * 2ull >= (1ull << 25)) return QGEMV_EUNSUPPORTED;  // activation bytes < 2^25
@@ -528,12 +645,23 @@ int validate_common(int fmt, const void* wq, const void* ws, const void* x, cons
   return QGEMV_OK;
 }
 
+// fz: optional fusions (RMSNorm prologue, bf16 output), or null
 int run_gemv(int fmt, const void* wq, const void* ws, const void* x, const float* res, float* y, int64_t Mout,
-             int64_t Mpacked, int64_t K, int N, bool swiglu, hipStream_t stream) {
+             int64_t Mpacked, int64_t K, int N, bool swiglu, const qgemv_fusion* fz, hipStream_t stream) {
   Geom g;
-  int rc = validate_common(fmt, wq, ws, x, y, Mpacked, K, N, &g);
+  int rc = validate_common(fmt, wq, ws, Mpacked, K, N, &g);
   if (rc) return rc;
-  if (res && !aligned4(res)) return QGEMV_EALIGN;
+  const bool norm = fz && fz->norm_src;
+  uint16_t* ybf = fz ? fz->out_bf16 : nullptr;
+  if (!norm && !x) return QGEMV_EINVAL;
+  if (!y && !ybf) return QGEMV_EINVAL;
+  if (x && !aligned16(x)) return QGEMV_EALIGN;
+  if ((y && !aligned4(y)) || (res && !aligned4(res)) || ((uintptr_t)ybf & 1u)) return QGEMV_EALIGN;
+  if (norm) {
+    if (!fz->norm_gamma) return QGEMV_EINVAL;
+    if (!aligned16(fz->norm_src) || !aligned16(fz->norm_gamma)) return QGEMV_EALIGN;
+    if (!(fz->norm_eps >= 0.0f) || fz->norm_eps > 3.0e38f) return QGEMV_EINVAL;
+  }
   GemvArgs a;
   a.wq = (const uint8_t*)wq;
   a.ws = (const uint8_t*)ws;
@@ -542,7 +670,7 @@ int run_gemv(int fmt, const void* wq, const void* ws, const void* x, const float
   a.y = y;
   a.wq_bytes = (uint32_t)g.wq_bytes;
   a.ws_bytes = (uint32_t)g.ws_bytes;
-  a.x_bytes = (uint32_t)((int64_t)N * K * 2);
+  a.x_bytes = x ? (uint32_t)((int64_t)N * K * 2) : 0u;
   a.hi_offset = (uint32_t)g.hi_offset;
   a.st_offset = (uint32_t)g.st_offset;
   a.M = (int)Mout;
@@ -552,7 +680,14 @@ int run_gemv(int fmt, const void* wq, const void* ws, const void* x, const float
   a.N = N;
   a.out_tiles = (int)((Mout + 15) / 16);
   a.up_tile0 = swiglu ? (int)(Mout / 16) : 0;
-  const LaunchShape ls = pick_shape(fmt, g.KS, a.out_tiles, N, swiglu);
+  a.nsrc = norm ? fz->norm_src : nullptr;
+  a.gamma = norm ? fz->norm_gamma : nullptr;
+  a.eps = norm ? fz->norm_eps : 0.0f;
+  a.nsrc_bytes = norm ? (uint32_t)((int64_t)N * K * 4) : 0u;
+  a.gamma_bytes = norm ? (uint32_t)(K * 4) : 0u;
+  a.ybf = ybf;
+  a.ystore = y != nullptr;
+  const LaunchShape ls = pick_shape(fmt, g.KS, a.out_tiles, N, swiglu, norm);
   a.ks_per_wave = ls.kpw;
   hipError_t e;
   switch (fmt) {
@@ -561,6 +696,7 @@ int run_gemv(int fmt, const void* wq, const void* ws, const void* x, const float
     case INT8: e = launch_gemv<INT8>(a, ls, swiglu, stream); break;
     default: e = launch_gemv<NVFP4>(a, ls, swiglu, stream); break;
   }
+  if (e == hipErrorNotSupported) return QGEMV_EUNSUPPORTED;
   return map_hip(e);
 }
 
@@ -584,14 +720,28 @@ extern "C" int qgemv_version(void) { return 100; }
 
 extern "C" int qgemv(int fmt, const void* wq, const void* ws, const void* x, const float* residual, float* y,
                      int64_t M, int64_t K, int N, hipStream_t stream) {
-  return run_gemv(fmt, wq, ws, x, residual, y, M, M, K, N, false, stream);
+  if (!y) return QGEMV_EINVAL;
+  return run_gemv(fmt, wq, ws, x, residual, y, M, M, K, N, false, nullptr, stream);
 }
 
 extern "C" int qgemv_swiglu(int fmt, const void* wq, const void* ws, const void* x, float* h, int64_t I, int64_t K,
                             int N, hipStream_t stream) {
   if (I < 1) return QGEMV_EINVAL;
   if (I % 16) return QGEMV_EALIGN;
-  return run_gemv(fmt, wq, ws, x, nullptr, h, I, 2 * I, K, N, true, stream);
+  if (!h) return QGEMV_EINVAL;
+  return run_gemv(fmt, wq, ws, x, nullptr, h, I, 2 * I, K, N, true, nullptr, stream);
+}
+
+extern "C" int qgemv_ex(int fmt, const void* wq, const void* ws, const void* x, const float* residual, float* y,
+                        int64_t M, int64_t K, int N, const qgemv_fusion* fusion, hipStream_t stream) {
+  return run_gemv(fmt, wq, ws, x, residual, y, M, M, K, N, false, fusion, stream);
+}
+
+extern "C" int qgemv_swiglu_ex(int fmt, const void* wq, const void* ws, const void* x, float* h, int64_t I,
+                               int64_t K, int N, const qgemv_fusion* fusion, hipStream_t stream) {
+  if (I < 1) return QGEMV_EINVAL;
+  if (I % 16) return QGEMV_EALIGN;
+  return run_gemv(fmt, wq, ws, x, nullptr, h, I, 2 * I, K, N, true, fusion, stream);
 }
 
 extern "C" int qgemv_dequant(int fmt, const void* wq, const void* ws, int64_t M, int64_t K, float* w_out,

@@ -135,6 +135,35 @@ int qgemv(int fmt, const void* wq, const void* ws, const void* x, const float* r
 int qgemv_swiglu(int fmt, const void* wq, const void* ws, const void* x, float* h,
                  int64_t I, int64_t K, int N, hipStream_t stream);
 
+/* Optional fusions of qgemv_ex / qgemv_swiglu_ex, for chaining layers without
+ * separate normalisation or conversion kernels (NInfer article, section 2:
+ * the per-format fused kernels do the normalisation, matmul, residual add and
+ * SwiGLU in one read and one write):
+ *   norm_src:   RMSNorm prologue. The activations become
+ *                 x[n][k] = norm_src[n][k] * norm_gamma[k] / sqrt(mean_k norm_src[n][k]^2 + norm_eps)
+ *               ([N][K] fp32 and [K] fp32, device, 16-byte aligned; the `x`
+ *               argument is then ignored and may be NULL). The GPU multiplies
+ *               bf16(norm_gamma * norm_src) and applies the per-token scale,
+ *               computed in fp32, to the dot products.
+ *   out_bf16:   also write the output (y, or h for SwiGLU) rounded to bf16
+ *               (nearest even), [N][M] or [N][I], device; the fp32 output
+ *               pointer may then be NULL.
+ * Zero-initialise unused fields. */
+typedef struct qgemv_fusion {
+  const float* norm_src;
+  const float* norm_gamma;
+  float norm_eps;
+  uint16_t* out_bf16;
+} qgemv_fusion;
+
+/* qgemv with the optional fusions above (fusion may be NULL). */
+int qgemv_ex(int fmt, const void* wq, const void* ws, const void* x, const float* residual, float* y,
+             int64_t M, int64_t K, int N, const qgemv_fusion* fusion, hipStream_t stream);
+
+/* qgemv_swiglu with the optional fusions above (fusion may be NULL). */
+int qgemv_swiglu_ex(int fmt, const void* wq, const void* ws, const void* x, float* h, int64_t I, int64_t K,
+                    int N, const qgemv_fusion* fusion, hipStream_t stream);
+
 /* Byte stride between consecutive experts in an expert-stacked weight or
  * scale buffer: the packed size rounded up to 256. */
 int qgemv_expert_stride(int fmt, int64_t M, int64_t K, size_t* wq_stride, size_t* ws_stride);

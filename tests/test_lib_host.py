@@ -194,3 +194,24 @@ def test_router_and_fused_moe_validation_codes():
     assert fused(fmt=9) == -2 and fused(H=2047) in (-1, -3)
     b = ctypes.c_size_t()
     assert L.qgemv_moe_fused_workspace_bytes(128, 2048, 768, 0, 8, ctypes.byref(b)) == -7
+
+
+def test_fusion_validation_codes():
+    """qgemv_ex / qgemv_swiglu_ex argument checks (before any launch)."""
+    L = qg.load(False)
+
+    def ex(x=FAKE, y=FAKE, src=None, gamma=None, eps=1e-6, ybf=None, M=64, K=128, N=1, sw=False):
+        fz = qg.Fusion(src, gamma, eps, ybf)
+        if sw:
+            return L.qgemv_swiglu_ex(1, FAKE, FAKE, x, y, M, K, N, ctypes.byref(fz), None)
+        return L.qgemv_ex(1, FAKE, FAKE, x, None, y, M, K, N, ctypes.byref(fz), None)
+    assert ex(src=FAKE, gamma=None) == -1                 # gamma required with the prologue
+    assert ex(src=FAKE + 4, gamma=FAKE) == -3              # 16-byte alignment of the source
+    assert ex(src=FAKE, gamma=FAKE + 8) == -3
+    assert ex(src=FAKE, gamma=FAKE, eps=-1.0) == -1
+    assert ex(src=FAKE, gamma=FAKE, eps=float("nan")) == -1
+    assert ex(x=None) == -1                                # no activations and no prologue
+    assert ex(y=None, ybf=None) == -1                      # no output at all
+    assert ex(y=None, ybf=FAKE + 1) == -3                  # bf16 output must be 2-byte aligned
+    assert ex(N=9, src=FAKE, gamma=FAKE) == -7
+    assert ex(sw=True, M=24) == -3                         # I % 16
