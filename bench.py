@@ -291,6 +291,45 @@ def extras(qg, torch, dev, stream, layers, args):
                                       "8 rotated copies", "weight_bytes": nv_w, **nv}
     log("nvfp4_layer", res["nvfp4_layer"])
 
+    # the MLP block chained on the device (NInfer article, section 2: norm,
+    # matmul, SwiGLU and residual fused): RMSNorm(r) -> gate/up + SwiGLU with a
+    # bf16 h -> down(h) + r, int5, N = 1; eager, and 16 rotated layers captured
+    # in one HIP graph and replayed
+    gamma = torch.from_numpy((1 + 0.1 * synthetic.rng_for(0, 7).standard_normal(5120)).astype(np.float32)).to(dev)
+    r1 = torch.from_numpy(synthetic.residual(synthetic.rng_for(0, 7, 1), 1, 5120)).to(dev)
+    hb = torch.zeros((1, 17408), dtype=torch.int16, device=dev)
+    ym = torch.empty((1, 5120), dtype=torch.float32, device=dev)
+
+    def mlp(i):
+        L = layers[i % len(layers)]
+        qg.qgemv_swiglu_ex("int5", *L["gate_up"], None, None, 17408, 5120, 1, norm_src=r1, norm_gamma=gamma,
+                           norm_eps=1e-6, out_bf16=hb)
+        qg.qgemv("int5", *L["down"], hb, ym, 5120, 17408, 1, residual=r1)
+    mlp_bytes = (weight_bytes(qg, "int5", 2 * 17408, 5120) + weight_bytes(qg, "int5", 5120, 17408)
+                 + 5120 * 4 * 2 + 5120 * 4 + 17408 * 2 * 2 + 5120 * 8)
+    ms_e = timeit(mlp, 64)
+    nl = len(layers)
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        for i in range(nl):
+            mlp(i)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(nl):
+            mlp(i)
+    ms_g = timeit(lambda i: graph.replay(), 8) / nl
+    res["mlp_chain"] = {"workload": "27B-class MLP block, N=1: RMSNorm + gate/up 2x17408x5120 int5 + SwiGLU -> bf16 h "
+                                    "-> down 5120x17408 int5 + residual, 2 launches per layer, rotated layers",
+                        "eager_us": round(ms_e * 1e3, 2), "eager_GB/s": round(mlp_bytes / (ms_e * 1e-3) / 1e9, 1),
+                        "graph_us_per_layer": round(ms_g * 1e3, 2),
+                        "graph_GB/s": round(mlp_bytes / (ms_g * 1e-3) / 1e9, 1),
+                        "graph_layers": nl}
+    del graph
+    log("mlp_chain", res["mlp_chain"])
+
     # per format on [17408][5120], N = 1, 2, 4, 8, rotated over >= 1 GB
     M, K = 17408, 5120
     rng = synthetic.rng_for(0, 3, M)

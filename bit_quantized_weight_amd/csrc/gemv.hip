@@ -212,7 +212,9 @@ __host__ __device__ constexpr int ring_stride() { return (16 / S) * 256 + 16; }
 // NT tiles per wave: plain GEMV uses NT output tiles, SwiGLU NT/2 gate tiles
 // followed by NT/2 up tiles. S: slots (16 / S tokens per slot >= N). KPS:
 // k-steps per weight prefetch buffer. XM: activation path.
-template <int FMT, int NT, int S, int KPS, bool SWIGLU, int XM>
+// NORM: the RMSNorm prologue (a separate instantiation, so kernels without
+// it keep their register budget)
+template <int FMT, int NT, int S, int KPS, bool SWIGLU, int XM, bool NORM>
 __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
   extern __shared__ __attribute__((aligned(16))) float red[];  // [W][NT][8][16], then the LDS activations
   __shared__ float s_ss[8][8];                                  // RMSNorm: [wave][token] sums of squares
@@ -243,7 +245,8 @@ __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
   for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int ks0 = wave * a.ks_per_wave;
   const int ks1 = min(a.KS, ks0 + a.ks_per_wave);
-  const bool norm = a.nsrc != nullptr;   // uniform
+  constexpr bool norm = NORM;
+  static_assert(!NORM || XM != XM_LOAD, "the prologue stages its activations in LDS");
   const __amdgpu_buffer_rsrc_t hr = make_rsrc(a.nsrc, a.nsrc_bytes);
   const __amdgpu_buffer_rsrc_t gr = make_rsrc(a.gamma, a.gamma_bytes);
   if (lane < 8) s_ss[wave][lane] = 0.0f;  // waves with an empty k-range add nothing
@@ -275,7 +278,7 @@ __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
       };
       // staged after the first weight loads are issued, so the two overlap
       auto pre = [&]() {
-        if (norm) stage_x_norm(xl, hr, gr, a.N, a.K, ks0, ks1, a.x_nks, lane, s_ss[wave]);
+        if constexpr (NORM) stage_x_norm(xl, hr, gr, a.N, a.K, ks0, ks1, a.x_nks, lane, s_ss[wave]);
         else stage_x(xl, xr, a.N, a.K, ks0, ks1, a.x_nks, lane);
       };
       kloop<FMT, NT, S, KPS, 1>(wq, ws, tile, a.KS, ks0, ks1, a.hi_offset, acts, acc, pre);
@@ -304,7 +307,7 @@ __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
           const int c = lane + 64 * h;
           const int t = c >> 4, col = k * 128 + (c & 15) * 8;
           const bool data = (c < nch) & (k < ks1) & (col < a.K);
-          if (norm) v[h] = norm_chunk(hr, gr, a.K, t, col, data, ssr[h]);
+          if constexpr (NORM) v[h] = norm_chunk(hr, gr, a.K, t, col, data, ssr[h]);
           else v[h] = ld128(xr, data ? (uint32_t)(t * a.K + col) * 2u : kOOB);
         }
       };
@@ -332,7 +335,7 @@ __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
         ring_store(v0, 0);
       };
       kloop<FMT, NT, S, KPS, 1>(wq, ws, tile, a.KS, ks0, ks1, a.hi_offset, acts, acc, pre);
-      if (norm && ks0 < ks1) {
+      if (NORM && ks0 < ks1) {
         // tokens (lane >> 4) and 4 + (lane >> 4): sum the 16 lanes of each row
 #pragma unroll
         for (int h = 0; h < 2; ++h)
@@ -368,7 +371,7 @@ __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
     const int col = ot * 16 + row;
     if (tok >= a.N || ot >= a.out_tiles || col >= a.M) continue;
     float sc = st;                        // NVFP4 tensor scale, times the RMSNorm scale
-    if (norm) {
+    if constexpr (NORM) {
       float ss = 0.f;
       for (int w = 0; w < W; ++w) ss += s_ss[w][tok];
       sc = sc * (1.0f / sqrtf(ss / (float)a.K + a.eps));
@@ -601,17 +604,20 @@ hipError_t launch_s(const GemvArgs& a0, const LaunchShape& ls, bool swiglu, hipS
     xm = XM_RING;
   }
   const size_t lds = red + (xm == XM_LDS ? whole : (xm == XM_RING ? ring : 0));
+  const bool norm = a.nsrc != nullptr;
+#define QG_LAUNCH(SW, XMV, NRM) hipLaunchKernelGGL((k_gemv<FMT, NT, S, KPS, SW, XMV, NRM>), grid, block, lds, stream, a)
   if constexpr (NT >= 2) {
     if (swiglu) {
-      if (xm == XM_LDS) hipLaunchKernelGGL((k_gemv<FMT, NT, S, KPS, true, XM_LDS>), grid, block, lds, stream, a);
-      else if (xm == XM_RING) hipLaunchKernelGGL((k_gemv<FMT, NT, S, KPS, true, XM_RING>), grid, block, lds, stream, a);
-      else hipLaunchKernelGGL((k_gemv<FMT, NT, S, KPS, true, XM_LOAD>), grid, block, lds, stream, a);
+      if (xm == XM_LDS) { if (norm) QG_LAUNCH(true, XM_LDS, true); else QG_LAUNCH(true, XM_LDS, false); }
+      else if (xm == XM_RING) { if (norm) QG_LAUNCH(true, XM_RING, true); else QG_LAUNCH(true, XM_RING, false); }
+      else QG_LAUNCH(true, XM_LOAD, false);
       return hipGetLastError();
     }
   }
-  if (xm == XM_LDS) hipLaunchKernelGGL((k_gemv<FMT, NT, S, KPS, false, XM_LDS>), grid, block, lds, stream, a);
-  else if (xm == XM_RING) hipLaunchKernelGGL((k_gemv<FMT, NT, S, KPS, false, XM_RING>), grid, block, lds, stream, a);
-  else hipLaunchKernelGGL((k_gemv<FMT, NT, S, KPS, false, XM_LOAD>), grid, block, lds, stream, a);
+  if (xm == XM_LDS) { if (norm) QG_LAUNCH(false, XM_LDS, true); else QG_LAUNCH(false, XM_LDS, false); }
+  else if (xm == XM_RING) { if (norm) QG_LAUNCH(false, XM_RING, true); else QG_LAUNCH(false, XM_RING, false); }
+  else QG_LAUNCH(false, XM_LOAD, false);
+#undef QG_LAUNCH
   return hipGetLastError();
 }
 

@@ -164,3 +164,46 @@ def test_chained_mlp_block():
     Th_b = Th + G.BF16_REL * (np.abs(href) + Th)          # h crosses the chain as bf16
     T = G.gemv_tolerance(np.abs(href) + Th_b, Wdn) + Th_b @ np.abs(Wdn).T
     check_tol(y.cpu().numpy(), y_ref, T, "chained MLP block")
+
+
+def test_chained_mlp_block_in_a_hip_graph():
+    """The chained MLP block (two launches, no allocation, no synchronisation)
+    captured in a HIP graph and replayed several times, with other eager GPU
+    work and synchronisations between the replays: every replay equals the
+    eager result bit for bit."""
+    I, H, N = 512, 2048, 2
+    rng = synthetic.rng_for(23, I, H)
+    wgu, sgu = (dev(a, torch) for a in qg().pack("int4", synthetic.weights(rng, 2 * I, H)))
+    wdn, sdn = (dev(a, torch) for a in qg().pack("int5", synthetic.weights(rng, H, I)))
+    res, gamma = _norm_inputs(6, N, H)
+    dres, dg = dev(res, torch), dev(gamma, torch)
+    hbuf = torch.zeros((N, I), dtype=torch.int16, device="cuda")
+    y = torch.zeros((N, H), dtype=torch.float32, device="cuda")
+
+    def chain():
+        qg().qgemv_swiglu_ex("int4", wgu, sgu, None, None, I, H, N, norm_src=dres, norm_gamma=dg, norm_eps=1e-6,
+                             out_bf16=hbuf)
+        qg().qgemv("int5", wdn, sdn, hbuf, y, H, I, N, residual=dres)
+
+    chain()
+    torch.cuda.synchronize()
+    eager = y.cpu().numpy().copy()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        chain()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        chain()
+    noise = torch.randn((N, H), device="cuda")
+    for rep in range(4):
+        y.fill_(float("nan"))
+        hbuf.zero_()
+        _ = (noise * rep).sum()                 # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = y.cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), eager.view(np.uint32)), f"replay {rep} differs"
