@@ -353,6 +353,15 @@ def extras(qg, torch, dev, stream, layers, args):
             gbs = b / (ms * 1e-3) / 1e9
             pf[fmt][f"N{n}"] = {"us": round(ms * 1e3, 2), "GB/s": round(gbs, 1), "frac": round(gbs / PEAK_GBS, 4),
                                 "of_probe": round(gbs / probe_gbs, 4)}
+        if fmt == "int4":
+            # the same calls with the batch-invariant summation order
+            inv = {}
+            for n in (1, 8):
+                xb = torch.from_numpy(synthetic.activations(rng, n, K, 0.01)).to(dev)
+                yy = torch.empty((n, M), dtype=torch.float32, device=dev)
+                ms = timeit(lambda i: qg.qgemv_ex(fmt, *d[i % copies], xb, yy, M, K, n, batch_invariant=True), 60)
+                inv[f"N{n}"] = {"us": round(ms * 1e3, 2), "GB/s": round((nb + n * K * 2 + n * M * 4) / (ms * 1e-3) / 1e9, 1)}
+            pf[fmt]["batch_invariant"] = inv
         del d
         log("per_format", fmt, pf[fmt])
     res["per_format"] = {"shape": [M, K], "formats": pf}

@@ -27,7 +27,10 @@ _lib = None
 class Fusion(ctypes.Structure):
     """qgemv_fusion (include/qgemv.h): RMSNorm prologue and bf16 output."""
     _fields_ = [("norm_src", ctypes.c_void_p), ("norm_gamma", ctypes.c_void_p), ("norm_eps", ctypes.c_float),
-                ("out_bf16", ctypes.c_void_p)]
+                ("out_bf16", ctypes.c_void_p), ("flags", ctypes.c_int)]
+
+
+BATCH_INVARIANT = 1
 
 
 class QgemvError(RuntimeError):
@@ -170,26 +173,28 @@ def qgemv_swiglu(fmt, wq, ws, x, h, I: int, K: int, N: int, stream=None) -> None
            "qgemv_swiglu")
 
 
-def _fusion(norm_src, norm_gamma, norm_eps, out_bf16):
-    if norm_src is None and out_bf16 is None:
+def _fusion(norm_src, norm_gamma, norm_eps, out_bf16, batch_invariant=False):
+    if norm_src is None and out_bf16 is None and not batch_invariant:
         return None
-    return ctypes.byref(Fusion(_ptr(norm_src), _ptr(norm_gamma), float(norm_eps), _ptr(out_bf16)))
+    return ctypes.byref(Fusion(_ptr(norm_src), _ptr(norm_gamma), float(norm_eps), _ptr(out_bf16),
+                               BATCH_INVARIANT if batch_invariant else 0))
 
 
 def qgemv_ex(fmt, wq, ws, x, y, M: int, K: int, N: int, residual=None, norm_src=None, norm_gamma=None,
-             norm_eps: float = 1e-6, out_bf16=None, stream=None) -> None:
+             norm_eps: float = 1e-6, out_bf16=None, batch_invariant=False, stream=None) -> None:
     """qgemv with the optional RMSNorm prologue (norm_src, norm_gamma,
-    norm_eps; x may be None then) and bf16 output copy (out_bf16; y may be
-    None then)."""
+    norm_eps; x may be None then), bf16 output copy (out_bf16; y may be None
+    then) and batch-invariant summation order."""
     _check(load().qgemv_ex(_fmt(fmt), _ptr(wq), _ptr(ws), _ptr(x), _ptr(residual), _ptr(y), M, K, N,
-                           _fusion(norm_src, norm_gamma, norm_eps, out_bf16), _stream(stream)), "qgemv_ex")
+                           _fusion(norm_src, norm_gamma, norm_eps, out_bf16, batch_invariant), _stream(stream)),
+           "qgemv_ex")
 
 
 def qgemv_swiglu_ex(fmt, wq, ws, x, h, I: int, K: int, N: int, norm_src=None, norm_gamma=None,
-                    norm_eps: float = 1e-6, out_bf16=None, stream=None) -> None:
+                    norm_eps: float = 1e-6, out_bf16=None, batch_invariant=False, stream=None) -> None:
     _check(load().qgemv_swiglu_ex(_fmt(fmt), _ptr(wq), _ptr(ws), _ptr(x), _ptr(h), I, K, N,
-                                  _fusion(norm_src, norm_gamma, norm_eps, out_bf16), _stream(stream)),
-           "qgemv_swiglu_ex")
+                                  _fusion(norm_src, norm_gamma, norm_eps, out_bf16, batch_invariant),
+                                  _stream(stream)), "qgemv_swiglu_ex")
 
 
 def moe_workspace_bytes(E: int, H: int, I: int, N: int, top_k: int) -> int:

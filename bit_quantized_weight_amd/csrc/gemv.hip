@@ -554,10 +554,30 @@ constexpr size_t kMaxLdsNorm = 64 * 1024;   // RMSNorm prologue: the ring may us
 constexpr int kMaxWaves = 8;
 constexpr int64_t kMinGridWaves = 900;
 
-LaunchShape pick_shape(int fmt, int64_t KS, int64_t out_tiles, int N, bool swiglu, bool norm) {
+// Batch-invariant mode: every choice that orders a token's sums (the slot
+// count, hence the scale-step cycles and the lane reduction, and the K split
+// over waves) depends on K alone, so a token's outputs are the same bits for
+// any N; the row tiles per workgroup (which do not touch the order) still
+// follow N.
+constexpr int kInvariantKsteps = 20;
+
+LaunchShape pick_shape(int fmt, int64_t KS, int64_t out_tiles, int N, bool swiglu, bool norm, bool inv) {
   LaunchShape ls;
   ls.kps = 2;
-  ls.slots = slots_for(N);
+  ls.slots = inv ? 2 : slots_for(N);
+  if (inv) {
+    const bool one = single_tile(fmt, N, swiglu, out_tiles);
+    ls.nt = one ? 1 : 2;
+    int64_t kpw = kInvariantKsteps;   // the slot count 2 has one-k-step cycles in every format
+    while ((KS + kpw - 1) / kpw > kMaxWaves) ++kpw;
+    if (norm) {                       // LDS ring budget, taken at two tiles so that it does not depend on N
+      const int64_t ring = 4 * (8 * 256 + 16) + 2 * 512;
+      while ((KS + kpw - 1) / kpw * ring > (int64_t)kMaxLdsNorm && kpw < KS) ++kpw;
+    }
+    ls.waves = (int)((KS + kpw - 1) / kpw);
+    ls.kpw = (int)kpw;
+    return ls;
+  }
   const int cyc = cycle_ksteps(fmt, ls.slots);
   const bool one = single_tile(fmt, N, swiglu, out_tiles);
   ls.nt = one ? 1 : 2;
@@ -693,7 +713,9 @@ int run_gemv(int fmt, const void* wq, const void* ws, const void* x, const float
   a.gamma_bytes = norm ? (uint32_t)(K * 4) : 0u;
   a.ybf = ybf;
   a.ystore = y != nullptr;
-  const LaunchShape ls = pick_shape(fmt, g.KS, a.out_tiles, N, swiglu, norm);
+  const bool inv = fz && (fz->flags & QGEMV_BATCH_INVARIANT);
+  if (fz && (fz->flags & ~QGEMV_BATCH_INVARIANT)) return QGEMV_EINVAL;
+  const LaunchShape ls = pick_shape(fmt, g.KS, a.out_tiles, N, swiglu, norm, inv);
   a.ks_per_wave = ls.kpw;
   hipError_t e;
   switch (fmt) {

@@ -148,12 +148,21 @@ int qgemv_swiglu(int fmt, const void* wq, const void* ws, const void* x, float* 
  *   out_bf16:   also write the output (y, or h for SwiGLU) rounded to bf16
  *               (nearest even), [N][M] or [N][I], device; the fp32 output
  *               pointer may then be NULL.
+ *   flags:      QGEMV_BATCH_INVARIANT: every token's outputs are the same
+ *               bits whatever N is and wherever the token sits in the batch
+ *               (the summation order then depends on K only), for
+ *               byte-identical speculative decoding (NInfer article, section
+ *               3: multi-token-prediction verify windows; RustingStrata page,
+ *               known issues: reordered floating-point work diverges). Costs
+ *               some speed at N < 8. Other bits: QGEMV_EINVAL.
  * Zero-initialise unused fields. */
+enum { QGEMV_BATCH_INVARIANT = 1 };
 typedef struct qgemv_fusion {
   const float* norm_src;
   const float* norm_gamma;
   float norm_eps;
   uint16_t* out_bf16;
+  int flags;
 } qgemv_fusion;
 
 /* qgemv with the optional fusions above (fusion may be NULL). */

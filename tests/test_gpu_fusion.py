@@ -207,3 +207,59 @@ def test_chained_mlp_block_in_a_hip_graph():
         torch.cuda.synchronize()
         got = y.cpu().numpy()
         assert np.array_equal(got.view(np.uint32), eager.view(np.uint32)), f"replay {rep} differs"
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("M,K,swiglu,norm", [(128, 1024, False, False), (37, 5120, False, True),
+                                             (64, 2048, True, False), (48, 640, True, True),
+                                             (17408, 5120, False, False)])
+def test_batch_invariant_mode(fmt, M, K, swiglu, norm):
+    """QGEMV_BATCH_INVARIANT: each token of an N = 8 call, of an N = 3 call on
+    rows 5..7 and of N = 1 calls gives the same bits, and all stay within the
+    oracle's bound."""
+    log("batch invariant", fmt, M, K, swiglu, norm)
+    Mp = 2 * M if swiglu else M
+    rng = synthetic.rng_for(24, M, K)
+    wq, ws = qg().pack(fmt, synthetic.weights(rng, Mp, K))
+    dq, dsc = dev(wq, torch), dev(ws, torch)
+    if norm:
+        h, gamma = _norm_inputs(M + K, 8, K)
+        dg = dev(gamma, torch)
+    else:
+        xb = synthetic.activations(rng, 8, K, 0.01)
+
+    def call(rows):
+        n = len(rows)
+        out = torch.full((n, M), float("nan"), dtype=torch.float32, device="cuda")
+        kw = dict(batch_invariant=True)
+        if norm:
+            kw.update(norm_src=dev(np.ascontiguousarray(h[rows]), torch), norm_gamma=dg, norm_eps=1e-6)
+            x = None
+        else:
+            x = dev(np.ascontiguousarray(xb[rows]), torch)
+        if swiglu:
+            qg().qgemv_swiglu_ex(fmt, dq, dsc, x, out, M, K, n, **kw)
+        else:
+            qg().qgemv_ex(fmt, dq, dsc, x, out, M, K, n, **kw)
+        torch.cuda.synchronize()
+        return out.cpu().numpy()
+    y8 = call(list(range(8)))
+    y3 = call([5, 6, 7])
+    for n in range(8):
+        y1 = call([n])
+        assert np.array_equal(y1.view(np.uint32)[0], y8.view(np.uint32)[n]), f"row {n}: N=1 differs from N=8"
+    assert np.array_equal(y3.view(np.uint32), y8.view(np.uint32)[5:8]), "N=3 differs from N=8"
+    if M > 1024:                                   # full size: check sampled tiles against the oracle
+        x64 = G.x_from_bits(xb)
+        for rt in (0, 511, 1087):
+            Wt = tile_rows(fmt, wq, ws, M, K, rt)
+            check_tol(y8[:, rt * 16:(rt + 1) * 16], G.gemv(x64, Wt), G.gemv_tolerance(x64, Wt), f"tile {rt}")
+        return
+    Wd = oracle_weights(fmt, wq, ws, Mp, K)
+    x64 = G.rmsnorm(h, gamma, 1e-6) if norm else G.x_from_bits(xb)
+    tol = G.norm_gemv_tolerance if norm else G.gemv_tolerance
+    if swiglu:
+        ref, T = G.swiglu_from(G.gemv(x64, Wd[:M]), G.gemv(x64, Wd[M:]), tol(x64, Wd[:M]), tol(x64, Wd[M:]))
+    else:
+        ref, T = G.gemv(x64, Wd), tol(x64, Wd)
+    check_tol(y8, ref, T, "batch invariant")

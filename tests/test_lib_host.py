@@ -200,8 +200,8 @@ def test_fusion_validation_codes():
     """qgemv_ex / qgemv_swiglu_ex argument checks (before any launch)."""
     L = qg.load(False)
 
-    def ex(x=FAKE, y=FAKE, src=None, gamma=None, eps=1e-6, ybf=None, M=64, K=128, N=1, sw=False):
-        fz = qg.Fusion(src, gamma, eps, ybf)
+    def ex(x=FAKE, y=FAKE, src=None, gamma=None, eps=1e-6, ybf=None, M=64, K=128, N=1, sw=False, flags=0):
+        fz = qg.Fusion(src, gamma, eps, ybf, flags)
         if sw:
             return L.qgemv_swiglu_ex(1, FAKE, FAKE, x, y, M, K, N, ctypes.byref(fz), None)
         return L.qgemv_ex(1, FAKE, FAKE, x, None, y, M, K, N, ctypes.byref(fz), None)
@@ -215,3 +215,4 @@ def test_fusion_validation_codes():
     assert ex(y=None, ybf=FAKE + 1) == -3                  # bf16 output must be 2-byte aligned
     assert ex(N=9, src=FAKE, gamma=FAKE) == -7
     assert ex(sw=True, M=24) == -3                         # I % 16
+    assert ex(flags=2) == -1 and ex(flags=-1) == -1       # unknown flag bits
