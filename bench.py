@@ -143,11 +143,14 @@ def main():
     gu_bytes = weight_bytes(qg, "int5", 2 * 17408, 5120) + N * 5120 * 2 + N * 17408 * 4
     log(f"layer weights {layer_w / 1e6:.1f} MB, rotation {args.layers} layers = {args.layers * layer_w / 1e9:.2f} GB")
 
+    # split-remainder workspace: the launches balance their last row blocks
+    wsp = qg.split_workspace(dev)
+
     def step(i):
         L = layers[i % args.layers]
-        qg.qgemv("int4", *L["qkv"], x, qkv, 7168, 5120, N)
-        qg.qgemv_swiglu("int5", *L["gate_up"], x, h, 17408, 5120, N)
-        qg.qgemv("int5", *L["down"], xd, y, 5120, 17408, N, residual=res)
+        qg.qgemv_ex("int4", *L["qkv"], x, qkv, 7168, 5120, N, workspace=wsp)
+        qg.qgemv_swiglu_ex("int5", *L["gate_up"], x, h, 17408, 5120, N, workspace=wsp)
+        qg.qgemv_ex("int5", *L["down"], xd, y, 5120, 17408, N, residual=res, workspace=wsp)
 
     for i in range(args.warmup):
         step(i)
@@ -182,10 +185,13 @@ def main():
         return float(np.median(out)), float(min(out)), float(max(out))
 
     kern = {}
-    kern["qkv_int4"] = (time_alone(lambda i: qg.qgemv("int4", *layers[i % args.layers]["qkv"], x, qkv, 7168, 5120, N), 100),
+    kern["qkv_int4"] = (time_alone(lambda i: qg.qgemv_ex("int4", *layers[i % args.layers]["qkv"], x, qkv, 7168, 5120, N,
+                                                         workspace=wsp), 100),
                         weight_bytes(qg, "int4", 7168, 5120) + N * 5120 * 2 + N * 7168 * 4)
-    kern["gate_up_swiglu_int5"] = (time_alone(lambda i: qg.qgemv_swiglu("int5", *layers[i % args.layers]["gate_up"], x, h, 17408, 5120, N), 50), gu_bytes)
-    kern["down_residual_int5"] = (time_alone(lambda i: qg.qgemv("int5", *layers[i % args.layers]["down"], xd, y, 5120, 17408, N, residual=res), 50),
+    kern["gate_up_swiglu_int5"] = (time_alone(lambda i: qg.qgemv_swiglu_ex("int5", *layers[i % args.layers]["gate_up"], x, h,
+                                                                            17408, 5120, N, workspace=wsp), 50), gu_bytes)
+    kern["down_residual_int5"] = (time_alone(lambda i: qg.qgemv_ex("int5", *layers[i % args.layers]["down"], xd, y, 5120,
+                                                                   17408, N, residual=res, workspace=wsp), 50),
                                   weight_bytes(qg, "int5", 5120, 17408) + N * 17408 * 2 + N * 5120 * 8)
     kernels = {k: {"us": round(t[0] * 1e3, 2), "us_min": round(t[1] * 1e3, 2), "us_max": round(t[2] * 1e3, 2),
                    "GB/s": round(b / (t[0] * 1e-3) / 1e9, 1)} for k, (t, b) in kern.items()}
@@ -194,14 +200,15 @@ def main():
     gu_gbs = gu_bytes / (gu_ms * 1e-3) / 1e9
 
     src_hash = kernel_source_hash()
-    roofline = {"bound": "hbm", "kernel": "k_gemv<int5, swiglu> (gate/up + SwiGLU)",
+    assert int(wsp[:4].view(torch.int32).item()) == 0, "a split-remainder wait timed out"
+    roofline = {"bound": "hbm", "kernel": "k_gemv<int5, swiglu> (gate/up + SwiGLU, split remainder)",
                 "achieved": round(gu_gbs, 1), "peak": PEAK_GBS, "unit": "GB/s", "frac": round(gu_gbs / PEAK_GBS, 4),
                 "traffic": pmc_traffic("gate_up_swiglu_int5", src_hash),
                 "algorithmic_bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_ms * 1e3, 2)}
 
     extra = {}
     if not args.no_extra:
-        extra = extras(qg, torch, dev, stream, layers, args)
+        extra = extras(qg, torch, dev, stream, layers, args, wsp)
         del layers
         torch.cuda.empty_cache()
         extra["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
@@ -234,7 +241,7 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def extras(qg, torch, dev, stream, layers, args):
+def extras(qg, torch, dev, stream, layers, args, wsp):
     import synthetic
     res = {}
 
@@ -278,9 +285,9 @@ def extras(qg, torch, dev, stream, layers, args):
 
         def nv_step(i):
             L = nv_layers[i % len(nv_layers)]
-            qg.qgemv("nvfp4", *L["qkv"], xn, qn, 7168, 5120, n)
-            qg.qgemv_swiglu("nvfp4", *L["gate_up"], xn, hn, 17408, 5120, n)
-            qg.qgemv("nvfp4", *L["down"], xdn, yn, 5120, 17408, n, residual=rn)
+            qg.qgemv_ex("nvfp4", *L["qkv"], xn, qn, 7168, 5120, n, workspace=wsp)
+            qg.qgemv_swiglu_ex("nvfp4", *L["gate_up"], xn, hn, 17408, 5120, n, workspace=wsp)
+            qg.qgemv_ex("nvfp4", *L["down"], xdn, yn, 5120, 17408, n, residual=rn, workspace=wsp)
         ms = timeit(nv_step, 40)
         b = nv_w + n * (5120 * 2 + 7168 * 4 + 5120 * 2 + 17408 * 4 + 17408 * 2 + 5120 * 8)
         nv[f"N{n}"] = {"us": round(ms * 1e3, 2), "GB/s": round(b / (ms * 1e-3) / 1e9, 1),
@@ -348,11 +355,12 @@ def extras(qg, torch, dev, stream, layers, args):
         for n in (1, 2, 4, 8):
             xb = torch.from_numpy(synthetic.activations(rng, n, K, 0.01)).to(dev)
             yy = torch.empty((n, M), dtype=torch.float32, device=dev)
-            ms = timeit(lambda i: qg.qgemv(fmt, *d[i % copies], xb, yy, M, K, n), 60)
+            ms = timeit(lambda i: qg.qgemv_ex(fmt, *d[i % copies], xb, yy, M, K, n, workspace=wsp), 60)
+            ms0 = timeit(lambda i: qg.qgemv(fmt, *d[i % copies], xb, yy, M, K, n), 60)
             b = nb + n * K * 2 + n * M * 4
             gbs = b / (ms * 1e-3) / 1e9
             pf[fmt][f"N{n}"] = {"us": round(ms * 1e3, 2), "GB/s": round(gbs, 1), "frac": round(gbs / PEAK_GBS, 4),
-                                "of_probe": round(gbs / probe_gbs, 4)}
+                                "of_probe": round(gbs / probe_gbs, 4), "us_no_workspace": round(ms0 * 1e3, 2)}
         if fmt == "int4":
             # the same calls with the batch-invariant summation order
             inv = {}

@@ -25,9 +25,11 @@ _lib = None
 
 
 class Fusion(ctypes.Structure):
-    """qgemv_fusion (include/qgemv.h): RMSNorm prologue and bf16 output."""
+    """qgemv_fusion (include/qgemv.h): RMSNorm prologue, bf16 output, flags
+    and the split-remainder workspace."""
     _fields_ = [("norm_src", ctypes.c_void_p), ("norm_gamma", ctypes.c_void_p), ("norm_eps", ctypes.c_float),
-                ("out_bf16", ctypes.c_void_p), ("flags", ctypes.c_int)]
+                ("out_bf16", ctypes.c_void_p), ("flags", ctypes.c_int), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t)]
 
 
 BATCH_INVARIANT = 1
@@ -66,6 +68,7 @@ def load(require_torch: bool = True):
         "qgemv_swiglu": (I32, [I32, P, P, P, P, I64, I64, I32, P]),
         "qgemv_ex": (I32, [I32, P, P, P, P, P, I64, I64, I32, ctypes.POINTER(Fusion), P]),
         "qgemv_swiglu_ex": (I32, [I32, P, P, P, P, I64, I64, I32, ctypes.POINTER(Fusion), P]),
+        "qgemv_split_workspace_bytes": (I32, [PSZ]),
         "qgemv_moe_workspace_bytes": (I32, [I32, I64, I64, I32, I32, PSZ]),
         "qgemv_moe": (I32, [I32, P, P, P, P, I32, I64, I64, P, P, P, I32, P, P, I32, P, SZ, P]),
         "qgemv_moe_index": (I32, [P, I32, I32, I32, P, P, P, P, P, P]),
@@ -86,7 +89,7 @@ def load(require_torch: bool = True):
 def symbols() -> list[str]:
     """Names of the entry points the binding declares (the C ABI)."""
     return ["qgemv_strerror", "qgemv_version", "qgemv_packed_bytes", "qgemv_expert_stride", "qgemv_pack",
-            "qgemv_pack_codes", "qgemv", "qgemv_swiglu", "qgemv_ex", "qgemv_swiglu_ex",
+            "qgemv_pack_codes", "qgemv", "qgemv_swiglu", "qgemv_ex", "qgemv_swiglu_ex", "qgemv_split_workspace_bytes",
             "qgemv_moe_workspace_bytes", "qgemv_moe",
             "qgemv_moe_index", "qgemv_moe_route", "qgemv_moe_fused_workspace_bytes", "qgemv_moe_fused",
             "qgemv_dequant", "qgemv_probe_read"]
@@ -173,27 +176,47 @@ def qgemv_swiglu(fmt, wq, ws, x, h, I: int, K: int, N: int, stream=None) -> None
            "qgemv_swiglu")
 
 
-def _fusion(norm_src, norm_gamma, norm_eps, out_bf16, batch_invariant=False):
-    if norm_src is None and out_bf16 is None and not batch_invariant:
+def _fusion(norm_src, norm_gamma, norm_eps, out_bf16, batch_invariant=False, workspace=None):
+    if norm_src is None and out_bf16 is None and not batch_invariant and workspace is None:
         return None
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     return ctypes.byref(Fusion(_ptr(norm_src), _ptr(norm_gamma), float(norm_eps), _ptr(out_bf16),
-                               BATCH_INVARIANT if batch_invariant else 0))
+                               BATCH_INVARIANT if batch_invariant else 0, _ptr(workspace), wbytes))
+
+
+def split_workspace_bytes() -> int:
+    """Bytes of the split-remainder workspace on the current device."""
+    b = ctypes.c_size_t(0)
+    _check(load().qgemv_split_workspace_bytes(ctypes.byref(b)), "qgemv_split_workspace_bytes")
+    return b.value
+
+
+def split_workspace(device):
+    """A zero-filled split-remainder workspace (uint8 tensor) for qgemv_ex /
+    qgemv_swiglu_ex on `device`. Calls that may overlap in time need their
+    own; word 0 (int32) turns nonzero if a wait ever timed out."""
+    import torch
+    with torch.cuda.device(device):
+        n = split_workspace_bytes()
+    return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
 def qgemv_ex(fmt, wq, ws, x, y, M: int, K: int, N: int, residual=None, norm_src=None, norm_gamma=None,
-             norm_eps: float = 1e-6, out_bf16=None, batch_invariant=False, stream=None) -> None:
+             norm_eps: float = 1e-6, out_bf16=None, batch_invariant=False, workspace=None, stream=None) -> None:
     """qgemv with the optional RMSNorm prologue (norm_src, norm_gamma,
     norm_eps; x may be None then), bf16 output copy (out_bf16; y may be None
-    then) and batch-invariant summation order."""
+    then), batch-invariant summation order and split-remainder workspace
+    (a tensor from split_workspace)."""
     _check(load().qgemv_ex(_fmt(fmt), _ptr(wq), _ptr(ws), _ptr(x), _ptr(residual), _ptr(y), M, K, N,
-                           _fusion(norm_src, norm_gamma, norm_eps, out_bf16, batch_invariant), _stream(stream)),
-           "qgemv_ex")
+                           _fusion(norm_src, norm_gamma, norm_eps, out_bf16, batch_invariant, workspace),
+                           _stream(stream)), "qgemv_ex")
 
 
 def qgemv_swiglu_ex(fmt, wq, ws, x, h, I: int, K: int, N: int, norm_src=None, norm_gamma=None,
-                    norm_eps: float = 1e-6, out_bf16=None, batch_invariant=False, stream=None) -> None:
+                    norm_eps: float = 1e-6, out_bf16=None, batch_invariant=False, workspace=None,
+                    stream=None) -> None:
     _check(load().qgemv_swiglu_ex(_fmt(fmt), _ptr(wq), _ptr(ws), _ptr(x), _ptr(h), I, K, N,
-                                  _fusion(norm_src, norm_gamma, norm_eps, out_bf16, batch_invariant),
+                                  _fusion(norm_src, norm_gamma, norm_eps, out_bf16, batch_invariant, workspace),
                                   _stream(stream)), "qgemv_swiglu_ex")
 
 

@@ -26,6 +26,11 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <atomic>
+#include <mutex>
+#include <numeric>
+#include <vector>
+
 #include "device.hpp"
 #include "kloop.hpp"
 #include "layout.hpp"
@@ -57,7 +62,26 @@ struct GemvArgs {
   uint32_t nsrc_bytes, gamma_bytes;
   uint16_t* ybf;          // bf16 copy of the output [N][M], or null
   bool ystore;            // write the fp32 output y
+  // Split remainder (frag > 1): workgroups [0, n_full) own whole row blocks;
+  // workgroup n_full + b * frag + f owns K fragment f of row block n_full + b.
+  // Fragments below the last publish partial sums (part) and raise a flag;
+  // the last fragment (the highest workgroup of its block) adds them.
+  int n_full, frag;
+  float* part;            // [(blocks - n_full) * (frag - 1)][NT * 128]
+  uint32_t* pflag;        // word 0: sticky error; flags from word 64, 16 words apart
 };
+
+// Device-scope accesses for data one workgroup hands to another (they bypass
+// the XCD-local L2, so a workgroup on another XCD reads the stored value)
+__device__ __forceinline__ void st_f32_dev(float* p, float v) {
+  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __builtin_bit_cast(uint32_t, v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_f32_dev(const float* p) {
+  return __builtin_bit_cast(float, __hip_atomic_load(reinterpret_cast<const uint32_t*>(p), __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT));
+}
+constexpr uint32_t kFragSpin = 1u << 20;   // polls before a wait gives up
 
 // bf16 round to nearest even of a finite or infinite fp32 (NaN stays NaN)
 __device__ __forceinline__ uint32_t bf16_bits(float f) {
@@ -232,10 +256,16 @@ __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
 
   // row tiles of this wave (clamped: out-of-range tiles compute a copy of the
   // last tile and are never stored)
+  int rblk = blockIdx.x, frag = -1;       // row block and K fragment (uniform)
+  if (a.frag > 1 && rblk >= a.n_full) {
+    const int q = rblk - a.n_full;
+    rblk = a.n_full + q / a.frag;
+    frag = q - (q / a.frag) * a.frag;
+  }
   int tile[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    int ot = blockIdx.x * TO + (SWIGLU ? (t % TO) : t);
+    int ot = rblk * TO + (SWIGLU ? (t % TO) : t);
     ot = ot < a.out_tiles ? ot : a.out_tiles - 1;
     tile[t] = (SWIGLU && t >= TO) ? a.up_tile0 + ot : ot;
   }
@@ -243,8 +273,16 @@ __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
   f32x4 acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int ks0 = wave * a.ks_per_wave;
-  const int ks1 = min(a.KS, ks0 + a.ks_per_wave);
+  int kb0 = 0, kb1 = a.KS, kpw = a.ks_per_wave;
+  if (frag >= 0) {                        // this fragment's K range in whole cycles, split over the waves
+    constexpr int CK = C::KSTEPS;
+    const int nc = (a.KS + CK - 1) / CK;
+    kb0 = frag * nc / a.frag * CK;
+    kb1 = min(a.KS, (frag + 1) * nc / a.frag * CK);
+    kpw = ((kb1 - kb0 + CK - 1) / CK + W - 1) / W * CK;
+  }
+  const int ks0 = kb0 + wave * kpw;
+  const int ks1 = min(kb1, ks0 + kpw);
   constexpr bool norm = NORM;
   static_assert(!NORM || XM != XM_LOAD, "the prologue stages its activations in LDS");
   const __amdgpu_buffer_rsrc_t hr = make_rsrc(a.nsrc, a.nsrc_bytes);
@@ -295,7 +333,7 @@ __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
       // onto the record's zero block, so neither side branches per lane; the
       // second chunk is skipped (uniformly) when N <= 4.
       const bool two = nch > 64;
-      const uint32_t sdst0 = (uint32_t)lane * 16u;
+      const uint32_t sdst0 = (uint32_t)min(lane, nch) * 16u;   // N < 4: lanes past the record hit its zero block
       const uint32_t sdst1 = (uint32_t)min(lane + 64, nch) * 16u;
       // RMSNorm: lane chunk c always belongs to token c >> 4, so each lane sums
       // the squares of its two chunks' tokens over the k-range in ssr
@@ -361,13 +399,53 @@ __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
   reduce_to_lds<S, NT>(acc, red, wave, lane);
   __syncthreads();
 
+  const int nslot = a.frag - 1;
+  const size_t slot0 = frag >= 0 ? (size_t)(rblk - a.n_full) * nslot : 0;
+  if (frag >= 0 && frag < nslot) {
+    // publish this fragment's partial sums (waves added in order) and raise its flag
+    float* dst = a.part + (slot0 + frag) * (NT * 128);
+    for (int o = threadIdx.x; o < NT * 128; o += blockDim.x) {
+      float v = 0.f;
+      for (int w = 0; w < W; ++w) v += red[(size_t)w * NT * 128 + o];
+      st_f32_dev(dst + o, v);
+    }
+    __builtin_amdgcn_s_waitcnt(0);        // this thread's stores have completed
+    __syncthreads();
+    if (threadIdx.x == 0)
+      __hip_atomic_store(a.pflag + 64 + (slot0 + frag) * 16, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  if (frag >= 0) {
+    // last fragment: wait for the others (dispatched before it), bounded
+    if (wave == 0 && lane < nslot) {
+      uint32_t* fl = a.pflag + 64 + (slot0 + lane) * 16;
+      uint32_t it = 0;
+      while (__hip_atomic_load(fl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+        if (++it >= kFragSpin) {
+          atomicOr(a.pflag, 1u);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+      __hip_atomic_store(fl, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // its only reader
+    }
+    __syncthreads();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  }
+
   float st = 1.0f;
   if constexpr (FMT == NVFP4) st = __builtin_bit_cast(float, ld32(ws, a.st_offset));
+  // sum of a (tile, token, row) over the earlier fragments, in fragment order
+  auto frag_sum = [&](int o) -> float {
+    float v = 0.f;
+    for (int f = 0; f < nslot; ++f) v += ld_f32_dev(a.part + (slot0 + f) * (NT * 128) + o);
+    return v;
+  };
   const int n_out = TO * 128;
   for (int o = threadIdx.x; o < n_out; o += blockDim.x) {
     const int to = o >> 7, rem = o & 127;
     const int tok = rem >> 4, row = rem & 15;
-    const int ot = blockIdx.x * TO + to;
+    const int ot = rblk * TO + to;
     const int col = ot * 16 + row;
     if (tok >= a.N || ot >= a.out_tiles || col >= a.M) continue;
     float sc = st;                        // NVFP4 tensor scale, times the RMSNorm scale
@@ -376,13 +454,25 @@ __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
       for (int w = 0; w < W; ++w) ss += s_ss[w][tok];
       sc = sc * (1.0f / sqrtf(ss / (float)a.K + a.eps));
     }
-    float v = 0.f;
-    for (int w = 0; w < W; ++w) v += red[((size_t)(w * NT + to) * 8 + tok) * 16 + row];
+    float v = 0.f, vo = 0.f;
+    for (int w = 0; w < W; ++w) vo += red[((size_t)(w * NT + to) * 8 + tok) * 16 + row];
+    if (frag >= 0) {
+      v = frag_sum(to * 128 + rem);
+      v += vo;
+    } else {
+      v = vo;
+    }
     v *= sc;
     const size_t at = (size_t)tok * a.M + col;
     if constexpr (SWIGLU) {
-      float u = 0.f;
-      for (int w = 0; w < W; ++w) u += red[((size_t)(w * NT + TO + to) * 8 + tok) * 16 + row];
+      float u = 0.f, uo = 0.f;
+      for (int w = 0; w < W; ++w) uo += red[((size_t)(w * NT + TO + to) * 8 + tok) * 16 + row];
+      if (frag >= 0) {
+        u = frag_sum((TO + to) * 128 + rem);
+        u += uo;
+      } else {
+        u = uo;
+      }
       u *= sc;
       v = v / (1.0f + expf(-v)) * u;
     } else {
@@ -519,8 +609,7 @@ int cycle_ksteps(int fmt, int S) {
 //   * A wave streams best with 12-20 k-steps of its tiles: 20 at N = 1 and
 //     N > 4, 12 at N = 2 and for int5/int8 at N = 4, 16 for int4/NVFP4 at
 //     N = 4; NVFP4 at N = 1 with 12; SwiGLU and long K at N > 4 take longer
-//     ranges (five waves per workgroup); int8 at N = 1 on two-tile
-//     workgroups keeps the whole K.
+//     ranges (five waves per workgroup).
 // The grid should hold at least ~900 waves so the chip's 1024 SIMDs have
 // work; below that the k-range per wave shrinks (never under one scale
 // cycle). Each wave's range is a whole number of cycles.
@@ -543,7 +632,7 @@ int ksteps_per_wave(int fmt, int N, bool swiglu, bool one_tile, int64_t KS) {
     if (N <= 4) return (fmt == INT4 || fmt == NVFP4) ? 16 : 12;
     return 20;
   }
-  if (N == 1) return fmt == INT8 ? 0 : 20;   // 0: whole K
+  if (N == 1) return 20;
   if (N == 2) return 12;
   if (N <= 4) return (fmt == INT8 || fmt == NVFP4) ? 12 : 20;
   return KS >= 64 ? (int)((KS + 4) / 5) : 20;   // long K at N > 4: five waves per workgroup
@@ -584,14 +673,10 @@ LaunchShape pick_shape(int fmt, int64_t KS, int64_t out_tiles, int N, bool swigl
   const int per = ksteps_per_wave(fmt, N, swiglu, one, KS);
   const int64_t to = swiglu ? ls.nt / 2 : ls.nt;     // output tiles per workgroup
   const int64_t wgs = (out_tiles + to - 1) / to;
-  const bool whole_k = per == 0;
-  int64_t target = whole_k ? KS : per;
   auto waves_for = [&](int64_t kpw) { return (KS + kpw - 1) / kpw; };
   auto round_cyc = [&](int64_t kpw) { return (kpw + cyc - 1) / cyc * cyc; };
-  int64_t kpw = round_cyc(target < 1 ? 1 : target);
-  if (!whole_k) {
-    while (kpw > cyc && wgs * waves_for(kpw) < kMinGridWaves) kpw = round_cyc(kpw - cyc > cyc ? kpw - cyc : cyc);
-  }
+  int64_t kpw = round_cyc(per);
+  while (kpw > cyc && wgs * waves_for(kpw) < kMinGridWaves) kpw = round_cyc(kpw - cyc > cyc ? kpw - cyc : cyc);
   while (waves_for(kpw) > kMaxWaves) kpw += cyc;
   if (norm) {
     // the RMSNorm prologue stages activations in LDS: keep the ring within budget
@@ -607,10 +692,76 @@ LaunchShape pick_shape(int fmt, int64_t KS, int64_t out_tiles, int N, bool swigl
 // (N = 1 and small N * K); larger ones use buffer loads.
 
 
+// Split remainder. With B row blocks on C compute units, B mod C blocks
+// would leave that many units with one workgroup more than the rest, and
+// the launch ends when those finish. The first floor(B / C) C blocks stay
+// whole; each remaining block's K range is cut into F = C / gcd(B mod C, C)
+// fragments, so every unit receives the same weight bytes. Taken when
+// B mod C <= C / 2 (a larger remainder already keeps most units busy to
+// the end, and the fragments' own cost won: measured on [7168][5120]),
+// F <= kMaxFrag, a fragment still gives each wave at least one scale cycle,
+// and every workgroup of the split grid is resident at once. The last fragment of a block adds the others' partial sums in
+// fragment order, so results are reproducible, but their bits differ from
+// the unsplit sum.
+constexpr int kMaxFrag = 8;
+constexpr int64_t kSplitHeader = 256;     // sticky error word, then padding
+
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev < 0 || dev >= 64) return 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 1) return 0;
+  cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+// flag words (64 bytes each) and partial-sum slots (NT <= 2 tiles of 8 x 16 floats)
+int64_t split_slots(int cus) { return (int64_t)(kMaxFrag - 1) * cus; }
+int64_t split_flag_bytes(int cus) { return (kSplitHeader + 64 * split_slots(cus) + 255) / 256 * 256; }
+int64_t split_bytes(int cus) { return split_flag_bytes(cus) + split_slots(cus) * 2 * 128 * 4; }
+
+void plan_split(int fmt, const LaunchShape& ls, bool swiglu, int64_t out_tiles, int64_t KS, int cus, GemvArgs& a) {
+  a.n_full = 0;
+  a.frag = 1;
+  if (cus < 1) return;
+  const int64_t to = swiglu ? ls.nt / 2 : ls.nt;
+  const int64_t blocks = (out_tiles + to - 1) / to;
+  const int64_t n_full = blocks / cus * cus, r = blocks - n_full;
+  if (r == 0 || 2 * r > cus) return;
+  const int64_t F = cus / std::gcd(r, (int64_t)cus);
+  if (F > kMaxFrag) return;
+  const int cyc = cycle_ksteps(fmt, ls.slots);
+  if ((KS + cyc - 1) / cyc / F < ls.waves) return;
+  a.n_full = (int)n_full;
+  a.frag = (int)F;
+}
+
+using KernelFn = void (*)(GemvArgs);
+
+// Workgroups of a kernel resident per compute unit (cached per device, kernel,
+// block size and LDS bytes); 0 if the runtime cannot say.
+int resident_per_cu(const void* fn, int threads, size_t lds) {
+  struct Entry { const void* fn; int threads; size_t lds; int dev; int n; };
+  static std::mutex mu;
+  static std::vector<Entry> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const Entry& e : cache)
+    if (e.fn == fn && e.threads == threads && e.lds == lds && e.dev == dev) return e.n;
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, threads, lds) != hipSuccess) n = 0;
+  cache.push_back(Entry{fn, threads, lds, dev, n});
+  return n;
+}
+
 template <int FMT, int NT, int S, int KPS>
 hipError_t launch_s(const GemvArgs& a0, const LaunchShape& ls, bool swiglu, hipStream_t stream) {
   const int TO = swiglu ? NT / 2 : NT;
-  const dim3 grid((unsigned)((a0.out_tiles + TO - 1) / TO));
+  const int64_t blocks = (a0.out_tiles + TO - 1) / TO;
   const dim3 block((unsigned)(64 * ls.waves));
   GemvArgs a = a0;
   const int U = 2 * KPS;   // k-steps per trip of the k-loop
@@ -625,19 +776,33 @@ hipError_t launch_s(const GemvArgs& a0, const LaunchShape& ls, bool swiglu, hipS
   }
   const size_t lds = red + (xm == XM_LDS ? whole : (xm == XM_RING ? ring : 0));
   const bool norm = a.nsrc != nullptr;
-#define QG_LAUNCH(SW, XMV, NRM) hipLaunchKernelGGL((k_gemv<FMT, NT, S, KPS, SW, XMV, NRM>), grid, block, lds, stream, a)
-  if constexpr (NT >= 2) {
-    if (swiglu) {
-      if (xm == XM_LDS) { if (norm) QG_LAUNCH(true, XM_LDS, true); else QG_LAUNCH(true, XM_LDS, false); }
-      else if (xm == XM_RING) { if (norm) QG_LAUNCH(true, XM_RING, true); else QG_LAUNCH(true, XM_RING, false); }
-      else QG_LAUNCH(true, XM_LOAD, false);
-      return hipGetLastError();
+  KernelFn fn = nullptr;
+#define QG_PICK(SW, XMV, NRM) fn = k_gemv<FMT, NT, S, KPS, SW, XMV, NRM>
+  if (NT >= 2 && swiglu) {
+    if constexpr (NT >= 2) {
+      if (xm == XM_LDS) { if (norm) QG_PICK(true, XM_LDS, true); else QG_PICK(true, XM_LDS, false); }
+      else if (xm == XM_RING) { if (norm) QG_PICK(true, XM_RING, true); else QG_PICK(true, XM_RING, false); }
+      else QG_PICK(true, XM_LOAD, false);
+    }
+  } else {
+    if (xm == XM_LDS) { if (norm) QG_PICK(false, XM_LDS, true); else QG_PICK(false, XM_LDS, false); }
+    else if (xm == XM_RING) { if (norm) QG_PICK(false, XM_RING, true); else QG_PICK(false, XM_RING, false); }
+    else QG_PICK(false, XM_LOAD, false);
+  }
+#undef QG_PICK
+  int64_t nwg = blocks;
+  if (a.frag > 1) {
+    // split only when every workgroup of the split grid is resident at once:
+    // in a second dispatch round the waiting workgroups hold the units idle
+    const int64_t g = a.n_full + (blocks - a.n_full) * a.frag;
+    if (g <= (int64_t)resident_per_cu(reinterpret_cast<const void*>(fn), (int)block.x, lds) * device_cus()) {
+      nwg = g;
+    } else {
+      a.frag = 1;
+      a.n_full = 0;
     }
   }
-  if (xm == XM_LDS) { if (norm) QG_LAUNCH(false, XM_LDS, true); else QG_LAUNCH(false, XM_LDS, false); }
-  else if (xm == XM_RING) { if (norm) QG_LAUNCH(false, XM_RING, true); else QG_LAUNCH(false, XM_RING, false); }
-  else QG_LAUNCH(false, XM_LOAD, false);
-#undef QG_LAUNCH
+  hipLaunchKernelGGL(fn, dim3((unsigned)nwg), block, lds, stream, a);
   return hipGetLastError();
 }
 
@@ -717,6 +882,19 @@ int run_gemv(int fmt, const void* wq, const void* ws, const void* x, const float
   if (fz && (fz->flags & ~QGEMV_BATCH_INVARIANT)) return QGEMV_EINVAL;
   const LaunchShape ls = pick_shape(fmt, g.KS, a.out_tiles, N, swiglu, norm, inv);
   a.ks_per_wave = ls.kpw;
+  a.n_full = 0;
+  a.frag = 1;
+  a.part = nullptr;
+  a.pflag = nullptr;
+  if (fz && fz->workspace) {
+    const int cus = device_cus();
+    if (cus < 1) return QGEMV_EHIP;
+    if (!aligned16(fz->workspace) || ((uintptr_t)fz->workspace & 255u)) return QGEMV_EALIGN;
+    if (fz->workspace_bytes < (size_t)split_bytes(cus)) return QGEMV_EWORKSPACE;
+    if (!norm && !inv) plan_split(fmt, ls, swiglu, a.out_tiles, g.KS, cus, a);
+    a.pflag = (uint32_t*)fz->workspace;
+    a.part = (float*)((uint8_t*)fz->workspace + split_flag_bytes(cus));
+  }
   hipError_t e;
   switch (fmt) {
     case INT4: e = launch_gemv<INT4>(a, ls, swiglu, stream); break;
@@ -758,6 +936,14 @@ extern "C" int qgemv_swiglu(int fmt, const void* wq, const void* ws, const void*
   if (I % 16) return QGEMV_EALIGN;
   if (!h) return QGEMV_EINVAL;
   return run_gemv(fmt, wq, ws, x, nullptr, h, I, 2 * I, K, N, true, nullptr, stream);
+}
+
+extern "C" int qgemv_split_workspace_bytes(size_t* bytes) {
+  if (!bytes) return QGEMV_EINVAL;
+  const int cus = device_cus();
+  if (cus < 1) return QGEMV_EHIP;
+  *bytes = (size_t)split_bytes(cus);
+  return QGEMV_OK;
 }
 
 extern "C" int qgemv_ex(int fmt, const void* wq, const void* ws, const void* x, const float* residual, float* y,

@@ -155,6 +155,22 @@ int qgemv_swiglu(int fmt, const void* wq, const void* ws, const void* x, float* 
  *               3: multi-token-prediction verify windows; RustingStrata page,
  *               known issues: reordered floating-point work diverges). Costs
  *               some speed at N < 8. Other bits: QGEMV_EINVAL.
+ *   workspace:  device memory of qgemv_split_workspace_bytes (256-byte
+ *               aligned, ZERO-FILLED BEFORE ITS FIRST USE) that lets the
+ *               launch balance its last row blocks: when the row blocks do not
+ *               divide evenly over the compute units, the leftover blocks'
+ *               K ranges are cut into fragments (at most 8) whose partial sums
+ *               meet in the workspace, added by the block's last fragment in
+ *               fragment order (the workgroups wait, bounded, only on
+ *               lower-numbered ones, which start first on every XCD). Results
+ *               stay reproducible from call to call but their bits differ
+ *               from a call without a workspace. Not used with norm_src or
+ *               QGEMV_BATCH_INVARIANT. Every call leaves the flags it used at
+ *               zero, so one fill serves later calls in stream order; calls
+ *               that may overlap in time need separate workspaces. The first
+ *               32-bit word is a sticky flag that becomes nonzero if a wait
+ *               ever timed out (that call's results are then invalid).
+ *               workspace_bytes: its size (QGEMV_EWORKSPACE if smaller).
  * Zero-initialise unused fields. */
 enum { QGEMV_BATCH_INVARIANT = 1 };
 typedef struct qgemv_fusion {
@@ -163,7 +179,13 @@ typedef struct qgemv_fusion {
   float norm_eps;
   uint16_t* out_bf16;
   int flags;
+  void* workspace;
+  size_t workspace_bytes;
 } qgemv_fusion;
+
+/* Bytes of the workspace above for the current device (it depends on the
+ * device's compute-unit count). */
+int qgemv_split_workspace_bytes(size_t* bytes);
 
 /* qgemv with the optional fusions above (fusion may be NULL). */
 int qgemv_ex(int fmt, const void* wq, const void* ws, const void* x, const float* residual, float* y,
@@ -240,8 +262,8 @@ int qgemv_moe_fused_workspace_bytes(int E, int64_t H, int64_t I, int N, int top_
  *   workspace is large enough). Calls that may overlap in time need separate
  *   workspaces. Byte offset 12 holds a sticky 32-bit flag that becomes
  *   nonzero if a dependency wait ever timed out (the results of that call are
- *   then invalid). The launch is cooperative: every workgroup is resident at
- *   once, which the dependency waits rely on.
+ *   then invalid). Workgroups wait only on lower-numbered ones, which start
+ *   first on every XCD, so the waits need no co-residency.
  * Other arguments and limits as qgemv_moe; 1 <= top_k <= min(E, 8). */
 int qgemv_moe_fused(int fmt, const void* wq_gu, const void* ws_gu, const void* wq_dn, const void* ws_dn,
                     int E, int64_t H, int64_t I, const void* x, const float* logits, int top_k,

@@ -64,7 +64,8 @@ def _run_ex(fmt, wq, ws, h, gamma, M, K, N, eps, residual=None, swiglu=False):
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
-@pytest.mark.parametrize("M,K,N", [(64, 512, 1), (37, 160, 3), (200, 1024, 8), (48, 4096, 2)])
+@pytest.mark.parametrize("M,K,N", [(64, 512, 1), (37, 160, 3), (200, 1024, 8), (48, 4096, 2), (40, 32768, 1),
+                                   (48, 32768, 2), (33, 32768, 3)])
 def test_norm_gemv_parity(fmt, M, K, N):
     log("norm gemv", fmt, M, K, N)
     W, _, wq, ws = make_case(fmt, M, K, N, seed=41)

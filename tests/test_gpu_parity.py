@@ -79,7 +79,9 @@ def test_dequant_dump_all_codes_and_scales(fmt):
 
 # ------------------------------------------------------------------- GEMV
 
-SHAPES = [(1024, 1024), (37, 160), (16, 32), (100, 5120), (64, 17408 // 4)]
+# (48, 32768): K long enough that every N stages its activations through the
+# four-record LDS ring (N < 4 leaves lanes past the record)
+SHAPES = [(1024, 1024), (37, 160), (16, 32), (100, 5120), (64, 17408 // 4), (48, 32768)]
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
@@ -297,9 +299,11 @@ def test_moe_index_bit_exact(N, k, E):
 
 # every launch shape the benchmark times: [17408][5120] (one tile per
 # workgroup) at N = 1, 2, 4, 8 in each format, the QKV shape (one tile from
-# N = 2, two at N = 1) and the down projection (two tiles)
+# N = 2, two at N = 1) and the down projection (two tiles; one for NVFP4 and
+# int8 at N = 2), whose long K stages activations through the LDS ring
 FULL = [("int4", 7168, 5120, 1), ("int4", 7168, 5120, 8), ("int4", 7168, 5120, 4), ("int5", 5120, 17408, 1),
-        ("int5", 5120, 17408, 8), ("nvfp4", 5120, 17408, 4), ("nvfp4", 7168, 5120, 2)] + \
+        ("int5", 5120, 17408, 8), ("nvfp4", 5120, 17408, 4), ("nvfp4", 7168, 5120, 2),
+        ("int4", 5120, 17408, 2), ("nvfp4", 5120, 17408, 2), ("int8", 5120, 17408, 2), ("int5", 5120, 17408, 3)] + \
        [(f, 17408, 5120, n) for f in ("int4", "int5", "int8", "nvfp4") for n in (1, 2, 4, 8)]
 
 
