@@ -12,6 +12,10 @@ definitions used here are the public ones:
     no infinities, only S.1111.111 is NaN, largest finite 448.
   * OCP FP4 E2M1: 1 sign, 2 exponent (bias 1), 1 mantissa bit, magnitudes
     {0, 0.5, 1, 1.5, 2, 3, 4, 6}; code 8 is negative zero.
+  * OCP E8M0 (the shared scale of the OCP microscaling (MX) formats, which the
+    Decapybara kernel list names for its MXFP8 GEMV and activation
+    quantiser): 8 exponent bits, bias 127, no sign and no mantissa, value
+    2^(bits - 127); 0xFF is NaN.
 
 Two independent implementations live here:
   * exact_* functions work on fractions.Fraction and round by the textbook
@@ -131,6 +135,15 @@ def exact_e4m3_value(bits: int):
     return -mag if s else mag
 
 
+def exact_e8m0_value(bits: int):
+    """E8M0 byte -> Fraction 2^(bits - 127), or float nan for 0xFF."""
+    if not 0 <= bits <= 0xFF:
+        raise ValueError("E8M0 is one byte")
+    if bits == 0xFF:
+        return math.nan
+    return Fraction(2) ** (bits - 127)
+
+
 def exact_e2m1_value(bits: int):
     s, e, m = (bits >> 3) & 1, (bits >> 1) & 0x3, bits & 0x1
     mag = Fraction(m, 2) if e == 0 else Fraction(2 + m) * Fraction(2) ** (e - 2)
@@ -193,6 +206,7 @@ def _f(v, negative: bool) -> float:
 
 E4M3_TABLE = np.array([_f(exact_e4m3_value(b), bool(b & 0x80)) for b in range(256)], dtype=np.float64)
 E2M1_TABLE = np.array([_f(exact_e2m1_value(b), bool(b & 0x8)) for b in range(16)], dtype=np.float64)
+E8M0_TABLE = np.array([_f(exact_e8m0_value(b), False) for b in range(256)], dtype=np.float64)
 # positive finite magnitudes in code order (codes 0..126 / 0..7 are increasing)
 _E4M3_POS = E4M3_TABLE[:127].copy()
 _E2M1_POS = E2M1_TABLE[:8].copy()
@@ -259,6 +273,22 @@ def e2m1_encode_sat(v: np.ndarray) -> np.ndarray:
     v = np.asarray(v, dtype=np.float64)
     mag = _nearest_even_code(np.abs(v), _E2M1_POS)
     return (mag | (np.signbit(v).astype(np.uint8) << np.uint8(3))).astype(np.uint8)
+
+
+def e4m3_encode_signed_sat(v: np.ndarray) -> np.ndarray:
+    """Values -> OCP E4M3 codes, nearest-even, saturating at +-448; the sign
+    bit follows the input's sign bit (a negative input that rounds to zero,
+    and -0, give code 0x80)."""
+    v = np.asarray(v, dtype=np.float64)
+    if np.any(np.isnan(v)):
+        raise ValueError("E4M3 element inputs must be numbers")
+    mag = _nearest_even_code(np.abs(v), _E4M3_POS)
+    return (mag | (np.signbit(v).astype(np.uint8) << np.uint8(7))).astype(np.uint8)
+
+
+def e8m0_decode(bits: np.ndarray) -> np.ndarray:
+    """E8M0 bytes -> float64 2^(bits - 127) (nan for 0xFF); exact."""
+    return E8M0_TABLE[np.asarray(bits, dtype=np.uint8)]
 
 
 def e4m3_decode(codes: np.ndarray) -> np.ndarray:

@@ -19,6 +19,13 @@ What the GPU path computes, written as plain definitions in fp64:
   * MoE routing index: the (token, slot) pairs grouped by expert, ordered by
     (expert, token, slot); counts, offsets, the ascending list of active
     experts and an error flag for ids outside [0, E).
+  * MX GEMV (Decapybara kernel list: an MXFP8 block-scaled GEMV fed by a
+    dynamic 32-element MXFP8 activation quantiser): the activations are
+    first quantised to MXFP8 (oracle.quant.mx_act_quant), then
+        y[n, m] = r[n, m] + sum_k xq[n, k] * W[m, k]
+    with xq the dequantised MXFP8 activations and W the dequantised MXFP8 or
+    MXFP4 weights (every product is exact in fp32, so the GEMV tolerance
+    below, which covers fp32 accumulation over K <= 2^17, applies as is).
   * Per-output tolerances for the fp32-accumulating GPU path:
         GEMV   T = 2e-3 * sum_k |x_k W_k| + 1e-5
         SwiGLU T_h = 1.1 (|u| + T_u) T_g + |silu(g)| T_u + 1e-6 |h| + 1e-5
@@ -41,6 +48,13 @@ ABS = 1e-5
 def x_from_bits(x_bits: np.ndarray) -> np.ndarray:
     """bf16 bit patterns [N][K] -> fp64 values."""
     return enc.f32_from_bf16_bits(x_bits).astype(np.float64)
+
+
+def mx_activations(x_bits: np.ndarray) -> np.ndarray:
+    """bf16 activations [N][K] -> their MXFP8 quantisation, dequantised (fp64)."""
+    from .quant import MX_BLOCK, mx_act_quant
+    codes, e = mx_act_quant(x_bits)
+    return enc.e4m3_decode(codes) * np.repeat(enc.e8m0_decode(e), MX_BLOCK, axis=1)
 
 
 def gemv(x: np.ndarray, W: np.ndarray, residual: np.ndarray | None = None) -> np.ndarray:

@@ -36,6 +36,16 @@ nvfp4  wq: tile = 1024 B; byte lam*16 + 4*j + (e >> 1), low nibble for even e,
        ws: tile = 128 B; byte r*8 + 4*h + j holds the E4M3 scale of the 16-block
            along K with index 8*ks + 2*j + h; after all tiles (offset
            RT*KS*128) the fp32 tensor scale, then 12 zero bytes.
+
+MX formats: the operand layout of gfx950's block-scaled 16x16x128 MFMA, so
+that each lane's load is its operand register as is (lane lam: row
+16*rt + lam % 16, g = lam // 16):
+mxfp8  wq: tile = 2048 B; byte h*1024 + lam*16 + i (h in {0, 1}, i < 16) holds
+           the E4M3 code of column 128*ks + 64*h + 16*g + i.
+mxfp4  wq: tile = 1024 B; byte lam*16 + i holds the E2M1 codes of columns
+           128*ks + 32*g + 2*i (low nibble) and + 2*i + 1 (high nibble).
+       ws (both): tile = 64 B; byte lam holds the E8M0 scale of the 32-block
+           along K with index 4*ks + g (padding bytes 0).
 """
 from __future__ import annotations
 
@@ -64,6 +74,10 @@ def packed_bytes(fmt: str, M: int, K: int) -> tuple[int, int]:
         return tiles * 2048, tiles * 128
     if fmt == "nvfp4":
         return tiles * 1024, tiles * 128 + 16
+    if fmt == "mxfp8":
+        return tiles * 2048, tiles * 64
+    if fmt == "mxfp4":
+        return tiles * 1024, tiles * 64
     raise ValueError(fmt)
 
 
@@ -190,6 +204,16 @@ def pack(qz: Quantized) -> tuple[np.ndarray, np.ndarray]:
         wq = t.astype(np.int8).reshape(-1).view(np.uint8).copy()
         d = _scales_tiled(_pad(qz.d, Mp, Kp // 32), RT, KS)
         ws = np.frombuffer(d.astype("<u2").tobytes(), dtype=np.uint8).copy()
+    elif fmt in ("mxfp8", "mxfp4"):
+        codes = _pad(qz.codes.astype(np.uint8), Mp, Kp)
+        if fmt == "mxfp8":
+            t = codes.reshape(RT, 16, KS, 2, 4, 16).transpose(0, 2, 3, 4, 1, 5)      # rt ks h g r i
+            wq = t.reshape(-1).copy()
+        else:
+            t = codes.reshape(RT, 16, KS, 4, 16, 2).transpose(0, 2, 3, 1, 4, 5)      # rt ks g r i pair
+            wq = ((t[..., 0] & np.uint8(0xF)) | ((t[..., 1] & np.uint8(0xF)) << np.uint8(4))).reshape(-1).copy()
+        e = _pad(qz.e.astype(np.uint8), Mp, Kp // 32)
+        ws = e.reshape(RT, 16, KS, 4).transpose(0, 2, 3, 1).reshape(-1).copy()         # rt ks g r
     else:
         raise ValueError(fmt)
     assert wq.size == wq_n and ws.size == ws_n, (wq.size, wq_n, ws.size, ws_n)
@@ -224,6 +248,15 @@ def unpack(fmt: str, M: int, K: int, wq: np.ndarray, ws: np.ndarray) -> Quantize
         d = (dm & np.uint32(0xFFFF)).astype(np.uint16)
         m = (dm >> np.uint32(16)).astype(np.uint16)
         return Quantized(fmt, M, K, codes.copy(), d=d, m=m)
+    if fmt in ("mxfp8", "mxfp4"):
+        if fmt == "mxfp8":
+            codes = wq.reshape(RT, KS, 2, 4, 16, 16).transpose(0, 4, 1, 2, 3, 5).reshape(Mp, Kp)
+        else:
+            b = wq.reshape(RT, KS, 4, 16, 16)                                        # rt ks g r i
+            t = np.stack([b & np.uint8(0xF), b >> np.uint8(4)], axis=-1)             # rt ks g r i pair
+            codes = t.transpose(0, 3, 1, 2, 4, 5).reshape(Mp, Kp)
+        e = ws.reshape(RT, KS, 4, 16).transpose(0, 3, 1, 2).reshape(Mp, Kp // 32)
+        return Quantized(fmt, M, K, codes[:M, :K].copy(), e=e[:M, : K // 32].copy())
     if fmt == "int8":
         t = wq.view(np.int8).reshape(RT, KS, 2, 64, 2, 8).transpose(0, 1, 3, 2, 4, 5)
         codes = _untile_codes(t.reshape(RT, KS, 64, 4, 8), RT, KS)[:M, :K]

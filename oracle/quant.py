@@ -16,6 +16,13 @@ listed with the design notes of the repository):
         (ties to even), q = 0 when d == 0;
   * symmetric int8, 32 per group: d = fp16(amax / 127) in fp32,
         q = clamp(rint(w / d), -127, 127) in fp64, q = 0 when d == 0;
+  * MXFP8 / MXFP4 (OCP microscaling; the Decapybara kernel list names an
+        MXFP8 block-scaled GEMV and a dynamic 32-element MXFP8 activation
+        quantiser): per 32 values along K one E8M0 scale 2^X with
+        X = floor(log2(amax)) - emax, emax = 8 (E4M3: 448 = 1.75 * 2^8) or
+        2 (E2M1: 6 = 1.5 * 2^2), clamped to [-127, 127], X = -127 when
+        amax == 0; elements = E4M3 / E2M1 of w / 2^X (exact in fp64),
+        nearest-even, saturating; the sign bit follows the input's;
   * NVFP4: tensor scale s_t = amax / (6 * 448) in fp32 (1 when that is 0),
         block scale (16 weights along K) b = E4M3(amax_b / (6 * s_t)) with the
         product and quotient in fp32, nearest-even, saturating;
@@ -28,6 +35,7 @@ each fp32 / fp64 operation by a correctly rounded step).
 """
 from __future__ import annotations
 
+import math
 from dataclasses import dataclass
 from fractions import Fraction
 
@@ -36,6 +44,8 @@ import numpy as np
 from . import encodings as enc
 
 GROUP = 32          # weights per scale group along K (int formats)
+MX_BLOCK = 32       # values per E8M0 scale along K (MX formats)
+MX_EMAX = {"mxfp8": 8, "mxfp4": 2}   # exponent of the element format's top binade
 NVFP4_BLOCK = 16    # weights per E4M3 block scale along K
 
 
@@ -53,6 +63,8 @@ class Quantized:
     m      uint16 [M][K/32] fp16 bits of the minimum (asymmetric formats)
     sb     uint8  [M][K/16] E4M3 block scales (nvfp4)
     st     float32 tensor scale (nvfp4)
+    e      uint8  [M][K/32] E8M0 block scales (mxfp8: codes are E4M3 bytes,
+           mxfp4: codes are E2M1 4-bit codes)
     """
     fmt: str
     M: int
@@ -62,6 +74,7 @@ class Quantized:
     m: np.ndarray | None = None
     sb: np.ndarray | None = None
     st: np.float32 | None = None
+    e: np.ndarray | None = None
 
 
 def _check(W: np.ndarray) -> tuple[int, int]:
@@ -130,7 +143,67 @@ def quantize(W: np.ndarray, fmt: str) -> Quantized:
         codes = enc.e2m1_encode_sat(np.where(sbv[..., None] == 0.0, 0.0, v))
         codes = np.where(sbv[..., None] == 0.0, np.uint8(0), codes).astype(np.uint8)
         return Quantized(fmt, M, K, codes.reshape(M, K), sb=sb, st=st)
+    if fmt in MX_EMAX:
+        codes, e = mx_quantize_blocks(W.reshape(M, K // MX_BLOCK, MX_BLOCK), fmt)
+        return Quantized(fmt, M, K, codes.reshape(M, K), e=e)
     raise ValueError(f"unknown format {fmt!r}")
+
+
+def mx_scale_exponent(amax: np.ndarray, emax: int) -> np.ndarray:
+    """X = floor(log2(amax)) - emax, clamped to [-127, 127]; -127 where
+    amax == 0. frexp gives amax = f * 2^p with f in [0.5, 1), exactly, so
+    floor(log2(amax)) = p - 1 for every positive finite amax."""
+    amax = np.asarray(amax, dtype=np.float64)
+    _, p = np.frexp(amax)
+    X = np.where(amax == 0.0, -127, (p - 1) - emax)
+    return np.clip(X, -127, 127).astype(np.int64)
+
+
+def mx_quantize_blocks(V: np.ndarray, fmt: str) -> tuple[np.ndarray, np.ndarray]:
+    """MX quantisation of blocks V[..., 32] (finite fp32 values): returns the
+    element codes [..., 32] (uint8) and the E8M0 scale bytes [...]."""
+    V = np.asarray(V)
+    if V.shape[-1] != MX_BLOCK:
+        raise ValueError("MX blocks hold 32 values")
+    amax = np.abs(V.astype(np.float64)).max(axis=-1)
+    X = mx_scale_exponent(amax, MX_EMAX[fmt])
+    v = V.astype(np.float64) / np.ldexp(1.0, X)[..., None]      # exact: a power of two
+    codes = enc.e4m3_encode_signed_sat(v) if fmt == "mxfp8" else enc.e2m1_encode_sat(v)
+    return codes.astype(np.uint8), (X + 127).astype(np.uint8)
+
+
+def mx_act_quant(x_bits: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Dynamic MXFP8 quantisation of bf16 activations [N][K] (bit patterns;
+    K a multiple of 32): E4M3 codes [N][K] and E8M0 scales [N][K/32], by the
+    MXFP8 rule above. The sign of a zero input is kept (-0 -> code 0x80)."""
+    x = enc.f32_from_bf16_bits(x_bits)
+    N, K = x.shape
+    if K % MX_BLOCK:
+        raise ValueError("K must be a multiple of 32")
+    if not np.all(np.isfinite(x)):
+        raise ValueError("activations must be finite")
+    codes, e = mx_quantize_blocks(x.reshape(N, K // MX_BLOCK, MX_BLOCK), "mxfp8")
+    return codes.reshape(N, K), e
+
+
+def mx_block_exact(ws: list, fmt: str) -> tuple[list[int], int]:
+    """One MX block in exact rational arithmetic: (element codes, E8M0 byte).
+    A negative input (or -0.0) gives a negative-signed code."""
+    vals = [Fraction(w) for w in ws]
+    amax = max(abs(v) for v in vals)
+    if amax == 0:
+        X = -127
+    else:
+        X = max(-127, min(127, enc._floor_log2(amax) - MX_EMAX[fmt]))
+    codes = []
+    for w, v in zip(ws, vals):
+        neg = v < 0 or (v == 0 and math.copysign(1.0, float(w)) < 0)
+        if fmt == "mxfp8":
+            c = enc.exact_e4m3_bits(enc.exact_round_e4m3_sat(abs(v) / Fraction(2) ** X)) | (0x80 if neg else 0)
+        else:
+            c = enc.exact_e2m1_bits(enc.exact_round_e2m1_sat(abs(v) / Fraction(2) ** X)) | (0x8 if neg else 0)
+        codes.append(c)
+    return codes, X + 127
 
 
 # ---------------------------------------------------------------------------
