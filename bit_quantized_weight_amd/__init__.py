@@ -16,7 +16,7 @@ import os
 
 import numpy as np
 
-FORMATS = {"int4": 1, "int5": 2, "int8": 3, "nvfp4": 4}
+FORMATS = {"int4": 1, "int5": 2, "int8": 3, "nvfp4": 4, "mxfp4": 5, "mxfp8": 6}
 STATUS = {0: "OK", -1: "EINVAL", -2: "EFORMAT", -3: "EALIGN", -4: "ERANGE", -5: "EWORKSPACE",
           -6: "EHIP", -7: "EUNSUPPORTED"}
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqgemv.so")
@@ -77,6 +77,8 @@ def load(require_torch: bool = True):
         "qgemv_moe_fused": (I32, [I32, P, P, P, P, I32, I64, I64, P, P, I32, P, P, I32, P, P, P, SZ, P]),
         "qgemv_dequant": (I32, [I32, P, P, I64, I64, P, P]),
         "qgemv_probe_read": (I32, [P, SZ, P, P]),
+        "qgemv_act_quant": (I32, [P, I32, I64, P, P, P]),
+        "qgemv_mx": (I32, [I32, P, P, P, P, P, P, I64, I64, I32, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -92,7 +94,7 @@ def symbols() -> list[str]:
             "qgemv_pack_codes", "qgemv", "qgemv_swiglu", "qgemv_ex", "qgemv_swiglu_ex", "qgemv_split_workspace_bytes",
             "qgemv_moe_workspace_bytes", "qgemv_moe",
             "qgemv_moe_index", "qgemv_moe_route", "qgemv_moe_fused_workspace_bytes", "qgemv_moe_fused",
-            "qgemv_dequant", "qgemv_probe_read"]
+            "qgemv_dequant", "qgemv_probe_read", "qgemv_act_quant", "qgemv_mx"]
 
 
 def strerror(status: int) -> str:
@@ -153,7 +155,7 @@ def pack_codes(fmt, codes: np.ndarray, scales: np.ndarray, mins: np.ndarray | No
                tensor_scale: float = 1.0) -> tuple[np.ndarray, np.ndarray]:
     f = _fmt(fmt)
     codes = np.ascontiguousarray(codes, dtype=np.int8 if f == 3 else np.uint8)
-    scales = np.ascontiguousarray(scales, dtype=np.uint8 if f == 4 else np.uint16)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8 if f in (4, 5, 6) else np.uint16)
     mins = None if mins is None else np.ascontiguousarray(mins, dtype=np.uint16)
     M, K = codes.shape
     nq, ns = packed_bytes(f, M, K)
@@ -260,6 +262,19 @@ def qgemv_moe_fused(fmt, wq_gu, ws_gu, wq_dn, ws_dn, E: int, H: int, I: int, x, 
 
 def qgemv_dequant(fmt, wq, ws, M: int, K: int, out, stream=None) -> None:
     _check(load().qgemv_dequant(_fmt(fmt), _ptr(wq), _ptr(ws), M, K, _ptr(out), _stream(stream)), "qgemv_dequant")
+
+
+def act_quant(x, codes, scales, N: int, K: int, stream=None) -> None:
+    """Dynamic MXFP8 quantisation of bf16 activations x [N][K] into codes
+    [N][K] (uint8) and E8M0 scales [N][K/32] (uint8), on the device."""
+    _check(load().qgemv_act_quant(_ptr(x), N, K, _ptr(codes), _ptr(scales), _stream(stream)), "qgemv_act_quant")
+
+
+def qgemv_mx(fmt, wq, ws, xq, xs, y, M: int, K: int, N: int, residual=None, stream=None) -> None:
+    """MX GEMV: MXFP8 / MXFP4 weights times MXFP8 activations (from
+    act_quant) on the block-scaled MFMA; y [N][M] fp32, N <= 16."""
+    _check(load().qgemv_mx(_fmt(fmt), _ptr(wq), _ptr(ws), _ptr(xq), _ptr(xs), _ptr(residual), _ptr(y), M, K, N,
+                           _stream(stream)), "qgemv_mx")
 
 
 def qgemv_probe_read(buf, nbytes: int, sink, stream=None) -> None:

@@ -23,7 +23,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libqgemv.so")
 
 ARCH = "gfx950"
-HIP_SOURCES = ["gemv.hip", "moe.hip"]
+HIP_SOURCES = ["gemv.hip", "moe.hip", "mx.hip"]
 # moe.hip: keep single-lane atomics as written (the atomic optimizer would
 # wave-aggregate the work-ticket claim and wait for its result at once,
 # instead of when the ticket is first needed)

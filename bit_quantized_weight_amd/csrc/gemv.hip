@@ -34,6 +34,7 @@
 #include "device.hpp"
 #include "kloop.hpp"
 #include "layout.hpp"
+#include "mx.hpp"
 #include "qgemv.h"
 
 namespace qg {
@@ -960,11 +961,12 @@ extern "C" int qgemv_swiglu_ex(int fmt, const void* wq, const void* ws, const vo
 
 extern "C" int qgemv_dequant(int fmt, const void* wq, const void* ws, int64_t M, int64_t K, float* w_out,
                              hipStream_t stream) {
-  if (fmt < INT4 || fmt > NVFP4) return QGEMV_EFORMAT;
+  if (fmt < INT4 || fmt > MXFP8) return QGEMV_EFORMAT;
   if (!wq || !ws || !w_out) return QGEMV_EINVAL;
   if (M < 1 || K < 32) return QGEMV_EINVAL;
   if (K % 32) return QGEMV_EALIGN;
   if (!aligned16(wq) || !aligned16(ws) || !aligned4(w_out)) return QGEMV_EALIGN;
+  if (fmt == MXFP4 || fmt == MXFP8) return mx_dequant(fmt, wq, ws, M, K, w_out, stream);
   Geom g;
   if (!geom(fmt, M, K, &g)) return QGEMV_EINVAL;
   if (g.wq_bytes >= (1ull << 32) || g.ws_bytes >= (1ull << 32)) return QGEMV_EUNSUPPORTED;

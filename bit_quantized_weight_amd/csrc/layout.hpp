@@ -23,13 +23,23 @@
 //   nvfp4 wq tile 1024 B: byte lam*16 + 4*j + e/2, low nibble even e.
 //         ws tile 128 B: E4M3 of 16-block 8*ks + 2*j + h at r*8 + 4*h + j;
 //         then the fp32 tensor scale at RT*KS*128, padded to 16 B.
+//
+// MX formats take the register layout of gfx950's block-scaled 16x16x128
+// MFMA instead (lane lam: row 16*rt + lam % 16, g = lam / 16), so each lane's
+// loads are its B operand as is:
+//   mxfp8 wq tile 2048 B: byte h*1024 + lam*16 + i = E4M3 code of column
+//         128*ks + 64*h + 16*g + i (h < 2, i < 16).
+//   mxfp4 wq tile 1024 B: byte lam*16 + i = E2M1 codes of columns
+//         128*ks + 32*g + 2*i (low nibble) and 2*i + 1 (high nibble).
+//   ws (both) tile 64 B: byte lam = E8M0 scale of row 16*rt + lam % 16,
+//         32-block 4*ks + g.
 #pragma once
 #include <stdint.h>
 #include <stddef.h>
 
 namespace qg {
 
-enum Fmt : int { INT4 = 1, INT5 = 2, INT8 = 3, NVFP4 = 4 };
+enum Fmt : int { INT4 = 1, INT5 = 2, INT8 = 3, NVFP4 = 4, MXFP4 = 5, MXFP8 = 6 };
 
 struct Geom {
   int64_t M, K, Mp, Kp, RT, KS;
@@ -54,6 +64,8 @@ inline bool geom(int fmt, int64_t M, int64_t K, Geom* g) {
     case INT5: g->wq_bytes = tiles * 1280; g->ws_bytes = tiles * 256; g->hi_offset = tiles * 1024; break;
     case INT8: g->wq_bytes = tiles * 2048; g->ws_bytes = tiles * 128; break;
     case NVFP4: g->wq_bytes = tiles * 1024; g->ws_bytes = tiles * 128 + 16; g->st_offset = tiles * 128; break;
+    case MXFP4: g->wq_bytes = tiles * 1024; g->ws_bytes = tiles * 64; break;
+    case MXFP8: g->wq_bytes = tiles * 2048; g->ws_bytes = tiles * 64; break;
     default: return false;
   }
   return true;

@@ -1,0 +1,381 @@
+// MX (microscaling) path on gfx950: MXFP8 / MXFP4 weights times MXFP8
+// activations on the block-scaled MFMA, and the dynamic activation quantiser
+// that feeds it (Decapybara page, kernel list: an MXFP8 block-scaled GEMV
+// and a dynamic 32-element MXFP8 activation quantiser). Format: the public
+// OCP microscaling definitions (one E8M0 scale per 32 values along K).
+//
+// v_mfma_scale_f32_16x16x128_f8f6f4 multiplies a 16x128 A by a 128x16 B
+// whose elements are FP8 / FP4 codes, each 32-block along K scaled by an E8M0
+// byte, and accumulates in fp32. Operand registers (measured on MI355X):
+//   FP8 operand, lane l (row l % 16, g = l / 16): bytes 0..15 hold K 16g..16g+15,
+//     bytes 16..31 hold K 64+16g..64+16g+15;
+//   FP4 operand, lane l: 16 bytes hold K 32g..32g+31, low nibble first;
+//   scale register of lane l: the E8M0 byte of (row l % 16, 32-block g).
+// A = activations (rows = tokens, N <= 16), B = weights (16 rows per tile),
+// so one MFMA per tile and k-step covers every token: there is no decode.
+// The weight layout (layout.hpp) stores each lane's operand bytes
+// contiguously; activation codes stay row-major [N][K], whose 16-byte runs
+// are the A operand's halves as they are.
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "device.hpp"
+#include "layout.hpp"
+#include "mx.hpp"
+#include "qgemv.h"
+
+namespace qg {
+
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+
+__device__ __forceinline__ uint32_t ld8s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);
+}
+
+// ---- MXFP8 quantisation (OCP microscaling) --------------------------------
+// E4M3 code of an fp32 value: nearest, ties to even, saturating at 448, sign
+// bit kept (NaN stays NaN). Every step below is exact except the one rintf.
+__device__ __forceinline__ uint32_t e4m3_rne_sat(float t) {
+  const uint32_t sign = (__float_as_uint(t) >> 24) & 0x80u;
+  const float a = fabsf(t);
+  uint32_t code;
+  if (a != a) {
+    code = 0x7Fu;
+  } else if (a >= 448.0f) {
+    code = 0x7Eu;
+  } else if (a < 0.015625f) {                  // below 2^-6: subnormal steps of 2^-9
+    code = (uint32_t)rintf(a * 512.0f);        // 8 rounds up to the least normal, code 8
+  } else {
+    const int e = (int)(__float_as_uint(a) >> 23) - 127;                  // floor(log2 a), -6..8
+    const float f = a * __uint_as_float((uint32_t)(127 - e) << 23);       // in [1, 2)
+    code = (uint32_t)(((e + 7) << 3) + (int)rintf((f - 1.0f) * 8.0f));    // carries into e + 1
+    code = min(code, 0x7Eu);
+  }
+  return sign | code;
+}
+
+// One MX block of 32 bf16 values (64 bytes in x): E4M3 codes into c (byte e
+// of the block in byte e % 4 of dword e / 4) and the E8M0 byte returned.
+// amax from the bf16 magnitudes as integers (their order is the values'),
+// X = floor(log2 amax) - 8 clamped to [-127, 127]; a bf16 subnormal amax has
+// floor(log2) < -126, so it clamps too. Scaling by 2^-X is exact.
+__device__ __forceinline__ uint32_t mx_quant_block(const u32x4 (&x)[4], uint32_t (&c)[8]) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t v = x[q][w];
+      m = max(m, max(v & 0x7FFFu, (v >> 16) & 0x7FFFu));
+    }
+  int X = (int)(m >> 7) - 127 - 8;
+  X = m == 0 ? -127 : max(-127, min(127, X));
+  const float s = __uint_as_float((uint32_t)(127 - X) << 23);   // 2^-X, X <= 120 here
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t v = x[q][w];
+      const uint32_t lo = e4m3_rne_sat(__uint_as_float(v << 16) * s);
+      const uint32_t hi = e4m3_rne_sat(__uint_as_float(v & 0xFFFF0000u) * s);
+      const int e = 8 * q + 2 * w;                                  // element index of lo
+      const uint32_t pair = lo | (hi << 8);
+      if ((e & 3) == 0) c[e >> 2] = pair;
+      else c[e >> 2] |= pair << 16;
+    }
+  return (uint32_t)(X + 127);
+}
+
+// One thread per (token, 32-block).
+__global__ __launch_bounds__(256) void k_act_quant(const uint16_t* x, int64_t nblk, uint8_t* codes, uint8_t* scales) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= nblk) return;
+  const u32x4* src = reinterpret_cast<const u32x4*>(x + i * 32);
+  u32x4 v[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) v[q] = src[q];
+  uint32_t c[8];
+  const uint32_t e = mx_quant_block(v, c);
+  u32x4* dst = reinterpret_cast<u32x4*>(codes + i * 32);
+  dst[0] = u32x4{c[0], c[1], c[2], c[3]};
+  dst[1] = u32x4{c[4], c[5], c[6], c[7]};
+  scales[i] = (uint8_t)e;
+}
+
+// ---- the block-scaled GEMV -------------------------------------------------
+struct MxArgs {
+  const uint8_t* wq;
+  const uint8_t* ws;
+  const uint8_t* xq;      // [N][K] E4M3 codes
+  const uint8_t* xs;      // [N][K/32] E8M0
+  const float* res;       // [N][M] or null (may alias y)
+  float* y;               // [N][M]
+  uint32_t wq_bytes, ws_bytes, xq_bytes, xs_bytes;
+  int M, K, KS, G, N, out_tiles, ks_per_wave;
+};
+
+// operands of one k-step: activations (shared by the tiles) and NT weight tiles
+template <int FMT, int NT>
+struct MxStep {
+  u32x4 a0, a1;
+  uint32_t sa;
+  u32x4 b0[NT], b1[NT];
+  uint32_t sb[NT];
+};
+
+template <int FMT, int NT>
+__device__ __forceinline__ void mx_load(MxStep<FMT, NT>& st, const MxArgs& a, __amdgpu_buffer_rsrc_t wq,
+                                        __amdgpu_buffer_rsrc_t ws, __amdgpu_buffer_rsrc_t xq,
+                                        __amdgpu_buffer_rsrc_t xs, const int (&tile)[NT], int k, int ks1,
+                                        uint32_t xrow, uint32_t srow, int lane) {
+  const int g = lane >> 4;
+  const bool ok = k < ks1;
+  const int col = k * 128 + 16 * g;
+  // activations: K tail chunks and k-steps past the range read as zeros
+  // (absent tokens have bases of 2^31 or more; OR-ing the mask keeps them there)
+  st.a0 = ld128s(xq, (xrow + (uint32_t)(16 * g)) | ((ok && col < a.K) ? 0u : kOOB), (uint32_t)k * 128u);
+  st.a1 = ld128s(xq, (xrow + (uint32_t)(64 + 16 * g)) | ((ok && col + 64 < a.K) ? 0u : kOOB), (uint32_t)k * 128u);
+  st.sa = ld8s(xs, (srow + (uint32_t)g) | ((ok && 4 * k + g < a.G) ? 0u : kOOB), (uint32_t)k * 4u);
+  const uint32_t bad = ok ? 0u : kOOB;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const uint32_t tau = (uint32_t)tile[t] * (uint32_t)a.KS + (uint32_t)k;
+    if constexpr (FMT == MXFP8) {
+      st.b0[t] = ld128s_nt(wq, (uint32_t)lane * 16u | bad, tau * 2048u);
+      st.b1[t] = ld128s_nt(wq, (1024u + (uint32_t)lane * 16u) | bad, tau * 2048u);
+    } else {
+      st.b0[t] = ld128s_nt(wq, (uint32_t)lane * 16u | bad, tau * 1024u);
+      st.b1[t] = u32x4{0u, 0u, 0u, 0u};
+    }
+    st.sb[t] = ld8s(ws, (uint32_t)lane | bad, tau * 64u);
+  }
+}
+
+__device__ __forceinline__ i32x8 join8(const u32x4& lo, const u32x4& hi) {
+  return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
+template <int FMT, int NT>
+__device__ __forceinline__ void mx_mma(f32x4 (&acc)[NT], const MxStep<FMT, NT>& st) {
+  const i32x8 A = join8(st.a0, st.a1);
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const i32x8 B = join8(st.b0[t], st.b1[t]);
+    // A: FP8 E4M3 (format 0); B: FP8 E4M3 (0) or FP4 E2M1 (4)
+    acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, acc[t], 0, FMT == MXFP8 ? 0 : 4, 0,
+                                                              (int)st.sa, 0, (int)st.sb[t]);
+  }
+}
+
+// Workgroup = NT row tiles; its W waves split the k-steps; the waves'
+// partial sums meet in LDS and are added in wave order (reproducible).
+template <int FMT, int NT>
+__global__ __launch_bounds__(512) void k_mxgemv(MxArgs a) {
+  extern __shared__ __attribute__((aligned(16))) float red[];   // [W][NT][64 lanes][4]
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int W = blockDim.x >> 6;
+  const int r = lane & 15;
+  const __amdgpu_buffer_rsrc_t wq = make_rsrc(a.wq, a.wq_bytes);
+  const __amdgpu_buffer_rsrc_t ws = make_rsrc(a.ws, a.ws_bytes);
+  const __amdgpu_buffer_rsrc_t xq = make_rsrc(a.xq, a.xq_bytes);
+  const __amdgpu_buffer_rsrc_t xs = make_rsrc(a.xs, a.xs_bytes);
+  int tile[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) tile[t] = min((int)blockIdx.x * NT + t, a.out_tiles - 1);
+  // A row r = token r: rows past N start out of range
+  const uint32_t xrow = r < a.N ? (uint32_t)(r * a.K) : kOOB;
+  const uint32_t srow = r < a.N ? (uint32_t)(r * a.G) : kOOB;
+  f32x4 acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int ks0 = wave * a.ks_per_wave;
+  const int ks1 = min(a.KS, ks0 + a.ks_per_wave);
+  if (ks0 < ks1) {
+    // software pipeline: two k-steps in flight while one is multiplied
+    MxStep<FMT, NT> s0, s1, s2;
+    mx_load<FMT, NT>(s0, a, wq, ws, xq, xs, tile, ks0, ks1, xrow, srow, lane);
+    mx_load<FMT, NT>(s1, a, wq, ws, xq, xs, tile, ks0 + 1, ks1, xrow, srow, lane);
+    for (int k = ks0; k < ks1; k += 3) {
+      mx_load<FMT, NT>(s2, a, wq, ws, xq, xs, tile, k + 2, ks1, xrow, srow, lane);
+      mx_mma<FMT, NT>(acc, s0);
+      if (k + 1 >= ks1) break;
+      mx_load<FMT, NT>(s0, a, wq, ws, xq, xs, tile, k + 3, ks1, xrow, srow, lane);
+      mx_mma<FMT, NT>(acc, s1);
+      if (k + 2 >= ks1) break;
+      mx_load<FMT, NT>(s1, a, wq, ws, xq, xs, tile, k + 4, ks1, xrow, srow, lane);
+      mx_mma<FMT, NT>(acc, s2);
+    }
+  }
+  // lane l holds D[token 4 (l / 16) + i][row l % 16]
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+    *reinterpret_cast<f32x4*>(red + ((size_t)(wave * NT + t) * 64 + lane) * 4) = acc[t];
+  __syncthreads();
+  for (int o = threadIdx.x; o < NT * 256; o += blockDim.x) {
+    const int t = o >> 8, tok = (o >> 4) & 15, row = o & 15;
+    const int ot = (int)blockIdx.x * NT + t;
+    const int col = ot * 16 + row;
+    if (tok >= a.N || ot >= a.out_tiles || col >= a.M) continue;
+    const int idx = ((tok >> 2) * 16 + row) * 4 + (tok & 3);
+    float v = 0.f;
+    for (int w = 0; w < W; ++w) v += red[(size_t)(w * NT + t) * 256 + idx];
+    const size_t at = (size_t)tok * a.M + col;
+    if (a.res) v += a.res[at];
+    a.y[at] = v;
+  }
+}
+
+// ---- dequantisation dump ----------------------------------------------------
+// One thread per (tile, k-step, lane): its 32 codes (MXFP8: two 16-code runs).
+template <int FMT>
+__global__ __launch_bounds__(256) void k_mx_dequant(const uint8_t* wqp, const uint8_t* wsp, int M, int K, int KS,
+                                                    int RT, float* out) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (int64_t)RT * KS * 64) return;
+  const int lane = (int)(gid & 63);
+  const int64_t tau = gid >> 6;
+  const int rt = (int)(tau / KS), ks = (int)(tau % KS);
+  const int r = lane & 15, g = lane >> 4;
+  const int row = rt * 16 + r;
+  if (row >= M) return;
+  const uint8_t* sc = wsp + tau * 64;
+  for (int e = 0; e < 32; ++e) {
+    int k;
+    uint32_t code;
+    if constexpr (FMT == MXFP8) {
+      const int h = e >> 4, i = e & 15;
+      k = 64 * h + 16 * g + i;
+      code = wqp[tau * 2048 + h * 1024 + lane * 16 + i];
+    } else {
+      k = 32 * g + e;
+      code = (wqp[tau * 1024 + lane * 16 + (e >> 1)] >> (4 * (e & 1))) & 15u;
+    }
+    const int kk = ks * 128 + k;
+    if (kk >= K) continue;
+    const int eb = sc[(k >> 5) * 16 + r];
+    float v;
+    if constexpr (FMT == MXFP8) {
+      const int ex = (code >> 3) & 15, m = code & 7;
+      v = ex ? ldexpf((float)(8 + m), ex - 10) : ldexpf((float)m, -9);
+      if ((code & 0x7F) == 0x7F) v = __builtin_nanf("");
+      if (code & 0x80) v = -v;
+    } else {
+      const float tab[8] = {0.f, 0.5f, 1.f, 1.5f, 2.f, 3.f, 4.f, 6.f};
+      v = tab[code & 7];
+      if (code & 8) v = -v;
+    }
+    out[(int64_t)row * K + kk] = eb == 255 ? __builtin_nanf("") : ldexpf(v, eb - 127);
+  }
+}
+
+}  // namespace qg
+
+// ============================================================================
+// Host side
+// ============================================================================
+using namespace qg;
+
+namespace {
+
+inline bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline bool al4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+struct MxShape {
+  int nt, waves, kpw;
+};
+
+// Tiles per workgroup and k-steps per wave: one tile per workgroup once the
+// matrix has >= 512 tiles (more, smaller workgroups spread over the 256
+// compute units), 16 k-steps per wave, fewer while the grid holds under ~900
+// waves, at most 8 waves.
+MxShape mx_shape(int64_t out_tiles, int64_t KS) {
+  MxShape s;
+  s.nt = out_tiles >= 512 ? 1 : 2;
+  const int64_t wgs = (out_tiles + s.nt - 1) / s.nt;
+  int64_t kpw = 16;
+  while (kpw > 1 && wgs * ((KS + kpw - 1) / kpw) < 900) --kpw;
+  while ((KS + kpw - 1) / kpw > 8) ++kpw;
+  s.waves = (int)((KS + kpw - 1) / kpw);
+  s.kpw = (int)kpw;
+  return s;
+}
+
+template <int FMT, int NT>
+hipError_t launch_mx(const MxArgs& a, const MxShape& s, hipStream_t stream) {
+  const dim3 grid((unsigned)((a.out_tiles + NT - 1) / NT));
+  const dim3 block((unsigned)(64 * s.waves));
+  const size_t lds = (size_t)s.waves * NT * 256 * sizeof(float);
+  hipLaunchKernelGGL((k_mxgemv<FMT, NT>), grid, block, lds, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int qg::mx_dequant(int fmt, const void* wq, const void* ws, int64_t M, int64_t K, float* w_out, hipStream_t stream) {
+  Geom g;
+  if (!geom(fmt, M, K, &g)) return QGEMV_EINVAL;
+  if (g.wq_bytes >= (1ull << 31) || (uint64_t)M * (uint64_t)K >= (1ull << 40)) return QGEMV_EUNSUPPORTED;
+  const int64_t threads = g.RT * g.KS * 64;
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  if (fmt == MXFP8)
+    hipLaunchKernelGGL((k_mx_dequant<MXFP8>), grid, dim3(256), 0, stream, (const uint8_t*)wq, (const uint8_t*)ws,
+                       (int)M, (int)K, (int)g.KS, (int)g.RT, w_out);
+  else
+    hipLaunchKernelGGL((k_mx_dequant<MXFP4>), grid, dim3(256), 0, stream, (const uint8_t*)wq, (const uint8_t*)ws,
+                       (int)M, (int)K, (int)g.KS, (int)g.RT, w_out);
+  return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
+}
+
+extern "C" int qgemv_act_quant(const void* x, int N, int64_t K, uint8_t* codes, uint8_t* scales,
+                               hipStream_t stream) {
+  if (!x || !codes || !scales) return QGEMV_EINVAL;
+  if (N < 1 || K < 32) return QGEMV_EINVAL;
+  if (K % 32) return QGEMV_EALIGN;
+  if (!al16(x) || !al16(codes)) return QGEMV_EALIGN;
+  if ((uint64_t)N * (uint64_t)K * 2ull >= (1ull << 40)) return QGEMV_EUNSUPPORTED;
+  const int64_t nblk = (int64_t)N * (K / 32);
+  const dim3 grid((unsigned)((nblk + 255) / 256));
+  hipLaunchKernelGGL(k_act_quant, grid, dim3(256), 0, stream, (const uint16_t*)x, nblk, codes, scales);
+  return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
+}
+
+extern "C" int qgemv_mx(int fmt, const void* wq, const void* ws, const uint8_t* xq, const uint8_t* xs,
+                        const float* residual, float* y, int64_t M, int64_t K, int N, hipStream_t stream) {
+  if (fmt != MXFP8 && fmt != MXFP4) return QGEMV_EFORMAT;
+  if (!wq || !ws || !xq || !xs || !y) return QGEMV_EINVAL;
+  if (M < 1 || K < 32 || M > (1 << 24)) return QGEMV_EINVAL;
+  if (K % 32) return QGEMV_EALIGN;
+  if (N < 1 || N > 16) return QGEMV_EUNSUPPORTED;
+  if (!al16(wq) || !al16(ws) || !al16(xq) || !al4(y) || (residual && !al4(residual))) return QGEMV_EALIGN;
+  Geom g;
+  if (!geom(fmt, M, K, &g)) return QGEMV_EINVAL;
+  // k-steps past a wave's range are loaded with an out-of-range lane offset
+  // (2^31 or more) on top of a tile offset up to 4 k-steps past the matrix:
+  // the sum must stay below 2^32
+  if (g.wq_bytes + 16384 >= (1ull << 31) || g.ws_bytes + 16384 >= (1ull << 31)) return QGEMV_EUNSUPPORTED;
+  if ((uint64_t)N * (uint64_t)K >= (1ull << 30)) return QGEMV_EUNSUPPORTED;
+  MxArgs a;
+  a.wq = (const uint8_t*)wq;
+  a.ws = (const uint8_t*)ws;
+  a.xq = xq;
+  a.xs = xs;
+  a.res = residual;
+  a.y = y;
+  a.wq_bytes = (uint32_t)g.wq_bytes;
+  a.ws_bytes = (uint32_t)g.ws_bytes;
+  a.xq_bytes = (uint32_t)((int64_t)N * K);
+  a.xs_bytes = (uint32_t)((int64_t)N * (K / 32));
+  a.M = (int)M;
+  a.K = (int)K;
+  a.KS = (int)g.KS;
+  a.G = (int)(K / 32);
+  a.N = N;
+  a.out_tiles = (int)((M + 15) / 16);
+  const MxShape s = mx_shape(a.out_tiles, g.KS);
+  a.ks_per_wave = s.kpw;
+  hipError_t e;
+  if (fmt == MXFP8) e = s.nt == 1 ? launch_mx<MXFP8, 1>(a, s, stream) : launch_mx<MXFP8, 2>(a, s, stream);
+  else e = s.nt == 1 ? launch_mx<MXFP4, 1>(a, s, stream) : launch_mx<MXFP4, 2>(a, s, stream);
+  return e == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
+}

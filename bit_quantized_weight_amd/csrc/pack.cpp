@@ -87,6 +87,33 @@ uint8_t e4m3_from_f32(float f) {
   return (uint8_t)code;
 }
 
+// E4M3 code for a double, nearest-even, saturating at +-448; sign bit = sign of v.
+uint8_t e4m3_from_f64_signed(double v) {
+  const uint8_t sign = signbit(v) ? 0x80 : 0;
+  const double a = fabs(v);
+  uint8_t mag;
+  if (a >= 448.0) {
+    mag = 0x7E;
+  } else if (a < 0.015625) {               // subnormal steps of 2^-9 (8 -> least normal, code 8)
+    mag = (uint8_t)nearbyint(a * 512.0);
+  } else {
+    int e;
+    const double fr = frexp(a, &e);        // a = fr * 2^e, fr in [0.5, 1)
+    const int n = (int)nearbyint((fr * 2.0 - 1.0) * 8.0);
+    mag = (uint8_t)std::min(0x7E, ((e - 1 + 7) << 3) + n);
+  }
+  return (uint8_t)(mag | sign);
+}
+
+// MX block scale exponent: floor(log2(amax)) - emax clamped to [-127, 127];
+// -127 for an all-zero block.
+int mx_exponent(double amax, int emax) {
+  if (amax == 0.0) return -127;
+  int p;
+  frexp(amax, &p);                          // amax = f * 2^p, f in [0.5, 1)
+  return std::max(-127, std::min(127, p - 1 - emax));
+}
+
 // E2M1 code for a double, nearest-even, saturating at +-6; sign bit = sign of v.
 uint8_t e2m1_from_f64(double v) {
   const uint8_t sign = signbit(v) ? 8 : 0;
@@ -113,6 +140,18 @@ struct Dest {
     const int64_t tau = rt * g->KS + ks, lane = s * 16 + r;
     if (fmt == qg::INT8) {
       wq[tau * 2048 + (j >> 1) * 1024 + lane * 16 + (j & 1) * 8 + e] = (uint8_t)(int8_t)c;
+      return;
+    }
+    if (fmt == qg::MXFP8 || fmt == qg::MXFP4) {
+      const int64_t kk = k & 127;
+      if (fmt == qg::MXFP8) {
+        const int64_t h = kk >> 6, gg = (kk >> 4) & 3, i = kk & 15;
+        wq[tau * 2048 + h * 1024 + (gg * 16 + r) * 16 + i] = (uint8_t)c;
+      } else {
+        const int64_t gg = kk >> 5, i = (kk & 31) >> 1, sh = 4 * (kk & 1);
+        uint8_t* p = wq + tau * 1024 + (gg * 16 + r) * 16 + i;
+        *p = (uint8_t)(*p | ((c & 15) << sh));
+      }
       return;
     }
     if (fmt == qg::INT5) {  // 5-bit fields, three pairs per dword; pair 15 spread over bit 15/31
@@ -165,6 +204,11 @@ struct Dest {
     ws[(rt * g->KS + ks) * 128 + r * 8 + 4 * h + j] = sb;
   }
   inline void tensor_scale(float st) const { memcpy(ws + g->st_offset, &st, 4); }
+  // MX E8M0 scale of 32-block bi along K
+  inline void mx_scale(int64_t m, int64_t bi, uint8_t e) const {
+    const int64_t rt = m >> 4, r = m & 15, ks = bi >> 2, gg = bi & 3;
+    ws[(rt * g->KS + ks) * 64 + gg * 16 + r] = e;
+  }
 };
 
 // Runs f(row_begin, row_end) over row ranges aligned to 16 on a few threads.
@@ -212,6 +256,25 @@ int quantize_rows(const Dest& D, const float* W, int64_t M, int64_t K) {
             const double w = (double)(row[b * 16 + i] + 0.0f);
             const uint8_t c = sbv == 0.0 ? 0 : e2m1_from_f64(w / (sbv * (double)st));
             D.code(m, b * 16 + i, c);
+          }
+        }
+      }
+    });
+    return QGEMV_OK;
+  }
+  if (fmt == qg::MXFP8 || fmt == qg::MXFP4) {
+    const int emax = fmt == qg::MXFP8 ? 8 : 2;
+    parallel_rows(M, [&](int64_t m0, int64_t m1) {
+      for (int64_t m = m0; m < m1; ++m) {
+        const float* row = W + m * K;
+        for (int64_t b = 0; b < K / 32; ++b) {
+          double amax = 0.0;
+          for (int i = 0; i < 32; ++i) amax = std::max(amax, (double)fabsf(row[b * 32 + i]));
+          const int X = mx_exponent(amax, emax);
+          D.mx_scale(m, b, (uint8_t)(X + 127));
+          for (int i = 0; i < 32; ++i) {
+            const double t = ldexp((double)(row[b * 32 + i] + 0.0f), -X);   // exact
+            D.code(m, b * 32 + i, fmt == qg::MXFP8 ? e4m3_from_f64_signed(t) : e2m1_from_f64(t));
           }
         }
       }
@@ -268,7 +331,7 @@ int quantize_rows(const Dest& D, const float* W, int64_t M, int64_t K) {
 }  // namespace
 
 extern "C" int qgemv_packed_bytes(int fmt, int64_t M, int64_t K, size_t* wq_bytes, size_t* ws_bytes) {
-  if (fmt < qg::INT4 || fmt > qg::NVFP4) return QGEMV_EFORMAT;
+  if (fmt < qg::INT4 || fmt > qg::MXFP8) return QGEMV_EFORMAT;
   if (!wq_bytes || !ws_bytes) return QGEMV_EINVAL;
   Geom g;
   if (!qg::geom(fmt, M, K, &g)) return QGEMV_EINVAL;
@@ -288,7 +351,7 @@ extern "C" int qgemv_expert_stride(int fmt, int64_t M, int64_t K, size_t* wq_str
 }
 
 extern "C" int qgemv_pack(int fmt, const float* W, int64_t M, int64_t K, void* wq, void* ws) {
-  if (fmt < qg::INT4 || fmt > qg::NVFP4) return QGEMV_EFORMAT;
+  if (fmt < qg::INT4 || fmt > qg::MXFP8) return QGEMV_EFORMAT;
   if (!W || !wq || !ws) return QGEMV_EINVAL;
   Geom g;
   if (!qg::geom(fmt, M, K, &g)) return QGEMV_EINVAL;
@@ -302,16 +365,22 @@ extern "C" int qgemv_pack(int fmt, const float* W, int64_t M, int64_t K, void* w
 
 extern "C" int qgemv_pack_codes(int fmt, const void* codes, const void* scales, const uint16_t* mins,
                                 float tensor_scale, int64_t M, int64_t K, void* wq, void* ws) {
-  if (fmt < qg::INT4 || fmt > qg::NVFP4) return QGEMV_EFORMAT;
+  if (fmt < qg::INT4 || fmt > qg::MXFP8) return QGEMV_EFORMAT;
   if (!codes || !scales || !wq || !ws) return QGEMV_EINVAL;
   if ((fmt == qg::INT4 || fmt == qg::INT5) && !mins) return QGEMV_EINVAL;
   Geom g;
   if (!qg::geom(fmt, M, K, &g)) return QGEMV_EINVAL;
   const int lo = fmt == qg::INT8 ? -128 : 0;
-  const int hi = fmt == qg::INT8 ? 127 : (fmt == qg::INT5 ? 31 : 15);
+  const int hi = fmt == qg::INT8 ? 127 : (fmt == qg::INT5 ? 31 : (fmt == qg::MXFP8 ? 255 : 15));
   for (int64_t i = 0; i < M * K; ++i) {
     const int c = fmt == qg::INT8 ? (int)((const int8_t*)codes)[i] : (int)((const uint8_t*)codes)[i];
     if (c < lo || c > hi) return QGEMV_EINVAL;
+    if (fmt == qg::MXFP8 && (c & 0x7F) == 0x7F) return QGEMV_EINVAL;   // E4M3 NaN
+  }
+  if (fmt == qg::MXFP8 || fmt == qg::MXFP4) {
+    const uint8_t* e = (const uint8_t*)scales;
+    for (int64_t i = 0; i < M * (K / 32); ++i)
+      if (e[i] == 0xFF) return QGEMV_EINVAL;                           // E8M0 NaN
   }
   memset(wq, 0, g.wq_bytes);
   memset(ws, 0, g.ws_bytes);
@@ -326,6 +395,10 @@ extern "C" int qgemv_pack_codes(int fmt, const void* codes, const void* scales, 
     for (int64_t m = 0; m < M; ++m)
       for (int64_t b = 0; b < K / 16; ++b) D.block(m, b, sb[m * (K / 16) + b]);
     D.tensor_scale(tensor_scale);
+  } else if (fmt == qg::MXFP8 || fmt == qg::MXFP4) {
+    const uint8_t* e = (const uint8_t*)scales;
+    for (int64_t m = 0; m < M; ++m)
+      for (int64_t b = 0; b < K / 32; ++b) D.mx_scale(m, b, e[m * (K / 32) + b]);
   } else {
     const uint16_t* d = (const uint16_t*)scales;
     for (int64_t m = 0; m < M; ++m)

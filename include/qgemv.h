@@ -31,6 +31,15 @@
  *   QGEMV_INT8   w = d*q,     q in -127..127 (two's complement), fp16 d per group
  *   QGEMV_NVFP4  w = s_t * e2m1(code) * e4m3(b), OCP FP4 E2M1 codes, one OCP
  *                FP8 E4M3 scale b per 16 weights, one fp32 tensor scale s_t
+ *   QGEMV_MXFP4  w = e2m1(code) * 2^(e - 127), one OCP E8M0 scale e per 32
+ *   QGEMV_MXFP8  w = e4m3(code) * 2^(e - 127), one OCP E8M0 scale e per 32
+ *                (OCP microscaling; the Decapybara kernel list names an
+ *                MXFP8 block-scaled GEMV). The packer picks
+ *                e = 127 + clamp(floor(log2 amax) - emax, -127, 127), emax 8
+ *                for E4M3 and 2 for E2M1, and rounds w / 2^(e - 127) to the
+ *                nearest code (ties to even, saturating). MX weights run on
+ *                qgemv_mx only; qgemv and the MoE entry points reject them
+ *                with QGEMV_EFORMAT.
  * The packed device layout is the library's own; qgemv_packed_bytes gives
  * its size. Weights are logically [K x M] and stored output-row-major.
  *
@@ -41,8 +50,10 @@
  *     call launches nothing and returns an error.
  *   - Device entry points are asynchronous on `stream` (0 = the null stream),
  *     never synchronise, and take device pointers owned by the caller. The
- *     library allocates nothing and keeps no global state: concurrent calls
- *     on different streams are safe when their output buffers do not overlap.
+ *     library allocates nothing; its only global state is a per-device cache
+ *     of the compute-unit count and kernel occupancy. Concurrent calls on
+ *     different streams are safe when their output buffers (and workspaces)
+ *     do not overlap.
  *   - Host entry points (pack) take host pointers and need no GPU.
  *   - Pointers to packed weights, scales and activations must be 16-byte
  *     aligned (QGEMV_EALIGN otherwise); float outputs 4-byte aligned.
@@ -64,7 +75,9 @@ typedef enum {
   QGEMV_INT4 = 1,
   QGEMV_INT5 = 2,
   QGEMV_INT8 = 3,
-  QGEMV_NVFP4 = 4
+  QGEMV_NVFP4 = 4,
+  QGEMV_MXFP4 = 5,
+  QGEMV_MXFP8 = 6
 } qgemv_format;
 
 typedef enum {
@@ -284,9 +297,34 @@ int qgemv_moe_index(const int32_t* ids, int N, int top_k, int E, int32_t* counts
 /* Debug / parity: write the fp32 weights the packed buffers encode,
  * w_out[m][k] for m < M, k < K. Values are exactly:
  *   int4/int5: fp32(d*q + m) rounded once; int8: d*q;
- *   nvfp4: fp32(s_t * (e2m1 * b)) rounded once. */
+ *   nvfp4: fp32(s_t * (e2m1 * b)) rounded once;
+ *   mxfp4 / mxfp8: e2m1 or e4m3 value * 2^(e - 127) (exact in fp32). */
 int qgemv_dequant(int fmt, const void* wq, const void* ws, int64_t M, int64_t K, float* w_out,
                   hipStream_t stream);
+
+/* Dynamic MXFP8 activation quantiser (Decapybara kernel list: a dynamic
+ * 32-element MXFP8 activation quantiser). For each token n < N and 32-block
+ * b along K, with the bf16 values v of x[n][32b .. 32b+31]:
+ *   X = floor(log2(max |v|)) - 8, clamped to [-127, 127]; -127 if all zero
+ *   scales[n][b] = X + 127                                 (E8M0)
+ *   codes[n][32b + i] = E4M3(v_i / 2^X): nearest, ties to even, saturating
+ *                       at +-448, sign bit kept (-0 -> 0x80), NaN -> NaN
+ *   x [N][K] bf16 bits, codes [N][K] bytes (both 16-byte aligned),
+ *   scales [N][K/32] bytes; device. K % 32 == 0. Exact: one correct result. */
+int qgemv_act_quant(const void* x, int N, int64_t K, uint8_t* codes, uint8_t* scales, hipStream_t stream);
+
+/* MX GEMV on gfx950's block-scaled MFMA (Decapybara kernel list: MXFP8
+ * block-scaled matrix-vector multiply):
+ *   y[n][m] = residual[n][m] + sum_k xq[n][k] * w[m][k]
+ * with xq[n][k] = e4m3(codes[n][k]) * 2^(scales[n][k/32] - 127) (the output
+ * of qgemv_act_quant) and w the MXFP8 or MXFP4 weights (QGEMV_MXFP8 /
+ * QGEMV_MXFP4, packed by qgemv_pack). Every product is exact; sums are fp32
+ * in a fixed order (reproducible run to run).
+ *   wq, ws: packed weights; xq [N][K] codes (16-byte aligned), xs [N][K/32]
+ *   E8M0 bytes; residual [N][M] fp32 or NULL (may equal y); y [N][M] fp32.
+ * 1 <= N <= 16. */
+int qgemv_mx(int fmt, const void* wq, const void* ws, const uint8_t* xq, const uint8_t* xs,
+             const float* residual, float* y, int64_t M, int64_t K, int N, hipStream_t stream);
 
 /* Measurement aid: stream-read `bytes` (multiple of 16) from `buf` with
  * 128-bit non-temporal loads, folding them into sink[0] (a device uint32).

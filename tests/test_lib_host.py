@@ -15,7 +15,7 @@ qg = pytest.importorskip("bit_quantized_weight_amd")
 if not os.path.exists(qg.LIB_PATH):
     pytest.skip("libqgemv.so not built (run __graft_entry__.build())", allow_module_level=True)
 
-FORMATS = ["int4", "int5", "int8", "nvfp4"]
+FORMATS = ["int4", "int5", "int8", "nvfp4", "mxfp4", "mxfp8"]
 
 
 def _header_functions():
@@ -72,11 +72,16 @@ def test_pack_bytes_equal_oracle_large(fmt):
 def test_pack_codes_equal_oracle(fmt):
     rng = np.random.default_rng(5)
     M, K = 33, 384
-    hi = {"int4": 16, "int5": 32, "nvfp4": 16}.get(fmt)
+    hi = {"int4": 16, "int5": 32, "nvfp4": 16, "mxfp4": 16, "mxfp8": 256}.get(fmt)
     codes = (rng.integers(-128, 128, (M, K)).astype(np.int8) if fmt == "int8"
              else rng.integers(0, hi, (M, K)).astype(np.uint8))
+    if fmt == "mxfp8":
+        codes[(codes & 0x7F) == 0x7F] = 0x7E          # E4M3 NaN codes are rejected
     qz = quant.Quantized(fmt, M, K, codes)
-    if fmt == "nvfp4":
+    if fmt in ("mxfp4", "mxfp8"):
+        qz.e = rng.integers(0, 255, (M, K // 32)).astype(np.uint8)
+        wq, ws = qg.pack_codes(fmt, codes, qz.e)
+    elif fmt == "nvfp4":
         qz.sb = rng.integers(0, 256, (M, K // 16)).astype(np.uint8)
         qz.st = np.float32(0.37)
         wq, ws = qg.pack_codes(fmt, codes, qz.sb, None, float(qz.st))
@@ -111,6 +116,20 @@ def test_pack_rejects_bad_input():
     with pytest.raises(qg.QgemvError) as e:
         qg.pack_codes("int4", codes, np.zeros((16, 2), np.uint16), np.zeros((16, 2), np.uint16))
     assert e.value.status == -1
+
+
+def test_pack_codes_rejects_mx_nan():
+    codes = np.zeros((16, 64), np.uint8)
+    e = np.full((16, 2), 127, np.uint8)
+    codes[2, 5] = 0x7F
+    with pytest.raises(qg.QgemvError) as ex:
+        qg.pack_codes("mxfp8", codes, e)
+    assert ex.value.status == -1
+    codes[2, 5] = 0
+    e[1, 1] = 0xFF
+    with pytest.raises(qg.QgemvError) as ex:
+        qg.pack_codes("mxfp8", codes, e)
+    assert ex.value.status == -1
 
 
 def test_expert_stride_is_256_aligned():
@@ -216,3 +235,25 @@ def test_fusion_validation_codes():
     assert ex(N=9, src=FAKE, gamma=FAKE) == -7
     assert ex(sw=True, M=24) == -3                         # I % 16
     assert ex(flags=2) == -1 and ex(flags=-1) == -1       # unknown flag bits
+
+
+def test_mx_validation_codes():
+    L = qg.load(False)
+
+    def mx(**kw):
+        a = dict(fmt=6, wq=FAKE, ws=FAKE, xq=FAKE, xs=FAKE, res=None, y=FAKE, M=64, K=128, N=1)
+        a.update(kw)
+        return L.qgemv_mx(a["fmt"], a["wq"], a["ws"], a["xq"], a["xs"], a["res"], a["y"], a["M"], a["K"], a["N"],
+                          None)
+    assert mx(fmt=1) == -2 and mx(fmt=7) == -2
+    assert mx(wq=None) == -1 and mx(xs=None) == -1 and mx(y=None) == -1
+    assert mx(N=0) == -7 and mx(N=17) == -7
+    assert mx(K=48) == -3 and mx(K=16) == -1 and mx(M=0) == -1
+    assert mx(xq=ODD) == -3 and mx(wq=ODD) == -3 and mx(y=FAKE + 2) == -3
+    # MX weights are rejected by the bf16-activation entry points
+    assert _gemv(fmt=5) == -2 and _gemv(fmt=6) == -2
+    aq = lambda **kw: L.qgemv_act_quant(kw.get("x", FAKE), kw.get("N", 1), kw.get("K", 64), kw.get("c", FAKE),
+                                         kw.get("s", FAKE), None)
+    assert aq(x=None) == -1 and aq(c=None) == -1 and aq(s=None) == -1
+    assert aq(N=0) == -1 and aq(K=48) == -3 and aq(K=16) == -1
+    assert aq(x=ODD) == -3 and aq(c=ODD) == -3
