@@ -17,7 +17,9 @@ Also reported on the same JSON line:
                 its average launch duration from HIP events on the launch
                 stream around batches of back-to-back launches (median batch)
   nvfp4_layer   the same layer in NVFP4 at N = 1, 2, 4, 8
-  per_format    qgemv on [17408][5120] for each format at N = 1, 2, 4, 8
+  per_format    qgemv on [17408][5120] for each format at N = 1, 2, 4, 8, and
+                qgemv_mx (MXFP4 / MXFP8 weights, MXFP8 activations) at
+                N = 1, 2, 4, 8, 16, alone and after qgemv_act_quant
   moe           qgemv_moe on the 128-expert, top-8 workload at N = 1 and 8
   probe         the plain streaming-read kernel on the same rotation
   cpu_baseline  the CPU oracle on a bounded sample of the layer
@@ -337,12 +339,12 @@ def extras(qg, torch, dev, stream, layers, args, wsp):
     del graph
     log("mlp_chain", res["mlp_chain"])
 
-    # per format on [17408][5120], N = 1, 2, 4, 8, rotated over >= 1 GB
+    # per format on [17408][5120], N = 1, 2, 4, 8 (MX: also 16), rotated over >= 1 GB
     M, K = 17408, 5120
     rng = synthetic.rng_for(0, 3, M)
     W = synthetic.weights(rng, M, K)
     pf = {}
-    for fmt in ("int4", "int5", "int8", "nvfp4"):
+    for fmt in ("int4", "int5", "int8", "nvfp4", "mxfp4", "mxfp8"):
         wq, ws = qg.pack(fmt, W)
         nb = wq.size + ws.size
         copies = max(2, int(np.ceil(1.2e9 / nb)))
@@ -352,9 +354,22 @@ def extras(qg, torch, dev, stream, layers, args, wsp):
         ms = timeit(lambda i: qg.qgemv_probe_read(d[i % copies][0], wq.size // 16 * 16, sink), 60)
         probe_gbs = (wq.size // 16 * 16) / (ms * 1e-3) / 1e9
         pf[fmt]["probe_GB/s"] = round(probe_gbs, 1)
-        for n in (1, 2, 4, 8):
+        for n in ((1, 2, 4, 8, 16) if fmt.startswith("mx") else (1, 2, 4, 8)):
             xb = torch.from_numpy(synthetic.activations(rng, n, K, 0.01)).to(dev)
             yy = torch.empty((n, M), dtype=torch.float32, device=dev)
+            if fmt.startswith("mx"):
+                # MXFP8 activations (qgemv_act_quant), then the block-scaled MFMA GEMV
+                xq = torch.empty((n, K), dtype=torch.uint8, device=dev)
+                xs = torch.empty((n, K // 32), dtype=torch.uint8, device=dev)
+                qg.act_quant(xb, xq, xs, n, K)
+                ms = timeit(lambda i: qg.qgemv_mx(fmt, *d[i % copies], xq, xs, yy, M, K, n), 60)
+                ms2 = timeit(lambda i: (qg.act_quant(xb, xq, xs, n, K),
+                                        qg.qgemv_mx(fmt, *d[i % copies], xq, xs, yy, M, K, n)), 60)
+                b = nb + n * K + n * (K // 32) + n * M * 4
+                gbs = b / (ms * 1e-3) / 1e9
+                pf[fmt][f"N{n}"] = {"us": round(ms * 1e3, 2), "GB/s": round(gbs, 1), "frac": round(gbs / PEAK_GBS, 4),
+                                    "of_probe": round(gbs / probe_gbs, 4), "us_with_act_quant": round(ms2 * 1e3, 2)}
+                continue
             ms = timeit(lambda i: qg.qgemv_ex(fmt, *d[i % copies], xb, yy, M, K, n, workspace=wsp), 60)
             ms0 = timeit(lambda i: qg.qgemv(fmt, *d[i % copies], xb, yy, M, K, n), 60)
             b = nb + n * K * 2 + n * M * 4

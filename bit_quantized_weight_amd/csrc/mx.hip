@@ -54,52 +54,29 @@ __device__ __forceinline__ uint32_t e4m3_rne_sat(float t) {
   return sign | code;
 }
 
-// One MX block of 32 bf16 values (64 bytes in x): E4M3 codes into c (byte e
-// of the block in byte e % 4 of dword e / 4) and the E8M0 byte returned.
-// amax from the bf16 magnitudes as integers (their order is the values'),
-// X = floor(log2 amax) - 8 clamped to [-127, 127]; a bf16 subnormal amax has
-// floor(log2) < -126, so it clamps too. Scaling by 2^-X is exact.
-__device__ __forceinline__ uint32_t mx_quant_block(const u32x4 (&x)[4], uint32_t (&c)[8]) {
-  uint32_t m = 0;
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t v = x[q][w];
-      m = max(m, max(v & 0x7FFFu, (v >> 16) & 0x7FFFu));
-    }
+// Eight lanes per MX block of 32 bf16 values, four values each: the block's
+// amax comes from the bf16 magnitudes as integers (their order is the
+// values') combined over the eight lanes, X = floor(log2 amax) - 8 clamped
+// to [-127, 127] (a bf16 subnormal amax has floor(log2) < -126, so it
+// clamps too), and each lane converts its four values scaled by 2^-X
+// (exact) into four E4M3 bytes.
+__global__ __launch_bounds__(256) void k_act_quant(const uint16_t* x, int64_t nblk, uint8_t* codes, uint8_t* scales) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t i = t >> 3;                 // block; its 8 lanes share i, so they leave together
+  if (i >= nblk) return;
+  const u32x2 v = *reinterpret_cast<const u32x2*>(x + t * 4);
+  uint32_t m = max(max(v.x & 0x7FFFu, (v.x >> 16) & 0x7FFFu), max(v.y & 0x7FFFu, (v.y >> 16) & 0x7FFFu));
+  m = max(m, (uint32_t)__shfl_xor((int)m, 1, 8));
+  m = max(m, (uint32_t)__shfl_xor((int)m, 2, 8));
+  m = max(m, (uint32_t)__shfl_xor((int)m, 4, 8));
   int X = (int)(m >> 7) - 127 - 8;
   X = m == 0 ? -127 : max(-127, min(127, X));
-  const float s = __uint_as_float((uint32_t)(127 - X) << 23);   // 2^-X, X <= 120 here
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t v = x[q][w];
-      const uint32_t lo = e4m3_rne_sat(__uint_as_float(v << 16) * s);
-      const uint32_t hi = e4m3_rne_sat(__uint_as_float(v & 0xFFFF0000u) * s);
-      const int e = 8 * q + 2 * w;                                  // element index of lo
-      const uint32_t pair = lo | (hi << 8);
-      if ((e & 3) == 0) c[e >> 2] = pair;
-      else c[e >> 2] |= pair << 16;
-    }
-  return (uint32_t)(X + 127);
-}
-
-// One thread per (token, 32-block).
-__global__ __launch_bounds__(256) void k_act_quant(const uint16_t* x, int64_t nblk, uint8_t* codes, uint8_t* scales) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= nblk) return;
-  const u32x4* src = reinterpret_cast<const u32x4*>(x + i * 32);
-  u32x4 v[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) v[q] = src[q];
-  uint32_t c[8];
-  const uint32_t e = mx_quant_block(v, c);
-  u32x4* dst = reinterpret_cast<u32x4*>(codes + i * 32);
-  dst[0] = u32x4{c[0], c[1], c[2], c[3]};
-  dst[1] = u32x4{c[4], c[5], c[6], c[7]};
-  scales[i] = (uint8_t)e;
+  const float sc = __uint_as_float((uint32_t)(127 - X) << 23);   // 2^-X (X <= 120 for bf16 inputs)
+  const uint32_t c = e4m3_rne_sat(__uint_as_float(v.x << 16) * sc) | (e4m3_rne_sat(__uint_as_float(v.x & 0xFFFF0000u) * sc) << 8) |
+                     (e4m3_rne_sat(__uint_as_float(v.y << 16) * sc) << 16) |
+                     (e4m3_rne_sat(__uint_as_float(v.y & 0xFFFF0000u) * sc) << 24);
+  *reinterpret_cast<uint32_t*>(codes + t * 4) = c;
+  if ((t & 7) == 0) scales[i] = (uint8_t)(X + 127);
 }
 
 // ---- the block-scaled GEMV -------------------------------------------------
@@ -285,15 +262,18 @@ struct MxShape {
   int nt, waves, kpw;
 };
 
-// Tiles per workgroup and k-steps per wave: one tile per workgroup once the
-// matrix has >= 512 tiles (more, smaller workgroups spread over the 256
-// compute units), 16 k-steps per wave, fewer while the grid holds under ~900
-// waves, at most 8 waves.
-MxShape mx_shape(int64_t out_tiles, int64_t KS) {
+// Tiles per workgroup and k-steps per wave, from sweeps on MI355X over
+// [17408][5120], [5120][17408] and [7168][5120], N = 1, 4, 8, 16, tiles per
+// workgroup 1 / 2 / 4 and 8-24 k-steps per wave: MXFP8 with >= 512 tiles at
+// N <= 8 takes one tile per workgroup, everything else two (two tiles halve
+// how often the activations are re-read, which matters from N = 16); 8
+// k-steps per wave, 16 for MXFP4 at N <= 4; fewer while the grid holds under
+// ~900 waves, at most 8 waves per workgroup.
+MxShape mx_shape(int fmt, int64_t out_tiles, int64_t KS, int N) {
   MxShape s;
-  s.nt = out_tiles >= 512 ? 1 : 2;
+  s.nt = (fmt == MXFP8 && out_tiles >= 512 && N <= 8) ? 1 : 2;
   const int64_t wgs = (out_tiles + s.nt - 1) / s.nt;
-  int64_t kpw = 16;
+  int64_t kpw = (fmt == MXFP4 && N <= 4) ? 16 : 8;
   while (kpw > 1 && wgs * ((KS + kpw - 1) / kpw) < 900) --kpw;
   while ((KS + kpw - 1) / kpw > 8) ++kpw;
   s.waves = (int)((KS + kpw - 1) / kpw);
@@ -335,7 +315,7 @@ extern "C" int qgemv_act_quant(const void* x, int N, int64_t K, uint8_t* codes, 
   if (!al16(x) || !al16(codes)) return QGEMV_EALIGN;
   if ((uint64_t)N * (uint64_t)K * 2ull >= (1ull << 40)) return QGEMV_EUNSUPPORTED;
   const int64_t nblk = (int64_t)N * (K / 32);
-  const dim3 grid((unsigned)((nblk + 255) / 256));
+  const dim3 grid((unsigned)((nblk * 8 + 255) / 256));
   hipLaunchKernelGGL(k_act_quant, grid, dim3(256), 0, stream, (const uint16_t*)x, nblk, codes, scales);
   return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
 }
@@ -372,7 +352,7 @@ extern "C" int qgemv_mx(int fmt, const void* wq, const void* ws, const uint8_t* 
   a.G = (int)(K / 32);
   a.N = N;
   a.out_tiles = (int)((M + 15) / 16);
-  const MxShape s = mx_shape(a.out_tiles, g.KS);
+  const MxShape s = mx_shape(fmt, a.out_tiles, g.KS, N);
   a.ks_per_wave = s.kpw;
   hipError_t e;
   if (fmt == MXFP8) e = s.nt == 1 ? launch_mx<MXFP8, 1>(a, s, stream) : launch_mx<MXFP8, 2>(a, s, stream);
