@@ -300,6 +300,49 @@ def extras(qg, torch, dev, stream, layers, args, wsp):
                                       "8 rotated copies", "weight_bytes": nv_w, **nv}
     log("nvfp4_layer", res["nvfp4_layer"])
 
+    # the same layer in MXFP4 on the block-scaled MFMA: each projection's bf16
+    # input quantised to MXFP8 on the device first (qgemv_act_quant), N = 1, 8, 16
+    mx_host = {}
+    for name, M_, K_, _ in LAYER:
+        rng_l = synthetic.rng_for(0, 3, 2, M_)
+        mx_host[name] = qg.pack("mxfp4", synthetic.weights(rng_l, M_, K_))
+    mx_layers = [{k: (torch.from_numpy(v[0]).to(dev), torch.from_numpy(v[1]).to(dev)) for k, v in mx_host.items()}
+                 for _ in range(8)]
+    mx_w = sum(v[0].size + v[1].size for v in mx_host.values())
+    del mx_host
+    mxr = {}
+    for n in (1, 8, 16):
+        rng_x = synthetic.rng_for(0, 3, 3, n)
+        xn = torch.from_numpy(synthetic.activations(rng_x, n, 5120)).to(dev)
+        xdn = torch.from_numpy(synthetic.activations(rng_x, n, 17408)).to(dev)
+        xq = torch.empty((n, 5120), dtype=torch.uint8, device=dev)
+        xs = torch.empty((n, 5120 // 32), dtype=torch.uint8, device=dev)
+        dq = torch.empty((n, 17408), dtype=torch.uint8, device=dev)
+        dsc = torch.empty((n, 17408 // 32), dtype=torch.uint8, device=dev)
+        qn = torch.empty((n, 7168), dtype=torch.float32, device=dev)
+        hn = torch.empty((n, 17408), dtype=torch.float32, device=dev)
+        rn = torch.from_numpy(synthetic.residual(rng_x, n, 5120)).to(dev)
+        yn = torch.empty((n, 5120), dtype=torch.float32, device=dev)
+
+        def mx_step(i):
+            L = mx_layers[i % len(mx_layers)]
+            qg.act_quant(xn, xq, xs, n, 5120)
+            qg.qgemv_mx("mxfp4", *L["qkv"], xq, xs, qn, 7168, 5120, n)
+            qg.qgemv_mx_swiglu("mxfp4", *L["gate_up"], xq, xs, hn, 17408, 5120, n)
+            qg.act_quant(xdn, dq, dsc, n, 17408)
+            qg.qgemv_mx("mxfp4", *L["down"], dq, dsc, yn, 5120, 17408, n, residual=rn)
+        ms = timeit(mx_step, 40)
+        b = mx_w + n * (5120 * 2 * 2 + 17408 * 2) + n * (5120 + 17408) * (1 + 1 / 32) * 2 \
+            + n * (7168 * 4 + 17408 * 4 + 5120 * 8)
+        mxr[f"N{n}"] = {"us": round(ms * 1e3, 2), "GB/s": round(b / (ms * 1e-3) / 1e9, 1),
+                        "frac": round(b / (ms * 1e-3) / 1e9 / PEAK_GBS, 4),
+                        "tok_per_s_64_layers": round(n / (64 * ms * 1e-3), 1)}
+    del mx_layers
+    res["mxfp4_layer"] = {"workload": "27B-class dense layer in MXFP4 with MXFP8 activations (2 activation "
+                                      "quantisers, QKV, gate/up + SwiGLU, down + residual), 8 rotated copies",
+                          "weight_bytes": mx_w, **mxr}
+    log("mxfp4_layer", res["mxfp4_layer"])
+
     # the MLP block chained on the device (NInfer article, section 2: norm,
     # matmul, SwiGLU and residual fused): RMSNorm(r) -> gate/up + SwiGLU with a
     # bf16 h -> down(h) + r, int5, N = 1; eager, and 16 rotated layers captured

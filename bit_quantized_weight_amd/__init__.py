@@ -79,6 +79,7 @@ def load(require_torch: bool = True):
         "qgemv_probe_read": (I32, [P, SZ, P, P]),
         "qgemv_act_quant": (I32, [P, I32, I64, P, P, P]),
         "qgemv_mx": (I32, [I32, P, P, P, P, P, P, I64, I64, I32, P]),
+        "qgemv_mx_swiglu": (I32, [I32, P, P, P, P, P, I64, I64, I32, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -94,7 +95,7 @@ def symbols() -> list[str]:
             "qgemv_pack_codes", "qgemv", "qgemv_swiglu", "qgemv_ex", "qgemv_swiglu_ex", "qgemv_split_workspace_bytes",
             "qgemv_moe_workspace_bytes", "qgemv_moe",
             "qgemv_moe_index", "qgemv_moe_route", "qgemv_moe_fused_workspace_bytes", "qgemv_moe_fused",
-            "qgemv_dequant", "qgemv_probe_read", "qgemv_act_quant", "qgemv_mx"]
+            "qgemv_dequant", "qgemv_probe_read", "qgemv_act_quant", "qgemv_mx", "qgemv_mx_swiglu"]
 
 
 def strerror(status: int) -> str:
@@ -275,6 +276,13 @@ def qgemv_mx(fmt, wq, ws, xq, xs, y, M: int, K: int, N: int, residual=None, stre
     act_quant) on the block-scaled MFMA; y [N][M] fp32, N <= 16."""
     _check(load().qgemv_mx(_fmt(fmt), _ptr(wq), _ptr(ws), _ptr(xq), _ptr(xs), _ptr(residual), _ptr(y), M, K, N,
                            _stream(stream)), "qgemv_mx")
+
+
+def qgemv_mx_swiglu(fmt, wq, ws, xq, xs, h, I: int, K: int, N: int, stream=None) -> None:
+    """qgemv_mx over [2I][K] weights (gate rows, then up rows) with SwiGLU:
+    h [N][I] = silu(gate) * up."""
+    _check(load().qgemv_mx_swiglu(_fmt(fmt), _ptr(wq), _ptr(ws), _ptr(xq), _ptr(xs), _ptr(h), I, K, N,
+                                  _stream(stream)), "qgemv_mx_swiglu")
 
 
 def qgemv_probe_read(buf, nbytes: int, sink, stream=None) -> None:

@@ -89,6 +89,7 @@ struct MxArgs {
   float* y;               // [N][M]
   uint32_t wq_bytes, ws_bytes, xq_bytes, xs_bytes;
   int M, K, KS, G, N, out_tiles, ks_per_wave;
+  int up_tile0;           // SwiGLU: row tile of the first up row (gate rows come first)
 };
 
 // operands of one k-step: activations (shared by the tiles) and NT weight tiles
@@ -144,9 +145,10 @@ __device__ __forceinline__ void mx_mma(f32x4 (&acc)[NT], const MxStep<FMT, NT>& 
   }
 }
 
-// Workgroup = NT row tiles; its W waves split the k-steps; the waves'
-// partial sums meet in LDS and are added in wave order (reproducible).
-template <int FMT, int NT>
+// Workgroup = NT row tiles (SwiGLU: a gate tile and its up tile); its W
+// waves split the k-steps; the waves' partial sums meet in LDS and are added
+// in wave order (reproducible).
+template <int FMT, int NT, bool SWIGLU>
 __global__ __launch_bounds__(512) void k_mxgemv(MxArgs a) {
   extern __shared__ __attribute__((aligned(16))) float red[];   // [W][NT][64 lanes][4]
   const int lane = threadIdx.x & 63;
@@ -157,9 +159,14 @@ __global__ __launch_bounds__(512) void k_mxgemv(MxArgs a) {
   const __amdgpu_buffer_rsrc_t ws = make_rsrc(a.ws, a.ws_bytes);
   const __amdgpu_buffer_rsrc_t xq = make_rsrc(a.xq, a.xq_bytes);
   const __amdgpu_buffer_rsrc_t xs = make_rsrc(a.xs, a.xs_bytes);
+  constexpr int TO = SWIGLU ? 1 : NT;     // output tiles per workgroup
+  static_assert(!SWIGLU || NT == 2, "SwiGLU pairs one gate tile with its up tile");
   int tile[NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) tile[t] = min((int)blockIdx.x * NT + t, a.out_tiles - 1);
+  for (int t = 0; t < NT; ++t) {
+    const int ot = min((int)blockIdx.x * TO + (SWIGLU ? 0 : t), a.out_tiles - 1);
+    tile[t] = (SWIGLU && t == 1) ? a.up_tile0 + ot : ot;
+  }
   // A row r = token r: rows past N start out of range
   const uint32_t xrow = r < a.N ? (uint32_t)(r * a.K) : kOOB;
   const uint32_t srow = r < a.N ? (uint32_t)(r * a.G) : kOOB;
@@ -189,16 +196,22 @@ __global__ __launch_bounds__(512) void k_mxgemv(MxArgs a) {
   for (int t = 0; t < NT; ++t)
     *reinterpret_cast<f32x4*>(red + ((size_t)(wave * NT + t) * 64 + lane) * 4) = acc[t];
   __syncthreads();
-  for (int o = threadIdx.x; o < NT * 256; o += blockDim.x) {
+  for (int o = threadIdx.x; o < TO * 256; o += blockDim.x) {
     const int t = o >> 8, tok = (o >> 4) & 15, row = o & 15;
-    const int ot = (int)blockIdx.x * NT + t;
+    const int ot = (int)blockIdx.x * TO + t;
     const int col = ot * 16 + row;
     if (tok >= a.N || ot >= a.out_tiles || col >= a.M) continue;
     const int idx = ((tok >> 2) * 16 + row) * 4 + (tok & 3);
     float v = 0.f;
     for (int w = 0; w < W; ++w) v += red[(size_t)(w * NT + t) * 256 + idx];
     const size_t at = (size_t)tok * a.M + col;
-    if (a.res) v += a.res[at];
+    if constexpr (SWIGLU) {
+      float u = 0.f;
+      for (int w = 0; w < W; ++w) u += red[(size_t)(w * NT + 1) * 256 + idx];
+      v = v / (1.0f + expf(-v)) * u;
+    } else {
+      if (a.res) v += a.res[at];
+    }
     a.y[at] = v;
   }
 }
@@ -281,12 +294,25 @@ MxShape mx_shape(int fmt, int64_t out_tiles, int64_t KS, int N) {
   return s;
 }
 
-template <int FMT, int NT>
+// SwiGLU: one gate/up pair per workgroup, the same k-steps per wave
+MxShape mx_shape_pairs(int fmt, int64_t pairs, int64_t KS, int N) {
+  MxShape s;
+  s.nt = 2;
+  int64_t kpw = (fmt == MXFP4 && N <= 4) ? 16 : 8;
+  while (kpw > 1 && pairs * ((KS + kpw - 1) / kpw) < 900) --kpw;
+  while ((KS + kpw - 1) / kpw > 8) ++kpw;
+  s.waves = (int)((KS + kpw - 1) / kpw);
+  s.kpw = (int)kpw;
+  return s;
+}
+
+template <int FMT, int NT, bool SWIGLU = false>
 hipError_t launch_mx(const MxArgs& a, const MxShape& s, hipStream_t stream) {
-  const dim3 grid((unsigned)((a.out_tiles + NT - 1) / NT));
+  const int TO = SWIGLU ? 1 : NT;
+  const dim3 grid((unsigned)((a.out_tiles + TO - 1) / TO));
   const dim3 block((unsigned)(64 * s.waves));
   const size_t lds = (size_t)s.waves * NT * 256 * sizeof(float);
-  hipLaunchKernelGGL((k_mxgemv<FMT, NT>), grid, block, lds, stream, a);
+  hipLaunchKernelGGL((k_mxgemv<FMT, NT, SWIGLU>), grid, block, lds, stream, a);
   return hipGetLastError();
 }
 
@@ -320,16 +346,19 @@ extern "C" int qgemv_act_quant(const void* x, int N, int64_t K, uint8_t* codes, 
   return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
 }
 
-extern "C" int qgemv_mx(int fmt, const void* wq, const void* ws, const uint8_t* xq, const uint8_t* xs,
-                        const float* residual, float* y, int64_t M, int64_t K, int N, hipStream_t stream) {
+namespace {
+
+// Mout output columns; Mpacked packed rows (SwiGLU: 2 Mout, gate rows first)
+int run_mx(int fmt, const void* wq, const void* ws, const uint8_t* xq, const uint8_t* xs, const float* residual,
+           float* y, int64_t Mout, int64_t Mpacked, int64_t K, int N, bool swiglu, hipStream_t stream) {
   if (fmt != MXFP8 && fmt != MXFP4) return QGEMV_EFORMAT;
   if (!wq || !ws || !xq || !xs || !y) return QGEMV_EINVAL;
-  if (M < 1 || K < 32 || M > (1 << 24)) return QGEMV_EINVAL;
+  if (Mout < 1 || K < 32 || Mpacked > (1 << 24)) return QGEMV_EINVAL;
   if (K % 32) return QGEMV_EALIGN;
   if (N < 1 || N > 16) return QGEMV_EUNSUPPORTED;
   if (!al16(wq) || !al16(ws) || !al16(xq) || !al4(y) || (residual && !al4(residual))) return QGEMV_EALIGN;
   Geom g;
-  if (!geom(fmt, M, K, &g)) return QGEMV_EINVAL;
+  if (!geom(fmt, Mpacked, K, &g)) return QGEMV_EINVAL;
   // k-steps past a wave's range are loaded with an out-of-range lane offset
   // (2^31 or more) on top of a tile offset up to 4 k-steps past the matrix:
   // the sum must stay below 2^32
@@ -346,16 +375,33 @@ extern "C" int qgemv_mx(int fmt, const void* wq, const void* ws, const uint8_t* 
   a.ws_bytes = (uint32_t)g.ws_bytes;
   a.xq_bytes = (uint32_t)((int64_t)N * K);
   a.xs_bytes = (uint32_t)((int64_t)N * (K / 32));
-  a.M = (int)M;
+  a.M = (int)Mout;
   a.K = (int)K;
   a.KS = (int)g.KS;
   a.G = (int)(K / 32);
   a.N = N;
-  a.out_tiles = (int)((M + 15) / 16);
-  const MxShape s = mx_shape(fmt, a.out_tiles, g.KS, N);
+  a.out_tiles = (int)((Mout + 15) / 16);
+  a.up_tile0 = swiglu ? (int)(Mout / 16) : 0;
+  MxShape s = mx_shape(fmt, a.out_tiles, g.KS, N);
+  if (swiglu) s = mx_shape_pairs(fmt, a.out_tiles, g.KS, N);
   a.ks_per_wave = s.kpw;
   hipError_t e;
-  if (fmt == MXFP8) e = s.nt == 1 ? launch_mx<MXFP8, 1>(a, s, stream) : launch_mx<MXFP8, 2>(a, s, stream);
+  if (swiglu) e = fmt == MXFP8 ? launch_mx<MXFP8, 2, true>(a, s, stream) : launch_mx<MXFP4, 2, true>(a, s, stream);
+  else if (fmt == MXFP8) e = s.nt == 1 ? launch_mx<MXFP8, 1>(a, s, stream) : launch_mx<MXFP8, 2>(a, s, stream);
   else e = s.nt == 1 ? launch_mx<MXFP4, 1>(a, s, stream) : launch_mx<MXFP4, 2>(a, s, stream);
   return e == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
+}
+
+}  // namespace
+
+extern "C" int qgemv_mx(int fmt, const void* wq, const void* ws, const uint8_t* xq, const uint8_t* xs,
+                        const float* residual, float* y, int64_t M, int64_t K, int N, hipStream_t stream) {
+  return run_mx(fmt, wq, ws, xq, xs, residual, y, M, M, K, N, false, stream);
+}
+
+extern "C" int qgemv_mx_swiglu(int fmt, const void* wq, const void* ws, const uint8_t* xq, const uint8_t* xs,
+                               float* h, int64_t I, int64_t K, int N, hipStream_t stream) {
+  if (I < 1) return QGEMV_EINVAL;
+  if (I % 16) return QGEMV_EALIGN;
+  return run_mx(fmt, wq, ws, xq, xs, nullptr, h, I, 2 * I, K, N, true, stream);
 }

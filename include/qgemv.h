@@ -326,6 +326,13 @@ int qgemv_act_quant(const void* x, int N, int64_t K, uint8_t* codes, uint8_t* sc
 int qgemv_mx(int fmt, const void* wq, const void* ws, const uint8_t* xq, const uint8_t* xs,
              const float* residual, float* y, int64_t M, int64_t K, int N, hipStream_t stream);
 
+/* qgemv_mx with the SwiGLU epilogue of qgemv_swiglu (NInfer article, section
+ * 2: SwiGLU fused into the matmul): wq, ws hold [2I][K] MX weights, gate rows
+ * [0, I) then up rows [I, 2I); h[n][i] = silu(g) * u with g, u the two MX
+ * GEMV outputs (no residual). I % 16 == 0; other arguments as qgemv_mx. */
+int qgemv_mx_swiglu(int fmt, const void* wq, const void* ws, const uint8_t* xq, const uint8_t* xs, float* h,
+                    int64_t I, int64_t K, int N, hipStream_t stream);
+
 /* Measurement aid: stream-read `bytes` (multiple of 16) from `buf` with
  * 128-bit non-temporal loads, folding them into sink[0] (a device uint32).
  * Gives the achievable read bandwidth that the GEMV kernels approach. */

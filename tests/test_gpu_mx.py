@@ -151,6 +151,45 @@ def test_mx_residual_aliasing_and_determinism(fmt):
     check_tol(y1, ref, T, "residual")
 
 
+@pytest.mark.parametrize("fmt", MX)
+@pytest.mark.parametrize("I,K,N", [(64, 512, 1), (48, 160, 3), (256, 2048, 8), (128, 1024, 16)])
+def test_mx_swiglu_parity(fmt, I, K, N):
+    log("mx swiglu", fmt, I, K, N)
+    wq, ws, xb = _mx_case(fmt, 2 * I, K, N, seed=I + N)
+    xq, xs = _device_quant(xb, N, K)
+    h = torch.full((N, I), float("nan"), dtype=torch.float32, device="cuda")
+    qg().qgemv_mx_swiglu(fmt, dev(wq, torch), dev(ws, torch), xq, xs, h, I, K, N)
+    torch.cuda.synchronize()
+    Wd = D.dequant(L.unpack(fmt, 2 * I, K, wq, ws))
+    x = G.mx_activations(xb)
+    href, Th = G.swiglu_from(G.gemv(x, Wd[:I]), G.gemv(x, Wd[I:]), G.gemv_tolerance(x, Wd[:I]),
+                             G.gemv_tolerance(x, Wd[I:]))
+    check_tol(h.cpu().numpy(), href, Th, f"mx swiglu {fmt} I={I} K={K} N={N}")
+
+
+def test_mx_swiglu_full_size_sampled_rows():
+    fmt, I, K, N = "mxfp4", 17408, 5120, 4
+    log("mx swiglu full", fmt, I, K, N)
+    rng = synthetic.rng_for(0, 35, I, K)
+    wq, ws = qg().pack(fmt, synthetic.weights(rng, 2 * I, K))
+    xb = synthetic.activations(rng, N, K, 0.01)
+    xq, xs = _device_quant(xb, N, K)
+    h = torch.full((N, I), float("nan"), dtype=torch.float32, device="cuda")
+    qg().qgemv_mx_swiglu(fmt, dev(wq, torch), dev(ws, torch), xq, xs, h, I, K, N)
+    torch.cuda.synchronize()
+    hg = h.cpu().numpy()
+    x = G.mx_activations(xb)
+    q = L.unpack(fmt, 2 * I, K, wq, ws)
+    RT = I // 16
+    for rt in sorted({0, RT // 2, RT - 1, *np.random.default_rng(5).integers(0, RT, 3).tolist()}):
+        def rows(t):
+            sl = slice(t * 16, (t + 1) * 16)
+            return D.dequant(Q.Quantized(fmt, 16, K, q.codes[sl], e=q.e[sl]))
+        Wg, Wu = rows(rt), rows(RT + rt)
+        href, Th = G.swiglu_from(G.gemv(x, Wg), G.gemv(x, Wu), G.gemv_tolerance(x, Wg), G.gemv_tolerance(x, Wu))
+        check_tol(hg[:, rt * 16:(rt + 1) * 16], href, Th, f"tile {rt}")
+
+
 @pytest.mark.parametrize("fmt,M,K,N", [("mxfp8", 17408, 5120, 1), ("mxfp4", 17408, 5120, 8),
                                        ("mxfp8", 5120, 17408, 16), ("mxfp4", 7168, 5120, 16)])
 def test_mx_full_size_sampled_rows(fmt, M, K, N):
