@@ -51,12 +51,19 @@ def weight_bytes(qg, fmt, M, K):
     return a + b
 
 
+# the sources the dense kernels (k_gemv) are compiled from
+DENSE_SOURCES = ["gemv.hip", "kloop.hpp", "device.hpp", "layout.hpp", "mx.hpp"]
+
+
 def kernel_source_hash() -> str:
+    """sha256 over the dense kernels' sources (and the ABI header)."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "bit_quantized_weight_amd", "csrc")
-    for f in sorted(os.listdir(d)):
+    for f in DENSE_SOURCES:
         with open(os.path.join(d, f), "rb") as fh:
             h.update(f.encode() + fh.read())
+    with open(os.path.join(ROOT, "include", "qgemv.h"), "rb") as fh:
+        h.update(b"qgemv.h" + fh.read())
     return h.hexdigest()[:16]
 
 
@@ -80,6 +87,41 @@ def pmc_traffic(name: str, src_hash: str):
     return None
 
 
+def mx_only(qg, torch, synthetic, dev, steps):
+    """MXFP8 / MXFP4 qgemv_mx on [17408][5120] at N = 1 after qgemv_act_quant,
+    rotated over >= 1.2 GB of weight copies; HIP events on the launch stream."""
+    M, K, N = 17408, 5120, 1
+    W = synthetic.weights(synthetic.rng_for(0, 3, M), M, K)
+    x = torch.from_numpy(synthetic.activations(synthetic.rng_for(0, 3, 4), N, K)).to(dev)
+    xq = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    xs = torch.empty((N, K // 32), dtype=torch.uint8, device=dev)
+    y = torch.empty((N, M), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    out = {"workload": "qgemv_mx [17408][5120], N=1, MXFP8 activations", "steps": steps}
+    for fmt in ("mxfp8", "mxfp4"):
+        wq, ws = qg.pack(fmt, W)
+        nb = wq.size + ws.size
+        copies = max(2, int(np.ceil(1.2e9 / nb)))
+        d = [(torch.from_numpy(wq).to(dev), torch.from_numpy(ws).to(dev)) for _ in range(copies)]
+        for i in range(10):
+            qg.act_quant(x, xq, xs, N, K)
+            qg.qgemv_mx(fmt, *d[i % copies], xq, xs, y, M, K, N)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(steps):
+            qg.act_quant(x, xq, xs, N, K)
+            qg.qgemv_mx(fmt, *d[i % copies], xq, xs, y, M, K, N)
+        b.record(stream)
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) / steps * 1e3
+        byt = nb + N * K + N * K // 32 + N * M * 4
+        out[fmt] = {"us_per_pair": round(us, 2), "weight_bytes": nb, "algorithmic_bytes": byt}
+        del d
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -91,6 +133,9 @@ def main():
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run a plain device-to-device copy of this many MiB three times "
                          "(the known-size reference that scales rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--mx-only", action="store_true",
+                    help="only the MX GEMV on [17408][5120] at N = 1 (MXFP8 and MXFP4, after the activation "
+                         "quantiser): a short run for profiling those kernels")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
@@ -102,6 +147,9 @@ def main():
 
     qg.load()
     dev = torch.device("cuda:0")
+    if args.mx_only:
+        print(json.dumps(mx_only(qg, torch, synthetic, dev, args.steps)), flush=True)
+        return
     stream = torch.cuda.current_stream()
     N = 1
     if args.calib_copy_mib > 0:
