@@ -119,15 +119,24 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// tokens per tile in the LDS reduction area: 16 with one slot, else 8
+template <int S>
+__host__ __device__ constexpr int red_tokens() { return S == 1 ? 16 : 8; }
+
 // Combine a lane's accumulators into per-(token, row) totals and write them
-// to LDS as red[((wave*NT + t)*8 + token)*16 + row]; fixed order throughout.
+// to LDS as red[((wave*NT + t)*TK + token)*16 + row] (TK = red_tokens<S>());
+// fixed order throughout.
 template <int S, int NT>
 __device__ __forceinline__ void reduce_to_lds(f32x4 (&acc)[NT], float* red, int wave, int lane) {
   const int r = lane & 15, s = lane >> 4;
+  constexpr int RB = red_tokens<S>() * 16;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    float* p = red + (size_t)(wave * NT + t) * 128;
-    if constexpr (S == 16) {          // every register a different slot, token 0
+    float* p = red + (size_t)(wave * NT + t) * RB;
+    if constexpr (S == 1) {           // one slot: register i = token 4s + i
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[(4 * s + i) * 16 + r] = acc[t][i];
+    } else if constexpr (S == 16) {          // every register a different slot, token 0
       float v = (acc[t][0] + acc[t][1]) + (acc[t][2] + acc[t][3]);
       v += __shfl_xor(v, 16);
       v += __shfl_xor(v, 32);
@@ -249,6 +258,8 @@ __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
   const int r = lane & 15, s = lane >> 4;
   constexpr int TO = SWIGLU ? NT / 2 : NT;
   constexpr int T = 16 / S;
+  constexpr int TK = red_tokens<S>();     // tokens per tile in the reduction area
+  constexpr int RB = TK * 16;             // floats per (wave, tile) there
   using C = Cyc<FMT, S>;
 
   const __amdgpu_buffer_rsrc_t wq = make_rsrc(a.wq, a.wq_bytes);
@@ -298,7 +309,7 @@ __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
     // constant, so slot addresses fold into the LDS instructions' offsets
     const int xs = XM == XM_RING ? ring_stride<S>() : a.N * 256 + 16;
     const int nrec = XM == XM_LDS ? a.x_nks : kRing;
-    uint8_t* xl = reinterpret_cast<uint8_t*>(red) + (size_t)W * NT * 512 + (size_t)wave * nrec * xs;
+    uint8_t* xl = reinterpret_cast<uint8_t*>(red) + (size_t)W * NT * RB * 4 + (size_t)wave * nrec * xs;
     // per (cycle position, group): this lane's data or the record's zero block
     uint32_t off[C::KSTEPS][4];
     const int sigma = r / T - (FMT == NVFP4 ? (s >> 1) : 0);
@@ -404,10 +415,10 @@ __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
   const size_t slot0 = frag >= 0 ? (size_t)(rblk - a.n_full) * nslot : 0;
   if (frag >= 0 && frag < nslot) {
     // publish this fragment's partial sums (waves added in order) and raise its flag
-    float* dst = a.part + (slot0 + frag) * (NT * 128);
-    for (int o = threadIdx.x; o < NT * 128; o += blockDim.x) {
+    float* dst = a.part + (slot0 + frag) * (NT * RB);
+    for (int o = threadIdx.x; o < NT * RB; o += blockDim.x) {
       float v = 0.f;
-      for (int w = 0; w < W; ++w) v += red[(size_t)w * NT * 128 + o];
+      for (int w = 0; w < W; ++w) v += red[(size_t)w * NT * RB + o];
       st_f32_dev(dst + o, v);
     }
     __builtin_amdgcn_s_waitcnt(0);        // this thread's stores have completed
@@ -439,12 +450,12 @@ __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
   // sum of a (tile, token, row) over the earlier fragments, in fragment order
   auto frag_sum = [&](int o) -> float {
     float v = 0.f;
-    for (int f = 0; f < nslot; ++f) v += ld_f32_dev(a.part + (slot0 + f) * (NT * 128) + o);
+    for (int f = 0; f < nslot; ++f) v += ld_f32_dev(a.part + (slot0 + f) * (NT * RB) + o);
     return v;
   };
-  const int n_out = TO * 128;
+  const int n_out = TO * RB;
   for (int o = threadIdx.x; o < n_out; o += blockDim.x) {
-    const int to = o >> 7, rem = o & 127;
+    const int to = o / RB, rem = o - to * RB;
     const int tok = rem >> 4, row = rem & 15;
     const int ot = rblk * TO + to;
     const int col = ot * 16 + row;
@@ -456,9 +467,9 @@ __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
       sc = sc * (1.0f / sqrtf(ss / (float)a.K + a.eps));
     }
     float v = 0.f, vo = 0.f;
-    for (int w = 0; w < W; ++w) vo += red[((size_t)(w * NT + to) * 8 + tok) * 16 + row];
+    for (int w = 0; w < W; ++w) vo += red[((size_t)(w * NT + to) * TK + tok) * 16 + row];
     if (frag >= 0) {
-      v = frag_sum(to * 128 + rem);
+      v = frag_sum(to * RB + rem);
       v += vo;
     } else {
       v = vo;
@@ -467,9 +478,9 @@ __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
     const size_t at = (size_t)tok * a.M + col;
     if constexpr (SWIGLU) {
       float u = 0.f, uo = 0.f;
-      for (int w = 0; w < W; ++w) uo += red[((size_t)(w * NT + TO + to) * 8 + tok) * 16 + row];
+      for (int w = 0; w < W; ++w) uo += red[((size_t)(w * NT + TO + to) * TK + tok) * 16 + row];
       if (frag >= 0) {
-        u = frag_sum((TO + to) * 128 + rem);
+        u = frag_sum((TO + to) * RB + rem);
         u += uo;
       } else {
         u = uo;
@@ -588,7 +599,7 @@ struct LaunchShape {
   int kps;      // k-steps per weight prefetch buffer
 };
 
-int slots_for(int N) { return N == 1 ? 16 : N == 2 ? 8 : N <= 4 ? 4 : 2; }
+int slots_for(int N) { return N == 1 ? 16 : N == 2 ? 8 : N <= 4 ? 4 : N <= 8 ? 2 : 1; }
 
 // k-steps per cycle for (format, slots): wave ranges are multiples of it
 int cycle_ksteps(int fmt, int S) {
@@ -615,7 +626,7 @@ int cycle_ksteps(int fmt, int S) {
 // work; below that the k-range per wave shrinks (never under one scale
 // cycle). Each wave's range is a whole number of cycles.
 bool single_tile(int fmt, int N, bool swiglu, int64_t out_tiles) {
-  if (swiglu) return false;
+  if (swiglu || N > 8) return false;      // 9-16 tokens: two tiles share each activation load
   if ((fmt == NVFP4 && N <= 2) || (fmt == INT8 && N == 2)) return true;   // every shape
   return out_tiles >= 768 || (N >= 2 && out_tiles >= 384);
 }
@@ -768,9 +779,10 @@ hipError_t launch_s(const GemvArgs& a0, const LaunchShape& ls, bool swiglu, hipS
   const int U = 2 * KPS;   // k-steps per trip of the k-loop
   a.x_nks = (ls.kpw + U - 1) / U * U + 1;
   const size_t rec = (size_t)a.N * 256 + 16;
-  const size_t red = (size_t)ls.waves * NT * 128 * sizeof(float);
+  const size_t red = (size_t)ls.waves * NT * red_tokens<S>() * 16 * sizeof(float);
   const size_t whole = (size_t)ls.waves * a.x_nks * rec, ring = (size_t)ls.waves * kRing * ring_stride<S>();
-  int xm = whole <= kMaxLdsActs ? XM_LDS : (ring <= kMaxLdsActs ? XM_RING : XM_LOAD);
+  // (the ring moves at most 8 tokens per record: one slot's 16 load directly)
+  int xm = whole <= kMaxLdsActs ? XM_LDS : ((ring <= kMaxLdsActs && S > 1) ? XM_RING : XM_LOAD);
   if (a.nsrc && xm == XM_LOAD) {         // the RMSNorm prologue stages its activations in LDS
     if (red + ring > kMaxLdsNorm) return hipErrorNotSupported;
     xm = XM_RING;
@@ -781,16 +793,27 @@ hipError_t launch_s(const GemvArgs& a0, const LaunchShape& ls, bool swiglu, hipS
 #define QG_PICK(SW, XMV, NRM) fn = k_gemv<FMT, NT, S, KPS, SW, XMV, NRM>
   if (NT >= 2 && swiglu) {
     if constexpr (NT >= 2) {
-      if (xm == XM_LDS) { if (norm) QG_PICK(true, XM_LDS, true); else QG_PICK(true, XM_LDS, false); }
-      else if (xm == XM_RING) { if (norm) QG_PICK(true, XM_RING, true); else QG_PICK(true, XM_RING, false); }
+      if (xm == XM_LDS) {
+        if constexpr (S > 1) { if (norm) QG_PICK(true, XM_LDS, true); else QG_PICK(true, XM_LDS, false); }
+        else QG_PICK(true, XM_LDS, false);
+      }
+      else if (xm == XM_RING) {
+        if constexpr (S > 1) { if (norm) QG_PICK(true, XM_RING, true); else QG_PICK(true, XM_RING, false); }
+      }
       else QG_PICK(true, XM_LOAD, false);
     }
   } else {
-    if (xm == XM_LDS) { if (norm) QG_PICK(false, XM_LDS, true); else QG_PICK(false, XM_LDS, false); }
-    else if (xm == XM_RING) { if (norm) QG_PICK(false, XM_RING, true); else QG_PICK(false, XM_RING, false); }
+    if (xm == XM_LDS) {
+      if constexpr (S > 1) { if (norm) QG_PICK(false, XM_LDS, true); else QG_PICK(false, XM_LDS, false); }
+      else QG_PICK(false, XM_LDS, false);
+    }
+    else if (xm == XM_RING) {
+      if constexpr (S > 1) { if (norm) QG_PICK(false, XM_RING, true); else QG_PICK(false, XM_RING, false); }
+    }
     else QG_PICK(false, XM_LOAD, false);
   }
 #undef QG_PICK
+  if (!fn) return hipErrorNotSupported;
   int64_t nwg = blocks;
   if (a.frag > 1) {
     // split only when every workgroup of the split grid is resident at once:
@@ -811,6 +834,9 @@ template <int FMT, int NT, int KPS>
 hipError_t launch_k(const GemvArgs& a, const LaunchShape& ls, bool swiglu, hipStream_t stream) {
   switch (ls.slots) {
     case 16: return launch_s<FMT, NT, 16, KPS>(a, ls, swiglu, stream);
+    case 1:
+      if constexpr (FMT != NVFP4) return launch_s<FMT, NT, 1, KPS>(a, ls, swiglu, stream);
+      return hipErrorNotSupported;
     case 8: return launch_s<FMT, NT, 8, KPS>(a, ls, swiglu, stream);
     case 4: return launch_s<FMT, NT, 4, KPS>(a, ls, swiglu, stream);
     default: return launch_s<FMT, NT, 2, KPS>(a, ls, swiglu, stream);
@@ -828,7 +854,7 @@ int validate_common(int fmt, const void* wq, const void* ws, int64_t M, int64_t 
   if (!wq || !ws) return QGEMV_EINVAL;
   if (M < 1 || K < 32 || M > (1 << 24)) return QGEMV_EINVAL;
   if (K % 32) return QGEMV_EALIGN;
-  if (N < 1 || N > 8) return QGEMV_EUNSUPPORTED;
+  if (N < 1 || N > 16) return QGEMV_EUNSUPPORTED;
   if (!aligned16(wq) || !aligned16(ws)) return QGEMV_EALIGN;
   if (!geom(fmt, M, K, g)) return QGEMV_EINVAL;
   if (g->wq_bytes >= (1ull << 32) || g->ws_bytes >= (1ull << 32)) return QGEMV_EUNSUPPORTED;
@@ -845,6 +871,9 @@ int run_gemv(int fmt, const void* wq, const void* ws, const void* x, const float
   if (rc) return rc;
   const bool norm = fz && fz->norm_src;
   uint16_t* ybf = fz ? fz->out_bf16 : nullptr;
+  // 9 to 16 tokens use one slot: int formats only (NVFP4 needs two slots per
+  // group), no RMSNorm prologue and no batch-invariant order
+  if (N > 8 && (fmt == NVFP4 || norm || (fz && (fz->flags & QGEMV_BATCH_INVARIANT)))) return QGEMV_EUNSUPPORTED;
   if (!norm && !x) return QGEMV_EINVAL;
   if (!y && !ybf) return QGEMV_EINVAL;
   if (x && !aligned16(x)) return QGEMV_EALIGN;
@@ -892,7 +921,7 @@ int run_gemv(int fmt, const void* wq, const void* ws, const void* x, const float
     if (cus < 1) return QGEMV_EHIP;
     if (!aligned16(fz->workspace) || ((uintptr_t)fz->workspace & 255u)) return QGEMV_EALIGN;
     if (fz->workspace_bytes < (size_t)split_bytes(cus)) return QGEMV_EWORKSPACE;
-    if (!norm && !inv) plan_split(fmt, ls, swiglu, a.out_tiles, g.KS, cus, a);
+    if (!norm && !inv && N <= 8) plan_split(fmt, ls, swiglu, a.out_tiles, g.KS, cus, a);
     a.pflag = (uint32_t*)fz->workspace;
     a.part = (float*)((uint8_t*)fz->workspace + split_flag_bytes(cus));
   }

@@ -14,7 +14,8 @@
 // slot. Consecutive scale units (int: 32-column groups; nvfp4: 16-column
 // blocks) go to consecutive slots, so one accumulator keeps S units apart and
 // the per-unit scale step runs once per S units ("cycle") instead of once per
-// unit. S = 16 at N = 1, 8 at N = 2, 4 at N <= 4, 2 at N <= 8. A lane whose
+// unit. S = 16 at N = 1, 8 at N = 2, 4 at N <= 4, 2 at N <= 8, 1 (int formats
+// only) at N <= 16, where every group runs its own scale step. A lane whose
 // row is not in a unit's slot gets its offset moved by the slot difference
 // times 2^25 (activations stay below 2^25 bytes), so the buffer range check
 // returns zeros without a memory access. Rows of absent tokens start at
@@ -42,6 +43,7 @@ struct Cyc {
   static constexpr int T = 16 / S;                          // tokens per slot
   static constexpr int UNITS_PER_GROUP = FMT == NVFP4 ? 2 : 1;
   static constexpr int GROUPS = S / UNITS_PER_GROUP;        // groups per cycle (>= 1)
+  static_assert(GROUPS >= 1, "NVFP4 needs two slots per group (N <= 8)");
   static constexpr int KSTEPS = GROUPS >= 4 ? GROUPS / 4 : 1;   // k-steps per cycle
   static constexpr int UNROLL = KSTEPS >= 2 ? KSTEPS : 2;   // k-steps per loop trip (even)
 };
@@ -91,6 +93,8 @@ __device__ __forceinline__ u32x4 load_scales(__amdgpu_buffer_rsrc_t ws, uint32_t
     const uint32_t row = (uint32_t)r * 16u | mask;
     if constexpr (S == 16) {          // groups 16c + 4s + i: record of k-step 4c + s, all four
       v = ld128s(ws, row + (uint32_t)s * 256u, so);
+    } else if constexpr (S == 1) {    // every lane: the four groups of its row's record, pos order
+      v = ld128s(ws, row, so);
     } else if constexpr (S == 8) {    // groups 8c + 2s + (i>>1): record 2c + (s>>1), j = 2(s&1) + (i>>1)
       const uint32_t b = row + (uint32_t)(s >> 1) * 256u;
       v.x = ld32s(ws, b + 4u * (uint32_t)(s & 1), so);          // pos(j) = s & 1 for i < 2
@@ -107,6 +111,10 @@ __device__ __forceinline__ u32x4 load_scales(__amdgpu_buffer_rsrc_t ws, uint32_t
     const uint32_t row = (uint32_t)r * 8u | mask;
     if constexpr (S == 16) {
       const u32x2 t = ld64s(ws, row + (uint32_t)s * 128u, so);
+      v.x = t.x;
+      v.y = t.y;
+    } else if constexpr (S == 1) {    // the row's four fp16 scales, pos order
+      const u32x2 t = ld64s(ws, row, so);
       v.x = t.x;
       v.y = t.y;
     } else if constexpr (S == 8) {
@@ -169,6 +177,10 @@ __device__ __forceinline__ void flush(f32x4& acc, const f32x4& D, const f32x4& D
   if constexpr (FMT == INT4 || FMT == INT5) {
     uint32_t w[4];
     if constexpr (S == 16) { w[0] = sc.x; w[1] = sc.z; w[2] = sc.y; w[3] = sc.w; }      // pos(i)
+    else if constexpr (S == 1) {      // group c of the k-step, every A row: word pos(c)
+      const uint32_t wc = c == 0 ? sc.x : c == 1 ? sc.z : c == 2 ? sc.y : sc.w;
+      w[0] = w[1] = w[2] = w[3] = wc;
+    }
     else if constexpr (S == 8) { w[0] = w[1] = sc.x; w[2] = w[3] = sc.y; }
     else if constexpr (S == 4) { w[0] = w[1] = w[2] = w[3] = sc.x; }
     else { w[0] = w[1] = w[2] = w[3] = (c == 0 ? sc.x : sc.y); }
@@ -182,6 +194,10 @@ __device__ __forceinline__ void flush(f32x4& acc, const f32x4& D, const f32x4& D
   } else if constexpr (FMT == INT8) {
     float d[4];
     if constexpr (S == 16) { d[0] = f16_lo(sc.x); d[1] = f16_lo(sc.y); d[2] = f16_hi(sc.x); d[3] = f16_hi(sc.y); }
+    else if constexpr (S == 1) {      // group c: fp16 at pos(c)
+      const float dc = c == 0 ? f16_lo(sc.x) : c == 1 ? f16_lo(sc.y) : c == 2 ? f16_hi(sc.x) : f16_hi(sc.y);
+      d[0] = d[1] = d[2] = d[3] = dc;
+    }
     else if constexpr (S == 8) { d[0] = d[1] = f16_lo(sc.x); d[2] = d[3] = f16_lo(sc.y); }
     else if constexpr (S == 4) { d[0] = d[1] = d[2] = d[3] = f16_lo(sc.x); }
     else { d[0] = d[1] = d[2] = d[3] = (c == 0 ? f16_lo(sc.x) : f16_hi(sc.x)); }

@@ -57,7 +57,11 @@
  *   - Host entry points (pack) take host pointers and need no GPU.
  *   - Pointers to packed weights, scales and activations must be 16-byte
  *     aligned (QGEMV_EALIGN otherwise); float outputs 4-byte aligned.
- *   - Limits: 1 <= N <= 8 (QGEMV_EUNSUPPORTED otherwise), K % 32 == 0,
+ *   - Limits: 1 <= N <= 16 for the int formats on qgemv / qgemv_swiglu /
+ *     qgemv_ex / qgemv_swiglu_ex (9 to 16 tokens share one MFMA operand
+ *     slot: verify windows of speculative decoding, NInfer article, section
+ *     3); N <= 8 for NVFP4, the RMSNorm prologue, the batch-invariant order
+ *     and the MoE entry points (QGEMV_EUNSUPPORTED otherwise); K % 32 == 0,
  *     M >= 1, packed matrix under 4 GiB.
  */
 #ifndef QGEMV_H
