@@ -17,9 +17,10 @@ Also reported on the same JSON line:
                 its average launch duration from HIP events on the launch
                 stream around batches of back-to-back launches (median batch)
   nvfp4_layer   the same layer in NVFP4 at N = 1, 2, 4, 8
-  per_format    qgemv on [17408][5120] for each format at N = 1, 2, 4, 8, and
-                qgemv_mx (MXFP4 / MXFP8 weights, MXFP8 activations) at
-                N = 1, 2, 4, 8, 16, alone and after qgemv_act_quant
+  per_format    qgemv on [17408][5120] for each format at N = 1, 2, 4, 8 (and
+                16 for the int formats), and qgemv_mx (MXFP4 / MXFP8
+                weights, MXFP8 activations) at N = 1, 2, 4, 8, 16, 32, alone
+                and after qgemv_act_quant
   moe           qgemv_moe on the 128-expert, top-8 workload at N = 1 and 8
   probe         the plain streaming-read kernel on the same rotation
   cpu_baseline  the CPU oracle on a bounded sample of the layer
@@ -349,7 +350,7 @@ def extras(qg, torch, dev, stream, layers, args, wsp):
     log("nvfp4_layer", res["nvfp4_layer"])
 
     # the same layer in MXFP4 on the block-scaled MFMA: each projection's bf16
-    # input quantised to MXFP8 on the device first (qgemv_act_quant), N = 1, 8, 16
+    # input quantised to MXFP8 on the device first (qgemv_act_quant), N = 1, 8, 16, 32
     mx_host = {}
     for name, M_, K_, _ in LAYER:
         rng_l = synthetic.rng_for(0, 3, 2, M_)
@@ -359,7 +360,7 @@ def extras(qg, torch, dev, stream, layers, args, wsp):
     mx_w = sum(v[0].size + v[1].size for v in mx_host.values())
     del mx_host
     mxr = {}
-    for n in (1, 8, 16):
+    for n in (1, 8, 16, 32):
         rng_x = synthetic.rng_for(0, 3, 3, n)
         xn = torch.from_numpy(synthetic.activations(rng_x, n, 5120)).to(dev)
         xdn = torch.from_numpy(synthetic.activations(rng_x, n, 17408)).to(dev)
@@ -430,7 +431,7 @@ def extras(qg, torch, dev, stream, layers, args, wsp):
     del graph
     log("mlp_chain", res["mlp_chain"])
 
-    # per format on [17408][5120], N = 1, 2, 4, 8 (MX: also 16), rotated over >= 1 GB
+    # per format on [17408][5120], N = 1, 2, 4, 8 (int formats: also 16; MX: 16, 32), rotated over >= 1 GB
     M, K = 17408, 5120
     rng = synthetic.rng_for(0, 3, M)
     W = synthetic.weights(rng, M, K)
@@ -445,7 +446,8 @@ def extras(qg, torch, dev, stream, layers, args, wsp):
         ms = timeit(lambda i: qg.qgemv_probe_read(d[i % copies][0], wq.size // 16 * 16, sink), 60)
         probe_gbs = (wq.size // 16 * 16) / (ms * 1e-3) / 1e9
         pf[fmt]["probe_GB/s"] = round(probe_gbs, 1)
-        for n in ((1, 2, 4, 8, 16) if fmt.startswith("mx") else (1, 2, 4, 8)):
+        ns = (1, 2, 4, 8, 16, 32) if fmt.startswith("mx") else ((1, 2, 4, 8) if fmt == "nvfp4" else (1, 2, 4, 8, 16))
+        for n in ns:
             xb = torch.from_numpy(synthetic.activations(rng, n, K, 0.01)).to(dev)
             yy = torch.empty((n, M), dtype=torch.float32, device=dev)
             if fmt.startswith("mx"):

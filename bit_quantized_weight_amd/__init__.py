@@ -273,7 +273,7 @@ def act_quant(x, codes, scales, N: int, K: int, stream=None) -> None:
 
 def qgemv_mx(fmt, wq, ws, xq, xs, y, M: int, K: int, N: int, residual=None, stream=None) -> None:
     """MX GEMV: MXFP8 / MXFP4 weights times MXFP8 activations (from
-    act_quant) on the block-scaled MFMA; y [N][M] fp32, N <= 16."""
+    act_quant) on the block-scaled MFMA; y [N][M] fp32, N <= 32."""
     _check(load().qgemv_mx(_fmt(fmt), _ptr(wq), _ptr(ws), _ptr(xq), _ptr(xs), _ptr(residual), _ptr(y), M, K, N,
                            _stream(stream)), "qgemv_mx")
 

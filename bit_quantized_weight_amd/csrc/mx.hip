@@ -92,28 +92,34 @@ struct MxArgs {
   int up_tile0;           // SwiGLU: row tile of the first up row (gate rows come first)
 };
 
-// operands of one k-step: activations (shared by the tiles) and NT weight tiles
-template <int FMT, int NT>
+// operands of one k-step: activations of TB blocks of 16 tokens (shared by
+// the tiles) and NT weight tiles
+template <int FMT, int NT, int TB>
 struct MxStep {
-  u32x4 a0, a1;
-  uint32_t sa;
+  u32x4 a0[TB], a1[TB];
+  uint32_t sa[TB];
   u32x4 b0[NT], b1[NT];
   uint32_t sb[NT];
 };
 
-template <int FMT, int NT>
-__device__ __forceinline__ void mx_load(MxStep<FMT, NT>& st, const MxArgs& a, __amdgpu_buffer_rsrc_t wq,
+template <int FMT, int NT, int TB>
+__device__ __forceinline__ void mx_load(MxStep<FMT, NT, TB>& st, const MxArgs& a, __amdgpu_buffer_rsrc_t wq,
                                         __amdgpu_buffer_rsrc_t ws, __amdgpu_buffer_rsrc_t xq,
                                         __amdgpu_buffer_rsrc_t xs, const int (&tile)[NT], int k, int ks1,
-                                        uint32_t xrow, uint32_t srow, int lane) {
+                                        const uint32_t (&xrow)[TB], const uint32_t (&srow)[TB], int lane) {
   const int g = lane >> 4;
   const bool ok = k < ks1;
   const int col = k * 128 + 16 * g;
   // activations: K tail chunks and k-steps past the range read as zeros
   // (absent tokens have bases of 2^31 or more; OR-ing the mask keeps them there)
-  st.a0 = ld128s(xq, (xrow + (uint32_t)(16 * g)) | ((ok && col < a.K) ? 0u : kOOB), (uint32_t)k * 128u);
-  st.a1 = ld128s(xq, (xrow + (uint32_t)(64 + 16 * g)) | ((ok && col + 64 < a.K) ? 0u : kOOB), (uint32_t)k * 128u);
-  st.sa = ld8s(xs, (srow + (uint32_t)g) | ((ok && 4 * k + g < a.G) ? 0u : kOOB), (uint32_t)k * 4u);
+  const uint32_t m0 = (ok && col < a.K) ? 0u : kOOB, m1 = (ok && col + 64 < a.K) ? 0u : kOOB;
+  const uint32_t ms = (ok && 4 * k + g < a.G) ? 0u : kOOB;
+#pragma unroll
+  for (int b = 0; b < TB; ++b) {
+    st.a0[b] = ld128s(xq, (xrow[b] + (uint32_t)(16 * g)) | m0, (uint32_t)k * 128u);
+    st.a1[b] = ld128s(xq, (xrow[b] + (uint32_t)(64 + 16 * g)) | m1, (uint32_t)k * 128u);
+    st.sa[b] = ld8s(xs, (srow[b] + (uint32_t)g) | ms, (uint32_t)k * 4u);
+  }
   const uint32_t bad = ok ? 0u : kOOB;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
@@ -133,24 +139,28 @@ __device__ __forceinline__ i32x8 join8(const u32x4& lo, const u32x4& hi) {
   return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
-template <int FMT, int NT>
-__device__ __forceinline__ void mx_mma(f32x4 (&acc)[NT], const MxStep<FMT, NT>& st) {
-  const i32x8 A = join8(st.a0, st.a1);
+template <int FMT, int NT, int TB>
+__device__ __forceinline__ void mx_mma(f32x4 (&acc)[NT][TB], const MxStep<FMT, NT, TB>& st) {
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const i32x8 B = join8(st.b0[t], st.b1[t]);
-    // A: FP8 E4M3 (format 0); B: FP8 E4M3 (0) or FP4 E2M1 (4)
-    acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, acc[t], 0, FMT == MXFP8 ? 0 : 4, 0,
-                                                              (int)st.sa, 0, (int)st.sb[t]);
+#pragma unroll
+    for (int b = 0; b < TB; ++b) {
+      // A: FP8 E4M3 (format 0); B: FP8 E4M3 (0) or FP4 E2M1 (4)
+      acc[t][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(join8(st.a0[b], st.a1[b]), B, acc[t][b], 0,
+                                                                   FMT == MXFP8 ? 0 : 4, 0, (int)st.sa[b], 0,
+                                                                   (int)st.sb[t]);
+    }
   }
 }
 
 // Workgroup = NT row tiles (SwiGLU: a gate tile and its up tile); its W
 // waves split the k-steps; the waves' partial sums meet in LDS and are added
-// in wave order (reproducible).
-template <int FMT, int NT, bool SWIGLU>
+// in wave order (reproducible). TB blocks of 16 tokens (N <= 16 TB) share
+// every weight operand: one MFMA per tile, block and k-step.
+template <int FMT, int NT, bool SWIGLU, int TB>
 __global__ __launch_bounds__(512) void k_mxgemv(MxArgs a) {
-  extern __shared__ __attribute__((aligned(16))) float red[];   // [W][NT][64 lanes][4]
+  extern __shared__ __attribute__((aligned(16))) float red[];   // [W][NT][TB][64 lanes][4]
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
   const int W = blockDim.x >> 6;
@@ -167,47 +177,58 @@ __global__ __launch_bounds__(512) void k_mxgemv(MxArgs a) {
     const int ot = min((int)blockIdx.x * TO + (SWIGLU ? 0 : t), a.out_tiles - 1);
     tile[t] = (SWIGLU && t == 1) ? a.up_tile0 + ot : ot;
   }
-  // A row r = token r: rows past N start out of range
-  const uint32_t xrow = r < a.N ? (uint32_t)(r * a.K) : kOOB;
-  const uint32_t srow = r < a.N ? (uint32_t)(r * a.G) : kOOB;
-  f32x4 acc[NT];
+  // A row r of block b = token 16 b + r: rows past N start out of range
+  uint32_t xrow[TB], srow[TB];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int b = 0; b < TB; ++b) {
+    const int tk = 16 * b + r;
+    xrow[b] = tk < a.N ? (uint32_t)(tk * a.K) : kOOB;
+    srow[b] = tk < a.N ? (uint32_t)(tk * a.G) : kOOB;
+  }
+  f32x4 acc[NT][TB];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int b = 0; b < TB; ++b) acc[t][b] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int ks0 = wave * a.ks_per_wave;
   const int ks1 = min(a.KS, ks0 + a.ks_per_wave);
   if (ks0 < ks1) {
     // software pipeline: two k-steps in flight while one is multiplied
-    MxStep<FMT, NT> s0, s1, s2;
-    mx_load<FMT, NT>(s0, a, wq, ws, xq, xs, tile, ks0, ks1, xrow, srow, lane);
-    mx_load<FMT, NT>(s1, a, wq, ws, xq, xs, tile, ks0 + 1, ks1, xrow, srow, lane);
+    MxStep<FMT, NT, TB> s0, s1, s2;
+    mx_load<FMT, NT, TB>(s0, a, wq, ws, xq, xs, tile, ks0, ks1, xrow, srow, lane);
+    mx_load<FMT, NT, TB>(s1, a, wq, ws, xq, xs, tile, ks0 + 1, ks1, xrow, srow, lane);
     for (int k = ks0; k < ks1; k += 3) {
-      mx_load<FMT, NT>(s2, a, wq, ws, xq, xs, tile, k + 2, ks1, xrow, srow, lane);
-      mx_mma<FMT, NT>(acc, s0);
+      mx_load<FMT, NT, TB>(s2, a, wq, ws, xq, xs, tile, k + 2, ks1, xrow, srow, lane);
+      mx_mma<FMT, NT, TB>(acc, s0);
       if (k + 1 >= ks1) break;
-      mx_load<FMT, NT>(s0, a, wq, ws, xq, xs, tile, k + 3, ks1, xrow, srow, lane);
-      mx_mma<FMT, NT>(acc, s1);
+      mx_load<FMT, NT, TB>(s0, a, wq, ws, xq, xs, tile, k + 3, ks1, xrow, srow, lane);
+      mx_mma<FMT, NT, TB>(acc, s1);
       if (k + 2 >= ks1) break;
-      mx_load<FMT, NT>(s1, a, wq, ws, xq, xs, tile, k + 4, ks1, xrow, srow, lane);
-      mx_mma<FMT, NT>(acc, s2);
+      mx_load<FMT, NT, TB>(s1, a, wq, ws, xq, xs, tile, k + 4, ks1, xrow, srow, lane);
+      mx_mma<FMT, NT, TB>(acc, s2);
     }
   }
-  // lane l holds D[token 4 (l / 16) + i][row l % 16]
+  // lane l holds D[token 16 b + 4 (l / 16) + i][row l % 16]
 #pragma unroll
   for (int t = 0; t < NT; ++t)
-    *reinterpret_cast<f32x4*>(red + ((size_t)(wave * NT + t) * 64 + lane) * 4) = acc[t];
+#pragma unroll
+    for (int b = 0; b < TB; ++b)
+      *reinterpret_cast<f32x4*>(red + ((size_t)((wave * NT + t) * TB + b) * 64 + lane) * 4) = acc[t][b];
   __syncthreads();
-  for (int o = threadIdx.x; o < TO * 256; o += blockDim.x) {
-    const int t = o >> 8, tok = (o >> 4) & 15, row = o & 15;
+  for (int o = threadIdx.x; o < TO * TB * 256; o += blockDim.x) {
+    const int t = o / (TB * 256), rem = o - t * TB * 256;
+    const int b = rem >> 8, tl = (rem >> 4) & 15, row = rem & 15;
+    const int tok = 16 * b + tl;
     const int ot = (int)blockIdx.x * TO + t;
     const int col = ot * 16 + row;
     if (tok >= a.N || ot >= a.out_tiles || col >= a.M) continue;
-    const int idx = ((tok >> 2) * 16 + row) * 4 + (tok & 3);
+    const int idx = b * 256 + ((tl >> 2) * 16 + row) * 4 + (tl & 3);
     float v = 0.f;
-    for (int w = 0; w < W; ++w) v += red[(size_t)(w * NT + t) * 256 + idx];
+    for (int w = 0; w < W; ++w) v += red[(size_t)(w * NT + t) * TB * 256 + idx];
     const size_t at = (size_t)tok * a.M + col;
     if constexpr (SWIGLU) {
       float u = 0.f;
-      for (int w = 0; w < W; ++w) u += red[(size_t)(w * NT + 1) * 256 + idx];
+      for (int w = 0; w < W; ++w) u += red[(size_t)(w * NT + 1) * TB * 256 + idx];
       v = v / (1.0f + expf(-v)) * u;
     } else {
       if (a.res) v += a.res[at];
@@ -306,14 +327,20 @@ MxShape mx_shape_pairs(int fmt, int64_t pairs, int64_t KS, int N) {
   return s;
 }
 
-template <int FMT, int NT, bool SWIGLU = false>
-hipError_t launch_mx(const MxArgs& a, const MxShape& s, hipStream_t stream) {
+template <int FMT, int NT, bool SWIGLU, int TB>
+hipError_t launch_mx_tb(const MxArgs& a, const MxShape& s, hipStream_t stream) {
   const int TO = SWIGLU ? 1 : NT;
   const dim3 grid((unsigned)((a.out_tiles + TO - 1) / TO));
   const dim3 block((unsigned)(64 * s.waves));
-  const size_t lds = (size_t)s.waves * NT * 256 * sizeof(float);
-  hipLaunchKernelGGL((k_mxgemv<FMT, NT, SWIGLU>), grid, block, lds, stream, a);
+  const size_t lds = (size_t)s.waves * NT * TB * 256 * sizeof(float);
+  hipLaunchKernelGGL((k_mxgemv<FMT, NT, SWIGLU, TB>), grid, block, lds, stream, a);
   return hipGetLastError();
+}
+
+// one or two blocks of 16 tokens
+template <int FMT, int NT, bool SWIGLU = false>
+hipError_t launch_mx(const MxArgs& a, const MxShape& s, hipStream_t stream) {
+  return a.N > 16 ? launch_mx_tb<FMT, NT, SWIGLU, 2>(a, s, stream) : launch_mx_tb<FMT, NT, SWIGLU, 1>(a, s, stream);
 }
 
 }  // namespace
@@ -355,7 +382,7 @@ int run_mx(int fmt, const void* wq, const void* ws, const uint8_t* xq, const uin
   if (!wq || !ws || !xq || !xs || !y) return QGEMV_EINVAL;
   if (Mout < 1 || K < 32 || Mpacked > (1 << 24)) return QGEMV_EINVAL;
   if (K % 32) return QGEMV_EALIGN;
-  if (N < 1 || N > 16) return QGEMV_EUNSUPPORTED;
+  if (N < 1 || N > 32) return QGEMV_EUNSUPPORTED;
   if (!al16(wq) || !al16(ws) || !al16(xq) || !al4(y) || (residual && !al4(residual))) return QGEMV_EALIGN;
   Geom g;
   if (!geom(fmt, Mpacked, K, &g)) return QGEMV_EINVAL;

@@ -92,7 +92,7 @@ typedef enum {
   QGEMV_ERANGE = -4,       /* a scale field overflows its encoding */
   QGEMV_EWORKSPACE = -5,   /* workspace missing or too small */
   QGEMV_EHIP = -6,         /* the HIP runtime reported an error at launch */
-  QGEMV_EUNSUPPORTED = -7  /* a size outside the supported range (e.g. N > 8) */
+  QGEMV_EUNSUPPORTED = -7  /* a size outside the supported range (e.g. N > 16) */
 } qgemv_status;
 
 /* Text for a status code (static storage). */
@@ -326,7 +326,7 @@ int qgemv_act_quant(const void* x, int N, int64_t K, uint8_t* codes, uint8_t* sc
  * in a fixed order (reproducible run to run).
  *   wq, ws: packed weights; xq [N][K] codes (16-byte aligned), xs [N][K/32]
  *   E8M0 bytes; residual [N][M] fp32 or NULL (may equal y); y [N][M] fp32.
- * 1 <= N <= 16. */
+ * 1 <= N <= 32 (two blocks of 16 tokens share each weight operand). */
 int qgemv_mx(int fmt, const void* wq, const void* ws, const uint8_t* xq, const uint8_t* xs,
              const float* residual, float* y, int64_t M, int64_t K, int N, hipStream_t stream);
 

@@ -126,7 +126,7 @@ def _ref(fmt, wq, ws, xb, M, K, residual=None):
 
 @pytest.mark.parametrize("fmt", MX)
 @pytest.mark.parametrize("M,K", [(64, 512), (37, 160), (16, 32), (300, 1024), (100, 5120), (48, 17408 // 4)])
-@pytest.mark.parametrize("N", [1, 2, 5, 8, 16])
+@pytest.mark.parametrize("N", [1, 2, 5, 8, 16, 17, 32])
 def test_mx_gemv_parity(fmt, M, K, N):
     log("mx gemv", fmt, M, K, N)
     wq, ws, xb = _mx_case(fmt, M, K, N, seed=N)
@@ -152,7 +152,7 @@ def test_mx_residual_aliasing_and_determinism(fmt):
 
 
 @pytest.mark.parametrize("fmt", MX)
-@pytest.mark.parametrize("I,K,N", [(64, 512, 1), (48, 160, 3), (256, 2048, 8), (128, 1024, 16)])
+@pytest.mark.parametrize("I,K,N", [(64, 512, 1), (48, 160, 3), (256, 2048, 8), (128, 1024, 16), (80, 640, 29)])
 def test_mx_swiglu_parity(fmt, I, K, N):
     log("mx swiglu", fmt, I, K, N)
     wq, ws, xb = _mx_case(fmt, 2 * I, K, N, seed=I + N)
@@ -191,7 +191,8 @@ def test_mx_swiglu_full_size_sampled_rows():
 
 
 @pytest.mark.parametrize("fmt,M,K,N", [("mxfp8", 17408, 5120, 1), ("mxfp4", 17408, 5120, 8),
-                                       ("mxfp8", 5120, 17408, 16), ("mxfp4", 7168, 5120, 16)])
+                                       ("mxfp8", 5120, 17408, 16), ("mxfp4", 7168, 5120, 16),
+                                       ("mxfp8", 17408, 5120, 32)])
 def test_mx_full_size_sampled_rows(fmt, M, K, N):
     log("mx full", fmt, M, K, N)
     rng = synthetic.rng_for(0, 34, M, K)

@@ -247,12 +247,12 @@ def test_mx_validation_codes():
                           None)
     assert mx(fmt=1) == -2 and mx(fmt=7) == -2
     assert mx(wq=None) == -1 and mx(xs=None) == -1 and mx(y=None) == -1
-    assert mx(N=0) == -7 and mx(N=17) == -7
+    assert mx(N=0) == -7 and mx(N=33) == -7
     assert mx(K=48) == -3 and mx(K=16) == -1 and mx(M=0) == -1
     assert mx(xq=ODD) == -3 and mx(wq=ODD) == -3 and mx(y=FAKE + 2) == -3
     sw = lambda **kw: L.qgemv_mx_swiglu(kw.get("fmt", 5), FAKE, FAKE, FAKE, FAKE, FAKE, kw.get("I", 64),
                                          kw.get("K", 128), kw.get("N", 1), None)
-    assert sw(fmt=3) == -2 and sw(I=0) == -1 and sw(I=24) == -3 and sw(N=17) == -7 and sw(K=40) == -3
+    assert sw(fmt=3) == -2 and sw(I=0) == -1 and sw(I=24) == -3 and sw(N=33) == -7 and sw(K=40) == -3
     # MX weights are rejected by the bf16-activation entry points
     assert _gemv(fmt=5) == -2 and _gemv(fmt=6) == -2
     aq = lambda **kw: L.qgemv_act_quant(kw.get("x", FAKE), kw.get("N", 1), kw.get("K", 64), kw.get("c", FAKE),
