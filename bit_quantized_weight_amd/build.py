@@ -54,21 +54,32 @@ def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     objs = []
     common = ["-O3", "-std=c++17", "-fPIC", "-I" + INCLUDE, "-I" + CSRC]
+    cmds = []
     for src in HIP_SOURCES:
         path = os.path.join(CSRC, src)
         if not os.path.exists(path):
             continue
         obj = os.path.join(BUILD, src + ".o")
-        _run([hipcc, "--offload-arch=" + ARCH, *common,
-              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", *EXTRA_FLAGS.get(src, []),
-              "-c", path, "-o", obj])
+        cmds.append([hipcc, "--offload-arch=" + ARCH, *common,
+                     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", *EXTRA_FLAGS.get(src, []),
+                     "-c", path, "-o", obj])
         objs.append(obj)
     for src in HOST_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
-        _run([hipcc, "-x", "c++", *common, "-I" + _rocm_include(), "-D__HIP_PLATFORM_AMD__=1",
-              "-ffp-contract=off", "-fno-fast-math",
-              "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([hipcc, "-x", "c++", *common, "-I" + _rocm_include(), "-D__HIP_PLATFORM_AMD__=1",
+                     "-ffp-contract=off", "-fno-fast-math",
+                     "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
+    # the translation units are independent: compile them side by side
+    procs = [(c, subprocess.Popen(c, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)) for c in cmds]
+    failed = None
+    for c, p in procs:
+        out, _ = p.communicate()
+        if p.returncode != 0 and failed is None:
+            sys.stderr.write(out)
+            failed = c
+    if failed:
+        raise RuntimeError("build step failed: " + " ".join(failed))
     tmp = LIB + ".tmp"
     _run([hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs, "-lpthread"])
     os.replace(tmp, LIB)
