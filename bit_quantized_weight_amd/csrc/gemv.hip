@@ -119,23 +119,26 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// tokens per tile in the LDS reduction area: 16 with one slot, else 8
-template <int S>
-__host__ __device__ constexpr int red_tokens() { return S == 1 ? 16 : 8; }
+// tokens per tile in the LDS reduction area: 16 per token block with one
+// slot, else 8
+template <int S, int TB = 1>
+__host__ __device__ constexpr int red_tokens() { return S == 1 ? 16 * TB : 8; }
 
 // Combine a lane's accumulators into per-(token, row) totals and write them
 // to LDS as red[((wave*NT + t)*TK + token)*16 + row] (TK = red_tokens<S>());
 // fixed order throughout.
-template <int S, int NT>
-__device__ __forceinline__ void reduce_to_lds(f32x4 (&acc)[NT], float* red, int wave, int lane) {
+template <int S, int NT, int TB = 1>
+__device__ __forceinline__ void reduce_to_lds(f32x4 (&acc)[NT * TB], float* red, int wave, int lane) {
   const int r = lane & 15, s = lane >> 4;
-  constexpr int RB = red_tokens<S>() * 16;
+  constexpr int RB = red_tokens<S, TB>() * 16;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     float* p = red + (size_t)(wave * NT + t) * RB;
-    if constexpr (S == 1) {           // one slot: register i = token 4s + i
+    if constexpr (S == 1) {           // one slot: register i of block b = token 16 b + 4 s + i
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p[(4 * s + i) * 16 + r] = acc[t][i];
+      for (int b = 0; b < TB; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[(16 * b + 4 * s + i) * 16 + r] = acc[t * TB + b][i];
     } else if constexpr (S == 16) {          // every register a different slot, token 0
       float v = (acc[t][0] + acc[t][1]) + (acc[t][2] + acc[t][3]);
       v += __shfl_xor(v, 16);
@@ -248,8 +251,11 @@ __host__ __device__ constexpr int ring_stride() { return (16 / S) * 256 + 16; }
 // k-steps per weight prefetch buffer. XM: activation path.
 // NORM: the RMSNorm prologue (a separate instantiation, so kernels without
 // it keep their register budget)
-template <int FMT, int NT, int S, int KPS, bool SWIGLU, int XM, bool NORM>
+// TB: blocks of 16 tokens (one slot only; 17 to 32 tokens take two, which
+// share every decoded weight operand)
+template <int FMT, int NT, int S, int KPS, bool SWIGLU, int XM, bool NORM, int TB = 1>
 __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
+  static_assert(TB == 1 || (XM == XM_LOAD && !NORM), "token blocks load their activations directly");
   extern __shared__ __attribute__((aligned(16))) float red[];  // [W][NT][8][16], then the LDS activations
   __shared__ float s_ss[8][8];                                  // RMSNorm: [wave][token] sums of squares
   const int lane = threadIdx.x & 63;
@@ -258,7 +264,7 @@ __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
   const int r = lane & 15, s = lane >> 4;
   constexpr int TO = SWIGLU ? NT / 2 : NT;
   constexpr int T = 16 / S;
-  constexpr int TK = red_tokens<S>();     // tokens per tile in the reduction area
+  constexpr int TK = red_tokens<S, TB>(); // tokens per tile in the reduction area
   constexpr int RB = TK * 16;             // floats per (wave, tile) there
   using C = Cyc<FMT, S>;
 
@@ -282,7 +288,7 @@ __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
     tile[t] = (SWIGLU && t >= TO) ? a.up_tile0 + ot : ot;
   }
 
-  f32x4 acc[NT];
+  f32x4 acc[NT * TB];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   int kb0 = 0, kb1 = a.KS, kpw = a.ks_per_wave;
@@ -400,15 +406,35 @@ __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
     }
   } else {
     // the lane's base offset carries its slot term; tokens >= N start past the buffer
-    const uint32_t xbase = (a_tok < a.N ? (uint32_t)(a_tok * a.K + 8 * s) * 2u : kAbsentRow) + lane_slot_term<FMT, S>(lane);
-    auto aload = [&](int g, uint32_t adj) -> bf16x8 {
-      return __builtin_bit_cast(bf16x8, ld128s(xr, xbase + adj, (uint32_t)g * 64u));
-    };
-    auto acts = [&](bf16x8 (&A)[4], int k, int pos) { load_acts<FMT, S>(A, k, ks1, a.G, pos % C::KSTEPS, aload); };
-    kloop<FMT, NT, S, KPS, 1>(wq, ws, tile, a.KS, ks0, ks1, a.hi_offset, acts, acc);
+    if constexpr (TB == 1) {
+      const uint32_t xbase = (a_tok < a.N ? (uint32_t)(a_tok * a.K + 8 * s) * 2u : kAbsentRow) + lane_slot_term<FMT, S>(lane);
+      auto aload = [&](int g, uint32_t adj) -> bf16x8 {
+        return __builtin_bit_cast(bf16x8, ld128s(xr, xbase + adj, (uint32_t)g * 64u));
+      };
+      auto acts = [&](bf16x8 (&A)[4], int k, int pos) { load_acts<FMT, S>(A, k, ks1, a.G, pos % C::KSTEPS, aload); };
+      kloop<FMT, NT, S, KPS, 1>(wq, ws, tile, a.KS, ks0, ks1, a.hi_offset, acts, acc);
+    } else {
+      // block b's A row r = token 16 b + r (one slot: no slot term)
+      uint32_t xbase[TB];
+#pragma unroll
+      for (int b = 0; b < TB; ++b) {
+        const int tk = 16 * b + a_tok;
+        xbase[b] = tk < a.N ? (uint32_t)(tk * a.K + 8 * s) * 2u : kAbsentRow;
+      }
+      auto acts = [&](bf16x8 (&A)[TB][4], int k, int pos) {
+#pragma unroll
+        for (int b = 0; b < TB; ++b) {
+          auto aload = [&](int g, uint32_t adj) -> bf16x8 {
+            return __builtin_bit_cast(bf16x8, ld128s(xr, xbase[b] + adj, (uint32_t)g * 64u));
+          };
+          load_acts<FMT, S>(A[b], k, ks1, a.G, pos % C::KSTEPS, aload);
+        }
+      };
+      kloop<FMT, NT, S, KPS, 1, TB>(wq, ws, tile, a.KS, ks0, ks1, a.hi_offset, acts, acc);
+    }
   }
 
-  reduce_to_lds<S, NT>(acc, red, wave, lane);
+  reduce_to_lds<S, NT, TB>(acc, red, wave, lane);
   __syncthreads();
 
   const int nslot = a.frag - 1;
@@ -599,7 +625,7 @@ struct LaunchShape {
   int kps;      // k-steps per weight prefetch buffer
 };
 
-int slots_for(int N) { return N == 1 ? 16 : N == 2 ? 8 : N <= 4 ? 4 : N <= 8 ? 2 : 1; }
+int slots_for(int N) { return N == 1 ? 16 : N == 2 ? 8 : N <= 4 ? 4 : N <= 8 ? 2 : 1; }   // N <= 32
 
 // k-steps per cycle for (format, slots): wave ranges are multiples of it
 int cycle_ksteps(int fmt, int S) {
@@ -779,10 +805,12 @@ hipError_t launch_s(const GemvArgs& a0, const LaunchShape& ls, bool swiglu, hipS
   const int U = 2 * KPS;   // k-steps per trip of the k-loop
   a.x_nks = (ls.kpw + U - 1) / U * U + 1;
   const size_t rec = (size_t)a.N * 256 + 16;
-  const size_t red = (size_t)ls.waves * NT * red_tokens<S>() * 16 * sizeof(float);
+  const bool two_blocks = S == 1 && a.N > 16;   // 17 to 32 tokens: two blocks of 16
+  const size_t red = (size_t)ls.waves * NT * red_tokens<S>() * (two_blocks ? 2 : 1) * 16 * sizeof(float);
   const size_t whole = (size_t)ls.waves * a.x_nks * rec, ring = (size_t)ls.waves * kRing * ring_stride<S>();
   // (the ring moves at most 8 tokens per record: one slot's 16 load directly)
   int xm = whole <= kMaxLdsActs ? XM_LDS : ((ring <= kMaxLdsActs && S > 1) ? XM_RING : XM_LOAD);
+  if (two_blocks) xm = XM_LOAD;
   if (a.nsrc && xm == XM_LOAD) {         // the RMSNorm prologue stages its activations in LDS
     if (red + ring > kMaxLdsNorm) return hipErrorNotSupported;
     xm = XM_RING;
@@ -813,6 +841,11 @@ hipError_t launch_s(const GemvArgs& a0, const LaunchShape& ls, bool swiglu, hipS
     else QG_PICK(false, XM_LOAD, false);
   }
 #undef QG_PICK
+  if constexpr (S == 1 && NT >= 2) {
+    // SwiGLU with 17 to 32 tokens: two token blocks share each decoded weight
+    // operand (the plain GEMV runs two launches instead)
+    if (two_blocks) fn = swiglu ? (KernelFn)k_gemv<FMT, NT, 1, KPS, true, XM_LOAD, false, 2> : nullptr;
+  }
   if (!fn) return hipErrorNotSupported;
   int64_t nwg = blocks;
   if (a.frag > 1) {
@@ -854,7 +887,7 @@ int validate_common(int fmt, const void* wq, const void* ws, int64_t M, int64_t 
   if (!wq || !ws) return QGEMV_EINVAL;
   if (M < 1 || K < 32 || M > (1 << 24)) return QGEMV_EINVAL;
   if (K % 32) return QGEMV_EALIGN;
-  if (N < 1 || N > 16) return QGEMV_EUNSUPPORTED;
+  if (N < 1 || N > 32) return QGEMV_EUNSUPPORTED;
   if (!aligned16(wq) || !aligned16(ws)) return QGEMV_EALIGN;
   if (!geom(fmt, M, K, g)) return QGEMV_EINVAL;
   if (g->wq_bytes >= (1ull << 32) || g->ws_bytes >= (1ull << 32)) return QGEMV_EUNSUPPORTED;
@@ -871,9 +904,22 @@ int run_gemv(int fmt, const void* wq, const void* ws, const void* x, const float
   if (rc) return rc;
   const bool norm = fz && fz->norm_src;
   uint16_t* ybf = fz ? fz->out_bf16 : nullptr;
-  // 9 to 16 tokens use one slot: int formats only (NVFP4 needs two slots per
+  // 9 to 32 tokens use one slot: int formats only (NVFP4 needs two slots per
   // group), no RMSNorm prologue and no batch-invariant order
   if (N > 8 && (fmt == NVFP4 || norm || (fz && (fz->flags & QGEMV_BATCH_INVARIANT)))) return QGEMV_EUNSUPPORTED;
+  if (!swiglu && N > 16) {
+    // plain GEMV: two launches of at most 16 tokens (measured faster than one
+    // launch with two token blocks, whose activation loads per weight byte
+    // double on one-tile workgroups)
+    if (x && !aligned16(x)) return QGEMV_EALIGN;
+    if ((y && !aligned4(y)) || (res && !aligned4(res)) || ((uintptr_t)ybf & 1u)) return QGEMV_EALIGN;
+    qgemv_fusion f2 = fz ? *fz : qgemv_fusion{};
+    int rc2 = run_gemv(fmt, wq, ws, x, res, y, Mout, Mpacked, K, 16, swiglu, fz, stream);
+    if (rc2) return rc2;
+    if (ybf) f2.out_bf16 = ybf + (size_t)16 * Mout;
+    return run_gemv(fmt, wq, ws, x ? (const uint16_t*)x + (size_t)16 * K : nullptr, res ? res + (size_t)16 * Mout : nullptr,
+                    y ? y + (size_t)16 * Mout : nullptr, Mout, Mpacked, K, N - 16, swiglu, fz ? &f2 : nullptr, stream);
+  }
   if (!norm && !x) return QGEMV_EINVAL;
   if (!y && !ybf) return QGEMV_EINVAL;
   if (x && !aligned16(x)) return QGEMV_EALIGN;

@@ -278,10 +278,14 @@ struct NoPrologue {
 // which sits at position pos of its loop trip (a compile-time constant at
 // each call; its cycle position is pos % KSTEPS) — zeros past ks1 or past G;
 // pre() runs once after the first weight loads are issued.
-template <int FMT, int NT, int S, int KPS, int AD, class Acts, class Pre = NoPrologue>
+// TB > 1 (one slot only): TB blocks of 16 tokens share every decoded weight
+// operand; acts then fills A[TB][4] and acc[t * TB + b] holds block b of
+// tile t.
+template <int FMT, int NT, int S, int KPS, int AD, int TB = 1, class Acts, class Pre = NoPrologue>
 __device__ __forceinline__ void kloop(__amdgpu_buffer_rsrc_t wq, __amdgpu_buffer_rsrc_t ws, const int (&tile)[NT],
                                       int KS, int ks0, int ks1, uint32_t hi_offset, const Acts& acts,
-                                      f32x4 (&acc)[NT], const Pre& pre = Pre()) {
+                                      f32x4 (&acc)[NT * TB], const Pre& pre = Pre()) {
+  static_assert(TB == 1 || S == 1, "token blocks need one slot");
   using C = Cyc<FMT, S>;
   constexpr int U = 2 * KPS;                     // k-steps per loop trip (a multiple of C::KSTEPS)
   constexpr int R = AD + 1;                      // activation ring
@@ -289,21 +293,26 @@ __device__ __forceinline__ void kloop(__amdgpu_buffer_rsrc_t wq, __amdgpu_buffer
   static_assert(U % R == 0, "the activation ring must divide the trip");
   const bf16x8 b128 = bf16x8_splat_128();
   Step<FMT, NT, KPS> buf[2];
-  bf16x8 xa[R][4];
+  bf16x8 xa[R][TB][4];
   u32x4 csc[NT];                                 // scale words of the current cycle (KSTEPS > 1)
-  f32x4 D[NT];
-  f32x4 Db = {0.f, 0.f, 0.f, 0.f};
+  f32x4 D[NT * TB];
+  f32x4 Db[TB];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    D[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    csc[t] = u32x4{0u, 0u, 0u, 0u};
-  }
+  for (int t = 0; t < NT; ++t) csc[t] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int t = 0; t < NT * TB; ++t) D[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int b = 0; b < TB; ++b) Db[b] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (ks0 >= ks1) return;
+  auto fetch = [&](bf16x8 (&X)[TB][4], int k, int pos) {
+    if constexpr (TB == 1) acts(X[0], k, pos);
+    else acts(X, k, pos);
+  };
 
   load_weights<FMT, NT, S, KPS, true>(buf[0], wq, ws, tile, KS, ks0, ks1, hi_offset);
   pre();
 #pragma unroll
-  for (int d = 0; d < AD; ++d) acts(xa[d], ks0 + d, d);
+  for (int d = 0; d < AD; ++d) fetch(xa[d], ks0 + d, d);
   for (int base = ks0; base < ks1; base += U) {
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
@@ -318,7 +327,7 @@ __device__ __forceinline__ void kloop(__amdgpu_buffer_rsrc_t wq, __amdgpu_buffer
           if (b == 0) load_weights<FMT, NT, S, KPS, cyc1>(buf[1], wq, ws, tile, KS, base + KPS, ks1, hi_offset);
           else load_weights<FMT, NT, S, KPS, cyc2>(buf[0], wq, ws, tile, KS, base + 2 * KPS, ks1, hi_offset);
         }
-        acts(xa[(kk + AD) % R], ks + AD, (kk + AD) % U);
+        fetch(xa[(kk + AD) % R], ks + AD, (kk + AD) % U);
         if constexpr (C::KSTEPS > 1) {
           if (ckk == 0) {                          // cycle start: its scale words came with this buffer
 #pragma unroll
@@ -338,8 +347,11 @@ __device__ __forceinline__ void kloop(__amdgpu_buffer_rsrc_t wq, __amdgpu_buffer
           const bool first = (gpos % C::GROUPS) == 0;
           const bool last = ((gpos + 1) % C::GROUPS) == 0;
           const int cidx = gpos / C::GROUPS;       // cycle index inside the k-step
-          const bf16x8 A = xa[kk % R][j];
-          if constexpr (FMT == INT4 || FMT == INT5) Db = mfma(A, b128, first ? f32x4{0.f, 0.f, 0.f, 0.f} : Db);
+          if constexpr (FMT == INT4 || FMT == INT5) {
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb)
+              Db[tb] = mfma(xa[kk % R][tb][j], b128, first ? f32x4{0.f, 0.f, 0.f, 0.f} : Db[tb]);
+          }
 #pragma unroll
           for (int t = 0; t < NT; ++t) {
             bf16x8 B;
@@ -354,10 +366,14 @@ __device__ __forceinline__ void kloop(__amdgpu_buffer_rsrc_t wq, __amdgpu_buffer
             } else {
               B = dec_nvfp4(j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w);
             }
-            D[t] = mfma(A, B, first ? f32x4{0.f, 0.f, 0.f, 0.f} : D[t]);
-            if (last) {
-              if constexpr (C::KSTEPS > 1) flush<FMT, S>(acc[t], D[t], Db, csc[t], cidx);
-              else flush<FMT, S>(acc[t], D[t], Db, cur.sc[i][t], cidx);
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) {
+              f32x4& Dt = D[t * TB + tb];
+              Dt = mfma(xa[kk % R][tb][j], B, first ? f32x4{0.f, 0.f, 0.f, 0.f} : Dt);
+              if (last) {
+                if constexpr (C::KSTEPS > 1) flush<FMT, S>(acc[t * TB + tb], Dt, Db[tb], csc[t], cidx);
+                else flush<FMT, S>(acc[t * TB + tb], Dt, Db[tb], cur.sc[i][t], cidx);
+              }
             }
           }
         }

@@ -57,12 +57,13 @@
  *   - Host entry points (pack) take host pointers and need no GPU.
  *   - Pointers to packed weights, scales and activations must be 16-byte
  *     aligned (QGEMV_EALIGN otherwise); float outputs 4-byte aligned.
- *   - Limits: 1 <= N <= 16 for the int formats on qgemv / qgemv_swiglu /
- *     qgemv_ex / qgemv_swiglu_ex (9 to 16 tokens share one MFMA operand
- *     slot: verify windows of speculative decoding, NInfer article, section
- *     3); N <= 8 for NVFP4, the RMSNorm prologue, the batch-invariant order
- *     and the MoE entry points (QGEMV_EUNSUPPORTED otherwise); K % 32 == 0,
- *     M >= 1, packed matrix under 4 GiB.
+ *   - Limits: 1 <= N <= 32 for the int formats on qgemv / qgemv_swiglu /
+ *     qgemv_ex / qgemv_swiglu_ex (9 to 32 tokens share one MFMA operand
+ *     slot per 16: verify windows of speculative decoding, NInfer article,
+ *     section 3; the plain GEMV runs 17 to 32 tokens as two launches of at
+ *     most 16); N <= 8 for NVFP4, the RMSNorm prologue, the batch-invariant
+ *     order and the MoE entry points (QGEMV_EUNSUPPORTED otherwise);
+ *     K % 32 == 0, M >= 1, packed matrix under 4 GiB.
  */
 #ifndef QGEMV_H
 #define QGEMV_H
@@ -92,7 +93,7 @@ typedef enum {
   QGEMV_ERANGE = -4,       /* a scale field overflows its encoding */
   QGEMV_EWORKSPACE = -5,   /* workspace missing or too small */
   QGEMV_EHIP = -6,         /* the HIP runtime reported an error at launch */
-  QGEMV_EUNSUPPORTED = -7  /* a size outside the supported range (e.g. N > 16) */
+  QGEMV_EUNSUPPORTED = -7  /* a size outside the supported range (e.g. N > 32) */
 } qgemv_status;
 
 /* Text for a status code (static storage). */

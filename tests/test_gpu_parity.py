@@ -86,7 +86,7 @@ SHAPES = [(1024, 1024), (37, 160), (16, 32), (100, 5120), (64, 17408 // 4), (48,
 
 @pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("M,K", SHAPES)
-@pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 8, 12, 16])
+@pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 8, 12, 16, 20, 32])
 def test_qgemv_parity(fmt, M, K, N):
     log("gemv", fmt, M, K, N)
     W, xb, wq, ws = make_case(fmt, M, K, N, seed=N)
@@ -200,7 +200,7 @@ def test_batch_invariance(fmt):
 
 @pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("I,K,N", [(64, 512, 1), (48, 160, 3), (256, 2048, 8), (768, 2048, 4), (96, 1024, 16),
-                                   (32, 32768, 11)])
+                                   (32, 32768, 11), (80, 640, 27), (64, 5120, 32)])
 def test_swiglu_parity(fmt, I, K, N):
     if fmt == "nvfp4" and N > 8:
         pytest.skip("NVFP4 takes N <= 8 (rejected with QGEMV_EUNSUPPORTED, checked in test_qgemv_parity)")
@@ -312,7 +312,8 @@ def test_moe_index_bit_exact(N, k, E):
 FULL = [("int4", 7168, 5120, 1), ("int4", 7168, 5120, 8), ("int4", 7168, 5120, 4), ("int5", 5120, 17408, 1),
         ("int5", 5120, 17408, 8), ("nvfp4", 5120, 17408, 4), ("nvfp4", 7168, 5120, 2),
         ("int4", 5120, 17408, 2), ("nvfp4", 5120, 17408, 2), ("int8", 5120, 17408, 2), ("int5", 5120, 17408, 3),
-        ("int5", 17408, 5120, 16), ("int8", 7168, 5120, 12), ("int4", 5120, 17408, 16)] + \
+        ("int5", 17408, 5120, 16), ("int8", 7168, 5120, 12), ("int4", 5120, 17408, 16), ("int4", 17408, 5120, 32),
+        ("int8", 5120, 17408, 24)] + \
        [(f, 17408, 5120, n) for f in ("int4", "int5", "int8", "nvfp4") for n in (1, 2, 4, 8)]
 
 

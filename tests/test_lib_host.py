@@ -154,13 +154,13 @@ def _gemv(**kw):
 def test_qgemv_validation_codes():
     assert _gemv(fmt=0) == -2 and _gemv(fmt=5) == -2
     assert _gemv(wq=None) == -1 and _gemv(x=None) == -1 and _gemv(y=None) == -1
-    assert _gemv(N=0) == -7 and _gemv(N=17) == -7 and _gemv(fmt=4, N=9) == -7   # NVFP4: N <= 8
+    assert _gemv(N=0) == -7 and _gemv(N=33) == -7 and _gemv(fmt=4, N=9) == -7   # NVFP4: N <= 8
     assert _gemv(K=48) == -3 and _gemv(K=0) == -1 and _gemv(M=0) == -1
     assert _gemv(wq=ODD) == -3 and _gemv(x=ODD) == -3 and _gemv(y=FAKE + 2) == -3
     assert _gemv(res=FAKE + 1, y=FAKE) == -3
     L = qg.load(False)
     assert L.qgemv_swiglu(1, FAKE, FAKE, FAKE, FAKE, 24, 128, 1, None) == -3      # I % 16
-    assert L.qgemv_swiglu(1, FAKE, FAKE, FAKE, FAKE, 32, 128, 17, None) == -7
+    assert L.qgemv_swiglu(1, FAKE, FAKE, FAKE, FAKE, 32, 128, 33, None) == -7
     assert L.qgemv_dequant(1, FAKE, FAKE, 16, 40, FAKE, None) == -3
     assert L.qgemv_dequant(7, FAKE, FAKE, 16, 64, FAKE, None) == -2
     assert L.qgemv_probe_read(FAKE, 100, FAKE, None) == -3
