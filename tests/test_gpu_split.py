@@ -154,3 +154,52 @@ def test_split_workspace_errors():
     qg().qgemv_ex(fmt, wqd, wsd, xd, y, M, K, N)
     torch.cuda.synchronize()
     assert torch.equal(y1.view(torch.int32), y.view(torch.int32))
+
+
+def test_split_and_mx_calls_in_a_hip_graph():
+    """Split-remainder calls (whose fragments hand partial sums over through
+    flags that every call clears itself) and an MX quantise + GEMV pair,
+    captured in one HIP graph and replayed with eager work in between: every
+    replay equals the eager result bit for bit, and the workspace's flags are
+    back at zero."""
+    K, I, N = 5120, 17408, 1
+    rng = synthetic.rng_for(0, 14, K)
+    W = synthetic.weights(rng, 2 * I, K)
+    wq, ws = (dev(a, torch) for a in qg().pack("int5", W))
+    mq, ms = (dev(a, torch) for a in qg().pack("mxfp4", W[:I]))
+    x = dev(synthetic.activations(rng, N, K), torch)
+    wsp = qg().split_workspace(torch.device("cuda:0"))
+    h = torch.zeros((N, I), dtype=torch.float32, device="cuda")
+    y = torch.zeros((N, I), dtype=torch.float32, device="cuda")
+    xq = torch.zeros((N, K), dtype=torch.uint8, device="cuda")
+    xs = torch.zeros((N, K // 32), dtype=torch.uint8, device="cuda")
+
+    def calls():
+        qg().qgemv_swiglu_ex("int5", wq, ws, x, h, I, K, N, workspace=wsp)
+        qg().act_quant(x, xq, xs, N, K)
+        qg().qgemv_mx("mxfp4", mq, ms, xq, xs, y, I, K, N)
+
+    calls()
+    torch.cuda.synchronize()
+    eh, ey = h.cpu().numpy().copy(), y.cpu().numpy().copy()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    noise = torch.randn((64, 1024), device="cuda")
+    for rep in range(4):
+        h.fill_(float("nan"))
+        y.fill_(float("nan"))
+        xq.zero_()
+        _ = (noise * rep).sum()                 # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(h.cpu().numpy().view(np.uint32), eh.view(np.uint32)), f"replay {rep}: split SwiGLU"
+        assert np.array_equal(y.cpu().numpy().view(np.uint32), ey.view(np.uint32)), f"replay {rep}: MX GEMV"
+        assert not wsp.cpu().numpy()[:_flag_bytes()].any(), f"replay {rep}: flags left set"
