@@ -11,12 +11,14 @@
 //     load per lane (a contiguous 1 KiB per wave) and feeds them to
 //     v_mfma_f32_16x16x32_bf16 as the B operand: n = weight row, k = 32
 //     columns = one scale group. The A operand holds the activations.
-//   * A rows are (slot, token) = 8*slot + token, 8 tokens max. Int formats
-//     put even groups in slot 0 and odd groups in slot 1, so one accumulator
-//     carries two groups' partial sums apart and the per-group scale step
-//     runs once per two groups. NVFP4 puts its two 16-column blocks of a
-//     group in the two slots. Lanes that must hold zeros load from an
-//     out-of-range buffer offset, which returns zeros.
+//   * A rows are (slot, token) = (16/S)*slot + token with S = 16, 8, 4, 2, 1
+//     slots for 1, 2, <= 4, <= 8, <= 16 tokens. Consecutive groups (NVFP4:
+//     16-column blocks) go to consecutive slots, so one accumulator carries
+//     S units' partial sums apart and the scale step runs once per S units.
+//     Lanes that must hold zeros load from an out-of-range buffer offset,
+//     which returns zeros. With one slot NVFP4 runs each block of a group
+//     through its own MFMA (the other block's activation lanes masked), and
+//     17 to 32 tokens take two blocks of 16 that share the decoded weights.
 //   * Int group epilogue: the B operand is bf16(128 + q); with D = sum x(128+q)
 //     and Db = 128 * sum x (one MFMA against a constant 128 operand, shared by
 //     all tiles of the wave): d*S + m*sum x = d*D + (m/128 - d)*Db.
@@ -318,7 +320,7 @@ __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
     uint8_t* xl = reinterpret_cast<uint8_t*>(red) + (size_t)W * NT * RB * 4 + (size_t)wave * nrec * xs;
     // per (cycle position, group): this lane's data or the record's zero block
     uint32_t off[C::KSTEPS][4];
-    const int sigma = r / T - (FMT == NVFP4 ? (s >> 1) : 0);
+    const int sigma = r / T - ((FMT == NVFP4 && S > 1) ? (s >> 1) : 0);
 #pragma unroll
     for (int c = 0; c < C::KSTEPS; ++c)
 #pragma unroll
@@ -867,9 +869,7 @@ template <int FMT, int NT, int KPS>
 hipError_t launch_k(const GemvArgs& a, const LaunchShape& ls, bool swiglu, hipStream_t stream) {
   switch (ls.slots) {
     case 16: return launch_s<FMT, NT, 16, KPS>(a, ls, swiglu, stream);
-    case 1:
-      if constexpr (FMT != NVFP4) return launch_s<FMT, NT, 1, KPS>(a, ls, swiglu, stream);
-      return hipErrorNotSupported;
+    case 1: return launch_s<FMT, NT, 1, KPS>(a, ls, swiglu, stream);
     case 8: return launch_s<FMT, NT, 8, KPS>(a, ls, swiglu, stream);
     case 4: return launch_s<FMT, NT, 4, KPS>(a, ls, swiglu, stream);
     default: return launch_s<FMT, NT, 2, KPS>(a, ls, swiglu, stream);
@@ -904,9 +904,8 @@ int run_gemv(int fmt, const void* wq, const void* ws, const void* x, const float
   if (rc) return rc;
   const bool norm = fz && fz->norm_src;
   uint16_t* ybf = fz ? fz->out_bf16 : nullptr;
-  // 9 to 32 tokens use one slot: int formats only (NVFP4 needs two slots per
-  // group), no RMSNorm prologue and no batch-invariant order
-  if (N > 8 && (fmt == NVFP4 || norm || (fz && (fz->flags & QGEMV_BATCH_INVARIANT)))) return QGEMV_EUNSUPPORTED;
+  // 9 to 32 tokens use one slot: no RMSNorm prologue and no batch-invariant order
+  if (N > 8 && (norm || (fz && (fz->flags & QGEMV_BATCH_INVARIANT)))) return QGEMV_EUNSUPPORTED;
   if (!swiglu && N > 16) {
     // plain GEMV: two launches of at most 16 tokens (measured faster than one
     // launch with two token blocks, whose activation loads per weight byte

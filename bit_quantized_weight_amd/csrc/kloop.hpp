@@ -14,8 +14,9 @@
 // slot. Consecutive scale units (int: 32-column groups; nvfp4: 16-column
 // blocks) go to consecutive slots, so one accumulator keeps S units apart and
 // the per-unit scale step runs once per S units ("cycle") instead of once per
-// unit. S = 16 at N = 1, 8 at N = 2, 4 at N <= 4, 2 at N <= 8, 1 (int formats
-// only) at N <= 16, where every group runs its own scale step. A lane whose
+// unit. S = 16 at N = 1, 8 at N = 2, 4 at N <= 4, 2 at N <= 8, 1 at N <= 16,
+// where every group runs its own scale step (nvfp4: each of a group's two
+// blocks, through an MFMA of its own, see HALVES). A lane whose
 // row is not in a unit's slot gets its offset moved by the slot difference
 // times 2^25 (activations stay below 2^25 bytes), so the buffer range check
 // returns zeros without a memory access. Rows of absent tokens start at
@@ -42,8 +43,12 @@ template <int FMT, int S>
 struct Cyc {
   static constexpr int T = 16 / S;                          // tokens per slot
   static constexpr int UNITS_PER_GROUP = FMT == NVFP4 ? 2 : 1;
-  static constexpr int GROUPS = S / UNITS_PER_GROUP;        // groups per cycle (>= 1)
-  static_assert(GROUPS >= 1, "NVFP4 needs two slots per group (N <= 8)");
+  // nvfp4 with one slot: the two 16-column blocks of a group share the slot,
+  // so each block takes its own MFMA with the other block's activation lanes
+  // masked to zero, and its own scale step
+  static constexpr bool HALVES = FMT == NVFP4 && S == 1;
+  static constexpr int GROUPS = HALVES ? 1 : S / UNITS_PER_GROUP;   // groups per cycle (>= 1)
+  static_assert(GROUPS >= 1, "slots per group");
   static constexpr int KSTEPS = GROUPS >= 4 ? GROUPS / 4 : 1;   // k-steps per cycle
   static constexpr int UNROLL = KSTEPS >= 2 ? KSTEPS : 2;   // k-steps per loop trip (even)
 };
@@ -61,7 +66,7 @@ __host__ __device__ constexpr int slot_pos(int kk, int j) {
 template <int FMT, int S>
 __device__ __forceinline__ uint32_t lane_slot_term(int lane) {
   const int r = lane & 15, s = lane >> 4;
-  const int sigma = r / Cyc<FMT, S>::T - (FMT == NVFP4 ? (s >> 1) : 0);
+  const int sigma = r / Cyc<FMT, S>::T - ((FMT == NVFP4 && S > 1) ? (s >> 1) : 0);
   return (uint32_t)sigma * kSlotStride;
 }
 
@@ -142,6 +147,10 @@ __device__ __forceinline__ u32x4 load_scales(__amdgpu_buffer_rsrc_t ws, uint32_t
       v.y = t.y >> sh;
     } else if constexpr (S == 4) {    // block 4c + s: j = 2c + (s>>1), h = s & 1
       v.x = ld32s(ws, row + 4u * (uint32_t)(s & 1), so) >> (8u * (uint32_t)(s >> 1));
+    } else if constexpr (S == 1) {    // every lane: its row's whole record (x: h = 0, y: h = 1; byte j)
+      const u32x2 t = ld64s(ws, row, so);
+      v.x = t.x;
+      v.y = t.y;
     } else {                          // S = 2: block 2j + (s>>1)
       v.x = ld32s(ws, row + 4u * (uint32_t)(s >> 1), so);
     }
@@ -168,6 +177,11 @@ __device__ __forceinline__ void dec_int5_step(const u32x4& q, uint32_t d4, bf16x
     const u32x4 v = {P[4 * j], P[4 * j + 1], P[4 * j + 2], P[4 * j + 3]};
     B[j] = __builtin_bit_cast(bf16x8, v);
   }
+}
+
+// E4M3 byte j (0..3, unrolled) of a scale word
+__device__ __forceinline__ float e4m3_sel(uint32_t w, int j) {
+  return j == 0 ? e4m3_byte<0>(w) : j == 1 ? e4m3_byte<1>(w) : j == 2 ? e4m3_byte<2>(w) : e4m3_byte<3>(w);
 }
 
 // ---- scale step at the end of a cycle ------------------------------------
@@ -292,6 +306,8 @@ __device__ __forceinline__ void kloop(__amdgpu_buffer_rsrc_t wq, __amdgpu_buffer
   static_assert(U % C::KSTEPS == 0, "cycle must divide the trip");
   static_assert(U % R == 0, "the activation ring must divide the trip");
   const bf16x8 b128 = bf16x8_splat_128();
+  // HALVES: operand lanes 0-31 hold a group's columns 0-15 (block 0), lanes 32-63 columns 16-31 (block 1)
+  const uint32_t lo_mask = (threadIdx.x & 32) ? 0u : 0xFFFFFFFFu;
   Step<FMT, NT, KPS> buf[2];
   bf16x8 xa[R][TB][4];
   u32x4 csc[NT];                                 // scale words of the current cycle (KSTEPS > 1)
@@ -343,36 +359,63 @@ __device__ __forceinline__ void kloop(__amdgpu_buffer_rsrc_t wq, __amdgpu_buffer
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int gpos = 4 * ckk + j;            // group position in the cycle
-          const bool first = (gpos % C::GROUPS) == 0;
-          const bool last = ((gpos + 1) % C::GROUPS) == 0;
-          const int cidx = gpos / C::GROUPS;       // cycle index inside the k-step
-          if constexpr (FMT == INT4 || FMT == INT5) {
-#pragma unroll
-            for (int tb = 0; tb < TB; ++tb)
-              Db[tb] = mfma(xa[kk % R][tb][j], b128, first ? f32x4{0.f, 0.f, 0.f, 0.f} : Db[tb]);
-          }
-#pragma unroll
-          for (int t = 0; t < NT; ++t) {
-            bf16x8 B;
-            const u32x4 q = cur.q[i][t];
-            if constexpr (FMT == INT4) {
-              B = dec_int4(j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w);
-            } else if constexpr (FMT == INT5) {
-              B = B5[t][j];
-            } else if constexpr (FMT == INT8) {
-              const u32x4 qq = j < 2 ? q : cur.q2[i][t];
-              B = (j & 1) ? dec_int8(qq.z, qq.w) : dec_int8(qq.x, qq.y);
-            } else {
-              B = dec_nvfp4(j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w);
-            }
+          if constexpr (C::HALVES) {
+            bf16x8 Ah[TB][2];                      // block 0 / block 1 activations, the other block's lanes zero
 #pragma unroll
             for (int tb = 0; tb < TB; ++tb) {
-              f32x4& Dt = D[t * TB + tb];
-              Dt = mfma(xa[kk % R][tb][j], B, first ? f32x4{0.f, 0.f, 0.f, 0.f} : Dt);
-              if (last) {
-                if constexpr (C::KSTEPS > 1) flush<FMT, S>(acc[t * TB + tb], Dt, Db[tb], csc[t], cidx);
-                else flush<FMT, S>(acc[t * TB + tb], Dt, Db[tb], cur.sc[i][t], cidx);
+              const u32x4 v = __builtin_bit_cast(u32x4, xa[kk % R][tb][j]);
+              const u32x4 v0 = {v.x & lo_mask, v.y & lo_mask, v.z & lo_mask, v.w & lo_mask};
+              const u32x4 v1 = {v.x & ~lo_mask, v.y & ~lo_mask, v.z & ~lo_mask, v.w & ~lo_mask};
+              Ah[tb][0] = __builtin_bit_cast(bf16x8, v0);
+              Ah[tb][1] = __builtin_bit_cast(bf16x8, v1);
+            }
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+              const u32x4 q = cur.q[i][t];
+              const bf16x8 B = dec_nvfp4(j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w);
+              const u32x4 sc = cur.sc[i][t];
+              const float b0 = e4m3_sel(sc.x, j), b1 = e4m3_sel(sc.y, j);
+#pragma unroll
+              for (int tb = 0; tb < TB; ++tb) {
+                const f32x4 D0 = mfma(Ah[tb][0], B, f32x4{0.f, 0.f, 0.f, 0.f});
+                const f32x4 D1 = mfma(Ah[tb][1], B, f32x4{0.f, 0.f, 0.f, 0.f});
+                f32x4& A = acc[t * TB + tb];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) A[e] = fmaf(b1, D1[e], fmaf(b0, D0[e], A[e]));
+              }
+            }
+          } else {
+            const int gpos = 4 * ckk + j;            // group position in the cycle
+            const bool first = (gpos % C::GROUPS) == 0;
+            const bool last = ((gpos + 1) % C::GROUPS) == 0;
+            const int cidx = gpos / C::GROUPS;       // cycle index inside the k-step
+            if constexpr (FMT == INT4 || FMT == INT5) {
+#pragma unroll
+              for (int tb = 0; tb < TB; ++tb)
+                Db[tb] = mfma(xa[kk % R][tb][j], b128, first ? f32x4{0.f, 0.f, 0.f, 0.f} : Db[tb]);
+            }
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+              bf16x8 B;
+              const u32x4 q = cur.q[i][t];
+              if constexpr (FMT == INT4) {
+                B = dec_int4(j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w);
+              } else if constexpr (FMT == INT5) {
+                B = B5[t][j];
+              } else if constexpr (FMT == INT8) {
+                const u32x4 qq = j < 2 ? q : cur.q2[i][t];
+                B = (j & 1) ? dec_int8(qq.z, qq.w) : dec_int8(qq.x, qq.y);
+              } else {
+                B = dec_nvfp4(j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w);
+              }
+#pragma unroll
+              for (int tb = 0; tb < TB; ++tb) {
+                f32x4& Dt = D[t * TB + tb];
+                Dt = mfma(xa[kk % R][tb][j], B, first ? f32x4{0.f, 0.f, 0.f, 0.f} : Dt);
+                if (last) {
+                  if constexpr (C::KSTEPS > 1) flush<FMT, S>(acc[t * TB + tb], Dt, Db[tb], csc[t], cidx);
+                  else flush<FMT, S>(acc[t * TB + tb], Dt, Db[tb], cur.sc[i][t], cidx);
+                }
               }
             }
           }

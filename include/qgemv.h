@@ -57,12 +57,12 @@
  *   - Host entry points (pack) take host pointers and need no GPU.
  *   - Pointers to packed weights, scales and activations must be 16-byte
  *     aligned (QGEMV_EALIGN otherwise); float outputs 4-byte aligned.
- *   - Limits: 1 <= N <= 32 for the int formats on qgemv / qgemv_swiglu /
- *     qgemv_ex / qgemv_swiglu_ex (9 to 32 tokens share one MFMA operand
+ *   - Limits: 1 <= N <= 32 on qgemv / qgemv_swiglu / qgemv_ex /
+ *     qgemv_swiglu_ex in every format (9 to 32 tokens share one MFMA operand
  *     slot per 16: verify windows of speculative decoding, NInfer article,
  *     section 3; the plain GEMV runs 17 to 32 tokens as two launches of at
- *     most 16); N <= 8 for NVFP4, the RMSNorm prologue, the batch-invariant
- *     order and the MoE entry points (QGEMV_EUNSUPPORTED otherwise);
+ *     most 16); N <= 8 with the RMSNorm prologue, the batch-invariant order
+ *     and on the MoE entry points (QGEMV_EUNSUPPORTED otherwise);
  *     K % 32 == 0, M >= 1, packed matrix under 4 GiB.
  */
 #ifndef QGEMV_H

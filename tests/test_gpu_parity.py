@@ -91,11 +91,6 @@ def test_qgemv_parity(fmt, M, K, N):
     log("gemv", fmt, M, K, N)
     W, xb, wq, ws = make_case(fmt, M, K, N, seed=N)
     y = torch.full((N, M), float("nan"), dtype=torch.float32, device="cuda")
-    if fmt == "nvfp4" and N > 8:      # NVFP4 keeps two slots per group: N <= 8
-        with pytest.raises(qg().QgemvError) as e:
-            qg().qgemv(fmt, dev(wq, torch), dev(ws, torch), dev(xb, torch), y, M, K, N)
-        assert e.value.status == -7
-        return
     yr, T = ref_gemv(fmt, wq, ws, xb, M, K)
     qg().qgemv(fmt, dev(wq, torch), dev(ws, torch), dev(xb, torch), y, M, K, N)
     torch.cuda.synchronize()
@@ -202,8 +197,6 @@ def test_batch_invariance(fmt):
 @pytest.mark.parametrize("I,K,N", [(64, 512, 1), (48, 160, 3), (256, 2048, 8), (768, 2048, 4), (96, 1024, 16),
                                    (32, 32768, 11), (80, 640, 27), (64, 5120, 32)])
 def test_swiglu_parity(fmt, I, K, N):
-    if fmt == "nvfp4" and N > 8:
-        pytest.skip("NVFP4 takes N <= 8 (rejected with QGEMV_EUNSUPPORTED, checked in test_qgemv_parity)")
     log("swiglu", fmt, I, K, N)
     W, xb, wq, ws = make_case(fmt, 2 * I, K, N, seed=31)
     Wd = oracle_weights(fmt, wq, ws, 2 * I, K)
@@ -308,12 +301,14 @@ def test_moe_index_bit_exact(N, k, E):
 # every launch shape the benchmark times: [17408][5120] (one tile per
 # workgroup) at N = 1, 2, 4, 8 in each format, the QKV shape (one tile from
 # N = 2, two at N = 1) and the down projection (two tiles; one for NVFP4 and
-# int8 at N = 2), whose long K stages activations through the LDS ring
+# int8 at N = 2), whose long K stages activations through the LDS ring; and
+# 9 to 32 tokens (one slot; 17 to 32 as two launches)
 FULL = [("int4", 7168, 5120, 1), ("int4", 7168, 5120, 8), ("int4", 7168, 5120, 4), ("int5", 5120, 17408, 1),
         ("int5", 5120, 17408, 8), ("nvfp4", 5120, 17408, 4), ("nvfp4", 7168, 5120, 2),
         ("int4", 5120, 17408, 2), ("nvfp4", 5120, 17408, 2), ("int8", 5120, 17408, 2), ("int5", 5120, 17408, 3),
         ("int5", 17408, 5120, 16), ("int8", 7168, 5120, 12), ("int4", 5120, 17408, 16), ("int4", 17408, 5120, 32),
-        ("int8", 5120, 17408, 24)] + \
+        ("int8", 5120, 17408, 24), ("nvfp4", 17408, 5120, 16), ("nvfp4", 5120, 17408, 12),
+        ("nvfp4", 7168, 5120, 32)] + \
        [(f, 17408, 5120, n) for f in ("int4", "int5", "int8", "nvfp4") for n in (1, 2, 4, 8)]
 
 
@@ -337,3 +332,25 @@ def test_full_size_sampled_rows(fmt, M, K, N):
         yr = G.gemv(x, Wt)
         T = G.gemv_tolerance(x, Wt)
         check_tol(yg[:, rt * 16:(rt + 1) * 16], yr, T, f"tile {rt}")
+
+
+@pytest.mark.parametrize("fmt,N", [("nvfp4", 12), ("nvfp4", 32), ("int5", 24), ("int4", 16), ("int8", 32)])
+def test_swiglu_full_size_many_tokens(fmt, N):
+    """Gate/up pairs [2 x 17408][5120] at 9 to 32 tokens (one slot; 17 to 32
+    as two token blocks sharing each decoded weight operand), sampled tiles."""
+    I, K = 17408, 5120
+    log("swiglu full", fmt, N)
+    rng = synthetic.rng_for(0, 6, I, K)
+    wq, ws = qg().pack(fmt, synthetic.weights(rng, 2 * I, K))
+    xb = synthetic.activations(rng, N, K, 0.01)
+    h = torch.full((N, I), float("nan"), dtype=torch.float32, device="cuda")
+    qg().qgemv_swiglu(fmt, dev(wq, torch), dev(ws, torch), dev(xb, torch), h, I, K, N)
+    torch.cuda.synchronize()
+    hg = h.cpu().numpy()
+    x = G.x_from_bits(xb)
+    RT = I // 16
+    for rt in sorted({0, RT // 2, RT - 1, *np.random.default_rng(N).integers(0, RT, 3).tolist()}):
+        Wg = tile_rows(fmt, wq, ws, 2 * I, K, rt)
+        Wu = tile_rows(fmt, wq, ws, 2 * I, K, RT + rt)
+        ref, T = G.swiglu_from(G.gemv(x, Wg), G.gemv(x, Wu), G.gemv_tolerance(x, Wg), G.gemv_tolerance(x, Wu))
+        check_tol(hg[:, rt * 16:(rt + 1) * 16], ref, T, f"tile {rt}")

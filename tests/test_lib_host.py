@@ -154,7 +154,7 @@ def _gemv(**kw):
 def test_qgemv_validation_codes():
     assert _gemv(fmt=0) == -2 and _gemv(fmt=5) == -2
     assert _gemv(wq=None) == -1 and _gemv(x=None) == -1 and _gemv(y=None) == -1
-    assert _gemv(N=0) == -7 and _gemv(N=33) == -7 and _gemv(fmt=4, N=9) == -7   # NVFP4: N <= 8
+    assert _gemv(N=0) == -7 and _gemv(N=33) == -7 and _gemv(fmt=4, N=33) == -7
     assert _gemv(K=48) == -3 and _gemv(K=0) == -1 and _gemv(M=0) == -1
     assert _gemv(wq=ODD) == -3 and _gemv(x=ODD) == -3 and _gemv(y=FAKE + 2) == -3
     assert _gemv(res=FAKE + 1, y=FAKE) == -3
