@@ -16,9 +16,9 @@ Also reported on the same JSON line:
   roofline      the dominant kernel (gate/up + SwiGLU, int5) against 8 TB/s:
                 its average launch duration from HIP events on the launch
                 stream around batches of back-to-back launches (median batch)
-  nvfp4_layer   the same layer in NVFP4 at N = 1, 2, 4, 8
-  per_format    qgemv on [17408][5120] for each format at N = 1, 2, 4, 8 (and
-                16 for the int formats), and qgemv_mx (MXFP4 / MXFP8
+  nvfp4_layer   the same layer in NVFP4 at N = 1, 2, 4, 8, 16, 32
+  per_format    qgemv on [17408][5120] for each format at N = 1, 2, 4, 8, 16,
+                and qgemv_mx (MXFP4 / MXFP8
                 weights, MXFP8 activations) at N = 1, 2, 4, 8, 16, 32, alone
                 and after qgemv_act_quant
   moe           qgemv_moe on the 128-expert, top-8 workload at N = 1 and 8
@@ -315,7 +315,8 @@ def extras(qg, torch, dev, stream, layers, args, wsp):
     res["probe"] = {"bytes": pb[0].numel(), "us": round(ms * 1e3, 2), "GB/s": round(pb[0].numel() / (ms * 1e-3) / 1e9, 1)}
     log("probe", res["probe"])
 
-    # the same layer in NVFP4 at N = 1, 2, 4, 8 (1-8 decode lanes), 8 rotated layer copies
+    # the same layer in NVFP4 at N = 1, 2, 4, 8 (1-8 decode lanes) and 16, 32
+    # (verify windows of 8 lanes), 8 rotated layer copies
     nv = {}
     nv_host = {}
     for name, M_, K_, _ in LAYER:
@@ -325,7 +326,7 @@ def extras(qg, torch, dev, stream, layers, args, wsp):
                  for _ in range(8)]
     nv_w = sum(v[0].size + v[1].size for v in nv_host.values())
     del nv_host
-    for n in (1, 2, 4, 8):
+    for n in (1, 2, 4, 8, 16, 32):
         rng_x = synthetic.rng_for(0, 3, 2, n)
         xn = torch.from_numpy(synthetic.activations(rng_x, n, 5120)).to(dev)
         xdn = torch.from_numpy(synthetic.activations(rng_x, n, 17408)).to(dev)
@@ -446,7 +447,7 @@ def extras(qg, torch, dev, stream, layers, args, wsp):
         ms = timeit(lambda i: qg.qgemv_probe_read(d[i % copies][0], wq.size // 16 * 16, sink), 60)
         probe_gbs = (wq.size // 16 * 16) / (ms * 1e-3) / 1e9
         pf[fmt]["probe_GB/s"] = round(probe_gbs, 1)
-        ns = (1, 2, 4, 8, 16, 32) if fmt.startswith("mx") else ((1, 2, 4, 8) if fmt == "nvfp4" else (1, 2, 4, 8, 16))
+        ns = (1, 2, 4, 8, 16, 32) if fmt.startswith("mx") else (1, 2, 4, 8, 16)
         for n in ns:
             xb = torch.from_numpy(synthetic.activations(rng, n, K, 0.01)).to(dev)
             yy = torch.empty((n, M), dtype=torch.float32, device=dev)
