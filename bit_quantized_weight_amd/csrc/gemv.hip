@@ -647,8 +647,10 @@ int cycle_ksteps(int fmt, int S) {
 //     at N <= 2 and int8 at N = 2, which take one tile on every shape.
 //     SwiGLU always keeps a gate tile and its up tile together.
 //   * A wave streams best with 12-20 k-steps of its tiles: 20 at N = 1 and
-//     N > 4, 12 at N = 2 and for int5/int8 at N = 4, 16 for int4/NVFP4 at
-//     N = 4; NVFP4 at N = 1 with 12; SwiGLU and long K at N > 4 take longer
+//     N > 4; on one-tile workgroups of large matrices 20 at N <= 4 (NVFP4
+//     16), on smaller ones 12 at N = 2 and for int5/int8 at N = 4, 16 for
+//     int4/NVFP4 at N = 4, NVFP4 at N = 1 with 12; gate/up pairs 20 at
+//     N <= 4 (int8 12 at N = 2-4); SwiGLU and long K at N > 4 take longer
 //     ranges (five waves per workgroup).
 // The grid should hold at least ~900 waves so the chip's 1024 SIMDs have
 // work; below that the k-range per wave shrinks (never under one scale
@@ -659,14 +661,14 @@ bool single_tile(int fmt, int N, bool swiglu, int64_t out_tiles) {
   return out_tiles >= 768 || (N >= 2 && out_tiles >= 384);
 }
 
-int ksteps_per_wave(int fmt, int N, bool swiglu, bool one_tile, int64_t KS) {
+int ksteps_per_wave(int fmt, int N, bool swiglu, bool one_tile, int64_t KS, int64_t out_tiles) {
   if (swiglu) {                          // gate/up pairs: [2 x 17408][5120] sweeps
     if (N == 1) return 20;
-    if (N == 2) return fmt == NVFP4 ? 20 : 12;
-    if (N <= 4) return 12;
+    if (N <= 4) return fmt == INT8 ? 12 : 20;
     return 40;
   }
   if (one_tile) {
+    if (N <= 4 && out_tiles >= 768) return fmt == NVFP4 ? 16 : 20;
     if (N == 1) return fmt == NVFP4 ? 12 : 20;
     if (N == 2) return fmt == INT8 ? 20 : 12;
     if (N <= 4) return (fmt == INT4 || fmt == NVFP4) ? 16 : 12;
@@ -710,7 +712,7 @@ LaunchShape pick_shape(int fmt, int64_t KS, int64_t out_tiles, int N, bool swigl
   const int cyc = cycle_ksteps(fmt, ls.slots);
   const bool one = single_tile(fmt, N, swiglu, out_tiles);
   ls.nt = one ? 1 : 2;
-  const int per = ksteps_per_wave(fmt, N, swiglu, one, KS);
+  const int per = ksteps_per_wave(fmt, N, swiglu, one, KS, out_tiles);
   const int64_t to = swiglu ? ls.nt / 2 : ls.nt;     // output tiles per workgroup
   const int64_t wgs = (out_tiles + to - 1) / to;
   auto waves_for = [&](int64_t kpw) { return (KS + kpw - 1) / kpw; };
@@ -728,8 +730,16 @@ LaunchShape pick_shape(int fmt, int64_t KS, int64_t out_tiles, int N, bool swigl
   return ls;
 }
 
-// Activations go to LDS when a workgroup's share stays within this budget
-// (N = 1 and small N * K); larger ones use buffer loads.
+// At N <= 4 a wave's activations could be staged whole in LDS before its
+// k-loop or stream through the four-record ring; the ring measured 2-20%
+// faster on the dense layer's shapes (every format, N = 1, 2, 4), except
+// for the int5 and int8 gate/up pairs and the int formats' two-tile long-K
+// projection (the down projection) at N = 1, which keep the whole range.
+bool ring_first(int fmt, int N, bool swiglu, int nt, int64_t KS) {
+  if (N == 1 && swiglu && (fmt == INT5 || fmt == INT8)) return false;
+  if (N == 1 && !swiglu && nt == 2 && KS >= 64 && fmt != NVFP4) return false;
+  return true;
+}
 
 
 // Split remainder. With B row blocks on C compute units, B mod C blocks
@@ -812,6 +822,8 @@ hipError_t launch_s(const GemvArgs& a0, const LaunchShape& ls, bool swiglu, hipS
   const size_t whole = (size_t)ls.waves * a.x_nks * rec, ring = (size_t)ls.waves * kRing * ring_stride<S>();
   // (the ring moves at most 8 tokens per record: one slot's 16 load directly)
   int xm = whole <= kMaxLdsActs ? XM_LDS : ((ring <= kMaxLdsActs && S > 1) ? XM_RING : XM_LOAD);
+  if (xm == XM_LDS && S >= 4 && !a.nsrc && ring <= kMaxLdsActs && ring_first(FMT, a.N, swiglu, NT, a.KS))
+    xm = XM_RING;
   if (two_blocks) xm = XM_LOAD;
   if (a.nsrc && xm == XM_LOAD) {         // the RMSNorm prologue stages its activations in LDS
     if (red + ring > kMaxLdsNorm) return hipErrorNotSupported;
