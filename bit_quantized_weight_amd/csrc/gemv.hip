@@ -441,13 +441,20 @@ __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
 
   const int nslot = a.frag - 1;
   const size_t slot0 = frag >= 0 ? (size_t)(rblk - a.n_full) * nslot : 0;
+  constexpr int PS = NT * RB + (NORM ? 8 : 0);   // floats per partial slot: sums, then the RMSNorm sums of squares
+  static_assert(S == 1 || PS <= 2 * 128 + 8, "partial slot larger than the workspace's (the split needs N <= 8)");
   if (frag >= 0 && frag < nslot) {
     // publish this fragment's partial sums (waves added in order) and raise its flag
-    float* dst = a.part + (slot0 + frag) * (NT * RB);
+    float* dst = a.part + (slot0 + frag) * PS;
     for (int o = threadIdx.x; o < NT * RB; o += blockDim.x) {
       float v = 0.f;
       for (int w = 0; w < W; ++w) v += red[(size_t)w * NT * RB + o];
       st_f32_dev(dst + o, v);
+    }
+    if (NORM && (int)threadIdx.x < a.N) {         // this fragment's share of each token's sum of squares
+      float ss = 0.f;
+      for (int w = 0; w < W; ++w) ss += s_ss[w][threadIdx.x];
+      st_f32_dev(dst + NT * RB + threadIdx.x, ss);
     }
     __builtin_amdgcn_s_waitcnt(0);        // this thread's stores have completed
     __syncthreads();
@@ -478,7 +485,7 @@ __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
   // sum of a (tile, token, row) over the earlier fragments, in fragment order
   auto frag_sum = [&](int o) -> float {
     float v = 0.f;
-    for (int f = 0; f < nslot; ++f) v += ld_f32_dev(a.part + (slot0 + f) * (NT * RB) + o);
+    for (int f = 0; f < nslot; ++f) v += ld_f32_dev(a.part + (slot0 + f) * PS + o);
     return v;
   };
   const int n_out = TO * RB;
@@ -491,6 +498,7 @@ __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
     float sc = st;                        // NVFP4 tensor scale, times the RMSNorm scale
     if constexpr (NORM) {
       float ss = 0.f;
+      if (frag >= 0) ss = frag_sum(NT * RB + tok);   // the other fragments' K ranges, in fragment order
       for (int w = 0; w < W; ++w) ss += s_ss[w][tok];
       sc = sc * (1.0f / sqrtf(ss / (float)a.K + a.eps));
     }
@@ -768,10 +776,12 @@ int device_cus() {
   return v;
 }
 
-// flag words (64 bytes each) and partial-sum slots (NT <= 2 tiles of 8 x 16 floats)
+// flag words (64 bytes each) and partial-sum slots (NT <= 2 tiles of 8 x 16
+// floats, then 8 RMSNorm sums of squares)
+constexpr int64_t kSlotFloats = 2 * 128 + 8;
 int64_t split_slots(int cus) { return (int64_t)(kMaxFrag - 1) * cus; }
 int64_t split_flag_bytes(int cus) { return (kSplitHeader + 64 * split_slots(cus) + 255) / 256 * 256; }
-int64_t split_bytes(int cus) { return split_flag_bytes(cus) + split_slots(cus) * 2 * 128 * 4; }
+int64_t split_bytes(int cus) { return split_flag_bytes(cus) + split_slots(cus) * kSlotFloats * 4; }
 
 void plan_split(int fmt, const LaunchShape& ls, bool swiglu, int64_t out_tiles, int64_t KS, int cus, GemvArgs& a) {
   a.n_full = 0;
@@ -978,7 +988,7 @@ int run_gemv(int fmt, const void* wq, const void* ws, const void* x, const float
     if (cus < 1) return QGEMV_EHIP;
     if (!aligned16(fz->workspace) || ((uintptr_t)fz->workspace & 255u)) return QGEMV_EALIGN;
     if (fz->workspace_bytes < (size_t)split_bytes(cus)) return QGEMV_EWORKSPACE;
-    if (!norm && !inv && N <= 8) plan_split(fmt, ls, swiglu, a.out_tiles, g.KS, cus, a);
+    if (!inv && N <= 8) plan_split(fmt, ls, swiglu, a.out_tiles, g.KS, cus, a);
     a.pflag = (uint32_t*)fz->workspace;
     a.part = (float*)((uint8_t*)fz->workspace + split_flag_bytes(cus));
   }

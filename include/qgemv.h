@@ -182,12 +182,14 @@ int qgemv_swiglu(int fmt, const void* wq, const void* ws, const void* x, float* 
  *               fragment order (the workgroups wait, bounded, only on
  *               lower-numbered ones, which start first on every XCD). Results
  *               stay reproducible from call to call but their bits differ
- *               from a call without a workspace. Not used with norm_src or
- *               QGEMV_BATCH_INVARIANT. Every call leaves the flags it used at
- *               zero, so one fill serves later calls in stream order; calls
- *               that may overlap in time need separate workspaces. The first
- *               32-bit word is a sticky flag that becomes nonzero if a wait
- *               ever timed out (that call's results are then invalid).
+ *               from a call without a workspace (with norm_src the fragments
+ *               also add their parts of each token's sum of squares). Not
+ *               used with QGEMV_BATCH_INVARIANT or N > 8. Every call leaves
+ *               the flags it used at zero, so one fill serves later calls in
+ *               stream order; calls that may overlap in time need separate
+ *               workspaces. The first 32-bit word is a sticky flag that
+ *               becomes nonzero if a wait ever timed out (that call's
+ *               results are then invalid).
  *               workspace_bytes: its size (QGEMV_EWORKSPACE if smaller).
  * Zero-initialise unused fields. */
 enum { QGEMV_BATCH_INVARIANT = 1 };

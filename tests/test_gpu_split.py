@@ -203,3 +203,52 @@ def test_split_and_mx_calls_in_a_hip_graph():
         assert np.array_equal(h.cpu().numpy().view(np.uint32), eh.view(np.uint32)), f"replay {rep}: split SwiGLU"
         assert np.array_equal(y.cpu().numpy().view(np.uint32), ey.view(np.uint32)), f"replay {rep}: MX GEMV"
         assert not wsp.cpu().numpy()[:_flag_bytes()].any(), f"replay {rep}: flags left set"
+
+
+# RMSNorm prologue with the split: the fragments also publish their parts of
+# each token's sum of squares (gate/up pairs at N = 1 and 8: 1024 + 64 x 4;
+# [17408][5120] one tile per workgroup: 1088 = 1024 + 64 x 4). At N = 4 the
+# NVFP4 prologue kernel's three-wave workgroups of the split grid (1280) do
+# not all fit the chip at once, so the split is declined there.
+NORM_SHAPES = [("int5", 2 * 17408, 5120, 1, True, True), ("int4", 2 * 17408, 5120, 8, True, True),
+               ("nvfp4", 17408, 5120, 4, False, False), ("int8", 17408, 5120, 1, False, True)]
+
+
+@pytest.mark.parametrize("fmt,M,K,N,sw,taken", NORM_SHAPES)
+def test_split_with_rmsnorm_prologue(fmt, M, K, N, sw, taken):
+    log("split norm", fmt, M, K, N, sw)
+    rng = synthetic.rng_for(0, 13, M, K)
+    wq, ws = qg().pack(fmt, synthetic.weights(rng, M, K))
+    h = (rng.standard_normal((N, K), dtype=np.float32) * np.float32(2.5)).astype(np.float32)
+    gamma = (1.0 + 0.2 * rng.standard_normal(K)).astype(np.float32)
+    Mo = M // 2 if sw else M
+    wqd, wsd, hd, gd = dev(wq, torch), dev(ws, torch), dev(h, torch), dev(gamma, torch)
+    wsp = qg().split_workspace(torch.device("cuda:0"))
+
+    def call(workspace):
+        y = torch.full((N, Mo), float("nan"), dtype=torch.float32, device="cuda")
+        f = qg().qgemv_swiglu_ex if sw else qg().qgemv_ex
+        f(fmt, wqd, wsd, None, y, Mo, K, N, norm_src=hd, norm_gamma=gd, norm_eps=1e-6, workspace=workspace)
+        torch.cuda.synchronize()
+        return y.cpu().numpy()
+
+    y = call(wsp)
+    assert not wsp.cpu().numpy()[:_flag_bytes()].any(), "flags or the error word not zero after the call"
+    y2 = call(wsp)
+    assert np.array_equal(y.view(np.uint32), y2.view(np.uint32)), "split result not reproducible"
+    y0 = call(None)
+    assert np.array_equal(y.view(np.uint32), y0.view(np.uint32)) != taken, "split taken" if not taken else "not taken"
+    x = G.rmsnorm(h, gamma, 1e-6)
+    RT = Mo // 16
+    for rt in _sample_tiles(RT, M + N):
+        cols = slice(rt * 16, (rt + 1) * 16)
+        if sw:
+            Wg = tile_rows(fmt, wq, ws, M, K, rt)
+            Wu = tile_rows(fmt, wq, ws, M, K, RT + rt)
+            ref, T = G.swiglu_from(G.gemv(x, Wg), G.gemv(x, Wu), G.norm_gemv_tolerance(x, Wg),
+                                   G.norm_gemv_tolerance(x, Wu))
+        else:
+            Wt = tile_rows(fmt, wq, ws, M, K, rt)
+            ref, T = G.gemv(x, Wt), G.norm_gemv_tolerance(x, Wt)
+        check_tol(y[:, cols], ref, T, f"split norm tile {rt}")
+        check_tol(y0[:, cols], ref, T, f"unsplit norm tile {rt}")
