@@ -657,9 +657,11 @@ int cycle_ksteps(int fmt, int S) {
 //   * A wave streams best with 12-20 k-steps of its tiles: 20 at N = 1 and
 //     N > 4; on one-tile workgroups of large matrices 20 at N <= 4 (NVFP4
 //     16), on smaller ones 12 at N = 2 and for int5/int8 at N = 4, 16 for
-//     int4/NVFP4 at N = 4, NVFP4 at N = 1 with 12; gate/up pairs 20 at
-//     N <= 4 (int8 12 at N = 2-4); SwiGLU and long K at N > 4 take longer
-//     ranges (five waves per workgroup).
+//     int4/NVFP4 at N = 4, NVFP4 at N = 1 with 12. Gate/up pairs take
+//     longer ranges: at N = 1 28 for int5/int8 (int4 20, NVFP4 24), at
+//     N = 2-4 int4 28, int5/int8 40 (one wave per workgroup; with the
+//     RMSNorm prologue 20, int8 12), NVFP4 24; SwiGLU and long K at N > 4
+//     take longer ranges too (five waves per workgroup).
 // The grid should hold at least ~900 waves so the chip's 1024 SIMDs have
 // work; below that the k-range per wave shrinks (never under one scale
 // cycle). Each wave's range is a whole number of cycles.
@@ -669,10 +671,14 @@ bool single_tile(int fmt, int N, bool swiglu, int64_t out_tiles) {
   return out_tiles >= 768 || (N >= 2 && out_tiles >= 384);
 }
 
-int ksteps_per_wave(int fmt, int N, bool swiglu, bool one_tile, int64_t KS, int64_t out_tiles) {
-  if (swiglu) {                          // gate/up pairs: [2 x 17408][5120] sweeps
-    if (N == 1) return 20;
-    if (N <= 4) return fmt == INT8 ? 12 : 20;
+int ksteps_per_wave(int fmt, int N, bool swiglu, bool one_tile, int64_t KS, int64_t out_tiles, bool norm) {
+  if (swiglu) {                          // gate/up pairs: [2 x 17408][5120] sweeps with the split remainder
+    if (fmt == NVFP4) return N <= 4 ? 24 : 40;
+    if (N == 1) return fmt == INT4 ? 20 : 28;
+    if (N <= 4) {
+      if (norm) return fmt == INT8 ? 12 : 20;   // the prologue's staging: 28-40 measured 3-45% slower here
+      return fmt == INT4 ? 28 : 40;
+    }
     return 40;
   }
   if (one_tile) {
@@ -720,7 +726,7 @@ LaunchShape pick_shape(int fmt, int64_t KS, int64_t out_tiles, int N, bool swigl
   const int cyc = cycle_ksteps(fmt, ls.slots);
   const bool one = single_tile(fmt, N, swiglu, out_tiles);
   ls.nt = one ? 1 : 2;
-  const int per = ksteps_per_wave(fmt, N, swiglu, one, KS, out_tiles);
+  const int per = ksteps_per_wave(fmt, N, swiglu, one, KS, out_tiles, norm);
   const int64_t to = swiglu ? ls.nt / 2 : ls.nt;     // output tiles per workgroup
   const int64_t wgs = (out_tiles + to - 1) / to;
   auto waves_for = [&](int64_t kpw) { return (KS + kpw - 1) / kpw; };
