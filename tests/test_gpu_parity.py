@@ -111,8 +111,10 @@ def test_config1_int4_1024():
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
-def test_residual_and_aliasing(fmt):
-    M, K, N = 96, 640, 3
+@pytest.mark.parametrize("N", [3, 12, 27])
+def test_residual_and_aliasing(fmt, N):
+    M, K = 96, 640
+    log("residual", fmt, N)
     W, xb, wq, ws = make_case(fmt, M, K, N, seed=11)
     r = synthetic.residual(np.random.default_rng(4), N, M)
     yr, T = ref_gemv(fmt, wq, ws, xb, M, K, residual=r)
@@ -127,8 +129,10 @@ def test_residual_and_aliasing(fmt):
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
-def test_determinism_and_canaries(fmt):
-    M, K, N = 200, 2048, 8
+@pytest.mark.parametrize("N", [8, 20])
+def test_determinism_and_canaries(fmt, N):
+    M, K = 200, 2048
+    log("canaries", fmt, N)
     W, xb, wq, ws = make_case(fmt, M, K, N, seed=12)
     pad = 64
     buf = torch.full((N * M + 2 * pad,), 12345.0, dtype=torch.float32, device="cuda")
@@ -168,6 +172,15 @@ def test_special_cases(fmt):
         torch.cuda.synchronize()
         T = G.gemv_tolerance(x.astype(np.float64), Wd)
         check_tol(y1.cpu().numpy(), Wd[:, k][None, :].astype(np.float64), T, f"one-hot k={k}")
+    # 16 one-hot tokens in one call (one operand slot): token t picks column ks[t]
+    ks = np.random.default_rng(6).choice(K, 16, replace=False)
+    x = np.zeros((16, K), np.float32)
+    x[np.arange(16), ks] = 1.0
+    y16 = torch.empty((16, M), dtype=torch.float32, device="cuda")
+    qg().qgemv(fmt, dev(wq, torch), dev(ws, torch), dev(synthetic.bf16_bits(x), torch), y16, M, K, 16)
+    torch.cuda.synchronize()
+    check_tol(y16.cpu().numpy(), Wd[:, ks].T.astype(np.float64), G.gemv_tolerance(x.astype(np.float64), Wd),
+              "one-hot batch of 16")
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
