@@ -30,8 +30,13 @@ What the GPU path computes, written as plain definitions in fp64:
         GEMV   T = 2e-3 * sum_k |x_k W_k| + 1e-5
         SwiGLU T_h = 1.1 (|u| + T_u) T_g + |silu(g)| T_u + 1e-6 |h| + 1e-5
                (max |silu'| < 1.1; the 1e-6 |h| term covers device exp/div)
-        MoE    T_y = sum_j |p_j| (2e-3 sum_c |h_c Wd_c| + sum_c |Wd_c| T_h,c
-                                   + 1e-5) + 1e-5
+        MoE    T_y = sum_j |p_j| (2e-3 sum_c (|h_c| + T_h,c) |Wd_c|
+                                   + sum_c |Wd_c| T_h,c + 1e-5) + 1e-5
+               (the down GEMV's own 2e-3 applies to the h it receives, whose
+               magnitude is at most |h| + T_h)
+        chain  a SwiGLU output h (bound T_h) handed to the next GEMV rounded
+               to bf16: T_hb = T_h + 2^-9 (|h| + T_h), then
+               T_y = 2e-3 sum_c (|h_c| + T_hb,c) |Wd_c| + sum_c T_hb,c |Wd_c| + 1e-5
 """
 from __future__ import annotations
 
@@ -121,6 +126,23 @@ def swiglu(x: np.ndarray, W_gu: np.ndarray):
     return h, Th
 
 
+def chain_tolerance(h: np.ndarray, Th: np.ndarray, Wd: np.ndarray) -> np.ndarray:
+    """Bound for y = r + bf16(h~) . Wd^T where h~ is a GPU evaluation of h
+    within Th (a SwiGLU output handed to the down projection as bf16, the
+    NInfer article's chained per-format kernels, section 2). The bf16
+    rounding adds at most 2^-9 |h~| <= 2^-9 (|h| + Th) to the input error;
+    the down GEMV then adds its own 2e-3 bound over the inputs it actually
+    sees (|h~| <= |h| + T_hb), and the input error propagates through |Wd|:
+        T_hb = Th + 2^-9 (|h| + Th)
+        T_y  = 2e-3 (|h| + T_hb) |Wd|^T + T_hb |Wd|^T + 1e-5
+    """
+    h = np.abs(np.asarray(h, np.float64))
+    Th = np.asarray(Th, np.float64)
+    Wa = np.abs(np.asarray(Wd, np.float64))
+    Thb = Th + BF16_REL * (h + Th)
+    return REL * ((h + Thb) @ Wa.T) + Thb @ Wa.T + ABS
+
+
 def moe_index(ids: np.ndarray, E: int):
     """Routing index for ids [N][k] (int32).
 
@@ -175,7 +197,7 @@ def moe(x: np.ndarray, ids: np.ndarray, gates: np.ndarray, W_gu: list, W_dn: lis
             Wd = np.asarray(W_dn[e], np.float64)
             o = h @ Wd.T
             y[t] += p * o[0]
-            To = REL * (np.abs(h) @ np.abs(Wd).T) + Th @ np.abs(Wd).T + ABS
+            To = REL * ((np.abs(h) + Th) @ np.abs(Wd).T) + Th @ np.abs(Wd).T + ABS
             T[t] += abs(p) * To[0]
             if gate_tol is not None:
                 T[t] += float(gate_tol[t, j]) * (np.abs(o[0]) + To[0])

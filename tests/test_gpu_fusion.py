@@ -162,8 +162,7 @@ def test_chained_mlp_block():
     href, Th = G.swiglu_from(G.gemv(x, Wgu[:I]), G.gemv(x, Wgu[I:]), G.norm_gemv_tolerance(x, Wgu[:I]),
                              G.norm_gemv_tolerance(x, Wgu[I:]))
     y_ref = G.gemv(href, Wdn, res)
-    Th_b = Th + G.BF16_REL * (np.abs(href) + Th)          # h crosses the chain as bf16
-    T = G.gemv_tolerance(np.abs(href) + Th_b, Wdn) + Th_b @ np.abs(Wdn).T
+    T = G.chain_tolerance(href, Th, Wdn)                  # h crosses the chain as bf16
     check_tol(y.cpu().numpy(), y_ref, T, "chained MLP block")
 
 

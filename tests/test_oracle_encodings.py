@@ -190,18 +190,26 @@ def test_exact_encoders_roundtrip_all_codes():
 @pytest.mark.parametrize("fn,p", [(enc.exact_round_f32, 24), (enc.exact_round_f64, 53)])
 def test_exact_round_matches_hardware_float(fn, p):
     rng = np.random.default_rng(3)
-    for _ in range(300):
-        a = Fraction(int(rng.integers(1, 2 ** 62)), int(rng.integers(1, 2 ** 62)))
-        a *= Fraction(2) ** int(rng.integers(-40, 40))
-        got = fn(a)
-        if p == 53:
-            want = Fraction(a.numerator / a.denominator) if a.numerator < 2 ** 1000 else None
-            # Python's int/int true division is correctly rounded
-            assert got == Fraction(a.numerator / a.denominator)
-        else:
-            f64 = a.numerator / a.denominator   # correctly rounded to double
-            # round the exact value (not the double) to fp32 and compare to
-            # numpy's fp32 cast of the double when the double is not a tie
-            f32 = np.float32(f64)
-            if Fraction(f64) == a:
-                assert got == Fraction(float(f32))
+    if p == 53:
+        # Python's int / int true division is correctly rounded to double
+        for _ in range(300):
+            a = Fraction(int(rng.integers(1, 2 ** 62)), int(rng.integers(1, 2 ** 62)))
+            a *= Fraction(2) ** int(rng.integers(-40, 40))
+            assert fn(a) == Fraction(a.numerator / a.denominator)
+        return
+    # fp32: exact doubles (every one a Fraction exactly), rounded by numpy's
+    # double -> float32 cast, which rounds to nearest even (IEEE 754)
+    samples = []
+    for _ in range(300):                        # random doubles across the fp32 range, subnormals included
+        m = int(rng.integers(2 ** 52, 2 ** 53))
+        samples.append(math.ldexp(m, int(rng.integers(-52 - 150, -52 + 128))))
+    for _ in range(100):                        # exact ties between neighbouring fp32 values
+        f = np.float32(rng.standard_normal() * 2.0 ** int(rng.integers(-130, 120)))
+        nxt = np.nextafter(f, np.float32(np.inf))
+        samples.append((float(f) + float(nxt)) / 2)
+    for d in samples:
+        for v in (d, -d):
+            want = Fraction(float(np.float32(v))) if abs(v) < float(np.finfo(np.float32).max) else None
+            if want is None or not math.isfinite(float(np.float32(v))):
+                continue
+            assert fn(Fraction(v)) == want, v

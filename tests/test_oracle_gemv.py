@@ -275,3 +275,166 @@ def test_norm_tolerance_covers_the_gpu_evaluation():
     no_scale = emul(lambda ss: np.ones_like(ss))
     for bad in (bad_sum, bad_gamma, no_scale):
         assert np.any(np.abs(bad - y_ref) > T)
+
+
+# ------------------------------------------- pins of the propagated bounds
+#
+# Sign-coherent inputs (every product x_k w_k of a row has the row's sign)
+# make sum|x w| = |sum x w|, so the GEMV bound is 2e-3 of the value itself
+# and a propagated bound that came out too loose by a plausible typo (a
+# factor 10 or 100) lets the planted mistakes below through.
+
+def _coherent(rng, rows, K, signs, scale):
+    """[rows][K] fp32 weights whose row r has the sign signs[r] throughout."""
+    w = rng.uniform(0.2, 1.8, (rows, K)) * scale / K
+    return (w * np.asarray(signs, np.float64)[:, None]).astype(np.float32)
+
+
+def _f32_dot(x, W):
+    """fp32 emulation of a GPU dot: fp32 products summed sequentially in fp32."""
+    x32, W32 = np.asarray(x, np.float32), np.asarray(W, np.float32)
+    acc = np.zeros((x32.shape[0], W32.shape[0]), np.float32)
+    for k in range(x32.shape[1]):
+        acc += x32[:, k:k + 1] * W32[None, :, k]
+    return acc
+
+
+def _f32_silu_mul(g, u):
+    g, u = np.asarray(g, np.float32), np.asarray(u, np.float32)
+    with np.errstate(over="ignore"):
+        return (g / (np.float32(1) + np.exp(-g)) * u).astype(np.float32)
+
+
+def _swiglu_case(seed=41, N=3, K=256, I=48):
+    rng = np.random.default_rng(seed)
+    x = G.x_from_bits(synthetic.bf16_bits(rng.uniform(0.5, 1.5, (N, K)).astype(np.float32)))
+    gs = np.where(np.arange(I) % 3 == 0, -1.0, 1.0)           # gates of both signs
+    Wg = _coherent(rng, I, K, gs, rng.uniform(0.3, 4.0, I)[:, None])
+    Wu = _coherent(rng, I, K, np.where(np.arange(I) % 4 == 1, -1.0, 1.0), rng.uniform(0.5, 3.0, I)[:, None])
+    return x, np.concatenate([Wg, Wu])
+
+
+def test_swiglu_bound_contains_the_gpu_evaluation_and_rejects_mistakes():
+    x, W = _swiglu_case()
+    I = W.shape[0] // 2
+    h, Th = G.swiglu(x, W)
+    g, u = G.gemv(x, W[:I]), G.gemv(x, W[I:])
+    Tg, Tu = G.gemv_tolerance(x, W[:I]), G.gemv_tolerance(x, W[I:])
+    # the GPU's evaluation: fp32 dots, then fp32 silu(g) * u
+    h32 = _f32_silu_mul(_f32_dot(x, W[:I]), _f32_dot(x, W[I:]))
+    assert np.all(np.abs(h32 - h) <= Th)
+    # worst-case inputs: g and u anywhere inside their own bounds
+    for sg in (-1, 1):
+        for su in (-1, 1):
+            hw = G.silu(g + sg * 0.999 * Tg) * (u + su * 0.999 * Tu)
+            assert np.all(np.abs(hw - h) <= Th)
+    # the bound is tight: a few times 2e-3 of |h| where silu(g) is not small
+    # against g (g > 0.5: silu(g) / g > 0.62)
+    big = g > 0.5
+    assert np.all(Th[big] <= 0.012 * np.abs(h[big]) + 2e-5)
+    # planted mistakes fall outside it
+    mistakes = {
+        "gate and up swapped": G.silu(u) * g,
+        "sigmoid instead of silu": g * 0 + 1.0 / (1.0 + np.exp(-g)) * u,
+        "gate row off by one": G.silu(np.roll(g, 1, axis=1)) * u,
+        "h scaled by 1.01": h * 1.01,
+        "silu(-g)": G.silu(-g) * u,
+    }
+    for what, bad in mistakes.items():
+        assert np.any(np.abs(bad - h) > Th), what
+
+
+def _moe_case(seed=43, N=2, H=64, I=32, E=3, k=2):
+    rng = np.random.default_rng(seed)
+    x = G.x_from_bits(synthetic.bf16_bits(rng.uniform(0.5, 1.5, (N, H)).astype(np.float32)))
+    Wgu = [np.concatenate([_coherent(rng, I, H, np.ones(I), rng.uniform(0.5, 3.0, I)[:, None]),
+                           _coherent(rng, I, H, np.ones(I), rng.uniform(0.5, 3.0, I)[:, None])]) for _ in range(E)]
+    Wdn = [_coherent(rng, H, I, np.ones(H), 2.0) for _ in range(E)]
+    ids = np.array([[0, 2], [1, 0]], np.int32)[:N, :k]
+    gates = np.array([[0.625, 0.375], [0.55, 0.45]], np.float32)[:N, :k]
+    return x, Wgu, Wdn, ids, gates
+
+
+def test_moe_bound_contains_the_gpu_evaluation_and_rejects_mistakes():
+    x, Wgu, Wdn, ids, gates = _moe_case()
+    N, k = ids.shape
+    I = Wgu[0].shape[0] // 2
+    y, T = G.moe(x, ids, gates, Wgu, Wdn)
+
+    def run(h_of, p_of=lambda t, j: float(gates[t, j]), e_of=lambda t, j: int(ids[t, j]), slots=range(k)):
+        out = np.zeros_like(y)
+        for t in range(N):
+            for j in slots:
+                e = e_of(t, j)
+                out[t] += p_of(t, j) * (h_of(t, e) @ np.asarray(Wdn[e], np.float64).T)[0]
+        return out
+
+    def h_exact(t, e):
+        return G.swiglu(x[t:t + 1], Wgu[e])[0]
+
+    # the GPU's evaluation: fp32 h, kept as a bf16 hi/lo pair, fp32 down dot,
+    # fp32 fused multiply-adds of the mixing weights in slot order
+    y32 = np.zeros(y.shape, np.float32)
+    for t in range(N):
+        for j in range(k):
+            e = int(ids[t, j])
+            h32 = _f32_silu_mul(_f32_dot(x[t:t + 1], Wgu[e][:I]), _f32_dot(x[t:t + 1], Wgu[e][I:]))
+            hi = enc.f32_from_bf16_bits(synthetic.bf16_bits(h32))
+            lo = enc.f32_from_bf16_bits(synthetic.bf16_bits((h32 - hi).astype(np.float32)))
+            o32 = (_f32_dot(hi, Wdn[e]) + _f32_dot(lo, Wdn[e])).astype(np.float32)
+            y32[t] = (np.float64(gates[t, j]) * o32[0] + y32[t]).astype(np.float32)
+    assert np.all(np.abs(y32 - y) <= T)
+    # worst case: h anywhere inside its own bound, then the down GEMV's 2e-3
+    for s in (-1, 1):
+        def h_worst(t, e, s=s):
+            hh, Th = G.swiglu(x[t:t + 1], Wgu[e])
+            return hh + s * 0.999 * Th
+        yw = run(h_worst)
+        assert np.all(np.abs(yw - y) + 0.999 * G.REL * np.abs(yw) <= T)
+    # the bound is tight: under 1% of |y| on these sign-coherent inputs
+    assert np.all(T <= 0.01 * np.abs(y))
+    # planted mistakes fall outside it
+    other = {0: 1, 1: 2, 2: 0}
+    mistakes = {
+        "mixing weights off by 1%": run(h_exact, p_of=lambda t, j: 1.01 * float(gates[t, j])),
+        "one slot dropped": run(h_exact, slots=range(k - 1)),
+        "wrong expert in one slot": run(h_exact, e_of=lambda t, j: other[int(ids[t, j])] if (t, j) == (0, 1)
+                                        else int(ids[t, j])),
+        "gate and up swapped": run(lambda t, e: (G.silu(G.gemv(x[t:t + 1], Wgu[e][I:]))
+                                                 * G.gemv(x[t:t + 1], Wgu[e][:I]))),
+        "unweighted sum of slots": run(h_exact, p_of=lambda t, j: 1.0 / k),
+    }
+    for what, bad in mistakes.items():
+        assert np.any(np.abs(bad - y) > T), what
+
+
+def test_chain_bound_contains_a_bf16_hand_off_and_rejects_mistakes():
+    """h (a SwiGLU output within T_h) crosses to the down projection as bf16."""
+    x, W = _swiglu_case(seed=45)
+    I = W.shape[0] // 2
+    rng = np.random.default_rng(46)
+    Wd = _coherent(rng, 40, I, np.ones(40), 1.5)
+    h, Th = G.swiglu(x, W)
+    y = G.gemv(h, Wd)
+    T = G.chain_tolerance(h, Th, Wd)
+
+    def bf16(v):
+        return enc.f32_from_bf16_bits(synthetic.bf16_bits(np.asarray(v, np.float32))).astype(np.float64)
+    # the GPU's evaluation: fp32 h, rounded to bf16, fp32 down dot
+    h32 = _f32_silu_mul(_f32_dot(x, W[:I]), _f32_dot(x, W[I:]))
+    assert np.all(np.abs(_f32_dot(bf16(h32), Wd) - y) <= T)
+    # worst case: h at the edge of its bound, rounded to bf16, down GEMV at its own 2e-3
+    for s in (-1, 1):
+        hw = bf16(h + s * 0.999 * Th)
+        yw = G.gemv(hw, Wd)
+        assert np.all(np.abs(yw - y) + 0.999 * G.REL * (np.abs(hw) @ np.abs(Wd).T) <= T)
+    mistakes = {
+        "h rounded to fp8 e4m3 instead of bf16": G.gemv(enc.e4m3_decode(
+            np.array([[enc.exact_e4m3_bits(enc.exact_round_e4m3_sat(Fraction(float(v)))) if v >= 0 else 0 for v in row]
+                      for row in h],
+                     np.uint8)), Wd),
+        "silu(g) handed over without u": G.gemv(G.silu(G.gemv(x, W[:I])), Wd),
+        "h scaled by 1.02": y * 1.02,
+    }
+    for what, bad in mistakes.items():
+        assert np.any(np.abs(bad - y) > T), what
