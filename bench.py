@@ -123,6 +123,239 @@ def mx_only(qg, torch, synthetic, dev, steps):
     return out
 
 
+# Cases of --profile-set, in run order: (name, kind, format, M, K, N). Each
+# runs `steps` launches (steps) after 3 warm-up steps; a 16-byte probe
+# launch before each case marks it in the kernel trace.
+PROFILE_CASES = [("layer_int_n1", "layer", "int", 0, 0, 1)] + \
+    [(f"perfmt_{f}_n{n}", "perfmt", f, 17408, 5120, n) for f in ("int4", "int5", "int8", "nvfp4") for n in (1, 8)] + \
+    [("layer_nvfp4_n8", "layer", "nvfp4", 0, 0, 8), ("moe_n1", "moe", "int4", 0, 0, 1), ("moe_n8", "moe", "int4", 0, 0, 8),
+     ("moe_fused_n1", "moe_fused", "int4", 0, 0, 1), ("moe_fused_n8", "moe_fused", "int4", 0, 0, 8)]
+
+
+def profile_set(qg, torch, synthetic, dev, steps, calib_mib):
+    """Run every PROFILE_CASES case for rocprofv3 (kernel trace, counters).
+    Prints one JSON line: per case the launches per step and the
+    algorithmic bytes per step, for --summarize-profile."""
+    stream = torch.cuda.current_stream()
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    mark = torch.zeros(16, dtype=torch.uint8, device=dev)
+    wsp = qg.split_workspace(dev)
+    out = {"steps": steps, "cases": {}}
+    if calib_mib > 0:
+        qg.qgemv_probe_read(mark, 16, sink)
+        src = torch.ones(calib_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        out["calib_copy_bytes"] = calib_mib << 20
+    for name, kind, fmt, M, K, N in PROFILE_CASES:
+        rng = synthetic.rng_for(0, 12, len(name))
+        if kind == "perfmt":
+            wq, ws = qg.pack(fmt, synthetic.weights(rng, M, K))
+            nb = wq.size + ws.size
+            copies = max(2, int(np.ceil(1.1e9 / nb)))
+            d = [(torch.from_numpy(wq).to(dev), torch.from_numpy(ws).to(dev)) for _ in range(copies)]
+            x = torch.from_numpy(synthetic.activations(rng, N, K, 0.01)).to(dev)
+            y = torch.empty((N, M), dtype=torch.float32, device=dev)
+            per = 1
+            byt = nb + N * K * 2 + N * M * 4
+
+            def step(i):
+                qg.qgemv_ex(fmt, *d[i % copies], x, y, M, K, N, workspace=wsp)
+        elif kind == "layer":
+            fm = {"qkv": "int4", "gate_up": "int5", "down": "int5"} if fmt == "int" else \
+                {"qkv": fmt, "gate_up": fmt, "down": fmt}
+            host = {nm: qg.pack(fm[nm], synthetic.weights(rng, Mm, Kk)) for nm, Mm, Kk, _ in LAYER}
+            nb = sum(a.size + b.size for a, b in host.values())
+            copies = max(2, int(np.ceil(1.1e9 / nb)))
+            d = [{k: (torch.from_numpy(v[0]).to(dev), torch.from_numpy(v[1]).to(dev)) for k, v in host.items()}
+                 for _ in range(copies)]
+            x = torch.from_numpy(synthetic.activations(rng, N, 5120)).to(dev)
+            xd = torch.from_numpy(synthetic.activations(rng, N, 17408)).to(dev)
+            qkv = torch.empty((N, 7168), dtype=torch.float32, device=dev)
+            h = torch.empty((N, 17408), dtype=torch.float32, device=dev)
+            r = torch.from_numpy(synthetic.residual(rng, N, 5120)).to(dev)
+            y = torch.empty((N, 5120), dtype=torch.float32, device=dev)
+            per = 3
+            byt = nb + N * (5120 * 2 + 7168 * 4 + 5120 * 2 + 17408 * 4 + 17408 * 2 + 5120 * 8)
+
+            def step(i):
+                L = d[i % copies]
+                qg.qgemv_ex(fm["qkv"], *L["qkv"], x, qkv, 7168, 5120, N, workspace=wsp)
+                qg.qgemv_swiglu_ex(fm["gate_up"], *L["gate_up"], x, h, 17408, 5120, N, workspace=wsp)
+                qg.qgemv_ex(fm["down"], *L["down"], xd, y, 5120, 17408, N, residual=r, workspace=wsp)
+        else:
+            E, H, I, k = 128, 2048, 768, 8
+            bufs, per_expert = moe_buffers(qg, synthetic, torch, dev, E, H, I, copies=8)
+            copies = len(bufs)
+            sets = [synthetic.router_logits(rng, N, E) for _ in range(16)]
+            uniq = [len({int(e) for e in np.argsort(-lg.astype(np.float64), axis=1, kind="stable")[:, :k].reshape(-1)})
+                    for lg in sets]
+            xb = torch.from_numpy(synthetic.activations(rng, N, H)).to(dev)
+            rr = torch.from_numpy(synthetic.residual(rng, N, H)).to(dev)
+            y = torch.empty((N, H), dtype=torch.float32, device=dev)
+            byt = float(np.mean(uniq)) * per_expert + N * H * 2 + N * H * 8 + N * k * 8
+            if kind == "moe":
+                idsg = []
+                for lg in sets:
+                    ids = np.argsort(-lg.astype(np.float64), axis=1, kind="stable")[:, :k].astype(np.int32)
+                    g = np.exp(np.take_along_axis(lg.astype(np.float64), ids, 1))
+                    idsg.append((torch.from_numpy(ids).to(dev), torch.from_numpy((g / g.sum(1, keepdims=True)).astype(np.float32)).to(dev)))
+                nbytes = qg.moe_workspace_bytes(E, H, I, N, k)
+                mw = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+                per = 3
+
+                def step(i):
+                    qg.qgemv_moe("int4", *bufs[i % copies], E, H, I, xb, *idsg[i % 16], k, y, N, mw, nbytes, residual=rr)
+            else:
+                lt = [torch.from_numpy(lg).to(dev) for lg in sets]
+                nbytes = qg.moe_fused_workspace_bytes(E, H, I, N, k)
+                mw = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+                per = 1 if N * k <= 8 else 4
+
+                def step(i):
+                    qg.qgemv_moe_fused("int4", *bufs[i % copies], E, H, I, xb, lt[i % 16], k, y, N, mw, nbytes,
+                                       residual=rr)
+        for i in range(3):
+            step(i)
+        torch.cuda.synchronize()
+        qg.qgemv_probe_read(mark, 16, sink)        # marker: the case's launches follow
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(steps):
+            step(3 + i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) / steps * 1e3
+        out["cases"][name] = {"launches_per_step": per, "algorithmic_bytes_per_step": int(byt),
+                              "us_per_step_events": round(us, 2)}
+        log(name, out["cases"][name])
+        del step
+        torch.cuda.empty_cache()
+    qg.check_split_workspace(wsp)
+    print(json.dumps(out), flush=True)
+
+
+def moe_buffers(qg, synthetic, torch, dev, E, H, I, copies):
+    """Expert-stacked int4 buffers of E experts ([2I][H] gate/up, [H][I]
+    down), packed once on the host, `copies` device copies."""
+    sq, ss = qg.expert_stride("int4", 2 * I, H)
+    dq, ds = qg.expert_stride("int4", H, I)
+    bufs = [np.zeros(E * sq, np.uint8), np.zeros(E * ss, np.uint8), np.zeros(E * dq, np.uint8), np.zeros(E * ds, np.uint8)]
+    rng = synthetic.rng_for(0, 5)
+    for e in range(E):
+        q, s = qg.pack("int4", synthetic.weights(rng, 2 * I, H))
+        bufs[0][e * sq: e * sq + q.size] = q
+        bufs[1][e * ss: e * ss + s.size] = s
+        q, s = qg.pack("int4", synthetic.weights(rng, H, I))
+        bufs[2][e * dq: e * dq + q.size] = q
+        bufs[3][e * ds: e * ds + s.size] = s
+    return [[torch.from_numpy(b).to(dev) for b in bufs] for _ in range(copies)], sq + ss + dq + ds
+
+
+def _csv_rows(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_profile(manifest_path, trace_dir, counter_dirs, out_path, command_lines):
+    """Text summary of a --profile-set run under rocprofv3: per case and
+    kernel, launches and average duration (kernel trace), and per launch the
+    counters of each --pmc run (FETCH_SIZE / WRITE_SIZE scaled by what they
+    read for the calibration copy)."""
+    import glob
+    man = None
+    with open(manifest_path) as f:
+        for ln in f:
+            ln = ln.strip()
+            if ln.startswith("{") and '"cases"' in ln:
+                man = json.loads(ln)
+    if man is None:
+        raise SystemExit(f"no --profile-set manifest line in {manifest_path}")
+
+    def split_cases(rows, key_name, key_start):
+        rows = sorted(rows, key=lambda r: int(r[key_start]))
+        groups, cur, calib = [], None, []
+        for r in rows:
+            nm = r[key_name]
+            if "k_probe" in nm:
+                cur = []
+                groups.append(cur)
+            elif cur is not None:
+                cur.append(r)
+            elif "copyBuffer" in nm or "copy" in nm.lower():
+                calib.append(r)
+        return groups, calib
+
+    names = list(man["cases"].keys())
+    lines = [f"# rocprofv3 summary of `bench.py --profile-set --steps {man['steps']}` (kernel sources: src_hash "
+             f"{kernel_source_hash()})", "", "commands (from /tmp, TMPDIR=/tmp; the last argument names the run):"]
+    lines += [f"  {c}" for c in command_lines] + [""]
+    tr = [p for p in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)]
+    trows = _csv_rows(tr[0]) if tr else []
+    tgroups, _ = split_cases(trows, "Kernel_Name", "Start_Timestamp") if trows else ([], [])
+    counters = {}
+    for cd in counter_dirs:
+        cc = glob.glob(os.path.join(cd, "**", "*counter_collection.csv"), recursive=True)
+        if not cc:
+            continue
+        rows = _csv_rows(cc[0])
+        by_disp = {}
+        for r in rows:
+            by_disp.setdefault(r["Dispatch_Id"], {"Kernel_Name": r["Kernel_Name"], "Dispatch_Id": r["Dispatch_Id"]})
+            c = by_disp[r["Dispatch_Id"]]
+            c[r["Counter_Name"]] = c.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        groups, calib = split_cases(list(by_disp.values()), "Kernel_Name", "Dispatch_Id")
+        counters[cd] = (groups, calib)
+    scale = {}
+    for cd, (groups, calib) in counters.items():
+        for cn in ("FETCH_SIZE", "WRITE_SIZE"):
+            vals = [c[cn] for c in calib if cn in c]
+            if vals and "calib_copy_bytes" in man:
+                scale[cn] = man["calib_copy_bytes"] / (float(np.median(vals)) * 1024)
+    if scale:
+        lines.append("calibration: a 1 GiB device copy reads FETCH_SIZE x {:.4f} / WRITE_SIZE x {:.4f} of its bytes "
+                     "(KiB -> bytes scale)".format(scale.get("FETCH_SIZE", float("nan")), scale.get("WRITE_SIZE", float("nan"))))
+        lines.append("")
+    hdr = f"{'case':16s} {'kernel':58s} {'calls':>6s} {'avg us':>8s}"
+    lines.append(hdr + "   counters per launch (averages)")
+    for ci, name in enumerate(names):
+        meta = man["cases"][name]
+        per_kernel = {}
+        if ci < len(tgroups):
+            for r in tgroups[ci]:
+                per_kernel.setdefault(r["Kernel_Name"], []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        tot_us = 0.0
+        for kn, durs in per_kernel.items():
+            short = kn.split("(")[0].replace("void ", "")[:58]
+            cs = []
+            for cd, (groups, _) in counters.items():
+                if ci < len(groups):
+                    sel = [c for c in groups[ci] if c["Kernel_Name"] == kn]
+                    if sel:
+                        keys = sorted(k for k in sel[0] if k not in ("Kernel_Name", "Dispatch_Id"))
+                        for k in keys:
+                            v = float(np.mean([c[k] for c in sel]))
+                            if k in scale:
+                                cs.append(f"{k}={v:.1f}KiB({v * 1024 * scale[k] / 1e6:.2f}MB)")
+                            else:
+                                cs.append(f"{k}={v:.4g}")
+            avg = float(np.mean(durs))
+            tot_us += avg * len(durs) / max(1, man["steps"])
+            lines.append(f"{name:16s} {short:58s} {len(durs):6d} {avg:8.2f}   " + " ".join(cs))
+        if per_kernel:
+            gbs = meta["algorithmic_bytes_per_step"] / (tot_us * 1e-6) / 1e9
+            lines.append(f"{name:16s} {'= per step: sum of kernel averages':58s} {'':6s} {tot_us:8.2f}   "
+                         f"algorithmic {meta['algorithmic_bytes_per_step']} B -> {gbs:.0f} GB/s "
+                         f"({gbs / PEAK_GBS:.3f} of 8 TB/s); events {meta['us_per_step_events']} us")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -134,10 +367,22 @@ def main():
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run a plain device-to-device copy of this many MiB three times "
                          "(the known-size reference that scales rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--profile-set", action="store_true",
+                    help="run the profiling cases (per-format [17408][5120] at N = 1 and 8, the dense layer, "
+                         "the NVFP4 layer at N = 8, MoE) under rocprofv3 and print their manifest")
+    ap.add_argument("--summarize-profile", nargs="+", metavar="ARG",
+                    help="MANIFEST_LOG TRACE_DIR OUT_TXT COMMANDS_TXT [COUNTER_DIR ...]: write the text summary "
+                         "of a --profile-set run (COMMANDS_TXT: the profiler command lines, one per line)")
     ap.add_argument("--mx-only", action="store_true",
                     help="only the MX GEMV on [17408][5120] at N = 1 (MXFP8 and MXFP4, after the activation "
                          "quantiser): a short run for profiling those kernels")
     args = ap.parse_args()
+    if args.summarize_profile:
+        a = args.summarize_profile
+        with open(a[3]) as f:
+            cmds = [ln.rstrip("\n") for ln in f if ln.strip()]
+        summarize_profile(a[0], a[1], a[4:], a[2], cmds)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
         sys.exit(2)
@@ -150,6 +395,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.mx_only:
         print(json.dumps(mx_only(qg, torch, synthetic, dev, args.steps)), flush=True)
+        return
+    if args.profile_set:
+        profile_set(qg, torch, synthetic, dev, args.steps, args.calib_copy_mib)
         return
     stream = torch.cuda.current_stream()
     N = 1
@@ -250,12 +498,47 @@ def main():
     gu_ms = kern["gate_up_swiglu_int5"][0][0]
     gu_gbs = gu_bytes / (gu_ms * 1e-3) / 1e9
 
+    # the same gate/up + SwiGLU kernel at N = 8 (eight decode lanes)
+    x8 = torch.from_numpy(synthetic.activations(synthetic.rng_for(0, 2, 98), 8, 5120)).to(dev)
+    h8 = torch.empty((8, 17408), dtype=torch.float32, device=dev)
+    gu8_bytes = weight_bytes(qg, "int5", 2 * 17408, 5120) + 8 * 5120 * 2 + 8 * 17408 * 4
+    gu8_ms = time_alone(lambda i: qg.qgemv_swiglu_ex("int5", *layers[i % args.layers]["gate_up"], x8, h8, 17408, 5120, 8,
+                                                     workspace=wsp), 50)[0]
+    gu8_gbs = gu8_bytes / (gu8_ms * 1e-3) / 1e9
+
+    # the MLP block chained on the device, each launch consuming the previous
+    # one's output (NInfer article, section 2: norm, matmul, SwiGLU and
+    # residual fused per format): RMSNorm(r) -> gate/up + SwiGLU -> bf16 h ->
+    # down(h) + r, int5, N = 1, rotated layers
+    gamma = torch.from_numpy((1 + 0.1 * synthetic.rng_for(0, 7).standard_normal(5120)).astype(np.float32)).to(dev)
+    r1 = torch.from_numpy(synthetic.residual(synthetic.rng_for(0, 7, 1), 1, 5120)).to(dev)
+    hb = torch.zeros((1, 17408), dtype=torch.int16, device=dev)
+    ym = torch.empty((1, 5120), dtype=torch.float32, device=dev)
+
+    def mlp(i):
+        L = layers[i % len(layers)]
+        qg.qgemv_swiglu_ex("int5", *L["gate_up"], None, None, 17408, 5120, 1, norm_src=r1, norm_gamma=gamma,
+                           norm_eps=1e-6, out_bf16=hb, workspace=wsp)
+        qg.qgemv_ex("int5", *L["down"], hb, ym, 5120, 17408, 1, residual=r1, workspace=wsp)
+    mlp_bytes = (weight_bytes(qg, "int5", 2 * 17408, 5120) + weight_bytes(qg, "int5", 5120, 17408)
+                 + 5120 * 4 * 2 + 5120 * 4 + 17408 * 2 * 2 + 5120 * 8)
+    mlp_ms = time_alone(mlp, 32)[0]
+
     src_hash = kernel_source_hash()
-    assert int(wsp[:4].view(torch.int32).item()) == 0, "a split-remainder wait timed out"
-    roofline = {"bound": "hbm", "kernel": "k_gemv<int5, swiglu> (gate/up + SwiGLU, split remainder)",
+    qg.check_split_workspace(wsp)
+    roofline = {"bound": "hbm", "kernel": "k_gemv<int5, swiglu> (gate/up + SwiGLU, split remainder), N=1",
                 "achieved": round(gu_gbs, 1), "peak": PEAK_GBS, "unit": "GB/s", "frac": round(gu_gbs / PEAK_GBS, 4),
                 "traffic": pmc_traffic("gate_up_swiglu_int5", src_hash),
                 "algorithmic_bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_ms * 1e3, 2)}
+    roofline_n8 = {"bound": "hbm", "kernel": "k_gemv<int5, swiglu> (gate/up + SwiGLU, split remainder), N=8",
+                   "achieved": round(gu8_gbs, 1), "peak": PEAK_GBS, "unit": "GB/s",
+                   "frac": round(gu8_gbs / PEAK_GBS, 4), "traffic": pmc_traffic("gate_up_swiglu_int5_n8", src_hash),
+                   "algorithmic_bytes_per_launch": gu8_bytes, "avg_launch_us": round(gu8_ms * 1e3, 2)}
+    mlp_chain = {"workload": "27B-class MLP block, N=1, dependent launches: RMSNorm + gate/up 2x17408x5120 int5 + "
+                             "SwiGLU -> bf16 h -> down 5120x17408 int5 + residual",
+                 "us_per_block": round(mlp_ms * 1e3, 2), "GB/s": round(mlp_bytes / (mlp_ms * 1e-3) / 1e9, 1),
+                 "frac": round(mlp_bytes / (mlp_ms * 1e-3) / 1e9 / PEAK_GBS, 4), "algorithmic_bytes": mlp_bytes}
+    log("roofline N=8", roofline_n8, "mlp_chain", mlp_chain)
 
     extra = {}
     if not args.no_extra:
@@ -279,11 +562,15 @@ def main():
         "data": "synthetic",
         "config": {"workload": "27B-class dense layer, N=1: QKV 7168x5120 int4 + gate/up 2x17408x5120 int5 "
                                "with SwiGLU + down 5120x17408 int5 with residual",
+                   "step": "three launches in stream order whose inputs do not depend on each other (QKV and "
+                           "gate/up read x, down reads a separate bf16 input); mlp_chain is the dependent chain",
                    "layers_rotated": args.layers, "rotation_GB": round(args.layers * layer_w / 1e9, 2),
                    "algorithmic_bytes_per_step": step_bytes, "frac_of_peak": round(value / PEAK_GBS, 4),
                    "tok_per_s_64_layers": round(1.0 / (64 * ms_step * 1e-3), 1),
                    "arithmetic": "bf16 MFMA operands (exact codes), fp32 accumulate"},
         "roofline": roofline,
+        "roofline_n8": roofline_n8,
+        "mlp_chain": mlp_chain,
         "kernels": kernels,
         "src_hash": src_hash,
     }
@@ -393,10 +680,8 @@ def extras(qg, torch, dev, stream, layers, args, wsp):
                           "weight_bytes": mx_w, **mxr}
     log("mxfp4_layer", res["mxfp4_layer"])
 
-    # the MLP block chained on the device (NInfer article, section 2: norm,
-    # matmul, SwiGLU and residual fused): RMSNorm(r) -> gate/up + SwiGLU with a
-    # bf16 h -> down(h) + r, int5, N = 1; eager, and 16 rotated layers captured
-    # in one HIP graph and replayed
+    # the chained MLP block (timed eagerly in the main line) captured for 16
+    # rotated layers in one HIP graph and replayed
     gamma = torch.from_numpy((1 + 0.1 * synthetic.rng_for(0, 7).standard_normal(5120)).astype(np.float32)).to(dev)
     r1 = torch.from_numpy(synthetic.residual(synthetic.rng_for(0, 7, 1), 1, 5120)).to(dev)
     hb = torch.zeros((1, 17408), dtype=torch.int16, device=dev)
@@ -409,7 +694,6 @@ def extras(qg, torch, dev, stream, layers, args, wsp):
         qg.qgemv_ex("int5", *L["down"], hb, ym, 5120, 17408, 1, residual=r1, workspace=wsp)
     mlp_bytes = (weight_bytes(qg, "int5", 2 * 17408, 5120) + weight_bytes(qg, "int5", 5120, 17408)
                  + 5120 * 4 * 2 + 5120 * 4 + 17408 * 2 * 2 + 5120 * 8)
-    ms_e = timeit(mlp, 64)
     nl = len(layers)
     side = torch.cuda.Stream()
     side.wait_stream(stream)
@@ -423,15 +707,24 @@ def extras(qg, torch, dev, stream, layers, args, wsp):
         for i in range(nl):
             mlp(i)
     ms_g = timeit(lambda i: graph.replay(), 8) / nl
-    res["mlp_chain"] = {"workload": "27B-class MLP block, N=1: RMSNorm + gate/up 2x17408x5120 int5 + SwiGLU -> bf16 h "
-                                    "-> down 5120x17408 int5 + residual, 2 launches per layer (split-remainder workspace), "
-                                    "rotated layers",
-                        "eager_us": round(ms_e * 1e3, 2), "eager_GB/s": round(mlp_bytes / (ms_e * 1e-3) / 1e9, 1),
-                        "graph_us_per_layer": round(ms_g * 1e3, 2),
-                        "graph_GB/s": round(mlp_bytes / (ms_g * 1e-3) / 1e9, 1),
-                        "graph_layers": nl}
+    res["mlp_chain_graph"] = {"workload": "the chained MLP block of mlp_chain, 16 rotated layers in one HIP graph",
+                              "graph_us_per_layer": round(ms_g * 1e3, 2),
+                              "graph_GB/s": round(mlp_bytes / (ms_g * 1e-3) / 1e9, 1), "graph_layers": nl}
     del graph
-    log("mlp_chain", res["mlp_chain"])
+
+    # the single-GEMV workload: M = K = 1024, int4, N = 1, seed 0 (fits the
+    # L2 and the Infinity Cache: a launch-latency figure, not a roofline row)
+    rng1 = np.random.default_rng(0)
+    W1 = synthetic.weights(rng1, 1024, 1024)
+    x1 = torch.from_numpy(synthetic.activations(rng1, 1, 1024)).to(dev)
+    q1, s1 = (torch.from_numpy(a).to(dev) for a in qg.pack("int4", W1))
+    y1 = torch.empty((1, 1024), dtype=torch.float32, device=dev)
+    ms1 = timeit(lambda i: qg.qgemv("int4", q1, s1, x1, y1, 1024, 1024, 1), 200)
+    b1 = q1.numel() + s1.numel() + 1024 * 2 + 1024 * 4
+    res["config1_int4_1024"] = {"workload": "single GEMV M=K=1024 int4, N=1, seed 0 (cache-resident)",
+                                "us": round(ms1 * 1e3, 2), "GB/s": round(b1 / (ms1 * 1e-3) / 1e9, 1),
+                                "algorithmic_bytes": b1}
+    log("mlp_chain_graph", res["mlp_chain_graph"], "config1", res["config1_int4_1024"])
 
     # per format on [17408][5120], N = 1, 2, 4, 8 (int formats: also 16; MX: 16, 32), rotated over >= 1 GB
     M, K = 17408, 5120
@@ -502,7 +795,7 @@ def extras(qg, torch, dev, stream, layers, args, wsp):
     dbufs = [[torch.from_numpy(b).to(dev) for b in bufs] for _ in range(copies)]
     per_expert = (sq + ss + dq + ds)
     moe = {}
-    for n in (1, 8):
+    for n in (1, 4, 8):
         logits = synthetic.router_logits(rng, n, E)
         ids = np.argsort(-logits.astype(np.float64), axis=1, kind="stable")[:, :k].astype(np.int32)
         g = np.exp(np.take_along_axis(logits.astype(np.float64), ids, 1))
@@ -524,7 +817,7 @@ def extras(qg, torch, dev, stream, layers, args, wsp):
     # logit sets in rotation so the routing changes every call;
     # algorithmic bytes: the selected experts' weights + x + logits + r + y
     fused = {}
-    for n in (1, 2, 8):
+    for n in (1, 2, 4, 8):
         sets = [synthetic.router_logits(rng, n, E) for _ in range(16)]
         uniq = [len({int(e) for e in np.argsort(-lg.astype(np.float64), axis=1, kind="stable")[:, :k].reshape(-1)})
                 for lg in sets]

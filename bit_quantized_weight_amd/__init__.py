@@ -72,6 +72,7 @@ def load(require_torch: bool = True):
         "qgemv_moe_workspace_bytes": (I32, [I32, I64, I64, I32, I32, PSZ]),
         "qgemv_moe": (I32, [I32, P, P, P, P, I32, I64, I64, P, P, P, I32, P, P, I32, P, SZ, P]),
         "qgemv_moe_index": (I32, [P, I32, I32, I32, P, P, P, P, P, P]),
+        "qgemv_moe_index_by": (I32, [I32, P, I32, I32, I32, P, P, P, P, P, P]),
         "qgemv_moe_route": (I32, [P, I32, I32, I32, P, P, P]),
         "qgemv_moe_fused_workspace_bytes": (I32, [I32, I64, I64, I32, I32, PSZ]),
         "qgemv_moe_fused": (I32, [I32, P, P, P, P, I32, I64, I64, P, P, I32, P, P, I32, P, P, P, SZ, P]),
@@ -94,7 +95,7 @@ def symbols() -> list[str]:
     return ["qgemv_strerror", "qgemv_version", "qgemv_packed_bytes", "qgemv_expert_stride", "qgemv_pack",
             "qgemv_pack_codes", "qgemv", "qgemv_swiglu", "qgemv_ex", "qgemv_swiglu_ex", "qgemv_split_workspace_bytes",
             "qgemv_moe_workspace_bytes", "qgemv_moe",
-            "qgemv_moe_index", "qgemv_moe_route", "qgemv_moe_fused_workspace_bytes", "qgemv_moe_fused",
+            "qgemv_moe_index", "qgemv_moe_index_by", "qgemv_moe_route", "qgemv_moe_fused_workspace_bytes", "qgemv_moe_fused",
             "qgemv_dequant", "qgemv_probe_read", "qgemv_act_quant", "qgemv_mx", "qgemv_mx_swiglu"]
 
 
@@ -204,6 +205,24 @@ def split_workspace(device):
     return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
+def check_split_workspace(workspace) -> None:
+    """Synchronise and raise if a wait of a call that used `workspace` (from
+    split_workspace) ever timed out: that call's results, and the workspace
+    itself, are then invalid until it is zeroed again."""
+    import torch
+    torch.cuda.synchronize(workspace.device)
+    if int(workspace[:4].view(torch.int32).item()) != 0:
+        raise RuntimeError("split-remainder wait timed out: results invalid; zero the workspace before reuse")
+
+
+def check_moe_fused_workspace(workspace) -> None:
+    """As check_split_workspace, for a qgemv_moe_fused workspace (byte 12)."""
+    import torch
+    torch.cuda.synchronize(workspace.device)
+    if int(workspace[12:16].view(torch.int32).item()) != 0:
+        raise RuntimeError("qgemv_moe_fused dependency wait timed out: results invalid; zero the workspace")
+
+
 def qgemv_ex(fmt, wq, ws, x, y, M: int, K: int, N: int, residual=None, norm_src=None, norm_gamma=None,
              norm_eps: float = 1e-6, out_bf16=None, batch_invariant=False, workspace=None, stream=None) -> None:
     """qgemv with the optional RMSNorm prologue (norm_src, norm_gamma,
@@ -239,6 +258,14 @@ def qgemv_moe(fmt, wq_gu, ws_gu, wq_dn, ws_dn, E: int, H: int, I: int, x, ids, g
 def qgemv_moe_index(ids, N: int, top_k: int, E: int, counts, offsets, pairs, active, meta, stream=None) -> None:
     _check(load().qgemv_moe_index(_ptr(ids), N, top_k, E, _ptr(counts), _ptr(offsets), _ptr(pairs), _ptr(active),
                                   _ptr(meta), _stream(stream)), "qgemv_moe_index")
+
+
+def qgemv_moe_index_by(routine: int, ids, N: int, top_k: int, E: int, counts, offsets, pairs, active, meta,
+                       stream=None) -> None:
+    """The routing index as one MoE path computes it: routine 0 = qgemv_moe's
+    per-slot routing, 1 = the single launch of qgemv_moe_fused."""
+    _check(load().qgemv_moe_index_by(int(routine), _ptr(ids), N, top_k, E, _ptr(counts), _ptr(offsets), _ptr(pairs),
+                                     _ptr(active), _ptr(meta), _stream(stream)), "qgemv_moe_index_by")
 
 
 def qgemv_moe_route(logits, N: int, E: int, top_k: int, ids, gates, stream=None) -> None:

@@ -5,10 +5,12 @@
 // 4/5-bit integers, NVFP4), the RustingStrata page (Q8_0-style int8) and the
 // Decapybara page (NVFP4 GEMV). Each decoder turns one lane's 8 codes of one
 // 32-column group into the bf16x8 B operand of v_mfma_f32_16x16x32_bf16:
-//   int4 / int5  bf16(128 + q): the code sits in the low mantissa bits under
-//                the exponent of 128 (bf16 0x4300), exact for q < 128; the
-//                128 * sum(x) bias is removed in the group epilogue (int5's
-//                decoder lives with the k-loop: it decodes a whole k-step)
+//   int4 / int5  bf16(B + q) with B = 16 (int4) or 32 (int5), the smallest
+//                power of two above the largest code: the code sits in the
+//                top mantissa bits under the exponent of B, so the value is
+//                exact; the bias B * sum(x) is removed in the group epilogue
+//                (int5's decoder lives with the k-loop: it decodes a whole
+//                k-step)
 //   int8         bf16(q), exact (|q| <= 128)
 //   nvfp4        bf16(e2m1), exact, via v_cvt_scalef32_pk_bf16_fp4 with scale 1
 //                (that instruction only applies the exponent of its scale, so
@@ -88,14 +90,25 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t b, uint32_t c) {
 
 // ---- decoders: 8 codes of one lane and group -> bf16x8 (slot e = element e)
 
+// Code bias of the asymmetric int formats (see the header comment): bf16
+// bit pattern of B in both halves of a dword, and 1 / B.
+constexpr uint32_t kBias4Bits = 0x41804180u;   // bf16(16) twice
+constexpr uint32_t kBias5Bits = 0x42004200u;   // bf16(32) twice
+template <int B_OF_FMT>
+struct CodeBias;
+template <> struct CodeBias<1> { static constexpr uint32_t bits = kBias4Bits; static constexpr float inv = 0.0625f; };
+template <> struct CodeBias<2> { static constexpr uint32_t bits = kBias5Bits; static constexpr float inv = 0.03125f; };
+
 // int4 dword: slot e in nibble (e even ? e/2 : 4 + e/2), so the nibble pairs
 // (0,4), (1,5), (2,6), (3,7) are the slot pairs (0,1), (2,3), (4,5), (6,7).
+// bf16(16 + q): the 4-bit code lands in mantissa bits 3..6 (one ulp of 16
+// is 1/8), so each half is shifted there and OR-ed under the exponent of 16.
 __device__ __forceinline__ bf16x8 dec_int4(uint32_t v) {
   u32x4 r;
-  r.x = and_or(v, 0x000F000Fu, 0x43004300u);
-  r.y = and_or(v >> 4, 0x000F000Fu, 0x43004300u);
-  r.z = and_or(v >> 8, 0x000F000Fu, 0x43004300u);
-  r.w = and_or(v >> 12, 0x000F000Fu, 0x43004300u);
+  r.x = and_or(v << 3, 0x00780078u, kBias4Bits);
+  r.y = and_or(v >> 1, 0x00780078u, kBias4Bits);
+  r.z = and_or(v >> 5, 0x00780078u, kBias4Bits);
+  r.w = and_or(v >> 9, 0x00780078u, kBias4Bits);
   return __builtin_bit_cast(bf16x8, r);
 }
 
@@ -136,8 +149,8 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ bf16x8 bf16x8_splat_128() {
-  const u32x4 r = {0x43004300u, 0x43004300u, 0x43004300u, 0x43004300u};
+__device__ __forceinline__ bf16x8 bf16x8_splat(uint32_t pair) {
+  const u32x4 r = {pair, pair, pair, pair};
   return __builtin_bit_cast(bf16x8, r);
 }
 

@@ -19,9 +19,10 @@
 //     which returns zeros. With one slot NVFP4 runs each block of a group
 //     through its own MFMA (the other block's activation lanes masked), and
 //     17 to 32 tokens take two blocks of 16 that share the decoded weights.
-//   * Int group epilogue: the B operand is bf16(128 + q); with D = sum x(128+q)
-//     and Db = 128 * sum x (one MFMA against a constant 128 operand, shared by
-//     all tiles of the wave): d*S + m*sum x = d*D + (m/128 - d)*Db.
+//   * Int group epilogue: the B operand is bf16(c + q) with c = 16 (int4) or
+//     32 (int5); with D = sum x(c+q) and Db = c * sum x (one MFMA against a
+//     constant c operand, shared by all tiles of the wave):
+//     d*S + m*sum x = (m/c)*Db + d*(D - Db).
 //   * Waves of a workgroup split K; their partial sums meet in LDS and are
 //     added in wave order, so results are bitwise reproducible. The sum over
 //     the two slots uses a fixed lane exchange.
@@ -255,8 +256,18 @@ __host__ __device__ constexpr int ring_stride() { return (16 / S) * 256 + 16; }
 // it keep their register budget)
 // TB: blocks of 16 tokens (one slot only; 17 to 32 tokens take two, which
 // share every decoded weight operand)
+// Waves per SIMD the register allocation must allow: the int5 two-tile
+// kernels at one and two tokens sit just past 168 VGPRs (two waves per SIMD
+// instead of three) without the bound, which measured 25% slower and leaves
+// the split-remainder grid too large to be resident.
+template <int FMT, int NT, int S, int XM, bool NORM, int TB>
+constexpr int min_waves_per_simd() {
+  return (FMT == INT5 && NT == 2 && S >= 8 && XM != 2 && !NORM && TB == 1) ? 3 : 1;
+}
+
 template <int FMT, int NT, int S, int KPS, bool SWIGLU, int XM, bool NORM, int TB = 1>
-__global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<FMT, NT, S, XM, NORM, TB>())))
+void k_gemv(GemvArgs a) {
   static_assert(TB == 1 || (XM == XM_LOAD && !NORM), "token blocks load their activations directly");
   extern __shared__ __attribute__((aligned(16))) float red[];  // [W][NT][8][16], then the LDS activations
   __shared__ float s_ss[8][8];                                  // RMSNorm: [wave][token] sums of squares
@@ -318,21 +329,29 @@ __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
     const int xs = XM == XM_RING ? ring_stride<S>() : a.N * 256 + 16;
     const int nrec = XM == XM_LDS ? a.x_nks : kRing;
     uint8_t* xl = reinterpret_cast<uint8_t*>(red) + (size_t)W * NT * RB * 4 + (size_t)wave * nrec * xs;
-    // per (cycle position, group): this lane's data or the record's zero block
-    uint32_t off[C::KSTEPS][4];
+    // per (cycle position, group): this lane's data or the record's zero
+    // block. Cycles of one k-step keep the four offsets in registers; longer
+    // cycles (one or two tokens) select them per read (a compare with a
+    // constant and a select), which keeps 8-16 registers free
     const int sigma = r / T - ((FMT == NVFP4 && S > 1) ? (s >> 1) : 0);
+    const uint32_t zoff = (uint32_t)(a.N * 256);
+    const uint32_t mine = a_tok < a.N ? (uint32_t)(a_tok * 256 + s * 16) : zoff;
+    const int sig = a_tok < a.N ? sigma : -1;
+    constexpr int OFFC = C::KSTEPS == 1 ? 1 : 0;   // table entries kept (one-k-step cycles)
+    uint32_t off_tab[OFFC ? 4 : 1];
 #pragma unroll
-    for (int c = 0; c < C::KSTEPS; ++c)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        off[c][j] = (sigma == slot_pos<FMT, S>(c, j) && a_tok < a.N) ? (uint32_t)(a_tok * 256 + j * 64 + s * 16)
-                                                                      : (uint32_t)(a.N * 256);
+    for (int j = 0; j < (OFFC ? 4 : 0); ++j)
+      off_tab[j] = sig == slot_pos<FMT, S>(0, j) ? mine + (uint32_t)(j * 64) : zoff;
+    auto off_of = [&](int c, int j) -> uint32_t {
+      if constexpr (OFFC) return off_tab[j];
+      else return sig == slot_pos<FMT, S>(c, j) ? mine + (uint32_t)(j * 64) : zoff;
+    };
     if constexpr (XM == XM_LDS) {
       auto acts = [&](bf16x8 (&A)[4], int k, int pos) {
         const uint8_t* rec = xl + (k - ks0) * xs;
         const int ckk = pos % C::KSTEPS;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) A[j] = *reinterpret_cast<const bf16x8*>(rec + off[ckk][j]);
+        for (int j = 0; j < 4; ++j) A[j] = *reinterpret_cast<const bf16x8*>(rec + off_of(ckk, j));
       };
       // staged after the first weight loads are issued, so the two overlap
       auto pre = [&]() {
@@ -381,7 +400,7 @@ __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
         const uint8_t* rec = xl + (pos % kRing) * ring_stride<S>();
         const int ckk = pos % C::KSTEPS;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) A[j] = *reinterpret_cast<const bf16x8*>(rec + off[ckk][j]);
+        for (int j = 0; j < 4; ++j) A[j] = *reinterpret_cast<const bf16x8*>(rec + off_of(ckk, j));
       };
       auto pre = [&]() {
         // zero blocks; record ks0 written now, ks0 + 1 and ks0 + 2 staged
@@ -456,7 +475,15 @@ __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
       for (int w = 0; w < W; ++w) ss += s_ss[w][threadIdx.x];
       st_f32_dev(dst + NT * RB + threadIdx.x, ss);
     }
-    __builtin_amdgcn_s_waitcnt(0);        // this thread's stores have completed
+    // Publication (the ordering argument, in full, with the flag poll
+    // below): the partial sums are agent-scope atomic stores, which bypass
+    // the XCD-local L2 and complete at the device's coherence point; every
+    // thread waits for its own to complete (s_waitcnt vmcnt(0) acknowledges
+    // them), the barrier puts all of that before thread 0's flag store, so
+    // the flag cannot become visible before the data. Release/acquire at
+    // agent scope would add an L2 writeback and invalidate per fragment:
+    // measured 2x slower for the whole launch.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (threadIdx.x == 0)
       __hip_atomic_store(a.pflag + 64 + (slot0 + frag) * 16, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -467,6 +494,10 @@ __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
     if (wave == 0 && lane < nslot) {
       uint32_t* fl = a.pflag + 64 + (slot0 + lane) * 16;
       uint32_t it = 0;
+      // The partial sums are read below with agent-scope atomic loads, which
+      // go to the coherence point; they are issued only after this loop has
+      // seen the flag (the branch depends on the loaded value, and the
+      // signal fence keeps the compiler from moving the reads above it).
       while (__hip_atomic_load(fl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
         if (++it >= kFragSpin) {
           atomicOr(a.pflag, 1u);
@@ -587,7 +618,8 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* wqp, const uint8
       if (k >= K) continue;
       const float b = (float)B[e];
       float w;
-      if (FMT == INT4 || FMT == INT5) w = fmaf(d, b - 128.0f, mn);  // d*q exact: one rounding
+      if (FMT == INT4) w = fmaf(d, b - 16.0f, mn);                  // d*q exact: one rounding
+      else if (FMT == INT5) w = fmaf(d, b - 32.0f, mn);
       else if (FMT == INT8) w = d * b;
       else w = st * (b * sb);                                        // b*sb exact
       out[(int64_t)row * K + k] = w;
@@ -904,6 +936,10 @@ hipError_t launch_k(const GemvArgs& a, const LaunchShape& ls, bool swiglu, hipSt
   }
 }
 
+// Two k-steps per weight buffer. Four (twice the loads in flight per wave)
+// measured 15-60% slower on one-tile workgroups and 2.7-4x slower on
+// two-tile ones, although a plain streaming probe at the same waves per SIMD
+// reads faster with four loads in flight than with two.
 template <int FMT>
 hipError_t launch_gemv(const GemvArgs& a, const LaunchShape& ls, bool swiglu, hipStream_t stream) {
   if (ls.nt == 1) return launch_k<FMT, 1, 2>(a, ls, false, stream);   // plain GEMV only

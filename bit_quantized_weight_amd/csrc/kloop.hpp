@@ -23,9 +23,16 @@
 // 2^30, and k-steps past the range or groups past K add 2^31: in every case
 // the offset lands at least 2^25 away from [0, 2^25).
 //
-// Int group scale: B = bf16(128 + q); with D = sum x (128 + q) and
-// Db = 128 sum x (an MFMA against a constant-128 operand shared by all
-// tiles), d * sum(x q) + m * sum(x) = d * D + (m / 128 - d) * Db.
+// Int group scale: B = bf16(c + q) with the code bias c = 16 (int4) or 32
+// (int5); with D = sum x (c + q) and Db = c sum x (an MFMA against a
+// constant-c operand shared by all tiles),
+//   d * sum(x q) + m * sum(x) = (m / c) * Db + d * (D - Db),
+// added to the accumulator in that order. Both MFMA sums carry rounding of
+// order 2^-24 c sum|x|, so the error of the step grows with c d sum|x|; the
+// smallest exact bias keeps it small, and forming D - Db before scaling by d
+// (instead of adding d * D and subtracting d * Db) avoids a rounding at the
+// magnitude of d * D. With a one-hot x of value 1 every sum is exact and the
+// step gives RN(d q + m), the dequantised weight itself.
 //
 // After the loop, lane l's acc[t][i] is the partial sum of A row 4*(l/16) + i
 // for weight row 16*tile[t] + (l % 16) (nvfp4: without the tensor scale).
@@ -158,19 +165,21 @@ __device__ __forceinline__ u32x4 load_scales(__amdgpu_buffer_rsrc_t ws, uint32_t
   return v;
 }
 
-// ---- int5: 16 pair-words (bf16x2 of 128 + q) from the lane's five dwords
+// ---- int5: 16 pair-words (bf16x2 of 32 + q) from the lane's five dwords;
+// the 5-bit code lands in mantissa bits 2..6 (one ulp of 32 is 1/4)
 __device__ __forceinline__ void dec_int5_step(const u32x4& q, uint32_t d4, bf16x8 (&B)[4]) {
   const uint32_t D[5] = {q.x, q.y, q.z, q.w, d4};
   uint32_t P[16];
 #pragma unroll
   for (int i = 0; i < 5; ++i) {
-    P[3 * i + 0] = and_or(D[i], 0x001F001Fu, 0x43004300u);
-    P[3 * i + 1] = and_or(D[i] >> 5, 0x001F001Fu, 0x43004300u);
-    P[3 * i + 2] = and_or(D[i] >> 10, 0x001F001Fu, 0x43004300u);
+    P[3 * i + 0] = and_or(D[i] << 2, 0x007C007Cu, kBias5Bits);
+    P[3 * i + 1] = and_or(D[i] >> 3, 0x007C007Cu, kBias5Bits);
+    P[3 * i + 2] = and_or(D[i] >> 8, 0x007C007Cu, kBias5Bits);
   }
-  uint32_t p15 = 0x43004300u;
+  // the 16th pair: code bit b is bit 15 (low half) / 31 (high half) of dword b
+  uint32_t p15 = kBias5Bits;
 #pragma unroll
-  for (int b = 0; b < 5; ++b) p15 = and_or(D[b] >> (15 - b), 0x00010001u << b, p15);
+  for (int b = 0; b < 5; ++b) p15 = and_or(D[b] >> (13 - b), 0x00010001u << (b + 2), p15);
   P[15] = p15;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -201,9 +210,9 @@ __device__ __forceinline__ void flush(f32x4& acc, const f32x4& D, const f32x4& D
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float d = f16_lo(w[i]), m = f16_hi(w[i]);
-      const float cc = fmaf(m, 0.0078125f, -d);
-      acc[i] = fmaf(d, D[i], acc[i]);
-      acc[i] = fmaf(cc, Db[i], acc[i]);
+      const float dq = D[i] - Db[i];                               // sum x q
+      acc[i] = fmaf(m * CodeBias<FMT>::inv, Db[i], acc[i]);        // m sum x (m / c exact)
+      acc[i] = fmaf(d, dq, acc[i]);
     }
   } else if constexpr (FMT == INT8) {
     float d[4];
@@ -304,8 +313,12 @@ __device__ __forceinline__ void kloop(__amdgpu_buffer_rsrc_t wq, __amdgpu_buffer
   constexpr int U = 2 * KPS;                     // k-steps per loop trip (a multiple of C::KSTEPS)
   constexpr int R = AD + 1;                      // activation ring
   static_assert(U % C::KSTEPS == 0, "cycle must divide the trip");
+  // a buffer carries the scale words of at most one cycle, the one starting
+  // at its first k-step (Step::cyc)
+  static_assert(C::KSTEPS == 1 || (KPS <= C::KSTEPS && C::KSTEPS % KPS == 0),
+                "a weight buffer may hold at most one scale-cycle start");
   static_assert(U % R == 0, "the activation ring must divide the trip");
-  const bf16x8 b128 = bf16x8_splat_128();
+  const bf16x8 bias_op = bf16x8_splat(FMT == INT5 ? kBias5Bits : kBias4Bits);   // int formats' code bias
   // HALVES: operand lanes 0-31 hold a group's columns 0-15 (block 0), lanes 32-63 columns 16-31 (block 1)
   const uint32_t lo_mask = (threadIdx.x & 32) ? 0u : 0xFFFFFFFFu;
   Step<FMT, NT, KPS> buf[2];
@@ -392,7 +405,7 @@ __device__ __forceinline__ void kloop(__amdgpu_buffer_rsrc_t wq, __amdgpu_buffer
             if constexpr (FMT == INT4 || FMT == INT5) {
 #pragma unroll
               for (int tb = 0; tb < TB; ++tb)
-                Db[tb] = mfma(xa[kk % R][tb][j], b128, first ? f32x4{0.f, 0.f, 0.f, 0.f} : Db[tb]);
+                Db[tb] = mfma(xa[kk % R][tb][j], bias_op, first ? f32x4{0.f, 0.f, 0.f, 0.f} : Db[tb]);
             }
 #pragma unroll
             for (int t = 0; t < NT; ++t) {

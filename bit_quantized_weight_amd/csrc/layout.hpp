@@ -15,8 +15,11 @@
 //         nibble (e even ? e/2 : 4 + e/2).  ws tile 256 B: row r's 16 B at
 //         r*16, group j's dword (d | m<<16, fp16 bits) at position
 //         2*(j&1) + (j>>1).
-//   int5  wq = int4 nibble plane (low code bits) then a hi-bit plane of
-//         256 B tiles: lane's dword at lam*4, bit 16*(e&1) + 4*j + (e>>1).
+//   int5  wq = plane A of 1024 B tiles (lane's dwords D0..D3 at lam*16) then
+//         plane B of 256 B tiles (lane's dword D4 at lam*4). The lane's 32
+//         codes form 16 pairs P = 4*j + (e>>1), half h = e & 1 (slot e of
+//         group j). For P < 15 the 5-bit code is bits 16*h + 5*(P%3) .. +4
+//         of dword D(P/3); for P = 15, code bit b is bit 16*h + 15 of D(b).
 //         ws as int4.
 //   int8  wq tile 2048 B: byte (j>>1)*1024 + lam*16 + (j&1)*8 + e.
 //         ws tile 128 B: fp16 d at r*8 + 2*(2*(j&1) + (j>>1)).

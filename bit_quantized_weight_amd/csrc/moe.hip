@@ -128,44 +128,101 @@ __device__ __forceinline__ void route_slot(const int32_t* ids, int NK, int E, in
   }
 }
 
-// qgemv_moe_index: one workgroup of 256 threads; wave 0 ranks the entries.
+// Per-slot routing of every active expert at once (one wave), as the
+// single-launch MoE runs it: slot a = the a-th smallest selected expert,
+// slot_e[a], its entries' offset slot_off[a] and count slot_cnt[a], and
+// pairs[slot_off[a] ..) those flat entries t * top_k + j in (t, j) order.
+// Returns the number of active experts (every lane).
+__device__ __forceinline__ int index_lanes(const int32_t* ids, int NK, int E, int* s_v, int* pairs, int* slot_e,
+                                           int* slot_off, int* slot_cnt) {
+  const int lane = threadIdx.x & 63;
+  const Route R = route_lanes(ids, NK, E, s_v);
+  if (R.v >= 0) {
+    int below = 0, same_before = 0, same = 0;
+    for (int j = 0; j < NK; ++j) {
+      const int u = s_v[j];
+      below += u >= 0 && u < R.v;
+      same_before += u == R.v && j < lane;
+      same += u == R.v;
+    }
+    pairs[below + same_before] = lane;
+    if (R.first) {
+      slot_e[R.rank] = R.v;
+      slot_off[R.rank] = below;
+      slot_cnt[R.rank] = same;
+    }
+  }
+  return __builtin_popcountll(R.act);
+}
+
+// Routing index dump (qgemv_moe_index_by): one workgroup of 256 threads.
+// ROUTINE 0 runs route_slot once per slot, exactly as every expert
+// workgroup of qgemv_moe does; ROUTINE 1 runs index_lanes, as every
+// workgroup of the single-launch qgemv_moe_fused does. Both leave per-slot
+// (expert, offset, count) and the pairs in LDS, from which the full index is
+// written: counts and offsets for every expert, pairs, active list, and
+// meta = {active experts, 1 if some entry was outside [0, E)}.
+template <int ROUTINE>
 __global__ __launch_bounds__(256) void k_moe_index(const int32_t* ids, int NK, int E, int32_t* counts,
                                                    int32_t* offsets, int32_t* pairs, int32_t* active,
                                                    int32_t* meta) {
+  __shared__ uint32_t s_bits[kMaxExperts / 32];
+  __shared__ int s_route[2 + 64];
   __shared__ int s_v[64];
-  __shared__ int s_meta[2];
+  __shared__ int s_pairs[64];
+  __shared__ int s_slot_e[64], s_slot_off[64], s_slot_cnt[64];
+  __shared__ int s_meta[2];               // active experts, routed entries
   const int tid = threadIdx.x;
   if (tid < 64) {
-    const Route R = route_lanes(ids, NK, E, s_v);
-    // pairs: position = (# valid entries with a smaller id) + (# equal ids before)
-    if (R.v >= 0) {
-      int pos = 0;
-      for (int j = 0; j < NK; ++j) pos += (s_v[j] >= 0 && s_v[j] < R.v) || (s_v[j] == R.v && j < tid);
-      pairs[pos] = tid;
-    }
-    if (R.first) active[R.rank] = R.v;
-    const uint64_t valid = __ballot(R.v >= 0);
-    const uint64_t bad = __ballot(R.v == -1);
-    if (tid == 0) {
-      s_meta[0] = __builtin_popcountll(R.act);
-      s_meta[1] = __builtin_popcountll(valid);
-      meta[0] = s_meta[0];
-      meta[1] = bad ? 1 : 0;
+    if constexpr (ROUTINE == 0) {
+      int a = 0, off = 0;
+      for (; a < min(E, NK); ++a) {
+        route_slot(ids, NK, E, a, s_bits, s_route);
+        __builtin_amdgcn_wave_barrier();
+        const int e = s_route[0], cnt = s_route[1];
+        if (e < 0) break;                 // uniform: fewer selected experts than slots
+        if (tid < cnt) s_pairs[off + tid] = s_route[2 + tid];
+        if (tid == 0) {
+          s_slot_e[a] = e;
+          s_slot_off[a] = off;
+          s_slot_cnt[a] = cnt;
+        }
+        off += cnt;
+        __builtin_amdgcn_wave_barrier();  // s_route is rewritten by the next slot
+      }
+      if (tid == 0) {
+        s_meta[0] = a;
+        s_meta[1] = off;
+      }
+    } else {
+      const int n = index_lanes(ids, NK, E, s_v, s_pairs, s_slot_e, s_slot_off, s_slot_cnt);
+      __builtin_amdgcn_wave_barrier();
+      if (tid == 0) {
+        int tot = 0;
+        for (int a = 0; a < n; ++a) tot += s_slot_cnt[a];
+        s_meta[0] = n;
+        s_meta[1] = tot;
+      }
     }
   }
   __syncthreads();
-  for (int p = s_meta[1] + tid; p < NK; p += blockDim.x) pairs[p] = -1;
+  const int n_active = s_meta[0], routed = s_meta[1];
+  for (int p = tid; p < NK; p += blockDim.x) pairs[p] = p < routed ? s_pairs[p] : -1;
   for (int e = tid; e < E; e += blockDim.x) {
     int c = 0, below = 0;
-    for (int j = 0; j < NK; ++j) {
-      c += s_v[j] == e;
-      below += s_v[j] >= 0 && s_v[j] < e;
+    for (int a = 0; a < n_active; ++a) {
+      c += s_slot_e[a] == e ? s_slot_cnt[a] : 0;
+      below += s_slot_e[a] < e ? s_slot_cnt[a] : 0;
     }
     counts[e] = c;
     offsets[e] = below;
-    if (e >= s_meta[0]) active[e] = -1;
+    active[e] = e < n_active ? s_slot_e[e] : -1;
   }
-  if (tid == 0) offsets[E] = s_meta[1];
+  if (tid == 0) {
+    offsets[E] = routed;
+    meta[0] = n_active;
+    meta[1] = routed < NK ? 1 : 0;
+  }
 }
 
 struct MoeArgs {
@@ -428,6 +485,17 @@ constexpr int kCtrError = 3, kCtrH = 4, kReadyWord = 32;
 constexpr int kReadyStride = 16;            // 64 bytes per flag
 constexpr uint32_t kSpinLimit = 1u << 20;   // polls before a wait gives up
 
+// Hand-offs between workgroups use agent-scope atomics with relaxed order:
+// h is written and read with device-scope (sc1) buffer accesses, which
+// bypass the per-XCD L2s and complete at the coherence point. A gate/up
+// item's threads wait for their h stores to complete (s_waitcnt) and meet at
+// a barrier before thread 0 adds to the slot counter, so the count cannot
+// run ahead of the data; the item that completes the slot stores the ready
+// flags after its counter result returns; an output wave issues its h loads
+// only after its poll has returned the flag (a value-dependent branch; the
+// signal fence keeps the compiler from hoisting the loads). Release/acquire
+// at agent scope would add an L2 writeback / invalidate per hand-off: on the
+// dense split remainder that measured 2x slower.
 __device__ __forceinline__ uint32_t ctr_load(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -510,23 +578,8 @@ __global__ __launch_bounds__(64 * kFusedWaves) void k_moe_fused(MoeFusedArgs f) 
   __syncthreads();
   // routing index: slot a = a-th smallest active expert, its entries in (t, j) order
   if (wave == 0) {
-    const Route R = route_lanes(s_ids, f.NK, f.E, s_v);
-    if (R.v >= 0) {
-      int below = 0, same_before = 0, same = 0;
-      for (int j = 0; j < f.NK; ++j) {
-        const int u = s_v[j];
-        below += u >= 0 && u < R.v;
-        same_before += u == R.v && j < lane;
-        same += u == R.v;
-      }
-      s_pairs[below + same_before] = lane;
-      if (R.first) {
-        s_slot_e[R.rank] = R.v;
-        s_slot_off[R.rank] = below;
-        s_slot_cnt[R.rank] = same;
-      }
-    }
-    if (lane == 0) s_meta[0] = __builtin_popcountll(R.act);
+    const int n = index_lanes(s_ids, f.NK, f.E, s_v, s_pairs, s_slot_e, s_slot_off, s_slot_cnt);
+    if (lane == 0) s_meta[0] = n;
   }
   if (blockIdx.x == 0 && threadIdx.x < f.NK) {
     if (f.ids_out) f.ids_out[threadIdx.x] = s_ids[threadIdx.x];
@@ -547,7 +600,8 @@ __global__ __launch_bounds__(64 * kFusedWaves) void k_moe_fused(MoeFusedArgs f) 
     __syncthreads();
     if (s_meta[1]) {                      // h of this slot is complete: release the output blocks
       if (threadIdx.x == 0) ctr_store(ctr + kCtrH + a, 0u);
-      for (int b = threadIdx.x; b < f.nB; b += blockDim.x) ctr_store(ready + ((size_t)a * f.nB + b) * kReadyStride, 1u);
+      for (int b = threadIdx.x; b < f.nB; b += blockDim.x)
+        ctr_store(ready + ((size_t)a * f.nB + b) * kReadyStride, 1u);
     }
     return;
   }
@@ -629,15 +683,27 @@ extern "C" int qgemv_moe_workspace_bytes(int E, int64_t H, int64_t I, int N, int
   return QGEMV_OK;
 }
 
-extern "C" int qgemv_moe_index(const int32_t* ids, int N, int top_k, int E, int32_t* counts, int32_t* offsets,
-                               int32_t* pairs, int32_t* active, int32_t* meta, hipStream_t stream) {
+extern "C" int qgemv_moe_index_by(int routine, const int32_t* ids, int N, int top_k, int E, int32_t* counts,
+                                  int32_t* offsets, int32_t* pairs, int32_t* active, int32_t* meta,
+                                  hipStream_t stream) {
+  if (routine != 0 && routine != 1) return QGEMV_EINVAL;
   if (!ids || !counts || !offsets || !pairs || !active || !meta) return QGEMV_EINVAL;
   if (E < 1) return QGEMV_EINVAL;
+  if (E > kMaxExperts) return QGEMV_EUNSUPPORTED;
   if (N < 1 || N > 8 || top_k < 1 || top_k > 8) return QGEMV_EUNSUPPORTED;
   if (!al4(ids) || !al4(counts) || !al4(offsets) || !al4(pairs) || !al4(active) || !al4(meta)) return QGEMV_EALIGN;
-  hipLaunchKernelGGL(k_moe_index, dim3(1), dim3(256), 0, stream, ids, N * top_k, E, counts, offsets, pairs, active,
-                     meta);
+  if (routine == 0)
+    hipLaunchKernelGGL(k_moe_index<0>, dim3(1), dim3(256), 0, stream, ids, N * top_k, E, counts, offsets, pairs,
+                       active, meta);
+  else
+    hipLaunchKernelGGL(k_moe_index<1>, dim3(1), dim3(256), 0, stream, ids, N * top_k, E, counts, offsets, pairs,
+                       active, meta);
   return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
+}
+
+extern "C" int qgemv_moe_index(const int32_t* ids, int N, int top_k, int E, int32_t* counts, int32_t* offsets,
+                               int32_t* pairs, int32_t* active, int32_t* meta, hipStream_t stream) {
+  return qgemv_moe_index_by(0, ids, N, top_k, E, counts, offsets, pairs, active, meta, stream);
 }
 
 namespace {

@@ -188,8 +188,12 @@ int qgemv_swiglu(int fmt, const void* wq, const void* ws, const void* x, float* 
  *               the flags it used at zero, so one fill serves later calls in
  *               stream order; calls that may overlap in time need separate
  *               workspaces. The first 32-bit word is a sticky flag that
- *               becomes nonzero if a wait ever timed out (that call's
- *               results are then invalid).
+ *               becomes nonzero if a wait ever timed out. The results of
+ *               that call are then invalid, and so is the workspace: a late
+ *               fragment may still raise its flag after the waiter gave up,
+ *               so zero the whole workspace again before reusing it. The
+ *               library never reads the word back (that would need a
+ *               synchronisation); the caller checks it after synchronising.
  *               workspace_bytes: its size (QGEMV_EWORKSPACE if smaller).
  * Zero-initialise unused fields. */
 enum { QGEMV_BATCH_INVARIANT = 1 };
@@ -238,7 +242,7 @@ int qgemv_moe_workspace_bytes(int E, int64_t H, int64_t I, int N, int top_k, siz
  * Only the experts some token selected are read. Ids outside [0, E) add
  * nothing and set the error flag that qgemv_moe_index reports. Duplicate
  * ids in a row are processed as separate slots. top_k <= 8, N <= 8,
- * I % 16 == 0. */
+ * H % 32 == 0 and I % 32 == 0 (QGEMV_EALIGN otherwise). */
 int qgemv_moe(int fmt, const void* wq_gu, const void* ws_gu, const void* wq_dn, const void* ws_dn,
               int E, int64_t H, int64_t I, const void* x, const int32_t* ids, const float* gates,
               int top_k, const float* residual, float* y, int N, void* workspace,
@@ -281,8 +285,9 @@ int qgemv_moe_fused_workspace_bytes(int E, int64_t H, int64_t I, int N, int top_
  *   region's size depends on H only; N, E, I and top_k may change if the
  *   workspace is large enough). Calls that may overlap in time need separate
  *   workspaces. Byte offset 12 holds a sticky 32-bit flag that becomes
- *   nonzero if a dependency wait ever timed out (the results of that call are
- *   then invalid). Workgroups wait only on lower-numbered ones, which start
+ *   nonzero if a dependency wait ever timed out. The results of that call
+ *   are then invalid, and so is the workspace (a late flag may be raised
+ *   after the waiter gave up): zero it again before reusing it. Workgroups wait only on lower-numbered ones, which start
  *   first on every XCD, so the waits need no co-residency.
  * Other arguments and limits as qgemv_moe; 1 <= top_k <= min(E, 8). */
 int qgemv_moe_fused(int fmt, const void* wq_gu, const void* ws_gu, const void* wq_dn, const void* ws_dn,
@@ -290,16 +295,29 @@ int qgemv_moe_fused(int fmt, const void* wq_gu, const void* ws_gu, const void* w
                     const float* residual, float* y, int N, int32_t* ids_out, float* gates_out,
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* MoE routing index (the step qgemv_moe runs first), into caller buffers:
+/* MoE routing index (the step qgemv_moe runs first; Decapybara page, CUDA
+ * kernel list: the top-8 MoE path groups each token's selected experts),
+ * into caller buffers (device, 4-byte aligned):
  *   counts [E]      slots routed to each expert
  *   offsets [E+1]   exclusive prefix sum of counts
  *   pairs [N*top_k] flat slot t*top_k + j, ordered by (expert, t, j); -1 after
  *                   offsets[E]
  *   active [E]      experts with a nonzero count, ascending; -1 after
  *   meta [2]        {number of active experts, 1 if any id was outside [0, E)}
- * Exact integer results. */
+ * Exact integer results, built from the same device routine that every
+ * expert workgroup of qgemv_moe runs (the a-th smallest selected expert and
+ * its entries, for each slot a). N <= 8, top_k <= 8, 1 <= E <= 16384
+ * (QGEMV_EUNSUPPORTED / QGEMV_EINVAL otherwise). */
 int qgemv_moe_index(const int32_t* ids, int N, int top_k, int E, int32_t* counts, int32_t* offsets,
                     int32_t* pairs, int32_t* active, int32_t* meta, hipStream_t stream);
+
+/* The same index built by the routine of a chosen MoE path, so that each
+ * path's routing can be compared bit for bit with its definition:
+ *   routine 0: the per-slot routing of qgemv_moe (= qgemv_moe_index);
+ *   routine 1: the all-slots lane ranking of qgemv_moe_fused's single launch.
+ * Other values: QGEMV_EINVAL. Arguments and results as qgemv_moe_index. */
+int qgemv_moe_index_by(int routine, const int32_t* ids, int N, int top_k, int E, int32_t* counts,
+                       int32_t* offsets, int32_t* pairs, int32_t* active, int32_t* meta, hipStream_t stream);
 
 /* Debug / parity: write the fp32 weights the packed buffers encode,
  * w_out[m][k] for m < M, k < K. Values are exactly:
