@@ -71,6 +71,8 @@ def load(require_torch: bool = True):
         "qgemv_split_workspace_bytes": (I32, [PSZ]),
         "qgemv_moe_workspace_bytes": (I32, [I32, I64, I64, I32, I32, PSZ]),
         "qgemv_moe": (I32, [I32, P, P, P, P, I32, I64, I64, P, P, P, I32, P, P, I32, P, SZ, P]),
+        "qgemv_moe_noalloc": (I32, [I32, P, P, P, P, I32, I64, I64, P, P, P, I32, P, P, I32, P]),
+        "qgemv_moe_noalloc_max_bytes": (I32, [PSZ]),
         "qgemv_moe_index": (I32, [P, I32, I32, I32, P, P, P, P, P, P]),
         "qgemv_moe_index_by": (I32, [I32, P, I32, I32, I32, P, P, P, P, P, P]),
         "qgemv_moe_route": (I32, [P, I32, I32, I32, P, P, P]),
@@ -94,7 +96,7 @@ def symbols() -> list[str]:
     """Names of the entry points the binding declares (the C ABI)."""
     return ["qgemv_strerror", "qgemv_version", "qgemv_packed_bytes", "qgemv_expert_stride", "qgemv_pack",
             "qgemv_pack_codes", "qgemv", "qgemv_swiglu", "qgemv_ex", "qgemv_swiglu_ex", "qgemv_split_workspace_bytes",
-            "qgemv_moe_workspace_bytes", "qgemv_moe",
+            "qgemv_moe_workspace_bytes", "qgemv_moe", "qgemv_moe_noalloc", "qgemv_moe_noalloc_max_bytes",
             "qgemv_moe_index", "qgemv_moe_index_by", "qgemv_moe_route", "qgemv_moe_fused_workspace_bytes", "qgemv_moe_fused",
             "qgemv_dequant", "qgemv_probe_read", "qgemv_act_quant", "qgemv_mx", "qgemv_mx_swiglu"]
 
@@ -258,6 +260,21 @@ def qgemv_moe(fmt, wq_gu, ws_gu, wq_dn, ws_dn, E: int, H: int, I: int, x, ids, g
 def qgemv_moe_index(ids, N: int, top_k: int, E: int, counts, offsets, pairs, active, meta, stream=None) -> None:
     _check(load().qgemv_moe_index(_ptr(ids), N, top_k, E, _ptr(counts), _ptr(offsets), _ptr(pairs), _ptr(active),
                                   _ptr(meta), _stream(stream)), "qgemv_moe_index")
+
+
+def qgemv_moe_noalloc(fmt, wq_gu, ws_gu, wq_dn, ws_dn, E: int, H: int, I: int, x, ids, gates, top_k: int, y, N: int,
+                      residual=None, stream=None) -> None:
+    """qgemv_moe with its scratch in the library's static per-GPU array (no
+    workspace argument; nothing is allocated)."""
+    _check(load().qgemv_moe_noalloc(_fmt(fmt), _ptr(wq_gu), _ptr(ws_gu), _ptr(wq_dn), _ptr(ws_dn), E, H, I, _ptr(x),
+                                    _ptr(ids), _ptr(gates), top_k, _ptr(residual), _ptr(y), N, _stream(stream)),
+           "qgemv_moe_noalloc")
+
+
+def moe_noalloc_max_bytes() -> int:
+    b = ctypes.c_size_t()
+    _check(load(False).qgemv_moe_noalloc_max_bytes(ctypes.byref(b)), "qgemv_moe_noalloc_max_bytes")
+    return b.value
 
 
 def qgemv_moe_index_by(routine: int, ids, N: int, top_k: int, E: int, counts, offsets, pairs, active, meta,

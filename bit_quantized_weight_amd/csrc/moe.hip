@@ -25,6 +25,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "device.hpp"
 #include "kloop.hpp"
@@ -826,6 +827,53 @@ extern "C" int qgemv_moe(int fmt, const void* wq_gu, const void* ws_gu, const vo
   hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, stream,
                      (const float*)(wsp + L.o_off), ids, gates, residual, y, N, (int)H, top_k, E);
   return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
+}
+
+// ---- allocation-free MoE (qgemv_moe_noalloc) ---------------------------------
+// The h / o scratch of qgemv_moe in a file-scope device array instead of a
+// caller workspace. Each GPU the library runs on holds its own copy until the
+// process ends; host code never passes the array's name to a kernel (on the
+// host it only stands for the symbol): the device address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+constexpr size_t kStaticScratchBytes = size_t(4) << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];
+
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return QGEMV_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return QGEMV_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return QGEMV_OK;
+}
+}  // namespace
+
+extern "C" int qgemv_moe_noalloc(int fmt, const void* wq_gu, const void* ws_gu, const void* wq_dn, const void* ws_dn,
+                                 int E, int64_t H, int64_t I, const void* x, const int32_t* ids, const float* gates,
+                                 int top_k, const float* residual, float* y, int N, hipStream_t stream) {
+  if (E < 1 || H < 1 || I < 1) return QGEMV_EINVAL;
+  if (N < 1 || N > 8 || top_k < 1 || top_k > 8) return QGEMV_EUNSUPPORTED;
+  const size_t need = moe_layout(E, H, I, N, top_k).total;
+  if (need > kStaticScratchBytes) return QGEMV_EWORKSPACE;
+  void* p = nullptr;
+  const int rc = scratch_of_current_device(&p);
+  if (rc) return rc;
+  return qgemv_moe(fmt, wq_gu, ws_gu, wq_dn, ws_dn, E, H, I, x, ids, gates, top_k, residual, y, N, p,
+                   kStaticScratchBytes, stream);
+}
+
+extern "C" int qgemv_moe_noalloc_max_bytes(size_t* bytes) {
+  if (!bytes) return QGEMV_EINVAL;
+  *bytes = kStaticScratchBytes;
+  return QGEMV_OK;
 }
 
 extern "C" int qgemv_moe_route(const float* logits, int N, int E, int top_k, int32_t* ids, float* gates,

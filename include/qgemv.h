@@ -248,6 +248,22 @@ int qgemv_moe(int fmt, const void* wq_gu, const void* ws_gu, const void* wq_dn, 
               int top_k, const float* residual, float* y, int N, void* workspace,
               size_t workspace_bytes, hipStream_t stream);
 
+/* qgemv_moe without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Its h / o scratch lives in a static
+ * device array of qgemv_moe_noalloc_max_bytes (4 MiB) per GPU, held until the
+ * process ends; the call allocates and frees nothing. Calls whose
+ * qgemv_moe_workspace_bytes exceed that return QGEMV_EWORKSPACE. Every call
+ * on one GPU shares that GPU's array, so calls that may overlap in time on
+ * one GPU (different streams) race; calls in one stream are safe. Arguments
+ * and results otherwise as qgemv_moe (same kernels, same bits). */
+int qgemv_moe_noalloc(int fmt, const void* wq_gu, const void* ws_gu, const void* wq_dn, const void* ws_dn,
+                      int E, int64_t H, int64_t I, const void* x, const int32_t* ids, const float* gates,
+                      int top_k, const float* residual, float* y, int N, hipStream_t stream);
+
+/* The size of qgemv_moe_noalloc's static scratch, in bytes. */
+int qgemv_moe_noalloc_max_bytes(size_t* bytes);
+
 /* Top-k softmax router (Decapybara page, CUDA kernel list: a top-8 softmax
  * router in front of the experts). For each token t < N:
  *   ids[t][j]   the j-th largest of logits[t][0..E) (j < top_k); equal
