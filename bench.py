@@ -52,6 +52,9 @@ def weight_bytes(qg, fmt, M, K):
     return a + b
 
 
+# the committed rocprofv3 summary of --profile-set (kernel trace and counters)
+PROFILE_SUMMARY = "qgemv_kernels_trace_and_counters.txt"
+
 # the sources the dense kernels (k_gemv) are compiled from
 DENSE_SOURCES = ["gemv.hip", "kloop.hpp", "device.hpp", "layout.hpp", "mx.hpp"]
 
@@ -69,11 +72,11 @@ def kernel_source_hash() -> str:
 
 
 def pmc_traffic(name: str, src_hash: str):
-    """HBM bytes per launch of kernel `name` from the committed rocprofv3
-    counter summary (FETCH_SIZE + WRITE_SIZE, each scaled by what the same
+    """HBM bytes per launch of profiling case `name` from the committed
+    rocprofv3 summary (FETCH_SIZE + WRITE_SIZE, each scaled by what the same
     counter reads for a 1 GiB device copy), or None when the summary is
     missing or was taken on other kernel sources."""
-    p = os.path.join(ROOT, "profiles", "dense_layer_n1_hbm_traffic.txt")
+    p = os.path.join(ROOT, "profiles", PROFILE_SUMMARY)
     try:
         with open(p) as f:
             lines = [ln.strip() for ln in f]
@@ -84,7 +87,7 @@ def pmc_traffic(name: str, src_hash: str):
     key = f"traffic {name}:"
     for ln in lines:
         if ln.startswith(key):
-            return int(ln[len(key):].strip())
+            return int(ln[len(key):].split()[0])
     return None
 
 
@@ -126,7 +129,8 @@ def mx_only(qg, torch, synthetic, dev, steps):
 # Cases of --profile-set, in run order: (name, kind, format, M, K, N). Each
 # runs `steps` launches (steps) after 3 warm-up steps; a 16-byte probe
 # launch before each case marks it in the kernel trace.
-PROFILE_CASES = [("layer_int_n1", "layer", "int", 0, 0, 1)] + \
+PROFILE_CASES = [("layer_int_n1", "layer", "int", 0, 0, 1), ("gu_int5_n1", "gu", "int5", 2 * 17408, 5120, 1),
+                 ("gu_int5_n8", "gu", "int5", 2 * 17408, 5120, 8)] + \
     [(f"perfmt_{f}_n{n}", "perfmt", f, 17408, 5120, n) for f in ("int4", "int5", "int8", "nvfp4") for n in (1, 8)] + \
     [("layer_nvfp4_n8", "layer", "nvfp4", 0, 0, 8), ("moe_n1", "moe", "int4", 0, 0, 1), ("moe_n8", "moe", "int4", 0, 0, 8),
      ("moe_fused_n1", "moe_fused", "int4", 0, 0, 1), ("moe_fused_n8", "moe_fused", "int4", 0, 0, 8)]
@@ -140,7 +144,7 @@ def profile_set(qg, torch, synthetic, dev, steps, calib_mib):
     sink = torch.zeros(4, dtype=torch.int32, device=dev)
     mark = torch.zeros(16, dtype=torch.uint8, device=dev)
     wsp = qg.split_workspace(dev)
-    out = {"steps": steps, "cases": {}}
+    out = {"steps": steps, "src_hash": kernel_source_hash(), "cases": {}}
     if calib_mib > 0:
         qg.qgemv_probe_read(mark, 16, sink)
         src = torch.ones(calib_mib << 20, dtype=torch.uint8, device=dev)
@@ -152,18 +156,23 @@ def profile_set(qg, torch, synthetic, dev, steps, calib_mib):
         out["calib_copy_bytes"] = calib_mib << 20
     for name, kind, fmt, M, K, N in PROFILE_CASES:
         rng = synthetic.rng_for(0, 12, len(name))
-        if kind == "perfmt":
+        if kind in ("perfmt", "gu"):
             wq, ws = qg.pack(fmt, synthetic.weights(rng, M, K))
             nb = wq.size + ws.size
             copies = max(2, int(np.ceil(1.1e9 / nb)))
             d = [(torch.from_numpy(wq).to(dev), torch.from_numpy(ws).to(dev)) for _ in range(copies)]
-            x = torch.from_numpy(synthetic.activations(rng, N, K, 0.01)).to(dev)
-            y = torch.empty((N, M), dtype=torch.float32, device=dev)
+            x = torch.from_numpy(synthetic.activations(rng, N, K, 0.01 if kind == "perfmt" else 0.0)).to(dev)
+            Mo = M // 2 if kind == "gu" else M
+            y = torch.empty((N, Mo), dtype=torch.float32, device=dev)
             per = 1
-            byt = nb + N * K * 2 + N * M * 4
+            byt = nb + N * K * 2 + N * Mo * 4
 
-            def step(i):
-                qg.qgemv_ex(fmt, *d[i % copies], x, y, M, K, N, workspace=wsp)
+            if kind == "gu":
+                def step(i):
+                    qg.qgemv_swiglu_ex(fmt, *d[i % copies], x, y, Mo, K, N, workspace=wsp)
+            else:
+                def step(i):
+                    qg.qgemv_ex(fmt, *d[i % copies], x, y, M, K, N, workspace=wsp)
         elif kind == "layer":
             fm = {"qkv": "int4", "gate_up": "int5", "down": "int5"} if fmt == "int" else \
                 {"qkv": fmt, "gate_up": fmt, "down": fmt}
@@ -261,96 +270,117 @@ def _csv_rows(path):
         return list(csv.DictReader(f))
 
 
-def summarize_profile(manifest_path, trace_dir, counter_dirs, out_path, command_lines):
-    """Text summary of a --profile-set run under rocprofv3: per case and
-    kernel, launches and average duration (kernel trace), and per launch the
-    counters of each --pmc run (FETCH_SIZE / WRITE_SIZE scaled by what they
-    read for the calibration copy)."""
-    import glob
-    man = None
-    with open(manifest_path) as f:
+def _manifest(log_path):
+    with open(log_path) as f:
         for ln in f:
             ln = ln.strip()
             if ln.startswith("{") and '"cases"' in ln:
-                man = json.loads(ln)
-    if man is None:
-        raise SystemExit(f"no --profile-set manifest line in {manifest_path}")
+                return json.loads(ln)
+    raise SystemExit(f"no --profile-set manifest line in {log_path}")
 
-    def split_cases(rows, key_name, key_start):
-        rows = sorted(rows, key=lambda r: int(r[key_start]))
-        groups, cur, calib = [], None, []
-        for r in rows:
-            nm = r[key_name]
-            if "k_probe" in nm:
-                cur = []
-                groups.append(cur)
-            elif cur is not None:
-                cur.append(r)
-            elif "copyBuffer" in nm or "copy" in nm.lower():
-                calib.append(r)
-        return groups, calib
 
-    names = list(man["cases"].keys())
-    lines = [f"# rocprofv3 summary of `bench.py --profile-set --steps {man['steps']}` (kernel sources: src_hash "
-             f"{kernel_source_hash()})", "", "commands (from /tmp, TMPDIR=/tmp; the last argument names the run):"]
-    lines += [f"  {c}" for c in command_lines] + [""]
-    tr = [p for p in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)]
-    trows = _csv_rows(tr[0]) if tr else []
-    tgroups, _ = split_cases(trows, "Kernel_Name", "Start_Timestamp") if trows else ([], [])
-    counters = {}
-    for cd in counter_dirs:
-        cc = glob.glob(os.path.join(cd, "**", "*counter_collection.csv"), recursive=True)
-        if not cc:
-            continue
-        rows = _csv_rows(cc[0])
+def _case_groups(rows, man, name_key, order_key):
+    """Split dispatch rows (dicts with a kernel name) into the manifest's
+    cases: after each case's marker (a k_probe launch) come its timed steps,
+    the first steps x launches_per_step library dispatches; before the first
+    case, the calibration copies (when the run had them)."""
+    rows = sorted(rows, key=lambda r: int(r[order_key]))
+    groups, cur, pre = [], None, []
+    for r in rows:
+        if "k_probe" in r[name_key]:
+            cur = []
+            groups.append(cur)
+        elif cur is None:
+            pre.append(r)
+        else:
+            cur.append(r)
+    calib = []
+    if "calib_copy_bytes" in man and groups:
+        calib = [r for r in groups[0] if "copy" in r[name_key].lower()]
+        groups = groups[1:]
+    out = {}
+    for (name, meta), g in zip(man["cases"].items(), groups):
+        n = man["steps"] * meta["launches_per_step"]
+        out[name] = [r for r in g if "qg::" in r[name_key]][:n]
+    return out, calib
+
+
+def summarize_profile(out_path, command_lines, trace, counter_runs):
+    """Text summary of --profile-set runs under rocprofv3: per case and
+    kernel, launches and average duration (kernel trace) and, per launch, the
+    counters of each --pmc run (FETCH_SIZE / WRITE_SIZE also as bytes,
+    scaled by what they read for the 1 GiB calibration copy).
+    trace, counter_runs: (directory, log with the run's manifest line)."""
+    import glob
+    tdir, tlog = trace
+    man = _manifest(tlog)
+    tr = glob.glob(os.path.join(tdir, "**", "*kernel_trace.csv"), recursive=True)
+    tcases, _ = _case_groups(_csv_rows(tr[0]), man, "Kernel_Name", "Start_Timestamp")
+    counters, scale = [], {}
+    for cdir, clog in counter_runs:
+        cman = _manifest(clog)
+        cc = glob.glob(os.path.join(cdir, "**", "*counter_collection.csv"), recursive=True)
         by_disp = {}
-        for r in rows:
-            by_disp.setdefault(r["Dispatch_Id"], {"Kernel_Name": r["Kernel_Name"], "Dispatch_Id": r["Dispatch_Id"]})
-            c = by_disp[r["Dispatch_Id"]]
+        for r in _csv_rows(cc[0]):
+            c = by_disp.setdefault(r["Dispatch_Id"], {"Kernel_Name": r["Kernel_Name"], "Dispatch_Id": r["Dispatch_Id"]})
             c[r["Counter_Name"]] = c.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
-        groups, calib = split_cases(list(by_disp.values()), "Kernel_Name", "Dispatch_Id")
-        counters[cd] = (groups, calib)
-    scale = {}
-    for cd, (groups, calib) in counters.items():
+        cases, calib = _case_groups(list(by_disp.values()), cman, "Kernel_Name", "Dispatch_Id")
         for cn in ("FETCH_SIZE", "WRITE_SIZE"):
             vals = [c[cn] for c in calib if cn in c]
-            if vals and "calib_copy_bytes" in man:
-                scale[cn] = man["calib_copy_bytes"] / (float(np.median(vals)) * 1024)
+            if vals:
+                scale[cn] = cman["calib_copy_bytes"] / (float(np.median(vals)) * 1024)
+        counters.append(cases)
+    src_hash = man.get("src_hash", "unrecorded")
+    lines = [f"# rocprofv3 summary of bench.py --profile-set (kernel sources: src_hash {src_hash})", "",
+             "commands (from /tmp with TMPDIR=/tmp; R = the repository root):"]
+    lines += [f"  {c}" for c in command_lines] + [""]
     if scale:
-        lines.append("calibration: a 1 GiB device copy reads FETCH_SIZE x {:.4f} / WRITE_SIZE x {:.4f} of its bytes "
-                     "(KiB -> bytes scale)".format(scale.get("FETCH_SIZE", float("nan")), scale.get("WRITE_SIZE", float("nan"))))
+        lines.append("calibration: for a 1 GiB device copy FETCH_SIZE reads {:.4f} and WRITE_SIZE {:.4f} of the "
+                     "bytes moved; the byte figures below are scaled by the inverse".format(
+                         1 / scale.get("FETCH_SIZE", float("nan")), 1 / scale.get("WRITE_SIZE", float("nan"))))
         lines.append("")
-    hdr = f"{'case':16s} {'kernel':58s} {'calls':>6s} {'avg us':>8s}"
-    lines.append(hdr + "   counters per launch (averages)")
-    for ci, name in enumerate(names):
-        meta = man["cases"][name]
+    lines.append(f"{'case':16s} {'kernel':52s} {'calls':>6s} {'avg us':>8s}   counters per launch (means)")
+    for name, meta in man["cases"].items():
         per_kernel = {}
-        if ci < len(tgroups):
-            for r in tgroups[ci]:
-                per_kernel.setdefault(r["Kernel_Name"], []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-        tot_us = 0.0
+        for r in tcases.get(name, []):
+            per_kernel.setdefault(r["Kernel_Name"], []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        step_us = 0.0
         for kn, durs in per_kernel.items():
-            short = kn.split("(")[0].replace("void ", "")[:58]
+            short = kn.replace("void ", "").split("(")[0].replace("qg::", "")[:52]
             cs = []
-            for cd, (groups, _) in counters.items():
-                if ci < len(groups):
-                    sel = [c for c in groups[ci] if c["Kernel_Name"] == kn]
-                    if sel:
-                        keys = sorted(k for k in sel[0] if k not in ("Kernel_Name", "Dispatch_Id"))
-                        for k in keys:
-                            v = float(np.mean([c[k] for c in sel]))
-                            if k in scale:
-                                cs.append(f"{k}={v:.1f}KiB({v * 1024 * scale[k] / 1e6:.2f}MB)")
-                            else:
-                                cs.append(f"{k}={v:.4g}")
+            for cases in counters:
+                sel = [c for c in cases.get(name, []) if c["Kernel_Name"] == kn]
+                if not sel:
+                    continue
+                for k in sorted(k for k in sel[0] if k not in ("Kernel_Name", "Dispatch_Id")):
+                    v = float(np.mean([c[k] for c in sel]))
+                    if k in scale:
+                        cs.append(f"{k}={v:.0f}KiB={v * 1024 * scale[k] / 1e6:.2f}MB")
+                    else:
+                        cs.append(f"{k}={v:.4g}")
             avg = float(np.mean(durs))
-            tot_us += avg * len(durs) / max(1, man["steps"])
-            lines.append(f"{name:16s} {short:58s} {len(durs):6d} {avg:8.2f}   " + " ".join(cs))
+            step_us += avg * len(durs) / man["steps"]
+            lines.append(f"{name:16s} {short:52s} {len(durs):6d} {avg:8.2f}   " + " ".join(cs))
         if per_kernel:
-            gbs = meta["algorithmic_bytes_per_step"] / (tot_us * 1e-6) / 1e9
-            lines.append(f"{name:16s} {'= per step: sum of kernel averages':58s} {'':6s} {tot_us:8.2f}   "
-                         f"algorithmic {meta['algorithmic_bytes_per_step']} B -> {gbs:.0f} GB/s "
-                         f"({gbs / PEAK_GBS:.3f} of 8 TB/s); events {meta['us_per_step_events']} us")
+            gbs = meta["algorithmic_bytes_per_step"] / (step_us * 1e-6) / 1e9
+            lines.append(f"{name:16s} {'= step: sum of the kernel averages':52s} {'':6s} {step_us:8.2f}   "
+                         f"{meta['algorithmic_bytes_per_step']} algorithmic B -> {gbs:.0f} GB/s "
+                         f"({gbs / PEAK_GBS:.3f} of 8 TB/s); HIP events in the same run {meta['us_per_step_events']} us")
+    # machine-readable traffic per launch of the single-kernel cases (bench.py
+    # reads these for its roofline entries; they hold only for this src_hash)
+    if {"FETCH_SIZE", "WRITE_SIZE"} <= set(scale):
+        lines += ["", "machine-readable (HBM bytes per launch, scaled FETCH_SIZE + WRITE_SIZE):", f"src_hash: {src_hash}"]
+        for name, meta in man["cases"].items():
+            if meta["launches_per_step"] != 1:
+                continue
+            tot = 0.0
+            for cases in counters:
+                sel = cases.get(name, [])
+                for cn in ("FETCH_SIZE", "WRITE_SIZE"):
+                    vals = [c[cn] for c in sel if cn in c]
+                    if vals:
+                        tot += float(np.mean(vals)) * 1024 * scale[cn]
+            lines.append(f"traffic {name}: {int(round(tot))}  (algorithmic {meta['algorithmic_bytes_per_step']})")
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -371,17 +401,19 @@ def main():
                     help="run the profiling cases (per-format [17408][5120] at N = 1 and 8, the dense layer, "
                          "the NVFP4 layer at N = 8, MoE) under rocprofv3 and print their manifest")
     ap.add_argument("--summarize-profile", nargs="+", metavar="ARG",
-                    help="MANIFEST_LOG TRACE_DIR OUT_TXT COMMANDS_TXT [COUNTER_DIR ...]: write the text summary "
-                         "of a --profile-set run (COMMANDS_TXT: the profiler command lines, one per line)")
+                    help="OUT_TXT COMMANDS_TXT TRACE_DIR:LOG [COUNTER_DIR:LOG ...]: write the text summary of "
+                         "--profile-set runs (each directory with the log holding that run's manifest line; "
+                         "COMMANDS_TXT: the profiler command lines, one per line)")
     ap.add_argument("--mx-only", action="store_true",
                     help="only the MX GEMV on [17408][5120] at N = 1 (MXFP8 and MXFP4, after the activation "
                          "quantiser): a short run for profiling those kernels")
     args = ap.parse_args()
     if args.summarize_profile:
         a = args.summarize_profile
-        with open(a[3]) as f:
+        with open(a[1]) as f:
             cmds = [ln.rstrip("\n") for ln in f if ln.strip()]
-        summarize_profile(a[0], a[1], a[4:], a[2], cmds)
+        pairs = [tuple(x.split(":", 1)) for x in a[2:]]
+        summarize_profile(a[0], cmds, pairs[0], pairs[1:])
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
@@ -528,11 +560,11 @@ def main():
     qg.check_split_workspace(wsp)
     roofline = {"bound": "hbm", "kernel": "k_gemv<int5, swiglu> (gate/up + SwiGLU, split remainder), N=1",
                 "achieved": round(gu_gbs, 1), "peak": PEAK_GBS, "unit": "GB/s", "frac": round(gu_gbs / PEAK_GBS, 4),
-                "traffic": pmc_traffic("gate_up_swiglu_int5", src_hash),
+                "traffic": pmc_traffic("gu_int5_n1", src_hash),
                 "algorithmic_bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_ms * 1e3, 2)}
     roofline_n8 = {"bound": "hbm", "kernel": "k_gemv<int5, swiglu> (gate/up + SwiGLU, split remainder), N=8",
                    "achieved": round(gu8_gbs, 1), "peak": PEAK_GBS, "unit": "GB/s",
-                   "frac": round(gu8_gbs / PEAK_GBS, 4), "traffic": pmc_traffic("gate_up_swiglu_int5_n8", src_hash),
+                   "frac": round(gu8_gbs / PEAK_GBS, 4), "traffic": pmc_traffic("gu_int5_n8", src_hash),
                    "algorithmic_bytes_per_launch": gu8_bytes, "avg_launch_us": round(gu8_ms * 1e3, 2)}
     mlp_chain = {"workload": "27B-class MLP block, N=1, dependent launches: RMSNorm + gate/up 2x17408x5120 int5 + "
                              "SwiGLU -> bf16 h -> down 5120x17408 int5 + residual",

@@ -42,20 +42,33 @@
 
 namespace qg {
 
+// The fields a wave needs to issue its first weight loads come first, so the
+// kernel fetches them with one scalar load of the argument block and starts
+// streaming after a single round trip (the rest arrives meanwhile).
 struct GemvArgs {
   const uint8_t* wq;
   const uint8_t* ws;
+  uint32_t wq_bytes, ws_bytes;
+  uint32_t hi_offset;
+  int KS;
+  int ks_per_wave;
+  int out_tiles;          // 16-row output tiles (M/16 rounded up)
+  int up_tile0;           // swiglu: tile index of the first "up" row tile
+  // Split remainder (frag > 1): workgroups [0, n_full) own whole row blocks;
+  // workgroup n_full + b * frag + f owns K fragment f of row block n_full + b
+  // (frag a power of two, 2^frag_log2). A fragment's waves take frag_kpw
+  // k-steps each (enough for the largest fragment). Fragments below the
+  // last publish partial sums (part) and raise a flag; the last fragment
+  // (the highest workgroup of its block) adds them.
+  int n_full, frag, frag_log2, frag_kpw;
+  int waves;              // waves per workgroup (the block holds 64 * waves lanes)
   const uint16_t* x;      // bf16 [N][K]
   const float* res;       // [N][M] or null
   float* y;               // [N][M]  (swiglu: [N][I])
-  uint32_t wq_bytes, ws_bytes, x_bytes;
-  uint32_t hi_offset, st_offset;
+  uint32_t x_bytes, st_offset;
   int M;                  // output columns (I for swiglu)
-  int K, KS, G;           // G = K / 32 groups that hold data
+  int K, G;               // G = K / 32 groups that hold data
   int N;
-  int out_tiles;          // 16-row output tiles (M/16 rounded up)
-  int up_tile0;           // swiglu: tile index of the first "up" row tile
-  int ks_per_wave;
   int x_nks;              // LDS activation records per wave (XM_LDS kernels)
   // RMSNorm prologue (nsrc != null): activations are bf16(gamma * nsrc), and
   // the per-token scale 1 / sqrt(mean(nsrc^2) + eps) multiplies the dot
@@ -66,11 +79,6 @@ struct GemvArgs {
   uint32_t nsrc_bytes, gamma_bytes;
   uint16_t* ybf;          // bf16 copy of the output [N][M], or null
   bool ystore;            // write the fp32 output y
-  // Split remainder (frag > 1): workgroups [0, n_full) own whole row blocks;
-  // workgroup n_full + b * frag + f owns K fragment f of row block n_full + b.
-  // Fragments below the last publish partial sums (part) and raise a flag;
-  // the last fragment (the highest workgroup of its block) adds them.
-  int n_full, frag;
   float* part;            // [(blocks - n_full) * (frag - 1)][NT * 128]
   uint32_t* pflag;        // word 0: sticky error; flags from word 64, 16 words apart
 };
@@ -273,7 +281,7 @@ void k_gemv(GemvArgs a) {
   __shared__ float s_ss[8][8];                                  // RMSNorm: [wave][token] sums of squares
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
-  const int W = blockDim.x >> 6;
+  const int W = a.waves;
   const int r = lane & 15, s = lane >> 4;
   constexpr int TO = SWIGLU ? NT / 2 : NT;
   constexpr int T = 16 / S;
@@ -281,37 +289,46 @@ void k_gemv(GemvArgs a) {
   constexpr int RB = TK * 16;             // floats per (wave, tile) there
   using C = Cyc<FMT, S>;
 
-  const __amdgpu_buffer_rsrc_t wq = make_rsrc(a.wq, a.wq_bytes);
-  const __amdgpu_buffer_rsrc_t ws = make_rsrc(a.ws, a.ws_bytes);
+  // Every argument the first weight loads need, fetched in one batch: the
+  // empty asm takes them as scalar-register inputs, so the compiler issues
+  // their loads together here instead of next to each use behind the
+  // branches below (three dependent round trips to the argument block)
+  const uint8_t* const a_wq = a.wq;
+  const uint8_t* const a_ws = a.ws;
+  const uint32_t a_wqb = a.wq_bytes, a_wsb = a.ws_bytes, a_hi = a.hi_offset;
+  const int a_KS = a.KS, a_kpw = a.ks_per_wave, a_ot = a.out_tiles, a_up = a.up_tile0;
+  const int a_nf = a.n_full, a_fr = a.frag, a_fl = a.frag_log2, a_fk = a.frag_kpw;
+  asm volatile("" ::"s"(a_wq), "s"(a_ws), "s"(a_wqb), "s"(a_wsb), "s"(a_hi), "s"(a_KS), "s"(a_kpw), "s"(a_ot),
+               "s"(a_up), "s"(a_nf), "s"(a_fr), "s"(a_fl), "s"(a_fk), "s"(W));
+  const __amdgpu_buffer_rsrc_t wq = make_rsrc(a_wq, a_wqb);
+  const __amdgpu_buffer_rsrc_t ws = make_rsrc(a_ws, a_wsb);
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, a.x_bytes);
 
   // row tiles of this wave (clamped: out-of-range tiles compute a copy of the
   // last tile and are never stored)
-  int rblk = blockIdx.x, frag = -1;       // row block and K fragment (uniform)
-  if (a.frag > 1 && rblk >= a.n_full) {
-    const int q = rblk - a.n_full;
-    rblk = a.n_full + q / a.frag;
-    frag = q - (q / a.frag) * a.frag;
-  }
+  // row block and K fragment (uniform), without branches or divisions
+  const int bid = blockIdx.x;
+  const bool isfrag = a_fr > 1 && bid >= a_nf;
+  const int fq = bid - a_nf;
+  const int rblk = isfrag ? a_nf + (fq >> a_fl) : bid;
+  const int frag = isfrag ? (fq & (a_fr - 1)) : -1;
   int tile[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     int ot = rblk * TO + (SWIGLU ? (t % TO) : t);
-    ot = ot < a.out_tiles ? ot : a.out_tiles - 1;
-    tile[t] = (SWIGLU && t >= TO) ? a.up_tile0 + ot : ot;
+    ot = ot < a_ot ? ot : a_ot - 1;
+    tile[t] = (SWIGLU && t >= TO) ? a_up + ot : ot;
   }
 
   f32x4 acc[NT * TB];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  int kb0 = 0, kb1 = a.KS, kpw = a.ks_per_wave;
-  if (frag >= 0) {                        // this fragment's K range in whole cycles, split over the waves
-    constexpr int CK = C::KSTEPS;
-    const int nc = (a.KS + CK - 1) / CK;
-    kb0 = frag * nc / a.frag * CK;
-    kb1 = min(a.KS, (frag + 1) * nc / a.frag * CK);
-    kpw = ((kb1 - kb0 + CK - 1) / CK + W - 1) / W * CK;
-  }
+  // a fragment's K range: whole cycles, fragment f of 2^frag_log2
+  constexpr int CK = C::KSTEPS;
+  const int nc = (a_KS + CK - 1) / CK;
+  const int kb0 = isfrag ? ((frag * nc) >> a_fl) * CK : 0;
+  const int kb1 = isfrag ? min(a_KS, (((frag + 1) * nc) >> a_fl) * CK) : a_KS;
+  const int kpw = isfrag ? a_fk : a_kpw;
   const int ks0 = kb0 + wave * kpw;
   const int ks1 = min(kb1, ks0 + kpw);
   constexpr bool norm = NORM;
@@ -358,7 +375,7 @@ void k_gemv(GemvArgs a) {
         if constexpr (NORM) stage_x_norm(xl, hr, gr, a.N, a.K, ks0, ks1, a.x_nks, lane, s_ss[wave]);
         else stage_x(xl, xr, a.N, a.K, ks0, ks1, a.x_nks, lane);
       };
-      kloop<FMT, NT, S, KPS, 1>(wq, ws, tile, a.KS, ks0, ks1, a.hi_offset, acts, acc, pre);
+      kloop<FMT, NT, S, KPS, 1>(wq, ws, tile, a_KS, ks0, ks1, a_hi, acts, acc, pre);
     } else {
       // Ring slot of k-step k: (k - ks0) % kRing, which equals its trip
       // position modulo kRing (trips start at ks0 + a multiple of 2 * KPS).
@@ -411,7 +428,7 @@ void k_gemv(GemvArgs a) {
         ring_load(stg[1], ks0 + 2);
         ring_store(v0, 0);
       };
-      kloop<FMT, NT, S, KPS, 1>(wq, ws, tile, a.KS, ks0, ks1, a.hi_offset, acts, acc, pre);
+      kloop<FMT, NT, S, KPS, 1>(wq, ws, tile, a_KS, ks0, ks1, a_hi, acts, acc, pre);
       if (NORM && ks0 < ks1) {
         // tokens (lane >> 4) and 4 + (lane >> 4): sum the 16 lanes of each row
 #pragma unroll
@@ -433,7 +450,7 @@ void k_gemv(GemvArgs a) {
         return __builtin_bit_cast(bf16x8, ld128s(xr, xbase + adj, (uint32_t)g * 64u));
       };
       auto acts = [&](bf16x8 (&A)[4], int k, int pos) { load_acts<FMT, S>(A, k, ks1, a.G, pos % C::KSTEPS, aload); };
-      kloop<FMT, NT, S, KPS, 1>(wq, ws, tile, a.KS, ks0, ks1, a.hi_offset, acts, acc);
+      kloop<FMT, NT, S, KPS, 1>(wq, ws, tile, a_KS, ks0, ks1, a_hi, acts, acc);
     } else {
       // block b's A row r = token 16 b + r (one slot: no slot term)
       uint32_t xbase[TB];
@@ -451,7 +468,7 @@ void k_gemv(GemvArgs a) {
           load_acts<FMT, S>(A[b], k, ks1, a.G, pos % C::KSTEPS, aload);
         }
       };
-      kloop<FMT, NT, S, KPS, 1, TB>(wq, ws, tile, a.KS, ks0, ks1, a.hi_offset, acts, acc);
+      kloop<FMT, NT, S, KPS, 1, TB>(wq, ws, tile, a_KS, ks0, ks1, a_hi, acts, acc);
     }
   }
 
@@ -824,17 +841,33 @@ int64_t split_bytes(int cus) { return split_flag_bytes(cus) + split_slots(cus) *
 void plan_split(int fmt, const LaunchShape& ls, bool swiglu, int64_t out_tiles, int64_t KS, int cus, GemvArgs& a) {
   a.n_full = 0;
   a.frag = 1;
+  a.frag_log2 = 0;
+  a.frag_kpw = 0;
   if (cus < 1) return;
   const int64_t to = swiglu ? ls.nt / 2 : ls.nt;
   const int64_t blocks = (out_tiles + to - 1) / to;
   const int64_t n_full = blocks / cus * cus, r = blocks - n_full;
   if (r == 0 || 2 * r > cus) return;
   const int64_t F = cus / std::gcd(r, (int64_t)cus);
-  if (F > kMaxFrag) return;
+  if (F > kMaxFrag || (F & (F - 1))) return;        // the kernel divides by shifts
   const int cyc = cycle_ksteps(fmt, ls.slots);
-  if ((KS + cyc - 1) / cyc / F < ls.waves) return;
+  const int64_t nc = (KS + cyc - 1) / cyc;
+  if (nc / F < ls.waves) return;
+  int lg = 0;
+  while ((int64_t(1) << lg) < F) ++lg;
+  // k-steps per wave that cover the largest fragment (never more than the
+  // unsplit range, which sizes the LDS activation records)
+  int64_t kpw = 0;
+  for (int64_t f = 0; f < F; ++f) {
+    const int64_t b0 = ((f * nc) >> lg) * cyc, b1 = std::min(KS, (((f + 1) * nc) >> lg) * cyc);
+    const int64_t c = ((b1 - b0 + cyc - 1) / cyc + ls.waves - 1) / ls.waves * cyc;
+    kpw = std::max(kpw, c);
+  }
+  if (kpw > ls.kpw) return;
   a.n_full = (int)n_full;
   a.frag = (int)F;
+  a.frag_log2 = lg;
+  a.frag_kpw = (int)kpw;
 }
 
 using KernelFn = void (*)(GemvArgs);
@@ -862,6 +895,7 @@ hipError_t launch_s(const GemvArgs& a0, const LaunchShape& ls, bool swiglu, hipS
   const int64_t blocks = (a0.out_tiles + TO - 1) / TO;
   const dim3 block((unsigned)(64 * ls.waves));
   GemvArgs a = a0;
+  a.waves = ls.waves;
   const int U = 2 * KPS;   // k-steps per trip of the k-loop
   a.x_nks = (ls.kpw + U - 1) / U * U + 1;
   const size_t rec = (size_t)a.N * 256 + 16;
@@ -1023,6 +1057,8 @@ int run_gemv(int fmt, const void* wq, const void* ws, const void* x, const float
   a.ks_per_wave = ls.kpw;
   a.n_full = 0;
   a.frag = 1;
+  a.frag_log2 = 0;
+  a.frag_kpw = 0;
   a.part = nullptr;
   a.pflag = nullptr;
   if (fz && fz->workspace) {
