@@ -222,7 +222,7 @@ def check_moe_fused_workspace(workspace) -> None:
     import torch
     torch.cuda.synchronize(workspace.device)
     if int(workspace[12:16].view(torch.int32).item()) != 0:
-        raise RuntimeError("qgemv_moe_fused dependency wait timed out: results invalid; zero the workspace")
+        raise RuntimeError("qgemv_moe_fused dependency wait timed out: results invalid; clear bytes 12-15")
 
 
 def qgemv_ex(fmt, wq, ws, x, y, M: int, K: int, N: int, residual=None, norm_src=None, norm_gamma=None,

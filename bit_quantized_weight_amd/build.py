@@ -24,10 +24,12 @@ LIB = os.path.join(HERE, "libqgemv.so")
 
 ARCH = "gfx950"
 HIP_SOURCES = ["gemv.hip", "moe.hip", "mx.hip"]
-# moe.hip: keep single-lane atomics as written (the atomic optimizer would
-# wave-aggregate the work-ticket claim and wait for its result at once,
-# instead of when the ticket is first needed)
-EXTRA_FLAGS = {"moe.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
+# moe.hip: atomics (the routing bitmap's LDS ORs, the sticky error word) stay
+# single-lane as written. gemv.hip: the kernel's leading scalar arguments are
+# preloaded into SGPRs at wave launch (gfx950 kernel argument preloading), so
+# a wave issues its first weight loads without reading the argument block.
+EXTRA_FLAGS = {"moe.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"],
+               "gemv.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"]}
 HOST_SOURCES = ["pack.cpp"]
 
 

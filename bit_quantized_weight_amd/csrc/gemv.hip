@@ -275,7 +275,8 @@ constexpr int min_waves_per_simd() {
 
 template <int FMT, int NT, int S, int KPS, bool SWIGLU, int XM, bool NORM, int TB = 1>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<FMT, NT, S, XM, NORM, TB>())))
-void k_gemv(GemvArgs a) {
+void k_gemv(const uint8_t* a_wq, const uint8_t* a_ws, uint32_t a_wqb, uint32_t a_wsb, uint32_t a_hi, int a_KS,
+            int a_kpw, int a_ot, int a_up, int a_nf, int a_fl, int a_fk, GemvArgs a) {
   static_assert(TB == 1 || (XM == XM_LOAD && !NORM), "token blocks load their activations directly");
   extern __shared__ __attribute__((aligned(16))) float red[];  // [W][NT][8][16], then the LDS activations
   __shared__ float s_ss[8][8];                                  // RMSNorm: [wave][token] sums of squares
@@ -289,29 +290,24 @@ void k_gemv(GemvArgs a) {
   constexpr int RB = TK * 16;             // floats per (wave, tile) there
   using C = Cyc<FMT, S>;
 
-  // Every argument the first weight loads need, fetched in one batch: the
-  // empty asm takes them as scalar-register inputs, so the compiler issues
-  // their loads together here instead of next to each use behind the
-  // branches below (three dependent round trips to the argument block)
-  const uint8_t* const a_wq = a.wq;
-  const uint8_t* const a_ws = a.ws;
-  const uint32_t a_wqb = a.wq_bytes, a_wsb = a.ws_bytes, a_hi = a.hi_offset;
-  const int a_KS = a.KS, a_kpw = a.ks_per_wave, a_ot = a.out_tiles, a_up = a.up_tile0;
-  const int a_nf = a.n_full, a_fr = a.frag, a_fl = a.frag_log2, a_fk = a.frag_kpw;
-  asm volatile("" ::"s"(a_wq), "s"(a_ws), "s"(a_wqb), "s"(a_wsb), "s"(a_hi), "s"(a_KS), "s"(a_kpw), "s"(a_ot),
-               "s"(a_up), "s"(a_nf), "s"(a_fr), "s"(a_fl), "s"(a_fk), "s"(W));
+  // The a_* arguments (copies of GemvArgs fields) are everything the first
+  // weight loads need. As leading scalar kernel arguments they are preloaded
+  // into SGPRs when the wave starts (the library is built with kernel
+  // argument preloading), so a wave issues its first loads without a round
+  // trip to the argument block.
+  const int a_fr = 1 << a_fl;
   const __amdgpu_buffer_rsrc_t wq = make_rsrc(a_wq, a_wqb);
   const __amdgpu_buffer_rsrc_t ws = make_rsrc(a_ws, a_wsb);
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, a.x_bytes);
 
-  // row tiles of this wave (clamped: out-of-range tiles compute a copy of the
-  // last tile and are never stored)
   // row block and K fragment (uniform), without branches or divisions
   const int bid = blockIdx.x;
   const bool isfrag = a_fr > 1 && bid >= a_nf;
   const int fq = bid - a_nf;
   const int rblk = isfrag ? a_nf + (fq >> a_fl) : bid;
   const int frag = isfrag ? (fq & (a_fr - 1)) : -1;
+  // row tiles of this wave (clamped: out-of-range tiles compute a copy of the
+  // last tile and are never stored)
   int tile[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
@@ -322,7 +318,7 @@ void k_gemv(GemvArgs a) {
 
   f32x4 acc[NT * TB];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < NT * TB; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   // a fragment's K range: whole cycles, fragment f of 2^frag_log2
   constexpr int CK = C::KSTEPS;
   const int nc = (a_KS + CK - 1) / CK;
@@ -331,6 +327,10 @@ void k_gemv(GemvArgs a) {
   const int kpw = isfrag ? a_fk : a_kpw;
   const int ks0 = kb0 + wave * kpw;
   const int ks1 = min(kb1, ks0 + kpw);
+  // the first weight loads, before the activation set-up below reads any
+  // argument of the block that is not preloaded
+  Step<FMT, NT, KPS> wbuf[2];
+  kloop_start<FMT, NT, S, KPS>(wbuf, wq, ws, tile, a_KS, ks0, ks1, a_hi);
   constexpr bool norm = NORM;
   static_assert(!NORM || XM != XM_LOAD, "the prologue stages its activations in LDS");
   const __amdgpu_buffer_rsrc_t hr = make_rsrc(a.nsrc, a.nsrc_bytes);
@@ -375,7 +375,7 @@ void k_gemv(GemvArgs a) {
         if constexpr (NORM) stage_x_norm(xl, hr, gr, a.N, a.K, ks0, ks1, a.x_nks, lane, s_ss[wave]);
         else stage_x(xl, xr, a.N, a.K, ks0, ks1, a.x_nks, lane);
       };
-      kloop<FMT, NT, S, KPS, 1>(wq, ws, tile, a_KS, ks0, ks1, a_hi, acts, acc, pre);
+      kloop_run<FMT, NT, S, KPS, 1>(wbuf, wq, ws, tile, a_KS, ks0, ks1, a_hi, acts, acc, pre);
     } else {
       // Ring slot of k-step k: (k - ks0) % kRing, which equals its trip
       // position modulo kRing (trips start at ks0 + a multiple of 2 * KPS).
@@ -428,7 +428,7 @@ void k_gemv(GemvArgs a) {
         ring_load(stg[1], ks0 + 2);
         ring_store(v0, 0);
       };
-      kloop<FMT, NT, S, KPS, 1>(wq, ws, tile, a_KS, ks0, ks1, a_hi, acts, acc, pre);
+      kloop_run<FMT, NT, S, KPS, 1>(wbuf, wq, ws, tile, a_KS, ks0, ks1, a_hi, acts, acc, pre);
       if (NORM && ks0 < ks1) {
         // tokens (lane >> 4) and 4 + (lane >> 4): sum the 16 lanes of each row
 #pragma unroll
@@ -450,7 +450,7 @@ void k_gemv(GemvArgs a) {
         return __builtin_bit_cast(bf16x8, ld128s(xr, xbase + adj, (uint32_t)g * 64u));
       };
       auto acts = [&](bf16x8 (&A)[4], int k, int pos) { load_acts<FMT, S>(A, k, ks1, a.G, pos % C::KSTEPS, aload); };
-      kloop<FMT, NT, S, KPS, 1>(wq, ws, tile, a_KS, ks0, ks1, a_hi, acts, acc);
+      kloop_run<FMT, NT, S, KPS, 1>(wbuf, wq, ws, tile, a_KS, ks0, ks1, a_hi, acts, acc);
     } else {
       // block b's A row r = token 16 b + r (one slot: no slot term)
       uint32_t xbase[TB];
@@ -468,15 +468,15 @@ void k_gemv(GemvArgs a) {
           load_acts<FMT, S>(A[b], k, ks1, a.G, pos % C::KSTEPS, aload);
         }
       };
-      kloop<FMT, NT, S, KPS, 1, TB>(wq, ws, tile, a_KS, ks0, ks1, a_hi, acts, acc);
+      kloop_run<FMT, NT, S, KPS, 1, TB>(wbuf, wq, ws, tile, a_KS, ks0, ks1, a_hi, acts, acc);
     }
   }
 
   reduce_to_lds<S, NT, TB>(acc, red, wave, lane);
   __syncthreads();
 
-  const int nslot = a.frag - 1;
-  const size_t slot0 = frag >= 0 ? (size_t)(rblk - a.n_full) * nslot : 0;
+  const int nslot = a_fr - 1;
+  const size_t slot0 = frag >= 0 ? (size_t)(rblk - a_nf) * nslot : 0;
   constexpr int PS = NT * RB + (NORM ? 8 : 0);   // floats per partial slot: sums, then the RMSNorm sums of squares
   static_assert(S == 1 || PS <= 2 * 128 + 8, "partial slot larger than the workspace's (the split needs N <= 8)");
   if (frag >= 0 && frag < nslot) {
@@ -542,7 +542,7 @@ void k_gemv(GemvArgs a) {
     const int tok = rem >> 4, row = rem & 15;
     const int ot = rblk * TO + to;
     const int col = ot * 16 + row;
-    if (tok >= a.N || ot >= a.out_tiles || col >= a.M) continue;
+    if (tok >= a.N || ot >= a_ot || col >= a.M) continue;
     float sc = st;                        // NVFP4 tensor scale, times the RMSNorm scale
     if constexpr (NORM) {
       float ss = 0.f;
@@ -870,7 +870,8 @@ void plan_split(int fmt, const LaunchShape& ls, bool swiglu, int64_t out_tiles, 
   a.frag_kpw = (int)kpw;
 }
 
-using KernelFn = void (*)(GemvArgs);
+using KernelFn = void (*)(const uint8_t*, const uint8_t*, uint32_t, uint32_t, uint32_t, int, int, int, int, int, int,
+                          int, GemvArgs);
 
 // Workgroups of a kernel resident per compute unit (cached per device, kernel,
 // block size and LDS bytes); 0 if the runtime cannot say.
@@ -952,10 +953,12 @@ hipError_t launch_s(const GemvArgs& a0, const LaunchShape& ls, bool swiglu, hipS
       nwg = g;
     } else {
       a.frag = 1;
+      a.frag_log2 = 0;
       a.n_full = 0;
     }
   }
-  hipLaunchKernelGGL(fn, dim3((unsigned)nwg), block, lds, stream, a);
+  hipLaunchKernelGGL(fn, dim3((unsigned)nwg), block, lds, stream, a.wq, a.ws, a.wq_bytes, a.ws_bytes, a.hi_offset, a.KS,
+                     a.ks_per_wave, a.out_tiles, a.up_tile0, a.n_full, a.frag_log2, a.frag_kpw, a);
   return hipGetLastError();
 }
 

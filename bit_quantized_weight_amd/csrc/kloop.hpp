@@ -300,14 +300,36 @@ struct NoPrologue {
 // they hide). acts(A, k, pos) fetches the four A operands of k-step k,
 // which sits at position pos of its loop trip (a compile-time constant at
 // each call; its cycle position is pos % KSTEPS) — zeros past ks1 or past G;
-// pre() runs once after the first weight loads are issued.
+// pre() runs once after the first weight loads are issued (EARLY: after
+// the first two buffers', so a wave that waits in pre() has 2 * KPS k-steps
+// of weights in flight meanwhile).
+// kloop = kloop_start + kloop_run. A caller may run kloop_start itself,
+// before its activation set-up: the wave's first weight loads then go out
+// before any instruction that waits for kernel arguments still in flight.
 // TB > 1 (one slot only): TB blocks of 16 tokens share every decoded weight
 // operand; acts then fills A[TB][4] and acc[t * TB + b] holds block b of
 // tile t.
-template <int FMT, int NT, int S, int KPS, int AD, int TB = 1, class Acts, class Pre = NoPrologue>
-__device__ __forceinline__ void kloop(__amdgpu_buffer_rsrc_t wq, __amdgpu_buffer_rsrc_t ws, const int (&tile)[NT],
-                                      int KS, int ks0, int ks1, uint32_t hi_offset, const Acts& acts,
-                                      f32x4 (&acc)[NT * TB], const Pre& pre = Pre()) {
+template <int FMT, int NT, int S, int KPS, bool EARLY = false>
+__device__ __forceinline__ void kloop_start(Step<FMT, NT, KPS> (&buf)[2], __amdgpu_buffer_rsrc_t wq,
+                                            __amdgpu_buffer_rsrc_t ws, const int (&tile)[NT], int KS, int ks0, int ks1,
+                                            uint32_t hi_offset) {
+  using C = Cyc<FMT, S>;
+  if (ks0 < ks1) {
+    load_weights<FMT, NT, S, KPS, true>(buf[0], wq, ws, tile, KS, ks0, ks1, hi_offset);
+    if constexpr (EARLY) {
+      constexpr bool cyc1 = KPS % C::KSTEPS == 0;
+      load_weights<FMT, NT, S, KPS, cyc1>(buf[1], wq, ws, tile, KS, ks0 + KPS, ks1, hi_offset);
+    }
+  }
+  // nothing the scheduler could place in front of these loads
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int FMT, int NT, int S, int KPS, int AD, int TB = 1, bool EARLY = false, class Acts, class Pre = NoPrologue>
+__device__ __forceinline__ void kloop_run(Step<FMT, NT, KPS> (&buf)[2], __amdgpu_buffer_rsrc_t wq,
+                                          __amdgpu_buffer_rsrc_t ws, const int (&tile)[NT], int KS, int ks0, int ks1,
+                                          uint32_t hi_offset, const Acts& acts, f32x4 (&acc)[NT * TB],
+                                          const Pre& pre = Pre()) {
   static_assert(TB == 1 || S == 1, "token blocks need one slot");
   using C = Cyc<FMT, S>;
   constexpr int U = 2 * KPS;                     // k-steps per loop trip (a multiple of C::KSTEPS)
@@ -321,7 +343,6 @@ __device__ __forceinline__ void kloop(__amdgpu_buffer_rsrc_t wq, __amdgpu_buffer
   const bf16x8 bias_op = bf16x8_splat(FMT == INT5 ? kBias5Bits : kBias4Bits);   // int formats' code bias
   // HALVES: operand lanes 0-31 hold a group's columns 0-15 (block 0), lanes 32-63 columns 16-31 (block 1)
   const uint32_t lo_mask = (threadIdx.x & 32) ? 0u : 0xFFFFFFFFu;
-  Step<FMT, NT, KPS> buf[2];
   bf16x8 xa[R][TB][4];
   u32x4 csc[NT];                                 // scale words of the current cycle (KSTEPS > 1)
   f32x4 D[NT * TB];
@@ -338,7 +359,6 @@ __device__ __forceinline__ void kloop(__amdgpu_buffer_rsrc_t wq, __amdgpu_buffer
     else acts(X, k, pos);
   };
 
-  load_weights<FMT, NT, S, KPS, true>(buf[0], wq, ws, tile, KS, ks0, ks1, hi_offset);
   pre();
 #pragma unroll
   for (int d = 0; d < AD; ++d) fetch(xa[d], ks0 + d, d);
@@ -353,7 +373,9 @@ __device__ __forceinline__ void kloop(__amdgpu_buffer_rsrc_t wq, __amdgpu_buffer
         if (i == 0) {                              // next weight buffer (and its cycle's scales)
           constexpr bool cyc1 = KPS % C::KSTEPS == 0;        // buffer base + KPS starts a cycle
           constexpr bool cyc2 = (2 * KPS) % C::KSTEPS == 0;  // buffer base + 2 KPS does
-          if (b == 0) load_weights<FMT, NT, S, KPS, cyc1>(buf[1], wq, ws, tile, KS, base + KPS, ks1, hi_offset);
+          if (b == 0) {
+            if (!EARLY || base != ks0) load_weights<FMT, NT, S, KPS, cyc1>(buf[1], wq, ws, tile, KS, base + KPS, ks1, hi_offset);
+          }
           else load_weights<FMT, NT, S, KPS, cyc2>(buf[0], wq, ws, tile, KS, base + 2 * KPS, ks1, hi_offset);
         }
         fetch(xa[(kk + AD) % R], ks + AD, (kk + AD) % U);
@@ -436,6 +458,15 @@ __device__ __forceinline__ void kloop(__amdgpu_buffer_rsrc_t wq, __amdgpu_buffer
       }
     }
   }
+}
+
+template <int FMT, int NT, int S, int KPS, int AD, int TB = 1, bool EARLY = false, class Acts, class Pre = NoPrologue>
+__device__ __forceinline__ void kloop(__amdgpu_buffer_rsrc_t wq, __amdgpu_buffer_rsrc_t ws, const int (&tile)[NT],
+                                      int KS, int ks0, int ks1, uint32_t hi_offset, const Acts& acts,
+                                      f32x4 (&acc)[NT * TB], const Pre& pre = Pre()) {
+  Step<FMT, NT, KPS> buf[2];
+  kloop_start<FMT, NT, S, KPS, EARLY>(buf, wq, ws, tile, KS, ks0, ks1, hi_offset);
+  kloop_run<FMT, NT, S, KPS, AD, TB, EARLY>(buf, wq, ws, tile, KS, ks0, ks1, hi_offset, acts, acc, pre);
 }
 
 }  // namespace qg

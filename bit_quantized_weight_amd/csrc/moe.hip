@@ -25,6 +25,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 
 #include "device.hpp"
@@ -36,36 +37,6 @@
 namespace qg {
 
 // ---- routing (exact integer work on the N * top_k <= 64 selected ids) -----
-// Wave-level: lane i holds entry i (flat index t * top_k + j) for i < NK.
-struct Route {
-  int v;          // this lane's expert id, -1 if outside [0, E), -2 past NK
-  bool first;     // first occurrence of its expert among valid entries
-  int rank;       // first occurrences: rank of its expert among active experts
-  uint64_t act;   // lanes that are first occurrences
-};
-
-__device__ __forceinline__ Route route_lanes(const int32_t* ids, int NK, int E, int* s_v) {
-  const int lane = threadIdx.x & 63;
-  Route R;
-  int v = -2;
-  if (lane < NK) {
-    const int id = ids[lane];
-    v = (id >= 0 && id < E) ? id : -1;
-  }
-  R.v = v;
-  s_v[lane] = v;   // one wave: its LDS accesses complete in order
-  bool first = v >= 0;
-  for (int j = 0; j < NK; ++j) first &= !(j < lane && s_v[j] == v);
-  R.first = first;
-  R.act = __ballot(first);
-  int rank = 0;
-  for (uint64_t m = R.act; m; m &= m - 1) {
-    const int j = __builtin_ctzll(m);
-    rank += s_v[j] < v;
-  }
-  R.rank = rank;
-  return R;
-}
 
 // Largest expert count qgemv_moe accepts: the routing bitmap lives in LDS.
 constexpr int kMaxExperts = 16384;
@@ -133,27 +104,41 @@ __device__ __forceinline__ void route_slot(const int32_t* ids, int NK, int E, in
 // single-launch MoE runs it: slot a = the a-th smallest selected expert,
 // slot_e[a], its entries' offset slot_off[a] and count slot_cnt[a], and
 // pairs[slot_off[a] ..) those flat entries t * top_k + j in (t, j) order.
+// Lane i holds entry i (i < NK); every comparison with another entry reads
+// that entry's id from its lane (v_readlane, a scalar result), so the work
+// is a few register operations per entry with no memory round trips.
 // Returns the number of active experts (every lane).
-__device__ __forceinline__ int index_lanes(const int32_t* ids, int NK, int E, int* s_v, int* pairs, int* slot_e,
-                                           int* slot_off, int* slot_cnt) {
+__device__ __forceinline__ int index_lanes(const int32_t* ids, int NK, int E, int* pairs, int* slot_e, int* slot_off,
+                                           int* slot_cnt) {
   const int lane = threadIdx.x & 63;
-  const Route R = route_lanes(ids, NK, E, s_v);
-  if (R.v >= 0) {
-    int below = 0, same_before = 0, same = 0;
-    for (int j = 0; j < NK; ++j) {
-      const int u = s_v[j];
-      below += u >= 0 && u < R.v;
-      same_before += u == R.v && j < lane;
-      same += u == R.v;
-    }
-    pairs[below + same_before] = lane;
-    if (R.first) {
-      slot_e[R.rank] = R.v;
-      slot_off[R.rank] = below;
-      slot_cnt[R.rank] = same;
+  int v = -2;                    // -1: outside [0, E); -2: past NK
+  if (lane < NK) {
+    const int id = ids[lane];
+    v = (id >= 0 && id < E) ? id : -1;
+  }
+  bool first = v >= 0;           // first occurrence of its expert among the entries
+  int below = 0, same_before = 0, same = 0;
+  for (int j = 0; j < NK; ++j) {
+    const int u = __builtin_amdgcn_readlane(v, j);
+    below += u >= 0 && u < v;
+    same += u == v;
+    if (j < lane && u == v) {
+      ++same_before;
+      first = false;
     }
   }
-  return __builtin_popcountll(R.act);
+  const uint64_t act = __ballot(first);
+  int rank = 0;                  // active experts with a smaller id
+  for (uint64_t m = act; m; m &= m - 1) rank += __builtin_amdgcn_readlane(v, (int)__builtin_ctzll(m)) < v;
+  if (v >= 0) {
+    pairs[below + same_before] = lane;
+    if (first) {
+      slot_e[rank] = v;
+      slot_off[rank] = below;
+      slot_cnt[rank] = same;
+    }
+  }
+  return __builtin_popcountll(act);
 }
 
 // Routing index dump (qgemv_moe_index_by): one workgroup of 256 threads.
@@ -169,7 +154,6 @@ __global__ __launch_bounds__(256) void k_moe_index(const int32_t* ids, int NK, i
                                                    int32_t* meta) {
   __shared__ uint32_t s_bits[kMaxExperts / 32];
   __shared__ int s_route[2 + 64];
-  __shared__ int s_v[64];
   __shared__ int s_pairs[64];
   __shared__ int s_slot_e[64], s_slot_off[64], s_slot_cnt[64];
   __shared__ int s_meta[2];               // active experts, routed entries
@@ -196,7 +180,7 @@ __global__ __launch_bounds__(256) void k_moe_index(const int32_t* ids, int NK, i
         s_meta[1] = off;
       }
     } else {
-      const int n = index_lanes(ids, NK, E, s_v, s_pairs, s_slot_e, s_slot_off, s_slot_cnt);
+      const int n = index_lanes(ids, NK, E, s_pairs, s_slot_e, s_slot_off, s_slot_cnt);
       __builtin_amdgcn_wave_barrier();
       if (tid == 0) {
         int tot = 0;
@@ -450,60 +434,64 @@ __global__ __launch_bounds__(256) void k_moe_route(const float* logits, int N, i
 }
 
 // ---- single-launch MoE FFN (few routed rows) ---------------------------------
-// One workgroup of four waves per work item, launched in item order: first
-// one item per (slot, gate/up row block), then one per 16-column block of the
+// One workgroup of FW waves per work item, launched in item order: first one
+// item per (slot, gate/up row block), then one per 16-column block of the
 // output y.
-//   gate/up item: writes its rows of h at device scope, then counts itself in
-//     h_done[slot]; the item that completes the slot clears h_done[slot] and
-//     raises one ready flag per output block (each flag in its own 64-byte
-//     line, so no two waiting waves poll the same address).
-//   output item: wave w computes o = h . W_dn[e] for slots w, w + 4, ... over
-//     the whole K, its weight loads issued before it polls (bounded) and clears
-//     its (slot, block) flag and reads h at device scope; the o values meet in
+//   gate/up item: writes its rows of h at device scope, waits until those
+//     stores have completed, and raises its own flag (slot, row block) to
+//     this call's epoch: one store, no read-modify-write on the way.
+//   output item: wave w computes o = h . W_dn[e] for slots w, w + FW, ...
+//     over the whole K. Its weight loads are issued first; then it polls the
+//     flags of every row block of its slot (one load per lane, bounded) until
+//     all hold the epoch, and reads h at device scope. The o values meet in
 //     LDS and the workgroup sums y = r + sum_j p_j o_j in fixed j order.
+// Epochs: the host numbers the calls of the process 1, 2, ... (64-bit, so
+// they never repeat), so a flag left by an earlier call on the same
+// workspace never matches and nothing has to be cleared after use.
 // Deadlock-free without co-residency: workgroups are dispatched in increasing
 // order on every XCD, gate/up workgroups precede every output workgroup and
 // never wait, so a waiting wave only waits for workgroups already running or
 // done. A time-out sets the sticky error word and lets the kernel finish.
-// Every counter and flag is cleared by its last user, so the workspace is
-// zero again after each call.
 struct MoeFusedArgs {
-  MoeArgs gu, dn;
+  MoeArgs g[2];            // [0] gate/up items (grid row 0), [1] output items (grid row 1)
   const float* logits;     // [N][E]
   const float* res;        // [N][H] or null
   float* y;                // [N][H]
   int32_t* ids_out;        // [N][top_k] or null
   float* gates_out;        // [N][top_k] or null
-  uint32_t* ctr;           // workspace counters (see kCtr*)
+  uint32_t* ctr;           // workspace: sticky error word, then the item flags
+  uint64_t epoch;          // this call's number (> 0)
   int N, H, E, top_k, NK, slots;
   int nA, nB;              // gate/up row blocks per slot; 16-column output blocks
 };
 constexpr int kFusedMaxRows = 8;            // N * top_k handled by the single launch
-constexpr int kFusedWaves = 4;              // waves per workgroup of the single launch
-// counter words: [3] sticky error, [4, 4 + 16) h_done per slot, then ready
-// flags [slot][output block] at kReadyStride-word spacing from word 32
-constexpr int kCtrError = 3, kCtrH = 4, kReadyWord = 32;
-constexpr int kReadyStride = 16;            // 64 bytes per flag
+// workspace words: [3] sticky error; 64-bit item flags [slot][row block] from byte 256
+constexpr int kCtrError = 3;
+constexpr int kFlagByte = 256;
 constexpr uint32_t kSpinLimit = 1u << 20;   // polls before a wait gives up
+
+// Waves per workgroup: eight (one output expert per wave at up to eight
+// active experts, two k-steps per gate/up wave) where the kernel fits four
+// waves per SIMD (int4, nvfp4); four where its registers allow three.
+template <int FMT>
+constexpr int fused_waves() { return (FMT == INT4 || FMT == NVFP4) ? 8 : 4; }
+template <int FMT>
+constexpr int fused_min_waves_per_simd() { return fused_waves<FMT>() == 8 ? 4 : 1; }
 
 // Hand-offs between workgroups use agent-scope atomics with relaxed order:
 // h is written and read with device-scope (sc1) buffer accesses, which
 // bypass the per-XCD L2s and complete at the coherence point. A gate/up
 // item's threads wait for their h stores to complete (s_waitcnt) and meet at
-// a barrier before thread 0 adds to the slot counter, so the count cannot
-// run ahead of the data; the item that completes the slot stores the ready
-// flags after its counter result returns; an output wave issues its h loads
-// only after its poll has returned the flag (a value-dependent branch; the
-// signal fence keeps the compiler from hoisting the loads). Release/acquire
-// at agent scope would add an L2 writeback / invalidate per hand-off: on the
+// a barrier before thread 0 stores the item's flag, so the flag cannot run
+// ahead of the data; an output wave issues its h loads only after its poll
+// has returned every flag of its slot (a value-dependent branch; the signal
+// fence keeps the compiler from hoisting the loads). Release/acquire at
+// agent scope would add an L2 writeback / invalidate per hand-off: on the
 // dense split remainder that measured 2x slower.
-__device__ __forceinline__ uint32_t ctr_load(const uint32_t* p) {
+__device__ __forceinline__ uint64_t flag_load(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ uint32_t ctr_add(uint32_t* p, uint32_t v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void ctr_store(uint32_t* p, uint32_t v) {
+__device__ __forceinline__ void flag_store(uint64_t* p, uint64_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -535,7 +523,7 @@ __device__ __forceinline__ void down_tile_wave(const MoeArgs& a, int e, int cnt,
       load_acts<FMT, 2>(A, k, a.KS, a.G, pos % Cyc<FMT, 2>::KSTEPS, aload);
     };
     f32x4 acc[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
-    if (c0 == 0) kloop<FMT, 1, 2, 3, 1>(wq, ws, tile, a.KS, 0, a.KS, a.hi_offset, acts, acc, wait);
+    if (c0 == 0) kloop<FMT, 1, 2, 3, 1, 1, true>(wq, ws, tile, a.KS, 0, a.KS, a.hi_offset, acts, acc, wait);
     else kloop<FMT, 1, 2, 3, 1>(wq, ws, tile, a.KS, 0, a.KS, a.hi_offset, acts, acc);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -551,23 +539,36 @@ __device__ __forceinline__ void down_tile_wave(const MoeArgs& a, int e, int cnt,
 }
 
 template <int FMT>
-__global__ __launch_bounds__(64 * kFusedWaves) void k_moe_fused(MoeFusedArgs f) {
-  extern __shared__ float red[];          // [4][2][32][4] (gate/up), then o [16][16]
+__global__ __launch_bounds__(64 * fused_waves<FMT>())
+__attribute__((amdgpu_waves_per_eu(fused_min_waves_per_simd<FMT>()))) void k_moe_fused(MoeFusedArgs f) {
+  constexpr int FW = fused_waves<FMT>();
+  extern __shared__ float red[];          // [FW][2][32][4] (gate/up), then o [8][16]
   __shared__ int32_t s_ids[64];
   __shared__ float s_gates[64];
-  __shared__ int s_v[64];
   __shared__ int s_pairs[64];
   __shared__ int s_slot_e[64], s_slot_off[64], s_slot_cnt[64];
-  __shared__ int s_meta[4];               // n_active, last-of-slot flag
+  __shared__ int s_meta[1];               // active experts
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
-  const int W = blockDim.x >> 6;
-  uint32_t* ctr = f.ctr;
-  uint32_t* ready = ctr + kReadyWord;
+  uint64_t* flags = (uint64_t*)((uint8_t*)f.ctr + kFlagByte);
+  const int row = blockIdx.y;              // 0: gate/up items, 1: output items
+  const int tk = blockIdx.x;
+  // This workgroup's expert GEMV arguments, fetched with everything else
+  // before the router runs: the grid row selects them without a load, and
+  // the empty asm takes them as scalar-register inputs, so their loads go
+  // out in the kernel's first batch instead of one dependent round trip to
+  // the argument block at a time further down.
+  const MoeArgs m = f.g[row];
+  asm volatile("" ::"s"(m.wq), "s"(m.ws), "s"(m.wq_stride), "s"(m.ws_stride), "s"(m.wq_bytes), "s"(m.ws_bytes),
+               "s"(m.hi_offset), "s"(m.st_offset), "s"(m.in), "s"(m.in_bytes), "s"(m.out), "s"(m.out_bytes),
+               "s"(m.NK), "s"(m.Mout), "s"(m.K), "s"(m.KS), "s"(m.G), "s"(m.out_tiles), "s"(m.up_tile0),
+               "s"(m.ks_per_wave), "s"(f.epoch), "s"(f.nA), "s"(f.N), "s"(f.E), "s"(f.top_k), "s"(f.NK),
+               "s"(f.logits), "s"(f.ctr), "s"(f.slots), "s"(f.nB));
+  if (tk >= (row == 0 ? f.slots * f.nA : f.nB)) return;   // the shorter row's spare workgroups
 
   // router: every workgroup routes every token itself (no launch, no wait),
   // one wave per token
-  for (int t = wave; t < f.N; t += W) {
+  for (int t = wave; t < f.N; t += FW) {
     int id;
     float g;
     route_token_any(f.logits + (size_t)t * f.E, f.E, f.top_k, &id, &g);
@@ -579,7 +580,7 @@ __global__ __launch_bounds__(64 * kFusedWaves) void k_moe_fused(MoeFusedArgs f) 
   __syncthreads();
   // routing index: slot a = a-th smallest active expert, its entries in (t, j) order
   if (wave == 0) {
-    const int n = index_lanes(s_ids, f.NK, f.E, s_v, s_pairs, s_slot_e, s_slot_off, s_slot_cnt);
+    const int n = index_lanes(s_ids, f.NK, f.E, s_pairs, s_slot_e, s_slot_off, s_slot_cnt);
     if (lane == 0) s_meta[0] = n;
   }
   if (blockIdx.x == 0 && threadIdx.x < f.NK) {
@@ -588,43 +589,37 @@ __global__ __launch_bounds__(64 * kFusedWaves) void k_moe_fused(MoeFusedArgs f) 
   }
   __syncthreads();
   const int n_active = s_meta[0];
-  const int nA_all = f.slots * f.nA;
-  const int tk = blockIdx.x;
 
-  if (tk < nA_all) {
+  if (row == 0) {
     const int a = tk / f.nA, rb = tk - a * f.nA;
-    if (a >= n_active) return;            // uniform
-    moe_item<FMT, 2, false, true>(f.gu, s_slot_e[a], s_slot_cnt[a], s_pairs + s_slot_off[a], rb, red);
+    if (a >= n_active) return;            // uniform (also the row's spare workgroups)
+    moe_item<FMT, 2, false, true>(m, s_slot_e[a], s_slot_cnt[a], s_pairs + s_slot_off[a], rb, red);
     __builtin_amdgcn_s_waitcnt(0);        // this thread's h stores have completed
     __syncthreads();
-    if (threadIdx.x == 0) s_meta[1] = ctr_add(ctr + kCtrH + a, 1u) == (uint32_t)(f.nA - 1);
-    __syncthreads();
-    if (s_meta[1]) {                      // h of this slot is complete: release the output blocks
-      if (threadIdx.x == 0) ctr_store(ctr + kCtrH + a, 0u);
-      for (int b = threadIdx.x; b < f.nB; b += blockDim.x)
-        ctr_store(ready + ((size_t)a * f.nB + b) * kReadyStride, 1u);
-    }
+    if (threadIdx.x == 0) flag_store(flags + (size_t)a * f.nA + rb, f.epoch);
     return;
   }
 
   // output block rt: 16 columns of y for every token
-  const int rt = tk - nA_all;
-  float* o_lds = red + kFusedWaves * 2 * 32 * 4;   // [NK][16]
-  for (int a = wave; a < n_active; a += W) {
-    uint32_t* flag = ready + ((size_t)a * f.nB + rt) * kReadyStride;
+  const int rt = tk;
+  float* o_lds = red + FW * 2 * 32 * 4;   // [NK][16]
+  for (int a = wave; a < n_active; a += FW) {
+    const uint64_t* fl = flags + (size_t)a * f.nA;
     auto wait = [&]() {
       uint32_t it = 0;
-      while (ctr_load(flag) == 0u) {
+      for (;;) {
+        bool ok = true;
+        for (int i = lane; i < f.nA; i += 64) ok &= flag_load(fl + i) == f.epoch;
+        if (__all(ok)) break;             // uniform
         if (++it >= kSpinLimit) {
-          if (lane == 0) atomicOr(ctr + kCtrError, 1u);
+          if (lane == 0) atomicOr(f.ctr + kCtrError, 1u);
           break;
         }
         __builtin_amdgcn_s_sleep(2);
       }
-      ctr_store(flag, 0u);                // this wave is the flag's only reader
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
     };
-    down_tile_wave<FMT>(f.dn, s_slot_e[a], s_slot_cnt[a], s_pairs + s_slot_off[a], rt, o_lds, wait);
+    down_tile_wave<FMT>(m, s_slot_e[a], s_slot_cnt[a], s_pairs + s_slot_off[a], rt, o_lds, wait);
   }
   __syncthreads();
   for (int o = threadIdx.x; o < f.N * 16; o += blockDim.x) {
@@ -892,29 +887,33 @@ struct FusedLayout {
   size_t ctr_bytes, route_off, h_off, o_off, total;
 };
 
-// Counters and flags first (their size depends on H only, so calls with the
-// same H may share a workspace whatever their N, E, I), then ids and weights
-// of the routing (when the caller passes no buffers for them), h and o.
+// The error word and the item flags first (their size depends on I only,
+// so calls with the same I may share a workspace whatever their N, E, H),
+// then ids and weights of the routing (when the caller passes no buffers for
+// them), h and o.
 FusedLayout fused_layout(int64_t H, int64_t I, int N, int top_k) {
   const size_t NK = (size_t)N * top_k;
-  const size_t nB = (size_t)((H + 15) / 16);
+  const size_t nA = (size_t)((I + 15) / 16);
   FusedLayout L;
-  L.ctr_bytes = up256(((size_t)kReadyWord + (size_t)kFusedMaxRows * nB * kReadyStride) * 4);
+  L.ctr_bytes = up256((size_t)kFlagByte + (size_t)kFusedMaxRows * nA * 8);
   L.route_off = L.ctr_bytes;
   L.h_off = L.route_off + 512;            // 64 ids + 64 weights
   L.o_off = L.h_off + up256(NK * (size_t)I * 4);
   L.total = L.o_off + up256(NK * (size_t)H * 4);
   return L;
 }
-
+std::atomic<uint64_t> g_fused_epoch{0};
 template <int FMT>
 hipError_t launch_fused(const MoeFusedArgs& f, hipStream_t stream) {
-  const size_t lds = (size_t)(kFusedWaves * 2 * 32 * 4 + kFusedMaxRows * 16) * sizeof(float);
-  const unsigned grid = (unsigned)(f.slots * f.nA + f.nB);
-  hipLaunchKernelGGL(k_moe_fused<FMT>, dim3(grid), dim3(64 * kFusedWaves), lds, stream, f);
+  constexpr int FW = fused_waves<FMT>();
+  const size_t lds = (size_t)(FW * 2 * 32 * 4 + kFusedMaxRows * 16) * sizeof(float);
+  // row 0: one workgroup per (slot, gate/up row block); row 1: one per output
+  // block. Linear workgroup ids run along x first, so every output
+  // workgroup comes after every gate/up workgroup in dispatch order.
+  const unsigned gx = (unsigned)std::max(f.slots * f.nA, f.nB);
+  hipLaunchKernelGGL(k_moe_fused<FMT>, dim3(gx, 2), dim3(64 * FW), lds, stream, f);
   return hipGetLastError();
 }
-
 }  // namespace
 
 extern "C" int qgemv_moe_fused_workspace_bytes(int E, int64_t H, int64_t I, int N, int top_k, size_t* bytes) {
@@ -941,7 +940,7 @@ extern "C" int qgemv_moe_fused(int fmt, const void* wq_gu, const void* ws_gu, co
   MoeFusedArgs f;
   int wgu, wdn;
   const int rc = moe_setup(fmt, wq_gu, ws_gu, wq_dn, ws_dn, E, H, I, x, top_k, residual, y, N, wsp + L.h_off,
-                           (float*)(wsp + L.o_off), &f.gu, &f.dn, &wgu, &wdn);
+                           (float*)(wsp + L.o_off), &f.g[0], &f.g[1], &wgu, &wdn);
   if (rc) return rc;
   f.logits = logits;
   f.res = residual;
@@ -961,13 +960,13 @@ extern "C" int qgemv_moe_fused(int fmt, const void* wq_gu, const void* ws_gu, co
     int32_t* ids = ids_out ? ids_out : (int32_t*)(wsp + L.route_off);
     float* gates = gates_out ? gates_out : (float*)(wsp + L.route_off + 256);
     launch_route(logits, N, E, top_k, ids, gates, stream);
-    f.gu.ids = ids;
-    f.dn.ids = ids;
+    f.g[0].ids = ids;
+    f.g[1].ids = ids;
     switch (fmt) {
-      case INT4: launch_moe_pair<INT4>(f.gu, f.dn, wgu, wdn, f.slots, stream); break;
-      case INT5: launch_moe_pair<INT5>(f.gu, f.dn, wgu, wdn, f.slots, stream); break;
-      case INT8: launch_moe_pair<INT8>(f.gu, f.dn, wgu, wdn, f.slots, stream); break;
-      default: launch_moe_pair<NVFP4>(f.gu, f.dn, wgu, wdn, f.slots, stream); break;
+      case INT4: launch_moe_pair<INT4>(f.g[0], f.g[1], wgu, wdn, f.slots, stream); break;
+      case INT5: launch_moe_pair<INT5>(f.g[0], f.g[1], wgu, wdn, f.slots, stream); break;
+      case INT8: launch_moe_pair<INT8>(f.g[0], f.g[1], wgu, wdn, f.slots, stream); break;
+      default: launch_moe_pair<NVFP4>(f.g[0], f.g[1], wgu, wdn, f.slots, stream); break;
     }
     const int64_t tot = (int64_t)N * H;
     hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, stream,
@@ -975,11 +974,13 @@ extern "C" int qgemv_moe_fused(int fmt, const void* wq_gu, const void* ws_gu, co
     return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
   }
   // few routed rows: one launch; gate/up items split K over its waves
-  f.gu.ks_per_wave = (f.gu.KS + kFusedWaves - 1) / kFusedWaves;
+  const int fw = (fmt == INT4 || fmt == NVFP4) ? fused_waves<INT4>() : fused_waves<INT5>();
+  f.g[0].ks_per_wave = (f.g[0].KS + fw - 1) / fw;
+  f.epoch = g_fused_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
   f.ids_out = ids_out;
   f.gates_out = gates_out;
-  f.nA = f.gu.out_tiles;                    // one gate tile and its up tile per item
-  f.nB = f.dn.out_tiles;                    // 16 output columns per item
+  f.nA = f.g[0].out_tiles;                  // one gate tile and its up tile per item
+  f.nB = f.g[1].out_tiles;                  // 16 output columns per item
   hipError_t e;
   switch (fmt) {
     case INT4: e = launch_fused<INT4>(f, stream); break;

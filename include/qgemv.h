@@ -286,8 +286,10 @@ int qgemv_moe_fused_workspace_bytes(int E, int64_t H, int64_t I, int N, int top_
  *   ids, gates = route(logits [N][E], top_k)
  *   y[t] = residual[t] + sum_j gates[t][j] * down_e(SwiGLU(gate_up_e(x[t])))
  * With N * top_k <= 8 routed rows (batch-1 decode at top-8) it is one
- * launch: gate/up work items publish h and raise ready flags in the
- * workspace; each output item waits (bounded) for its experts' flags, computes
+ * launch: each gate/up work item publishes its rows of h and raises its
+ * own flag in the workspace to the call's number (the library numbers its
+ * calls in the process 1, 2, ... in 64 bits); each output item waits
+ * (bounded) until every flag of its experts holds that number, computes
  * every expert's output for 16 columns of y and sums them in fixed order in
  * LDS. With more rows it runs qgemv_moe_route and then the launches of
  * qgemv_moe, whose bits it then reproduces for the same ids and gates.
@@ -295,16 +297,17 @@ int qgemv_moe_fused_workspace_bytes(int E, int64_t H, int64_t I, int N, int top_
  *   ids_out [N][top_k], gates_out [N][top_k]: receive the routing (device),
  *   or NULL.
  *   workspace: device memory of qgemv_moe_fused_workspace_bytes, 16-byte
- *   aligned, ZERO-FILLED BEFORE ITS FIRST USE. It starts with counters and
- *   flags that every call returns to zero when it completes, so one fill
- *   serves every later call in stream order with the same H (the counter
- *   region's size depends on H only; N, E, I and top_k may change if the
- *   workspace is large enough). Calls that may overlap in time need separate
- *   workspaces. Byte offset 12 holds a sticky 32-bit flag that becomes
- *   nonzero if a dependency wait ever timed out. The results of that call
- *   are then invalid, and so is the workspace (a late flag may be raised
- *   after the waiter gave up): zero it again before reusing it. Workgroups wait only on lower-numbered ones, which start
- *   first on every XCD, so the waits need no co-residency.
+ *   aligned, ZERO-FILLED BEFORE ITS FIRST USE. It starts with an error word
+ *   and the flags, which no later call mistakes for its own (each call
+ *   waits for its own number), so one fill serves every later call in
+ *   stream order with the same I (the flag region's size depends on I only;
+ *   N, E, H and top_k may change if the workspace is large enough). Calls
+ *   that may overlap in time need separate workspaces. Byte offset 12 holds
+ *   a sticky 32-bit flag that becomes nonzero if a dependency wait ever
+ *   timed out: the results of that call are then invalid; the flag stays
+ *   set until the caller clears it. Workgroups wait only on lower-numbered
+ *   ones, which start first on every XCD, so the waits need no
+ *   co-residency.
  * Other arguments and limits as qgemv_moe; 1 <= top_k <= min(E, 8). */
 int qgemv_moe_fused(int fmt, const void* wq_gu, const void* ws_gu, const void* wq_dn, const void* ws_dn,
                     int E, int64_t H, int64_t I, const void* x, const float* logits, int top_k,

@@ -128,21 +128,30 @@ def _run_fused(fmt, bufs, E, H, I, xb, logits, k, N, r, wsp=None, calls=1):
     return out, ids.cpu().numpy(), gates.cpu().numpy(), w, d
 
 
-def _counter_words(E, H, I, N, k):
-    """Words of the fused workspace's counter and flag region: the total minus
-    the routing (512 bytes), h and o regions (each 256-byte rounded)."""
-    up = lambda v: (v + 255) // 256 * 256
-    total = qg().moe_fused_workspace_bytes(E, H, I, N, k)
-    return (total - 512 - up(N * k * I * 4) - up(N * k * H * 4)) // 4
+def _check_flags(w, I, N, k, ids):
+    """The fused workspace's head: the sticky error word (byte 12) and the
+    64-bit item flags [8 slots][I / 16 row blocks] from byte 256. After calls
+    on a fresh workspace, every item of an active slot holds the last call's
+    number and nothing else was written; with more than 8 routed rows the
+    single launch does not run and the head stays zero."""
+    assert w[3] == 0, "a dependency wait timed out"
+    assert np.all(w[:64] == 0), np.nonzero(w[:64])
+    nA = (I + 15) // 16
+    fl = w[64: 64 + 2 * 8 * nA].view(np.uint64).reshape(8, nA)
+    if N * k > 8:
+        assert np.all(fl == 0)
+        return
+    n_active = len(np.unique(ids))
+    last = fl[0, 0]
+    assert last > 0 and np.all(fl[:n_active] == last), fl[:n_active]
+    assert np.all(fl[n_active:] == 0)
 
 
 def _check_fused(fmt, E, H, I, N, k, seed, calls=2):
     logits, bufs, Wgu, Wdn, xb, ids_ref, _, r = _fused_case(fmt, E, H, I, N, k, seed)
     ys, ids, gates, w, d = _run_fused(fmt, bufs, E, H, I, xb, logits, k, N, r, calls=calls)
-    assert w[3] == 0, "a dependency wait timed out"
-    nctr = _counter_words(E, H, I, N, k)
-    assert np.all(w[:nctr] == 0), np.nonzero(w[:nctr])    # every counter and flag back at zero
     assert np.array_equal(ids, ids_ref), (ids, ids_ref)
+    _check_flags(w, I, N, k, ids)
     ref_g = _ref_gates(logits, ids_ref)
     Tg = G.route_tolerance(logits, ids_ref, ref_g)
     check_tol(gates, ref_g, Tg, "fused gates")
@@ -194,17 +203,19 @@ def test_fused_moe_odd_shapes(E, H, I, N, k):
 
 
 def test_fused_moe_no_residual_and_workspace_reuse():
-    """No residual; one workspace reused across calls of different N (the
-    counters return to zero after every call, and their region depends on H
-    only, so a smaller call's data never lands on a larger call's flags)."""
+    """No residual; one workspace reused across calls of different N, single
+    launches (N <= 2) among them back to back: flags left by an earlier call
+    never satisfy a later call's waits (each waits for its own number), and
+    the flag region depends on I only, so a smaller call's data never lands
+    on a larger call's flags."""
     E, H, I, k = 16, 256, 64, 4
     nbytes = qg().moe_fused_workspace_bytes(E, H, I, 8, k)
     wsp = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
-    for N in (8, 1, 5):
+    for N in (8, 1, 2, 1, 5):
         logits, bufs, Wgu, Wdn, xb, ids_ref, _, _ = _fused_case("nvfp4", E, H, I, N, k, seed=90 + N)
         assert qg().moe_fused_workspace_bytes(E, H, I, N, k) <= nbytes
         ys, ids, gates, w, _ = _run_fused("nvfp4", bufs, E, H, I, xb, logits, k, N, None, wsp=wsp)
-        assert np.all(w[:_counter_words(E, H, I, 8, k)] == 0)
+        assert w[3] == 0 and np.all(w[:64] == 0), "a dependency wait timed out"
         ref_g = _ref_gates(logits, ids_ref)
         Tg = G.route_tolerance(logits, ids_ref, ref_g)
         y_ref, T = G.moe(G.x_from_bits(xb), ids_ref, ref_g, Wgu, Wdn, None, gate_tol=Tg)
