@@ -25,10 +25,11 @@ LIB = os.path.join(HERE, "libqgemv.so")
 ARCH = "gfx950"
 HIP_SOURCES = ["gemv.hip", "moe.hip", "mx.hip"]
 # moe.hip: atomics (the routing bitmap's LDS ORs, the sticky error word) stay
-# single-lane as written. gemv.hip: the kernel's leading scalar arguments are
+# single-lane as written. Both: the kernels' leading scalar arguments are
 # preloaded into SGPRs at wave launch (gfx950 kernel argument preloading), so
-# a wave issues its first weight loads without reading the argument block.
-EXTRA_FLAGS = {"moe.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"],
+# a wave issues its first loads without reading the argument block.
+EXTRA_FLAGS = {"moe.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None", "-mllvm",
+                           "-amdgpu-kernarg-preload-count=16"],
                "gemv.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"]}
 HOST_SOURCES = ["pack.cpp"]
 

@@ -46,19 +46,15 @@ constexpr int kMaxExperts = 16384;
 // s_route[1] = the number of pairs routed to it, s_route[2..] = those flat
 // entries t * top_k + j, ascending. A bitmap of selected experts (OR is
 // order-independent) is scanned with one prefix sum over the lanes' chunks.
-__device__ __forceinline__ void route_slot(const int32_t* ids, int NK, int E, int a, uint32_t* s_bits,
-                                           int* s_route) {
+__device__ __forceinline__ void route_slot(int id, int NK, int E, int a, uint32_t* s_bits, int* s_route) {
   const int lane = threadIdx.x & 63;
   const int W = (E + 31) >> 5, c = (W + 63) >> 6;   // bitmap words, words per lane
   for (int i = 0; i < c; ++i) {
     const int w = lane * c + i;
     if (w < W) s_bits[w] = 0u;
   }
-  int v = -1;
-  if (lane < NK) {
-    const int id = ids[lane];
-    v = (id >= 0 && id < E) ? id : -1;
-  }
+  // id: the lane's entry (lane < NK; anything elsewhere)
+  const int v = (lane < NK && id >= 0 && id < E) ? id : -1;
   // one wave: its LDS operations complete in issue order (clears, ORs, reads)
   __builtin_amdgcn_wave_barrier();
   if (v >= 0) atomicOr(s_bits + (v >> 5), 1u << (v & 31));
@@ -161,8 +157,9 @@ __global__ __launch_bounds__(256) void k_moe_index(const int32_t* ids, int NK, i
   if (tid < 64) {
     if constexpr (ROUTINE == 0) {
       int a = 0, off = 0;
+      const int id = tid < NK ? ids[tid] : 0;
       for (; a < min(E, NK); ++a) {
-        route_slot(ids, NK, E, a, s_bits, s_route);
+        route_slot(id, NK, E, a, s_bits, s_route);
         __builtin_amdgcn_wave_barrier();
         const int e = s_route[0], cnt = s_route[1];
         if (e < 0) break;                 // uniform: fewer selected experts than slots
@@ -382,12 +379,20 @@ __device__ __forceinline__ void moe_item(const MoeArgs& a, int e, int cnt, const
 }
 
 // Grid (row blocks, active-expert slot): routes in LDS, then one item.
+// ids, NK, E: copies of a's fields, leading scalar arguments so that they are
+// preloaded into SGPRs at wave launch and the ids load goes out at once.
 template <int FMT, int NT, bool DOWN>
-__global__ __launch_bounds__(512) void k_moe_gemv(MoeArgs a) {
+__global__ __launch_bounds__(512) void k_moe_gemv(const int32_t* ids, int NK, int E, MoeArgs a) {
   extern __shared__ float red[];  // [W][NT][32][4]
   __shared__ uint32_t s_bits[kMaxExperts / 32];
   __shared__ int s_route[2 + 64];
-  if (threadIdx.x < 64) route_slot(a.ids, a.NK, a.E, blockIdx.y, s_bits, s_route);
+  const int lane = threadIdx.x & 63;
+  const int id = (threadIdx.x < 64 && lane < NK) ? ids[lane] : 0;
+  // the expert GEMV's arguments in one batch while the ids load is in flight
+  asm volatile("" ::"s"(a.wq), "s"(a.ws), "s"(a.wq_stride), "s"(a.ws_stride), "s"(a.wq_bytes), "s"(a.ws_bytes),
+               "s"(a.hi_offset), "s"(a.st_offset), "s"(a.in), "s"(a.in_bytes), "s"(a.KS), "s"(a.ks_per_wave),
+               "s"(a.out_tiles), "s"(a.up_tile0), "s"(a.K), "s"(a.G));
+  if (threadIdx.x < 64) route_slot(id, NK, E, blockIdx.y, s_bits, s_route);
   __syncthreads();
   const int e = s_route[0];
   if (e < 0) return;                   // uniform: fewer selected experts than slots
@@ -470,13 +475,10 @@ constexpr int kCtrError = 3;
 constexpr int kFlagByte = 256;
 constexpr uint32_t kSpinLimit = 1u << 20;   // polls before a wait gives up
 
-// Waves per workgroup: eight (one output expert per wave at up to eight
-// active experts, two k-steps per gate/up wave) where the kernel fits four
-// waves per SIMD (int4, nvfp4); four where its registers allow three.
-template <int FMT>
-constexpr int fused_waves() { return (FMT == INT4 || FMT == NVFP4) ? 8 : 4; }
-template <int FMT>
-constexpr int fused_min_waves_per_simd() { return fused_waves<FMT>() == 8 ? 4 : 1; }
+// Waves per workgroup. Eight (one output expert per wave at eight active
+// experts) measured 12% slower on the 128-expert top-8 workload at N = 1:
+// the extra output waves' weight loads queue in front of the gate/up items'.
+constexpr int kFusedWaves = 4;
 
 // Hand-offs between workgroups use agent-scope atomics with relaxed order:
 // h is written and read with device-scope (sc1) buffer accesses, which
@@ -538,10 +540,13 @@ __device__ __forceinline__ void down_tile_wave(const MoeArgs& a, int e, int cnt,
   }
 }
 
+// logits, E, top_k, N: copies of f's fields, leading scalar arguments
+// preloaded into SGPRs at wave launch, so each wave's first logits load goes
+// out at once.
 template <int FMT>
-__global__ __launch_bounds__(64 * fused_waves<FMT>())
-__attribute__((amdgpu_waves_per_eu(fused_min_waves_per_simd<FMT>()))) void k_moe_fused(MoeFusedArgs f) {
-  constexpr int FW = fused_waves<FMT>();
+__global__ __launch_bounds__(64 * kFusedWaves) void k_moe_fused(const float* logits, int E, int top_k, int N,
+                                                                MoeFusedArgs f) {
+  constexpr int FW = kFusedWaves;
   extern __shared__ float red[];          // [FW][2][32][4] (gate/up), then o [8][16]
   __shared__ int32_t s_ids[64];
   __shared__ float s_gates[64];
@@ -550,7 +555,6 @@ __attribute__((amdgpu_waves_per_eu(fused_min_waves_per_simd<FMT>()))) void k_moe
   __shared__ int s_meta[1];               // active experts
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
-  uint64_t* flags = (uint64_t*)((uint8_t*)f.ctr + kFlagByte);
   const int row = blockIdx.y;              // 0: gate/up items, 1: output items
   const int tk = blockIdx.x;
   // This workgroup's expert GEMV arguments, fetched with everything else
@@ -558,29 +562,38 @@ __attribute__((amdgpu_waves_per_eu(fused_min_waves_per_simd<FMT>()))) void k_moe
   // the empty asm takes them as scalar-register inputs, so their loads go
   // out in the kernel's first batch instead of one dependent round trip to
   // the argument block at a time further down.
+  // the wave's first token: its keys' logits load goes out before the batch
+  // below (E <= 128, the register-cached router)
+  float lv0[2] = {0.0f, 0.0f};
+  if (E <= 128 && wave < N) route_logits<2>(logits + (size_t)wave * E, E, lv0);
   const MoeArgs m = f.g[row];
   asm volatile("" ::"s"(m.wq), "s"(m.ws), "s"(m.wq_stride), "s"(m.ws_stride), "s"(m.wq_bytes), "s"(m.ws_bytes),
                "s"(m.hi_offset), "s"(m.st_offset), "s"(m.in), "s"(m.in_bytes), "s"(m.out), "s"(m.out_bytes),
                "s"(m.NK), "s"(m.Mout), "s"(m.K), "s"(m.KS), "s"(m.G), "s"(m.out_tiles), "s"(m.up_tile0),
-               "s"(m.ks_per_wave), "s"(f.epoch), "s"(f.nA), "s"(f.N), "s"(f.E), "s"(f.top_k), "s"(f.NK),
-               "s"(f.logits), "s"(f.ctr), "s"(f.slots), "s"(f.nB));
+               "s"(m.ks_per_wave), "s"(f.nA), "s"(f.NK), "s"(f.slots), "s"(f.nB)
+               : "memory");
   if (tk >= (row == 0 ? f.slots * f.nA : f.nB)) return;   // the shorter row's spare workgroups
 
   // router: every workgroup routes every token itself (no launch, no wait),
   // one wave per token
-  for (int t = wave; t < f.N; t += FW) {
+  for (int t = wave; t < N; t += FW) {
     int id;
     float g;
-    route_token_any(f.logits + (size_t)t * f.E, f.E, f.top_k, &id, &g);
-    if (lane < f.top_k) {
-      s_ids[t * f.top_k + lane] = id;
-      s_gates[t * f.top_k + lane] = g;
+    if (E <= 128 && t == wave) {
+      uint64_t key0[2];
+      route_keys<2>(lv0, E, key0);
+      route_select<2>(key0, nullptr, E, top_k, &id, &g);
+    }
+    else route_token_any(logits + (size_t)t * E, E, top_k, &id, &g);
+    if (lane < top_k) {
+      s_ids[t * top_k + lane] = id;
+      s_gates[t * top_k + lane] = g;
     }
   }
   __syncthreads();
   // routing index: slot a = a-th smallest active expert, its entries in (t, j) order
   if (wave == 0) {
-    const int n = index_lanes(s_ids, f.NK, f.E, s_pairs, s_slot_e, s_slot_off, s_slot_cnt);
+    const int n = index_lanes(s_ids, f.NK, E, s_pairs, s_slot_e, s_slot_off, s_slot_cnt);
     if (lane == 0) s_meta[0] = n;
   }
   if (blockIdx.x == 0 && threadIdx.x < f.NK) {
@@ -589,6 +602,7 @@ __attribute__((amdgpu_waves_per_eu(fused_min_waves_per_simd<FMT>()))) void k_moe
   }
   __syncthreads();
   const int n_active = s_meta[0];
+  uint64_t* flags = (uint64_t*)((uint8_t*)f.ctr + kFlagByte);
 
   if (row == 0) {
     const int a = tk / f.nA, rb = tk - a * f.nA;
@@ -622,12 +636,12 @@ __attribute__((amdgpu_waves_per_eu(fused_min_waves_per_simd<FMT>()))) void k_moe
     down_tile_wave<FMT>(m, s_slot_e[a], s_slot_cnt[a], s_pairs + s_slot_off[a], rt, o_lds, wait);
   }
   __syncthreads();
-  for (int o = threadIdx.x; o < f.N * 16; o += blockDim.x) {
+  for (int o = threadIdx.x; o < N * 16; o += blockDim.x) {
     const int t = o >> 4, c = o & 15;
     const int col = rt * 16 + c;
     if (col >= f.H) continue;
     float v = f.res ? f.res[(size_t)t * f.H + col] : 0.0f;
-    for (int j = 0; j < f.top_k; ++j) v = fmaf(s_gates[t * f.top_k + j], o_lds[(t * f.top_k + j) * 16 + c], v);
+    for (int j = 0; j < top_k; ++j) v = fmaf(s_gates[t * top_k + j], o_lds[(t * top_k + j) * 16 + c], v);
     f.y[(size_t)t * f.H + col] = v;
   }
 }
@@ -661,7 +675,7 @@ void launch_moe(const MoeArgs& a, int waves, int slots, hipStream_t stream) {
   constexpr int TO = DOWN ? NT : NT / 2;
   const dim3 grid((unsigned)((a.out_tiles + TO - 1) / TO), (unsigned)slots);
   const size_t lds = (size_t)waves * NT * 32 * 4 * sizeof(float);
-  hipLaunchKernelGGL((k_moe_gemv<FMT, NT, DOWN>), grid, dim3(64 * waves), lds, stream, a);
+  hipLaunchKernelGGL((k_moe_gemv<FMT, NT, DOWN>), grid, dim3(64 * waves), lds, stream, a.ids, a.NK, a.E, a);
 }
 
 template <int FMT>
@@ -905,13 +919,13 @@ FusedLayout fused_layout(int64_t H, int64_t I, int N, int top_k) {
 std::atomic<uint64_t> g_fused_epoch{0};
 template <int FMT>
 hipError_t launch_fused(const MoeFusedArgs& f, hipStream_t stream) {
-  constexpr int FW = fused_waves<FMT>();
+  constexpr int FW = kFusedWaves;
   const size_t lds = (size_t)(FW * 2 * 32 * 4 + kFusedMaxRows * 16) * sizeof(float);
   // row 0: one workgroup per (slot, gate/up row block); row 1: one per output
   // block. Linear workgroup ids run along x first, so every output
   // workgroup comes after every gate/up workgroup in dispatch order.
   const unsigned gx = (unsigned)std::max(f.slots * f.nA, f.nB);
-  hipLaunchKernelGGL(k_moe_fused<FMT>, dim3(gx, 2), dim3(64 * FW), lds, stream, f);
+  hipLaunchKernelGGL(k_moe_fused<FMT>, dim3(gx, 2), dim3(64 * FW), lds, stream, f.logits, f.E, f.top_k, f.N, f);
   return hipGetLastError();
 }
 }  // namespace
@@ -974,8 +988,7 @@ extern "C" int qgemv_moe_fused(int fmt, const void* wq_gu, const void* ws_gu, co
     return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
   }
   // few routed rows: one launch; gate/up items split K over its waves
-  const int fw = (fmt == INT4 || fmt == NVFP4) ? fused_waves<INT4>() : fused_waves<INT5>();
-  f.g[0].ks_per_wave = (f.g[0].KS + fw - 1) / fw;
+  f.g[0].ks_per_wave = (f.g[0].KS + kFusedWaves - 1) / kFusedWaves;
   f.epoch = g_fused_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
   f.ids_out = ids_out;
   f.gates_out = gates_out;

@@ -43,56 +43,74 @@ __device__ __forceinline__ float logit_from_order(uint32_t k) {
   return __builtin_bit_cast(float, (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-// One max step of a 64-bit key against the value DPP control CTRL brings in.
+// Max of an unsigned word over the wave, in every lane: quad butterflies and
+// the half-row and row mirrors (DPP, each fused into the max) give each row
+// of 16 its maximum; the gfx950 lane swaps of rows (permlane16) and halves
+// (permlane32) finish the wave.
 template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_max_step(uint64_t v) {
-  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)v, CTRL, 0xf, 0xf, false);
-  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(v >> 32), CTRL, 0xf, 0xf, false);
-  const uint64_t o = ((uint64_t)hi << 32) | lo;
+__device__ __forceinline__ uint32_t dpp_max_u32(uint32_t v) {
+  const uint32_t o = __builtin_amdgcn_update_dpp(0u, v, CTRL, 0xf, 0xf, false);
   return o > v ? o : v;
 }
-
-// Max of a 64-bit key over the wave, in every lane: quad butterflies and the
-// half-row and row mirrors (DPP) give each row of 16 its maximum; the gfx950
-// lane swaps of rows (permlane16) and halves (permlane32) finish the wave.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  v = dpp_max_step<0xB1>(v);    // quad_perm [1,0,3,2]
-  v = dpp_max_step<0x4E>(v);    // quad_perm [2,3,0,1]
-  v = dpp_max_step<0x141>(v);   // row_half_mirror
-  v = dpp_max_step<0x140>(v);   // row_mirror
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = dpp_max_u32<0xB1>(v);    // quad_perm [1,0,3,2]
+  v = dpp_max_u32<0x4E>(v);    // quad_perm [2,3,0,1]
+  v = dpp_max_u32<0x141>(v);   // row_half_mirror
+  v = dpp_max_u32<0x140>(v);   // row_mirror
   {
-    const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
-    const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(v >> 32), (uint32_t)(v >> 32), false, false);
-    const uint64_t a = ((uint64_t)hi[0] << 32) | lo[0], b = ((uint64_t)hi[1] << 32) | lo[1];
-    v = a > b ? a : b;
+    const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = p[0] > p[1] ? p[0] : p[1];
   }
   {
-    const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
-    const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(v >> 32), (uint32_t)(v >> 32), false, false);
-    const uint64_t a = ((uint64_t)hi[0] << 32) | lo[0], b = ((uint64_t)hi[1] << 32) | lo[1];
-    v = a > b ? a : b;
+    const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    v = p[0] > p[1] ? p[0] : p[1];
   }
   return v;
 }
 
-// Routes one token with the whole wave: lg points at its E logits (any
-// memory the wave can read). On return lane j < top_k holds the j-th
-// selected expert in *id and its weight in *gate; other lanes hold -1 / 0.
-// Every real key exceeds 0 (its low word is at least 2^32 - E), so 0 marks
-// "nothing left", which cannot happen while top_k <= E. RK > 0: the lane's
-// keys (experts lane, lane + 64, ...) stay in registers, E <= 64 * RK;
-// RK = 0: any E, keys recomputed from memory on every pass.
+// Max of a 64-bit key over the wave, in every lane: the largest high word,
+// then the largest low word among the lanes that hold it (two 32-bit wave
+// maxima instead of one 64-bit one: each step is a single fused max).
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  const uint32_t hi = wave_max_u32((uint32_t)(v >> 32));
+  const uint32_t lo = wave_max_u32((uint32_t)(v >> 32) == hi ? (uint32_t)v : 0u);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// The lane's logits of one token for the register-cached keys: experts lane,
+// lane + 64, ... from its E logits at lg (any memory the wave can read); every
+// load is issued, clamped in range, before any is used.
 template <int RK>
-__device__ __forceinline__ void route_token(const float* lg, int E, int top_k, int* id, float* gate) {
+__device__ __forceinline__ void route_logits(const float* lg, int E, float (&v)[RK]) {
   const int lane = threadIdx.x & 63;
-  uint64_t key[RK > 0 ? RK : 1];
-  if constexpr (RK > 0) {
 #pragma unroll
-    for (int i = 0; i < RK; ++i) {
-      const int e = lane + 64 * i;
-      key[i] = e < E ? route_key(lg[e], e) : 0ull;
-    }
+  for (int i = 0; i < RK; ++i) {
+    const int e = lane + 64 * i;
+    v[i] = lg[e < E ? e : E - 1];
   }
+}
+
+// Their keys (0 past E).
+template <int RK>
+__device__ __forceinline__ void route_keys(const float (&v)[RK], int E, uint64_t (&key)[RK]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < RK; ++i) {
+    const int e = lane + 64 * i;
+    key[i] = e < E ? route_key(v[i], e) : 0ull;
+  }
+}
+
+// Routes one token with the whole wave. On return lane j < top_k holds the
+// j-th selected expert in *id and its weight in *gate; other lanes hold -1 /
+// 0. Every real key exceeds 0 (its low word is at least 2^32 - E), so 0
+// marks "nothing left", which cannot happen while top_k <= E. RK > 0: the
+// lane's keys come from route_keys (E <= 64 * RK; lg unused); RK = 0: any E,
+// keys recomputed from the logits at lg on every pass.
+template <int RK>
+__device__ __forceinline__ void route_select(const uint64_t* key, const float* lg, int E, int top_k, int* id,
+                                             float* gate) {
+  const int lane = threadIdx.x & 63;
   uint64_t prev = ~0ull;
   int my_id = -1;
   float my_v = 0.0f;
@@ -122,6 +140,19 @@ __device__ __forceinline__ void route_token(const float* lg, int E, int top_k, i
   for (int j = 0; j < top_k; ++j) sum += __shfl(ex, j);
   *id = my_id;
   *gate = lane < top_k ? ex / sum : 0.0f;
+}
+
+template <int RK>
+__device__ __forceinline__ void route_token(const float* lg, int E, int top_k, int* id, float* gate) {
+  if constexpr (RK > 0) {
+    float v[RK];
+    uint64_t key[RK];
+    route_logits<RK>(lg, E, v);
+    route_keys<RK>(v, E, key);
+    route_select<RK>(key, lg, E, top_k, id, gate);
+  } else {
+    route_select<0>(nullptr, lg, E, top_k, id, gate);
+  }
 }
 
 // route_token with the register-cached keys when E allows.
