@@ -19,7 +19,9 @@ import numpy as np
 FORMATS = {"int4": 1, "int5": 2, "int8": 3, "nvfp4": 4, "mxfp4": 5, "mxfp8": 6}
 STATUS = {0: "OK", -1: "EINVAL", -2: "EFORMAT", -3: "EALIGN", -4: "ERANGE", -5: "EWORKSPACE",
           -6: "EHIP", -7: "EUNSUPPORTED"}
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqgemv.so")
+# QGEMV_LIB names another build of the same library (the host-sanitizer test
+# loads an address/undefined-behaviour instrumented host build this way)
+LIB_PATH = os.environ.get("QGEMV_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqgemv.so")
 
 _lib = None
 

@@ -52,23 +52,45 @@ def _run(cmd):
         raise RuntimeError("build step failed: " + " ".join(cmd))
 
 
-def build(verbose: bool = False) -> str:
+# Host-sanitizer build: the same sources with AddressSanitizer and
+# UndefinedBehaviorSanitizer on the host side only (every -fsanitize goes to
+# the host compilation through -Xarch_host; device code is built as usual),
+# linked against the shared sanitizer runtime, which the loading process must
+# preload. It serves the host-code tests (packing, argument validation).
+SAN_DIR = os.path.join(BUILD, "san")
+SAN_LIB = os.path.join(SAN_DIR, "libqgemv_san.so")
+SAN_HOST_FLAGS = ["-Xarch_host", "-fsanitize=address,undefined", "-Xarch_host", "-fno-sanitize-recover=all",
+                  "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-g"]
+
+
+def sanitizer_runtime() -> str:
+    """Path of the shared AddressSanitizer runtime of the HIP toolchain's
+    compiler (to preload into a process that loads SAN_LIB)."""
+    r = subprocess.run([_hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    return r.stdout.strip()
+
+
+def build(verbose: bool = False, sanitize: bool = False) -> str:
     hipcc = _hipcc()
-    os.makedirs(BUILD, exist_ok=True)
+    out_dir = SAN_DIR if sanitize else BUILD
+    lib = SAN_LIB if sanitize else LIB
+    os.makedirs(out_dir, exist_ok=True)
     objs = []
-    common = ["-O3", "-std=c++17", "-fPIC", "-I" + INCLUDE, "-I" + CSRC]
+    common = ["-O2" if sanitize else "-O3", "-std=c++17", "-fPIC", "-I" + INCLUDE, "-I" + CSRC]
+    if sanitize:
+        common += SAN_HOST_FLAGS
     cmds = []
     for src in HIP_SOURCES:
         path = os.path.join(CSRC, src)
         if not os.path.exists(path):
             continue
-        obj = os.path.join(BUILD, src + ".o")
+        obj = os.path.join(out_dir, src + ".o")
         cmds.append([hipcc, "--offload-arch=" + ARCH, *common,
                      "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", *EXTRA_FLAGS.get(src, []),
                      "-c", path, "-o", obj])
         objs.append(obj)
     for src in HOST_SOURCES:
-        obj = os.path.join(BUILD, src + ".o")
+        obj = os.path.join(out_dir, src + ".o")
         cmds.append([hipcc, "-x", "c++", *common, "-I" + _rocm_include(), "-D__HIP_PLATFORM_AMD__=1",
                      "-ffp-contract=off", "-fno-fast-math",
                      "-c", os.path.join(CSRC, src), "-o", obj])
@@ -83,13 +105,14 @@ def build(verbose: bool = False) -> str:
             failed = c
     if failed:
         raise RuntimeError("build step failed: " + " ".join(failed))
-    tmp = LIB + ".tmp"
-    _run([hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs, "-lpthread"])
-    os.replace(tmp, LIB)
+    tmp = lib + ".tmp"
+    link = ["-shared-libsan", *SAN_HOST_FLAGS] if sanitize else []
+    _run([hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", *link, "-o", tmp, *objs, "-lpthread"])
+    os.replace(tmp, lib)
     if verbose:
-        print("built", LIB)
-    return LIB
+        print("built", lib)
+    return lib
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, sanitize="--sanitize" in sys.argv[1:])
