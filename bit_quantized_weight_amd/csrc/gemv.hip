@@ -747,8 +747,9 @@ int ksteps_per_wave(int fmt, int N, bool swiglu, bool one_tile, int64_t KS, int6
 // waves (K split evenly over the waves; MI355X, every format, N = 1, 2, 4,
 // 8, on 7168 x 5120 and 5120 x 17408): one row tile per workgroup and the
 // listed waves per workgroup; 6-30% faster than the general rule at N >= 4,
-// within 2% of the best measured choice. The long-K shape at N = 1 keeps the
-// general rule for int5 (two tiles).
+// within 2% of the best measured choice. int5 on the long-K shape at N = 1
+// stages each wave's whole activation range (ring_first): 6% faster than its
+// two-tile general rule, which the ring made slower.
 //   384 <= tiles < 768, K <= 8192 (QKV-like):  four waves.
 //   256 <= tiles < 384, K >= 8192 (down-like): by format and tokens below.
 bool medium_grid(int fmt, int N, int64_t out_tiles, int64_t KS, int* waves) {
@@ -761,7 +762,7 @@ bool medium_grid(int fmt, int N, int64_t out_tiles, int64_t KS, int* waves) {
     static const int8_t w[4][4] = {
         // N = 1, 2, 3-4, 5-8
         {7, 6, 5, 4},   // int4
-        {0, 4, 4, 4},   // int5
+        {5, 4, 4, 4},   // int5
         {4, 5, 5, 4},   // int8
         {8, 6, 6, 5},   // nvfp4
     };
@@ -833,10 +834,11 @@ LaunchShape pick_shape(int fmt, int64_t KS, int64_t out_tiles, int N, bool swigl
 // k-loop or stream through the four-record ring; the ring measured 2-20%
 // faster on the dense layer's shapes (every format, N = 1, 2, 4), except
 // for the int5 and int8 gate/up pairs and the int formats' two-tile long-K
-// projection (the down projection) at N = 1, which keep the whole range.
+// projection (the down projection) at N = 1, and int5's one-tile long-K
+// projection at N = 1, which keep the whole range.
 bool ring_first(int fmt, int N, bool swiglu, int nt, int64_t KS) {
   if (N == 1 && swiglu && (fmt == INT5 || fmt == INT8)) return false;
-  if (N == 1 && !swiglu && nt == 2 && KS >= 64 && fmt != NVFP4) return false;
+  if (N == 1 && !swiglu && KS >= 64 && (nt == 2 ? fmt != NVFP4 : fmt == INT5)) return false;
   return true;
 }
 
