@@ -394,9 +394,11 @@ __global__ __launch_bounds__(512) void k_moe_gemv(const int32_t* ids, int NK, in
                "s"(a.out_tiles), "s"(a.up_tile0), "s"(a.K), "s"(a.G));
   if (threadIdx.x < 64) route_slot(id, NK, E, blockIdx.y, s_bits, s_route);
   __syncthreads();
-  const int e = s_route[0];
-  if (e < 0) return;                   // uniform: fewer selected experts than slots
-  moe_item<FMT, NT, DOWN, false>(a, e, s_route[1], s_route + 2, blockIdx.x, red);
+  // values read from LDS are the same in every lane: readfirstlane makes that
+  // visible to the compiler (scalar branches, buffer descriptors in SGPRs)
+  const int e = uniform(s_route[0]);
+  if (e < 0) return;                   // fewer selected experts than slots
+  moe_item<FMT, NT, DOWN, false>(a, e, uniform(s_route[1]), s_route + 2, blockIdx.x, red);
 }
 
 __global__ __launch_bounds__(256) void k_moe_combine(const float* o, const int32_t* ids, const float* gates,
@@ -445,8 +447,8 @@ __global__ __launch_bounds__(256) void k_moe_route(const float* logits, int N, i
 //   gate/up item: writes its rows of h at device scope, waits until those
 //     stores have completed, and raises its own flag (slot, row block) to
 //     this call's epoch: one store, no read-modify-write on the way.
-//   output item: wave w computes o = h . W_dn[e] for slots w, w + FW, ...
-//     over the whole K. Its weight loads are issued first; then it polls the
+//   output item: wave w computes o = h . W_dn[e] for slots w and w + FW
+//     over the whole K. Both experts' weight loads are issued first; then it polls the
 //     flags of every row block of its slot (one load per lane, bounded) until
 //     all hold the epoch, and reads h at device scope. The o values meet in
 //     LDS and the workgroup sums y = r + sum_j p_j o_j in fixed j order.
@@ -498,10 +500,14 @@ __device__ __forceinline__ void flag_store(uint64_t* p, uint64_t v) {
 }
 
 // o of one expert for one 16-row tile of the down projection, computed by one
-// wave over the whole K: o_lds[pair][row] for the expert's cnt pairs.
+// wave over the whole K: o_lds[pair][row] for the expert's cnt pairs. pre:
+// the expert's first two weight buffers, already issued by
+// kloop_start<FMT, 1, 2, 3, true> on this expert's descriptors and tile rt
+// (the first pass of four routed rows continues from them). h is read at
+// device scope after wait() has seen it complete.
 template <int FMT, class Wait>
 __device__ __forceinline__ void down_tile_wave(const MoeArgs& a, int e, int cnt, const int* pairs, int rt,
-                                               float* o_lds, const Wait& wait) {
+                                               float* o_lds, const Wait& wait, Step<FMT, 1, 3> (&pre)[2]) {
   const int lane = threadIdx.x & 63;
   const int r = lane & 15, s = lane >> 4;
   const __amdgpu_buffer_rsrc_t wq = make_rsrc(a.wq + (uint64_t)e * a.wq_stride, a.wq_bytes);
@@ -525,7 +531,7 @@ __device__ __forceinline__ void down_tile_wave(const MoeArgs& a, int e, int cnt,
       load_acts<FMT, 2>(A, k, a.KS, a.G, pos % Cyc<FMT, 2>::KSTEPS, aload);
     };
     f32x4 acc[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
-    if (c0 == 0) kloop<FMT, 1, 2, 3, 1, 1, true>(wq, ws, tile, a.KS, 0, a.KS, a.hi_offset, acts, acc, wait);
+    if (c0 == 0) kloop_run<FMT, 1, 2, 3, 1, 1, true>(pre, wq, ws, tile, a.KS, 0, a.KS, a.hi_offset, acts, acc, wait);
     else kloop<FMT, 1, 2, 3, 1>(wq, ws, tile, a.KS, 0, a.KS, a.hi_offset, acts, acc);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -547,7 +553,7 @@ template <int FMT>
 __global__ __launch_bounds__(64 * kFusedWaves) void k_moe_fused(const float* logits, int E, int top_k, int N,
                                                                 MoeFusedArgs f) {
   constexpr int FW = kFusedWaves;
-  extern __shared__ float red[];          // [FW][2][32][4] (gate/up), then o [8][16]
+  extern __shared__ __attribute__((aligned(16))) float red[];   // [FW][2][32][4] (gate/up), then o [8][16]
   __shared__ int32_t s_ids[64];
   __shared__ float s_gates[64];
   __shared__ int s_pairs[64];
@@ -601,13 +607,16 @@ __global__ __launch_bounds__(64 * kFusedWaves) void k_moe_fused(const float* log
     if (f.gates_out) f.gates_out[threadIdx.x] = s_gates[threadIdx.x];
   }
   __syncthreads();
-  const int n_active = s_meta[0];
+  // values read from LDS are the same in every lane: readfirstlane makes that
+  // visible to the compiler (scalar branches, buffer descriptors in SGPRs)
+  const int n_active = uniform(s_meta[0]);
   uint64_t* flags = (uint64_t*)((uint8_t*)f.ctr + kFlagByte);
 
   if (row == 0) {
     const int a = tk / f.nA, rb = tk - a * f.nA;
     if (a >= n_active) return;            // uniform (also the row's spare workgroups)
-    moe_item<FMT, 2, false, true>(m, s_slot_e[a], s_slot_cnt[a], s_pairs + s_slot_off[a], rb, red);
+    moe_item<FMT, 2, false, true>(m, uniform(s_slot_e[a]), uniform(s_slot_cnt[a]), s_pairs + uniform(s_slot_off[a]), rb,
+                                  red);
     __builtin_amdgcn_s_waitcnt(0);        // this thread's h stores have completed
     __syncthreads();
     if (threadIdx.x == 0) flag_store(flags + (size_t)a * f.nA + rb, f.epoch);
@@ -617,23 +626,47 @@ __global__ __launch_bounds__(64 * kFusedWaves) void k_moe_fused(const float* log
   // output block rt: 16 columns of y for every token
   const int rt = tk;
   float* o_lds = red + FW * 2 * 32 * 4;   // [NK][16]
-  for (int a = wave; a < n_active; a += FW) {
+  // a wave takes slots wave and wave + FW (at most 8 active): int4 and nvfp4
+  // request both experts' down weights (the tile's whole K) before the first
+  // wait (24 more VGPRs, two waves per SIMD still); int5 and int8, whose
+  // kernels would then hold one wave per SIMD, request the second expert's
+  // after the first expert is done
+  static_assert(2 * FW >= kFusedMaxRows, "two slots per output wave cover every active expert");
+  constexpr bool PRE2 = FMT == INT4 || FMT == NVFP4;
+  Step<FMT, 1, 3> pre[2][2];
+  const int tile1[1] = {rt};
+  auto start = [&](int i) {
+    const int e = uniform(s_slot_e[wave + i * FW]);
+    kloop_start<FMT, 1, 2, 3, true>(pre[i], make_rsrc(m.wq + (uint64_t)e * m.wq_stride, m.wq_bytes),
+                                    make_rsrc(m.ws + (uint64_t)e * m.ws_stride, m.ws_bytes), tile1, m.KS, 0, m.KS,
+                                    m.hi_offset);
+  };
+  if (wave < n_active) start(0);
+  if (PRE2 && wave + FW < n_active) start(1);
+  // a slot's h is complete once every row block's flag holds this call's number
+  auto wait_slot = [&](int a) {
     const uint64_t* fl = flags + (size_t)a * f.nA;
-    auto wait = [&]() {
-      uint32_t it = 0;
-      for (;;) {
-        bool ok = true;
-        for (int i = lane; i < f.nA; i += 64) ok &= flag_load(fl + i) == f.epoch;
-        if (__all(ok)) break;             // uniform
-        if (++it >= kSpinLimit) {
-          if (lane == 0) atomicOr(f.ctr + kCtrError, 1u);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(2);
+    uint32_t it = 0;
+    for (;;) {
+      bool ok = true;
+      for (int i = lane; i < f.nA; i += 64) ok &= flag_load(fl + i) == f.epoch;
+      if (__all(ok)) break;             // uniform
+      if (++it >= kSpinLimit) {
+        if (lane == 0) atomicOr(f.ctr + kCtrError, 1u);
+        break;
       }
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    };
-    down_tile_wave<FMT>(m, s_slot_e[a], s_slot_cnt[a], s_pairs + s_slot_off[a], rt, o_lds, wait);
+      __builtin_amdgcn_s_sleep(2);
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  };
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int a = wave + i * FW;
+    if (a >= n_active) break;
+    if (i == 1 && !PRE2) start(1);
+    auto wait = [&]() { wait_slot(a); };
+    down_tile_wave<FMT>(m, uniform(s_slot_e[a]), uniform(s_slot_cnt[a]), s_pairs + uniform(s_slot_off[a]), rt, o_lds,
+                        wait, pre[i]);
   }
   __syncthreads();
   for (int o = threadIdx.x; o < N * 16; o += blockDim.x) {
