@@ -312,16 +312,21 @@ def test_moe_index_bit_exact(N, k, E):
 # --------------------------------------------------- full sizes, sampled rows
 
 # every launch shape the benchmark times: [17408][5120] (one tile per
-# workgroup) at N = 1, 2, 4, 8 in each format, the QKV shape (one tile from
-# N = 2, two at N = 1) and the down projection (two tiles; one for NVFP4 and
-# int8 at N = 2), whose long K stages activations through the LDS ring; and
-# 9 to 32 tokens (one slot; 17 to 32 as two launches)
+# workgroup) at N = 1, 2, 4, 8 in each format, the QKV shape and the down
+# projection (one tile and 4-8 waves per workgroup), whose long K stages
+# activations through the LDS ring or the whole range; and 9 to 32 tokens
+# (one slot; 17 to 32 as two launches)
 FULL = [("int4", 7168, 5120, 1), ("int4", 7168, 5120, 8), ("int4", 7168, 5120, 4), ("int5", 5120, 17408, 1),
         ("int5", 5120, 17408, 8), ("nvfp4", 5120, 17408, 4), ("nvfp4", 7168, 5120, 2),
         ("int4", 5120, 17408, 2), ("nvfp4", 5120, 17408, 2), ("int8", 5120, 17408, 2), ("int5", 5120, 17408, 3),
         ("int5", 17408, 5120, 16), ("int8", 7168, 5120, 12), ("int4", 5120, 17408, 16), ("int4", 17408, 5120, 32),
         ("int8", 5120, 17408, 24), ("nvfp4", 17408, 5120, 16), ("nvfp4", 5120, 17408, 12),
-        ("nvfp4", 7168, 5120, 32)] + \
+        ("nvfp4", 7168, 5120, 32),
+        # the medium-grid launch shapes: one tile, 4-8 waves (every format on
+        # the QKV-like and the down-like grid)
+        ("int5", 7168, 5120, 2), ("int8", 7168, 5120, 1), ("nvfp4", 7168, 5120, 8), ("int4", 5120, 17408, 1),
+        ("int4", 5120, 17408, 8), ("int8", 5120, 17408, 1), ("int8", 5120, 17408, 4), ("nvfp4", 5120, 17408, 1),
+        ("nvfp4", 5120, 17408, 8)] + \
        [(f, 17408, 5120, n) for f in ("int4", "int5", "int8", "nvfp4") for n in (1, 2, 4, 8)]
 
 
