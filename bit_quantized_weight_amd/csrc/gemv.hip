@@ -273,7 +273,7 @@ constexpr int min_waves_per_simd() {
   return (FMT == INT5 && NT == 2 && S >= 8 && XM != 2 && !NORM && TB == 1) ? 3 : 1;
 }
 
-template <int FMT, int NT, int S, int KPS, bool SWIGLU, int XM, bool NORM, int TB = 1>
+template <int FMT, int NT, int S, int KPS, bool SWIGLU, int XM, bool NORM, int TB = 1, bool PRIO = false>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<FMT, NT, S, XM, NORM, TB>())))
 void k_gemv(const uint8_t* a_wq, const uint8_t* a_ws, uint32_t a_wqb, uint32_t a_wsb, uint32_t a_hi, int a_KS,
             int a_kpw, int a_ot, int a_up, int a_nf, int a_fl, int a_fk, GemvArgs a) {
@@ -375,7 +375,7 @@ void k_gemv(const uint8_t* a_wq, const uint8_t* a_ws, uint32_t a_wqb, uint32_t a
         if constexpr (NORM) stage_x_norm(xl, hr, gr, a.N, a.K, ks0, ks1, a.x_nks, lane, s_ss[wave]);
         else stage_x(xl, xr, a.N, a.K, ks0, ks1, a.x_nks, lane);
       };
-      kloop_run<FMT, NT, S, KPS, 1>(wbuf, wq, ws, tile, a_KS, ks0, ks1, a_hi, acts, acc, pre);
+      kloop_run<FMT, NT, S, KPS, 1, 1, false, PRIO>(wbuf, wq, ws, tile, a_KS, ks0, ks1, a_hi, acts, acc, pre);
     } else {
       // Ring slot of k-step k: (k - ks0) % kRing, which equals its trip
       // position modulo kRing (trips start at ks0 + a multiple of 2 * KPS).
@@ -428,7 +428,7 @@ void k_gemv(const uint8_t* a_wq, const uint8_t* a_ws, uint32_t a_wqb, uint32_t a
         ring_load(stg[1], ks0 + 2);
         ring_store(v0, 0);
       };
-      kloop_run<FMT, NT, S, KPS, 1>(wbuf, wq, ws, tile, a_KS, ks0, ks1, a_hi, acts, acc, pre);
+      kloop_run<FMT, NT, S, KPS, 1, 1, false, PRIO>(wbuf, wq, ws, tile, a_KS, ks0, ks1, a_hi, acts, acc, pre);
       if (NORM && ks0 < ks1) {
         // tokens (lane >> 4) and 4 + (lane >> 4): sum the 16 lanes of each row
 #pragma unroll
@@ -682,6 +682,7 @@ struct LaunchShape {
   int slots;    // S
   int kpw;      // k-steps per wave (a multiple of the cycle)
   int kps;      // k-steps per weight prefetch buffer
+  int prio = 0; // k-loop wave priority from progress
 };
 
 int slots_for(int N) { return N == 1 ? 16 : N == 2 ? 8 : N <= 4 ? 4 : N <= 8 ? 2 : 1; }   // N <= 32
@@ -810,6 +811,10 @@ LaunchShape pick_shape(int fmt, int64_t KS, int64_t out_tiles, int N, bool swigl
   if (!swiglu && medium_grid(fmt, N, out_tiles, KS, &mw)) {
     ls.nt = 1;
     kpw = round_cyc((KS + mw - 1) / mw);
+    // progress priority (kloop_run): on the long-K shape at N = 1 int5 (five
+    // waves per workgroup) measured 4% faster, NVFP4 (eight) 3.5%; int4,
+    // int8, N >= 2, the QKV-like shape and gate/up pairs gained nothing or lost
+    ls.prio = N == 1 && KS >= 64 && out_tiles < 384 && (fmt == INT5 || fmt == NVFP4);
   } else {
     const bool one = single_tile(fmt, N, swiglu, out_tiles);
     ls.nt = one ? 1 : 2;
@@ -980,6 +985,12 @@ hipError_t launch_s(const GemvArgs& a0, const LaunchShape& ls, bool swiglu, hipS
     // SwiGLU with 17 to 32 tokens: two token blocks share each decoded weight
     // operand (the plain GEMV runs two launches instead)
     if (two_blocks) fn = swiglu ? (KernelFn)k_gemv<FMT, NT, 1, KPS, true, XM_LOAD, false, 2> : nullptr;
+  }
+  if constexpr (NT == 1 && S == 16 && (FMT == INT5 || FMT == NVFP4)) {
+    // the k-loop with progress priority (pick_shape decides where)
+    if (ls.prio && !swiglu && !norm && (xm == XM_LDS || xm == XM_RING))
+      fn = xm == XM_LDS ? (KernelFn)k_gemv<FMT, 1, 16, KPS, false, XM_LDS, false, 1, true>
+                        : (KernelFn)k_gemv<FMT, 1, 16, KPS, false, XM_RING, false, 1, true>;
   }
   if (!fn) return hipErrorNotSupported;
   int64_t nwg = blocks;

@@ -325,7 +325,8 @@ __device__ __forceinline__ void kloop_start(Step<FMT, NT, KPS> (&buf)[2], __amdg
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int FMT, int NT, int S, int KPS, int AD, int TB = 1, bool EARLY = false, class Acts, class Pre = NoPrologue>
+template <int FMT, int NT, int S, int KPS, int AD, int TB = 1, bool EARLY = false, bool PRIO = false, class Acts,
+          class Pre = NoPrologue>
 __device__ __forceinline__ void kloop_run(Step<FMT, NT, KPS> (&buf)[2], __amdgpu_buffer_rsrc_t wq,
                                           __amdgpu_buffer_rsrc_t ws, const int (&tile)[NT], int KS, int ks0, int ks1,
                                           uint32_t hi_offset, const Acts& acts, f32x4 (&acc)[NT * TB],
@@ -362,7 +363,20 @@ __device__ __forceinline__ void kloop_run(Step<FMT, NT, KPS> (&buf)[2], __amdgpu
   pre();
 #pragma unroll
   for (int d = 0; d < AD; ++d) fetch(xa[d], ks0 + d, d);
+  // PRIO: wave priority from the wave's own progress, 3 in the first
+  // quarter of its range down to 0 in the last. The sequencer issues the
+  // oldest ready wave first; where a unit holds more waves on some SIMDs than
+  // on others, the younger waves there fall behind and finish last. Ranking
+  // by progress instead lets a wave that lags catch up.
+  const int pq = (ks1 - ks0) >> 2;
+  const int pq1 = ks0 + pq, pq2 = ks0 + ((ks1 - ks0) >> 1), pq3 = ks1 - pq;
   for (int base = ks0; base < ks1; base += U) {
+    if constexpr (PRIO) {
+      if (base < pq1) __builtin_amdgcn_s_setprio(3);
+      else if (base < pq2) __builtin_amdgcn_s_setprio(2);
+      else if (base < pq3) __builtin_amdgcn_s_setprio(1);
+      else __builtin_amdgcn_s_setprio(0);
+    }
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
 #pragma unroll
@@ -458,6 +472,7 @@ __device__ __forceinline__ void kloop_run(Step<FMT, NT, KPS> (&buf)[2], __amdgpu
       }
     }
   }
+  if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
 }
 
 template <int FMT, int NT, int S, int KPS, int AD, int TB = 1, bool EARLY = false, class Acts, class Pre = NoPrologue>
