@@ -389,8 +389,8 @@ def summarize_profile(out_path, command_lines, trace, counter_runs):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--layers", type=int, default=16, help="distinct layer copies rotated on the device")
     ap.add_argument("--no-extra", action="store_true", help="skip per-format, MoE, probe and CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -517,12 +517,12 @@ def main():
 
     kern = {}
     kern["qkv_int4"] = (time_alone(lambda i: qg.qgemv_ex("int4", *layers[i % args.layers]["qkv"], x, qkv, 7168, 5120, N,
-                                                         workspace=wsp), 100),
+                                                         workspace=wsp), 300),
                         weight_bytes(qg, "int4", 7168, 5120) + N * 5120 * 2 + N * 7168 * 4)
     kern["gate_up_swiglu_int5"] = (time_alone(lambda i: qg.qgemv_swiglu_ex("int5", *layers[i % args.layers]["gate_up"], x, h,
-                                                                            17408, 5120, N, workspace=wsp), 50), gu_bytes)
+                                                                            17408, 5120, N, workspace=wsp), 150), gu_bytes)
     kern["down_residual_int5"] = (time_alone(lambda i: qg.qgemv_ex("int5", *layers[i % args.layers]["down"], xd, y, 5120,
-                                                                   17408, N, residual=res, workspace=wsp), 50),
+                                                                   17408, N, residual=res, workspace=wsp), 200),
                                   weight_bytes(qg, "int5", 5120, 17408) + N * 17408 * 2 + N * 5120 * 8)
     kernels = {k: {"us": round(t[0] * 1e3, 2), "us_min": round(t[1] * 1e3, 2), "us_max": round(t[2] * 1e3, 2),
                    "GB/s": round(b / (t[0] * 1e-3) / 1e9, 1)} for k, (t, b) in kern.items()}
@@ -535,7 +535,7 @@ def main():
     h8 = torch.empty((8, 17408), dtype=torch.float32, device=dev)
     gu8_bytes = weight_bytes(qg, "int5", 2 * 17408, 5120) + 8 * 5120 * 2 + 8 * 17408 * 4
     gu8_ms = time_alone(lambda i: qg.qgemv_swiglu_ex("int5", *layers[i % args.layers]["gate_up"], x8, h8, 17408, 5120, 8,
-                                                     workspace=wsp), 50)[0]
+                                                     workspace=wsp), 150)[0]
     gu8_gbs = gu8_bytes / (gu8_ms * 1e-3) / 1e9
 
     # the MLP block chained on the device, each launch consuming the previous
@@ -554,7 +554,7 @@ def main():
         qg.qgemv_ex("int5", *L["down"], hb, ym, 5120, 17408, 1, residual=r1, workspace=wsp)
     mlp_bytes = (weight_bytes(qg, "int5", 2 * 17408, 5120) + weight_bytes(qg, "int5", 5120, 17408)
                  + 5120 * 4 * 2 + 5120 * 4 + 17408 * 2 * 2 + 5120 * 8)
-    mlp_ms = time_alone(mlp, 32)[0]
+    mlp_ms = time_alone(mlp, 100)[0]
 
     src_hash = kernel_source_hash()
     qg.check_split_workspace(wsp)
@@ -615,17 +615,21 @@ def extras(qg, torch, dev, stream, layers, args, wsp):
     import synthetic
     res = {}
 
-    def timeit(fn, reps):
-        for i in range(4):
+    def timeit(fn, reps, batches=3):
+        # warm launches, then the median of `batches` event-timed batches
+        for i in range(16):
             fn(i)
         torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for i in range(reps):
-            fn(i)
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / reps
+        out = []
+        for bi in range(batches):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for i in range(reps):
+                fn(bi * reps + i)
+            b.record(stream)
+            torch.cuda.synchronize()
+            out.append(a.elapsed_time(b) / reps)
+        return float(np.median(out))
 
     # probe: plain streaming read of each 134 MB gate/up weight buffer
     sink = torch.zeros(4, dtype=torch.int32, device=dev)

@@ -113,20 +113,33 @@ def _check(rc: int, what: str):
 
 
 def _ptr(t):
-    """Device or host pointer of a torch tensor / numpy array / None."""
+    """Device or host pointer of a torch tensor / numpy array / int / None."""
     if t is None:
         return None
+    dp = getattr(t, "data_ptr", None)   # torch tensors (the common case) first
+    if dp is not None:
+        return dp()
     if isinstance(t, np.ndarray):
         return t.ctypes.data
     if isinstance(t, int):
         return t
-    return t.data_ptr()
+    raise TypeError(f"expected a torch tensor, numpy array, int or None, got {type(t).__name__}")
+
+
+_raw_stream = None
 
 
 def _stream(stream):
+    """HIP stream handle: an int as given, a torch stream's handle, or (None)
+    torch's current stream on the current device."""
+    global _raw_stream
     if stream is None:
-        import torch
-        return torch.cuda.current_stream().cuda_stream
+        if _raw_stream is None:
+            import torch
+            get = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+            _raw_stream = ((lambda: get(torch.cuda.current_device())) if get is not None
+                           else (lambda: torch.cuda.current_stream().cuda_stream))
+        return _raw_stream()
     if isinstance(stream, int):
         return stream
     return stream.cuda_stream
@@ -184,12 +197,24 @@ def qgemv_swiglu(fmt, wq, ws, x, h, I: int, K: int, N: int, stream=None) -> None
            "qgemv_swiglu")
 
 
+_fusion_cache: dict = {}
+
+
 def _fusion(norm_src, norm_gamma, norm_eps, out_bf16, batch_invariant=False, workspace=None):
+    """A qgemv_fusion for these arguments (None when all are defaults). The
+    struct is only read during the call; equal argument sets share one
+    cached object."""
     if norm_src is None and out_bf16 is None and not batch_invariant and workspace is None:
         return None
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    return ctypes.byref(Fusion(_ptr(norm_src), _ptr(norm_gamma), float(norm_eps), _ptr(out_bf16),
-                               BATCH_INVARIANT if batch_invariant else 0, _ptr(workspace), wbytes))
+    key = (_ptr(norm_src), _ptr(norm_gamma), float(norm_eps), _ptr(out_bf16),
+           BATCH_INVARIANT if batch_invariant else 0, _ptr(workspace), wbytes)
+    ref = _fusion_cache.get(key)
+    if ref is None:
+        if len(_fusion_cache) >= 256:
+            _fusion_cache.clear()
+        ref = _fusion_cache[key] = ctypes.byref(Fusion(*key))
+    return ref
 
 
 def split_workspace_bytes() -> int:
