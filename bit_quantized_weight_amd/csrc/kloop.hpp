@@ -244,16 +244,26 @@ __device__ __forceinline__ void flush(f32x4& acc, const f32x4& D, const f32x4& D
   }
 }
 
+// Weight and scale descriptors of a k-loop: one buffer for all NT tiles (a
+// plain descriptor), or one per tile (PerTile: tiles of different matrices,
+// e.g. the same row tile of two experts).
+template <int NT>
+struct PerTile {
+  __amdgpu_buffer_rsrc_t r[NT];
+};
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rs_at(__amdgpu_buffer_rsrc_t r, int) { return r; }
+template <int NT>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rs_at(const PerTile<NT>& r, int t) { return r.r[t]; }
+
 // Loads the packed weights of KPS k-steps starting at ks (wave-uniform) into
 // st. K-steps at or past ks1 read as zeros (out-of-range offsets, no memory
 // traffic).
 // CYC: this buffer's first k-step starts a scale cycle of several k-steps;
 // that cycle's scale words travel with the buffer, so they are in flight as
 // long as the weights (a cycle's flush comes KSTEPS k-steps after its start).
-template <int FMT, int NT, int S, int KPS, bool CYC>
-__device__ __forceinline__ void load_weights(Step<FMT, NT, KPS>& st, __amdgpu_buffer_rsrc_t wq,
-                                             __amdgpu_buffer_rsrc_t ws, const int (&tile)[NT], int KS, int ks,
-                                             int ks1, uint32_t hi_offset) {
+template <int FMT, int NT, int S, int KPS, bool CYC, class WQ, class WS>
+__device__ __forceinline__ void load_weights(Step<FMT, NT, KPS>& st, WQ wq, WS ws, const int (&tile)[NT], int KS,
+                                             int ks, int ks1, uint32_t hi_offset) {
   const int lane = threadIdx.x & 63;
   constexpr int TB = FMT == INT8 ? 2048 : 1024;
 #pragma unroll
@@ -265,12 +275,12 @@ __device__ __forceinline__ void load_weights(Step<FMT, NT, KPS>& st, __amdgpu_bu
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const uint32_t tau = (uint32_t)tile[t] * (uint32_t)KS + (uint32_t)k;
-      st.q[i][t] = ld128s_nt(wq, lo, tau * TB);
-      if constexpr (FMT == INT8) st.q2[i][t] = ld128s_nt(wq, lo, tau * TB + 1024u);
-      if constexpr (FMT == INT5) st.h[i][t] = ld32s_nt(wq, (uint32_t)lane * 4u | bad, hi_offset + tau * 256u);
-      if constexpr (Cyc<FMT, S>::KSTEPS == 1) st.sc[i][t] = load_scales<FMT, S>(ws, tau, lane, ok ? 1 : 0);
+      st.q[i][t] = ld128s_nt(rs_at(wq, t), lo, tau * TB);
+      if constexpr (FMT == INT8) st.q2[i][t] = ld128s_nt(rs_at(wq, t), lo, tau * TB + 1024u);
+      if constexpr (FMT == INT5) st.h[i][t] = ld32s_nt(rs_at(wq, t), (uint32_t)lane * 4u | bad, hi_offset + tau * 256u);
+      if constexpr (Cyc<FMT, S>::KSTEPS == 1) st.sc[i][t] = load_scales<FMT, S>(rs_at(ws, t), tau, lane, ok ? 1 : 0);
       if constexpr (Cyc<FMT, S>::KSTEPS > 1 && CYC) {
-        if (i == 0) st.cyc[t] = load_scales<FMT, S>(ws, tau, lane, ks1 - k);
+        if (i == 0) st.cyc[t] = load_scales<FMT, S>(rs_at(ws, t), tau, lane, ks1 - k);
       }
     }
   }
@@ -309,10 +319,9 @@ struct NoPrologue {
 // TB > 1 (one slot only): TB blocks of 16 tokens share every decoded weight
 // operand; acts then fills A[TB][4] and acc[t * TB + b] holds block b of
 // tile t.
-template <int FMT, int NT, int S, int KPS, bool EARLY = false>
-__device__ __forceinline__ void kloop_start(Step<FMT, NT, KPS> (&buf)[2], __amdgpu_buffer_rsrc_t wq,
-                                            __amdgpu_buffer_rsrc_t ws, const int (&tile)[NT], int KS, int ks0, int ks1,
-                                            uint32_t hi_offset) {
+template <int FMT, int NT, int S, int KPS, bool EARLY = false, class WQ, class WS>
+__device__ __forceinline__ void kloop_start(Step<FMT, NT, KPS> (&buf)[2], WQ wq, WS ws, const int (&tile)[NT], int KS,
+                                            int ks0, int ks1, uint32_t hi_offset) {
   using C = Cyc<FMT, S>;
   if (ks0 < ks1) {
     load_weights<FMT, NT, S, KPS, true>(buf[0], wq, ws, tile, KS, ks0, ks1, hi_offset);
@@ -325,12 +334,11 @@ __device__ __forceinline__ void kloop_start(Step<FMT, NT, KPS> (&buf)[2], __amdg
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int FMT, int NT, int S, int KPS, int AD, int TB = 1, bool EARLY = false, bool PRIO = false, class Acts,
-          class Pre = NoPrologue>
-__device__ __forceinline__ void kloop_run(Step<FMT, NT, KPS> (&buf)[2], __amdgpu_buffer_rsrc_t wq,
-                                          __amdgpu_buffer_rsrc_t ws, const int (&tile)[NT], int KS, int ks0, int ks1,
-                                          uint32_t hi_offset, const Acts& acts, f32x4 (&acc)[NT * TB],
-                                          const Pre& pre = Pre()) {
+template <int FMT, int NT, int S, int KPS, int AD, int TB = 1, bool EARLY = false, bool PRIO = false, class WQ,
+          class WS, class Acts, class Pre = NoPrologue>
+__device__ __forceinline__ void kloop_run(Step<FMT, NT, KPS> (&buf)[2], WQ wq, WS ws, const int (&tile)[NT], int KS,
+                                          int ks0, int ks1, uint32_t hi_offset, const Acts& acts,
+                                          f32x4 (&acc)[NT * TB], const Pre& pre = Pre()) {
   static_assert(TB == 1 || S == 1, "token blocks need one slot");
   using C = Cyc<FMT, S>;
   constexpr int U = 2 * KPS;                     // k-steps per loop trip (a multiple of C::KSTEPS)

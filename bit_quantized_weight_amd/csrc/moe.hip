@@ -546,6 +546,59 @@ __device__ __forceinline__ void down_tile_wave(const MoeArgs& a, int e, int cnt,
   }
 }
 
+// o of two experts for one 16-row tile of the down projection, in one k-loop
+// by one wave: the experts' weight tiles are the loop's two tiles (one
+// descriptor each) and their routed pairs share the A operand (pairs 0..n0-1
+// of the first expert, then n1 of the second; n0 + n1 <= 4). Tile t's dot
+// products with the other expert's rows are computed and dropped; in return
+// the two experts' MFMA and decode chains interleave instead of running one
+// after the other. pre: both tiles' first two weight buffers, already issued
+// by kloop_start<FMT, 2, 2, 3, true>. h is read at device scope: the caller
+// has seen both slots complete.
+template <int FMT>
+__device__ __forceinline__ void down_pair_wave(const MoeArgs& a, PerTile<2> wq, PerTile<2> ws, int n0, int n1,
+                                               const int* p0, const int* p1, int rt, float* o_lds,
+                                               Step<FMT, 2, 3> (&pre)[2]) {
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15, s = lane >> 4;
+  const __amdgpu_buffer_rsrc_t inr = make_rsrc(a.in, a.in_bytes);
+  const int tile[2] = {rt, rt};
+  float st0 = 1.0f, st1 = 1.0f;
+  if constexpr (FMT == NVFP4) {
+    st0 = __builtin_bit_cast(float, ld32(ws.r[0], a.st_offset));
+    st1 = __builtin_bit_cast(float, ld32(ws.r[1], a.st_offset));
+  }
+  const int ar = r & 3;
+  const bool row_ok = ar < n0 + n1;
+  const int pflat = ar < n0 ? p0[ar] : (row_ok ? p1[ar - n0] : 0);
+  const int part = (r >> 2) & 1;   // A rows 8*slot + 4*part + pair: hi / lo plane of h
+  const uint32_t base = (row_ok ? (uint32_t)((part * a.NK + pflat) * a.K + 8 * s) * 2u : kAbsentRow) +
+                        lane_slot_term<FMT, 2>(lane);
+  auto aload = [&](int g, uint32_t adj) -> bf16x8 {
+    return __builtin_bit_cast(bf16x8, ld128s_dev(inr, base + adj, (uint32_t)g * 64u));
+  };
+  auto acts = [&](bf16x8 (&A)[4], int k, int pos) {
+    load_acts<FMT, 2>(A, k, a.KS, a.G, pos % Cyc<FMT, 2>::KSTEPS, aload);
+  };
+  f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  kloop_run<FMT, 2, 2, 3, 1, 1, true>(pre, wq, ws, tile, a.KS, 0, a.KS, a.hi_offset, acts, acc);
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[t][i] += __shfl_xor(acc[t][i], 32);   // slots
+      acc[t][i] += __shfl_xor(acc[t][i], 16);   // hi + lo parts
+    }
+  }
+  if (lane < 16 && rt * 16 + lane < a.Mout) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (i < n0) o_lds[p0[i] * 16 + lane] = acc[0][i] * st0;
+      else if (i < n0 + n1) o_lds[p1[i - n0] * 16 + lane] = acc[1][i] * st1;
+    }
+  }
+}
+
 // logits, E, top_k, N: copies of f's fields, leading scalar arguments
 // preloaded into SGPRs at wave launch, so each wave's first logits load goes
 // out at once.
@@ -633,16 +686,6 @@ __global__ __launch_bounds__(64 * kFusedWaves) void k_moe_fused(const float* log
   // after the first expert is done
   static_assert(2 * FW >= kFusedMaxRows, "two slots per output wave cover every active expert");
   constexpr bool PRE2 = FMT == INT4 || FMT == NVFP4;
-  Step<FMT, 1, 3> pre[2][2];
-  const int tile1[1] = {rt};
-  auto start = [&](int i) {
-    const int e = uniform(s_slot_e[wave + i * FW]);
-    kloop_start<FMT, 1, 2, 3, true>(pre[i], make_rsrc(m.wq + (uint64_t)e * m.wq_stride, m.wq_bytes),
-                                    make_rsrc(m.ws + (uint64_t)e * m.ws_stride, m.ws_bytes), tile1, m.KS, 0, m.KS,
-                                    m.hi_offset);
-  };
-  if (wave < n_active) start(0);
-  if (PRE2 && wave + FW < n_active) start(1);
   // a slot's h is complete once every row block's flag holds this call's number
   auto wait_slot = [&](int a) {
     const uint64_t* fl = flags + (size_t)a * f.nA;
@@ -659,14 +702,44 @@ __global__ __launch_bounds__(64 * kFusedWaves) void k_moe_fused(const float* log
     }
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
   };
+  // int4 / NVFP4 with both slots and at most four routed pairs between them
+  // (always at N = 1): one two-tile k-loop over both experts, whose weights
+  // are requested here, before the waits
+  const int a1 = wave + FW;
+  const bool pair = PRE2 && a1 < n_active && uniform(s_slot_cnt[wave]) + uniform(s_slot_cnt[a1]) <= 4;
+  if (pair) {
+    const int e0 = uniform(s_slot_e[wave]), e1 = uniform(s_slot_e[a1]);
+    const PerTile<2> wq2 = {{make_rsrc(m.wq + (uint64_t)e0 * m.wq_stride, m.wq_bytes),
+                             make_rsrc(m.wq + (uint64_t)e1 * m.wq_stride, m.wq_bytes)}};
+    const PerTile<2> ws2 = {{make_rsrc(m.ws + (uint64_t)e0 * m.ws_stride, m.ws_bytes),
+                             make_rsrc(m.ws + (uint64_t)e1 * m.ws_stride, m.ws_bytes)}};
+    const int tile2[2] = {rt, rt};
+    Step<FMT, 2, 3> pb[2];
+    kloop_start<FMT, 2, 2, 3, true>(pb, wq2, ws2, tile2, m.KS, 0, m.KS, m.hi_offset);
+    wait_slot(wave);
+    wait_slot(a1);
+    down_pair_wave<FMT>(m, wq2, ws2, uniform(s_slot_cnt[wave]), uniform(s_slot_cnt[a1]),
+                        s_pairs + uniform(s_slot_off[wave]), s_pairs + uniform(s_slot_off[a1]), rt, o_lds, pb);
+  } else {
+    Step<FMT, 1, 3> pre[2][2];
+    const int tile1[1] = {rt};
+    auto start = [&](int i) {
+      const int e = uniform(s_slot_e[wave + i * FW]);
+      kloop_start<FMT, 1, 2, 3, true>(pre[i], make_rsrc(m.wq + (uint64_t)e * m.wq_stride, m.wq_bytes),
+                                      make_rsrc(m.ws + (uint64_t)e * m.ws_stride, m.ws_bytes), tile1, m.KS, 0, m.KS,
+                                      m.hi_offset);
+    };
+    if (wave < n_active) start(0);
+    if (PRE2 && wave + FW < n_active) start(1);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int a = wave + i * FW;
-    if (a >= n_active) break;
-    if (i == 1 && !PRE2) start(1);
-    auto wait = [&]() { wait_slot(a); };
-    down_tile_wave<FMT>(m, uniform(s_slot_e[a]), uniform(s_slot_cnt[a]), s_pairs + uniform(s_slot_off[a]), rt, o_lds,
-                        wait, pre[i]);
+    for (int i = 0; i < 2; ++i) {
+      const int a = wave + i * FW;
+      if (a >= n_active) break;
+      if (i == 1 && !PRE2) start(1);
+      auto wait = [&]() { wait_slot(a); };
+      down_tile_wave<FMT>(m, uniform(s_slot_e[a]), uniform(s_slot_cnt[a]), s_pairs + uniform(s_slot_off[a]), rt,
+                          o_lds, wait, pre[i]);
+    }
   }
   __syncthreads();
   for (int o = threadIdx.x; o < N * 16; o += blockDim.x) {
