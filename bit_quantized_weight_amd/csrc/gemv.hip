@@ -683,6 +683,7 @@ struct LaunchShape {
   int kpw;      // k-steps per wave (a multiple of the cycle)
   int kps;      // k-steps per weight prefetch buffer
   int prio = 0; // k-loop wave priority from progress
+  bool inv = false;  // batch-invariant mode (no choice that could order a sum may follow N)
 };
 
 int slots_for(int N) { return N == 1 ? 16 : N == 2 ? 8 : N <= 4 ? 4 : N <= 8 ? 2 : 1; }   // N <= 32
@@ -711,7 +712,12 @@ int cycle_ksteps(int fmt, int S) {
 //     longer ranges: at N = 1 28 for int5/int8 (int4 20, NVFP4 24), at
 //     N = 2-4 int4 28, int5/int8 40 (one wave per workgroup; with the
 //     RMSNorm prologue 20, int8 12), NVFP4 24; SwiGLU and long K at N > 4
-//     take longer ranges too (five waves per workgroup).
+//     take longer ranges too (five waves per workgroup). With the RMSNorm
+//     prologue (every wave converts and sums its own range of the source
+//     row) longer ranges win: at N = 1 the whole K in one wave for int4 and
+//     int5 (12% and 5% faster than 20 and 28 there), NVFP4 20, int8 28; at
+//     N = 2 the whole K for int4 and int5 (13%), NVFP4 and int8 20; at N = 3-4
+//     the whole K in every format with the activation ring (11-23% faster).
 // The grid should hold at least ~900 waves so the chip's 1024 SIMDs have
 // work; below that the k-range per wave shrinks (never under one scale
 // cycle). Each wave's range is a whole number of cycles.
@@ -723,12 +729,14 @@ bool single_tile(int fmt, int N, bool swiglu, int64_t out_tiles) {
 
 int ksteps_per_wave(int fmt, int N, bool swiglu, bool one_tile, int64_t KS, int64_t out_tiles, bool norm) {
   if (swiglu) {                          // gate/up pairs: [2 x 17408][5120] sweeps with the split remainder
+    if (norm && N <= 4) {                // RMSNorm prologue: mostly one wave per pair
+      if (N == 1) return fmt == NVFP4 ? 20 : fmt == INT8 ? 28 : 40;
+      if (N == 2) return (fmt == NVFP4 || fmt == INT8) ? 20 : 40;
+      return 40;                         // N = 3-4, with the activation ring (launch_s)
+    }
     if (fmt == NVFP4) return N <= 4 ? 24 : 40;
     if (N == 1) return fmt == INT4 ? 20 : 28;
-    if (N <= 4) {
-      if (norm) return fmt == INT8 ? 12 : 20;   // the prologue's staging: 28-40 measured 3-45% slower here
-      return fmt == INT4 ? 28 : 40;
-    }
+    if (N <= 4) return fmt == INT4 ? 28 : 40;
     return 40;
   }
   if (one_tile) {
@@ -791,6 +799,7 @@ LaunchShape pick_shape(int fmt, int64_t KS, int64_t out_tiles, int N, bool swigl
   ls.kps = 2;
   ls.slots = inv ? 2 : slots_for(N);
   if (inv) {
+    ls.inv = true;
     const bool one = single_tile(fmt, N, swiglu, out_tiles);
     ls.nt = one ? 1 : 2;
     int64_t kpw = kInvariantKsteps;   // the slot count 2 has one-k-step cycles in every format
@@ -951,6 +960,11 @@ hipError_t launch_s(const GemvArgs& a0, const LaunchShape& ls, bool swiglu, hipS
   if (xm == XM_LDS && S >= 4 && !a.nsrc && ring <= kMaxLdsActs && ring_first(FMT, a.N, swiglu, NT, a.KS))
     xm = XM_RING;
   if (two_blocks) xm = XM_LOAD;
+  // the RMSNorm prologue for gate/up pairs at N = 3-4 streams through the ring
+  // (not in batch-invariant mode: the two paths add a row's squares in
+  // different orders)
+  if (a.nsrc && swiglu && !ls.inv && a.N >= 3 && a.N <= 4 && xm == XM_LDS && S > 1 && red + ring <= kMaxLdsNorm)
+    xm = XM_RING;
   if (a.nsrc && xm == XM_LOAD) {         // the RMSNorm prologue stages its activations in LDS
     if (red + ring > kMaxLdsNorm) return hipErrorNotSupported;
     xm = XM_RING;
