@@ -706,7 +706,7 @@ int cycle_ksteps(int fmt, int S) {
 //     at N <= 2 and int8 at N = 2, which take one tile on every shape.
 //     SwiGLU always keeps a gate tile and its up tile together.
 //   * A wave streams best with 12-20 k-steps of its tiles: 20 at N = 1 and
-//     N > 4; on one-tile workgroups of large matrices 20 at N <= 4 (NVFP4
+//     N > 4; on one-tile workgroups of large matrices 20 at every N (NVFP4
 //     16), on smaller ones 12 at N = 2 and for int5/int8 at N = 4, 16 for
 //     int4/NVFP4 at N = 4, NVFP4 at N = 1 with 12. Gate/up pairs take
 //     longer ranges: at N = 1 28 for int5/int8 (int4 20, NVFP4 24), at
@@ -740,7 +740,7 @@ int ksteps_per_wave(int fmt, int N, bool swiglu, bool one_tile, int64_t KS, int6
     return 40;
   }
   if (one_tile) {
-    if (N <= 4 && out_tiles >= 768) return fmt == NVFP4 ? 16 : 20;
+    if (out_tiles >= 768) return fmt == NVFP4 ? 16 : 20;   // NVFP4 16 at every N (at N = 5-8 3-6% faster than 20)
     if (N == 1) return fmt == NVFP4 ? 12 : 20;
     if (N == 2) return fmt == INT8 ? 20 : 12;
     if (N <= 4) return (fmt == INT4 || fmt == NVFP4) ? 16 : 12;
