@@ -103,9 +103,10 @@ def test_route_rejects_bad_arguments():
 
 # ------------------------------------------------------------ fused MoE
 
-def _fused_case(fmt, E, H, I, N, k, seed):
-    rng = synthetic.rng_for(12, seed, E, N)
-    logits = synthetic.router_logits(rng, N, E) * np.float32(2)
+def _fused_case(fmt, E, H, I, N, k, seed, logits=None):
+    if logits is None:
+        rng = synthetic.rng_for(12, seed, E, N)
+        logits = synthetic.router_logits(rng, N, E) * np.float32(2)
     bufs, Wgu, Wdn, xb, ids, gates, r = moe_case(fmt, E, H, I, N, k, seed=seed, logits=logits)
     return logits, bufs, Wgu, Wdn, xb, ids, gates, r
 
@@ -147,8 +148,8 @@ def _check_flags(w, I, N, k, ids):
     assert np.all(fl[n_active:] == 0)
 
 
-def _check_fused(fmt, E, H, I, N, k, seed, calls=2):
-    logits, bufs, Wgu, Wdn, xb, ids_ref, _, r = _fused_case(fmt, E, H, I, N, k, seed)
+def _check_fused(fmt, E, H, I, N, k, seed, calls=2, logits=None):
+    logits, bufs, Wgu, Wdn, xb, ids_ref, _, r = _fused_case(fmt, E, H, I, N, k, seed, logits)
     ys, ids, gates, w, d = _run_fused(fmt, bufs, E, H, I, xb, logits, k, N, r, calls=calls)
     assert np.array_equal(ids, ids_ref), (ids, ids_ref)
     _check_flags(w, I, N, k, ids)
@@ -182,6 +183,23 @@ def _check_fused(fmt, E, H, I, N, k, seed, calls=2):
 def test_fused_moe_parity(fmt, N):
     log("fused moe", fmt, N)
     _check_fused(fmt, 16, 256, 64, N, 4, seed=N)
+
+
+@pytest.mark.parametrize("fmt", ["int4", "nvfp4", "int5"])
+@pytest.mark.parametrize("choice", [(2, 2, 2, 5, 7, 9, 11, 13), (2, 2, 2, 2, 5, 7, 9, 11)])
+def test_fused_moe_shared_experts(fmt, choice):
+    """Top-1 routing of eight tokens onto fewer experts, so that an output
+    wave's two slots (a and a + 4) carry several routed rows: three plus one
+    (int4 and NVFP4 then run both experts as the two tiles of one k-loop, the
+    A operand holding four pairs) and four plus one (more than four: one
+    expert after the other); int5 takes the one-at-a-time path throughout."""
+    E, N = 16, 8
+    rng = np.random.default_rng(sum(choice))
+    logits = (0.1 * rng.standard_normal((N, E))).astype(np.float32)
+    for t, e in enumerate(choice):
+        logits[t, e] = 4.0
+    log("fused moe shared experts", fmt, choice)
+    _check_fused(fmt, E, 256, 64, N, 1, seed=0, logits=logits)
 
 
 @pytest.mark.parametrize("N", [1, 2, 8])
