@@ -963,7 +963,7 @@ hipError_t launch_s(const GemvArgs& a0, const LaunchShape& ls, bool swiglu, hipS
   // gate/up pairs at N = 5-8 (two slots) read their activations straight from
   // memory: int4 9-10% and int5 3-4% faster than the ring, NVFP4 1-4%; int8,
   // and every plain GEMV shape measured, keep the staged paths
-  if (swiglu && S == 2 && FMT != INT8 && !a.nsrc) xm = XM_LOAD;
+  if (swiglu && S == 2 && a.N >= 5 && FMT != INT8 && !a.nsrc) xm = XM_LOAD;
   // the RMSNorm prologue for gate/up pairs at N = 3-4 streams through the ring
   // (not in batch-invariant mode: the two paths add a row's squares in
   // different orders)

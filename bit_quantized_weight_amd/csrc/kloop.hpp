@@ -277,8 +277,10 @@ __device__ __forceinline__ void load_weights(Step<FMT, NT, KPS>& st, WQ wq, WS w
       const uint32_t tau = (uint32_t)tile[t] * (uint32_t)KS + (uint32_t)k;
       st.q[i][t] = ld128s_nt(rs_at(wq, t), lo, tau * TB);
       if constexpr (FMT == INT8) st.q2[i][t] = ld128s_nt(rs_at(wq, t), lo, tau * TB + 1024u);
-      if constexpr (FMT == INT5) st.h[i][t] = ld32s_nt(rs_at(wq, t), (uint32_t)lane * 4u | bad, hi_offset + tau * 256u);
-      if constexpr (Cyc<FMT, S>::KSTEPS == 1) st.sc[i][t] = load_scales<FMT, S>(rs_at(ws, t), tau, lane, ok ? 1 : 0);
+      if constexpr (FMT == INT5)
+        st.h[i][t] = ld32s_nt(rs_at(wq, t), (uint32_t)lane * 4u | bad, hi_offset + tau * 256u);
+      if constexpr (Cyc<FMT, S>::KSTEPS == 1)
+        st.sc[i][t] = load_scales<FMT, S>(rs_at(ws, t), tau, lane, ok ? 1 : 0);
       if constexpr (Cyc<FMT, S>::KSTEPS > 1 && CYC) {
         if (i == 0) st.cyc[t] = load_scales<FMT, S>(rs_at(ws, t), tau, lane, ks1 - k);
       }
