@@ -115,10 +115,12 @@ def test_bf16_output_without_norm_equals_plain_call():
 
 @pytest.mark.parametrize("fmt,M,K,N,sw", [("int5", 2 * 17408, 5120, 1, True), ("int5", 2 * 17408, 5120, 8, True),
                                           ("int5", 5120, 17408, 8, False), ("nvfp4", 7168, 5120, 4, False),
-                                          ("int4", 17408, 5120, 1, False)])
+                                          ("int4", 17408, 5120, 1, False), ("int4", 2 * 17408, 5120, 2, True),
+                                          ("int5", 2 * 17408, 5120, 4, True), ("nvfp4", 2 * 17408, 5120, 3, True)])
 def test_norm_full_size_sampled_rows(fmt, M, K, N, sw):
     """Full-size shapes (both activation staging paths: whole range in LDS,
-    and the ring); the oracle recomputes sampled row tiles."""
+    and the ring; gate/up pairs with whole-K waves at 1-2 tokens and the ring
+    at 3-4); the oracle recomputes sampled row tiles."""
     log("norm full", fmt, M, K, N, sw)
     rng = synthetic.rng_for(0, 8, M, K)
     wq, ws = qg().pack(fmt, synthetic.weights(rng, M, K))

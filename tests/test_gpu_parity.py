@@ -326,7 +326,7 @@ FULL = [("int4", 7168, 5120, 1), ("int4", 7168, 5120, 8), ("int4", 7168, 5120, 4
         # the QKV-like and the down-like grid)
         ("int5", 7168, 5120, 2), ("int8", 7168, 5120, 1), ("nvfp4", 7168, 5120, 8), ("int4", 5120, 17408, 1),
         ("int4", 5120, 17408, 8), ("int8", 5120, 17408, 1), ("int8", 5120, 17408, 4), ("nvfp4", 5120, 17408, 1),
-        ("nvfp4", 5120, 17408, 8)] + \
+        ("nvfp4", 5120, 17408, 8), ("nvfp4", 7168, 5120, 1)] + \
        [(f, 17408, 5120, n) for f in ("int4", "int5", "int8", "nvfp4") for n in (1, 2, 4, 8)]
 
 

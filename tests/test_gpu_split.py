@@ -72,7 +72,9 @@ SHAPES = [("int5", 2 * 17408, 5120, 1, True, True), ("nvfp4", 2 * 17408, 5120, 1
           ("int4", 2 * 17408, 5120, 8, True, True), ("int8", 2 * 17408, 5120, 8, True, True),
           ("int4", 17408, 5120, 1, False, True), ("int8", 17408, 5120, 8, False, True),
           ("nvfp4", 5120, 17408, 2, False, True), ("int8", 5120, 17408, 2, False, True),
-          ("int4", 2 * 17408, 5120, 2, True, False), ("int4", 7168, 5120, 2, False, False)]
+          ("int4", 2 * 17408, 5120, 2, True, False), ("int4", 7168, 5120, 2, False, False),
+          # gate/up pairs at 5-8 tokens read their activations by direct loads
+          ("int5", 2 * 17408, 5120, 5, True, True), ("nvfp4", 2 * 17408, 5120, 6, True, True)]
 
 
 @pytest.mark.parametrize("fmt,M,K,N,sw,taken", SHAPES)
