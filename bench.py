@@ -416,7 +416,7 @@ def main():
         summarize_profile(a[0], cmds, pairs[0], pairs[1:])
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path (use --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
     import torch
