@@ -85,6 +85,7 @@ def load(require_torch: bool = True):
         "qgemv_act_quant": (I32, [P, I32, I64, P, P, P]),
         "qgemv_mx": (I32, [I32, P, P, P, P, P, P, I64, I64, I32, P]),
         "qgemv_mx_swiglu": (I32, [I32, P, P, P, P, P, I64, I64, I32, P]),
+        "qgemv_mx_swiglu_quant": (I32, [I32, P, P, P, P, P, P, P, I64, I64, I32, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -100,7 +101,8 @@ def symbols() -> list[str]:
             "qgemv_pack_codes", "qgemv", "qgemv_swiglu", "qgemv_ex", "qgemv_swiglu_ex", "qgemv_split_workspace_bytes",
             "qgemv_moe_workspace_bytes", "qgemv_moe", "qgemv_moe_noalloc", "qgemv_moe_noalloc_max_bytes",
             "qgemv_moe_index", "qgemv_moe_index_by", "qgemv_moe_route", "qgemv_moe_fused_workspace_bytes", "qgemv_moe_fused",
-            "qgemv_dequant", "qgemv_probe_read", "qgemv_act_quant", "qgemv_mx", "qgemv_mx_swiglu"]
+            "qgemv_dequant", "qgemv_probe_read", "qgemv_act_quant", "qgemv_mx", "qgemv_mx_swiglu",
+            "qgemv_mx_swiglu_quant"]
 
 
 def strerror(status: int) -> str:
@@ -354,6 +356,14 @@ def qgemv_mx_swiglu(fmt, wq, ws, xq, xs, h, I: int, K: int, N: int, stream=None)
     h [N][I] = silu(gate) * up."""
     _check(load().qgemv_mx_swiglu(_fmt(fmt), _ptr(wq), _ptr(ws), _ptr(xq), _ptr(xs), _ptr(h), I, K, N,
                                   _stream(stream)), "qgemv_mx_swiglu")
+
+
+def qgemv_mx_swiglu_quant(fmt, wq, ws, xq, xs, hq, hs, I: int, K: int, N: int, h=None, stream=None) -> None:
+    """qgemv_mx_swiglu whose output is bf16(h) quantised to MXFP8 as act_quant
+    does: codes hq [N][I] (uint8) and E8M0 scales hs [N][I/32] (uint8); h
+    [N][I] fp32, if given, also receives the h that was quantised."""
+    _check(load().qgemv_mx_swiglu_quant(_fmt(fmt), _ptr(wq), _ptr(ws), _ptr(xq), _ptr(xs), _ptr(h), _ptr(hq),
+                                        _ptr(hs), I, K, N, _stream(stream)), "qgemv_mx_swiglu_quant")
 
 
 def qgemv_probe_read(buf, nbytes: int, sink, stream=None) -> None:

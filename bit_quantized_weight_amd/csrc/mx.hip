@@ -19,6 +19,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <algorithm>
+
 #include "device.hpp"
 #include "layout.hpp"
 #include "mx.hpp"
@@ -90,7 +92,14 @@ struct MxArgs {
   uint32_t wq_bytes, ws_bytes, xq_bytes, xs_bytes;
   int M, K, KS, G, N, out_tiles, ks_per_wave;
   int up_tile0;           // SwiGLU: row tile of the first up row (gate rows come first)
+  uint8_t* hq;            // SwiGLU with quantised output: [N][M] E4M3 codes of bf16(h)
+  uint8_t* hs;            // and their E8M0 scales [N][M/32] (y, if not null, receives h too)
 };
+
+// bf16 bits of an fp32 value, round to nearest even
+__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
+}
 
 // operands of one k-step: activations of TB blocks of 16 tokens (shared by
 // the tiles) and NT weight tiles
@@ -154,11 +163,14 @@ __device__ __forceinline__ void mx_mma(f32x4 (&acc)[NT][TB], const MxStep<FMT, N
   }
 }
 
-// Workgroup = NT row tiles (SwiGLU: a gate tile and its up tile); its W
-// waves split the k-steps; the waves' partial sums meet in LDS and are added
-// in wave order (reproducible). TB blocks of 16 tokens (N <= 16 TB) share
-// every weight operand: one MFMA per tile, block and k-step.
-template <int FMT, int NT, bool SWIGLU, int TB>
+// Workgroup = NT row tiles (SwiGLU: NT/2 gate tiles and their up tiles); its
+// W waves split the k-steps; the waves' partial sums meet in LDS and are
+// added in wave order (reproducible). TB blocks of 16 tokens (N <= 16 TB)
+// share every weight operand: one MFMA per tile, block and k-step.
+// QH (SwiGLU, two gate/up pairs = 32 columns of h): the epilogue quantises
+// bf16(h) to MXFP8 exactly as qgemv_act_quant does, each 32-column block of a
+// token lying inside one workgroup; h itself is stored only if y is given.
+template <int FMT, int NT, bool SWIGLU, int TB, bool QH = false>
 __global__ __launch_bounds__(512) void k_mxgemv(MxArgs a) {
   extern __shared__ __attribute__((aligned(16))) float red[];   // [W][NT][TB][64 lanes][4]
   const int lane = threadIdx.x & 63;
@@ -169,13 +181,14 @@ __global__ __launch_bounds__(512) void k_mxgemv(MxArgs a) {
   const __amdgpu_buffer_rsrc_t ws = make_rsrc(a.ws, a.ws_bytes);
   const __amdgpu_buffer_rsrc_t xq = make_rsrc(a.xq, a.xq_bytes);
   const __amdgpu_buffer_rsrc_t xs = make_rsrc(a.xs, a.xs_bytes);
-  constexpr int TO = SWIGLU ? 1 : NT;     // output tiles per workgroup
-  static_assert(!SWIGLU || NT == 2, "SwiGLU pairs one gate tile with its up tile");
+  constexpr int TO = SWIGLU ? NT / 2 : NT;   // output tiles per workgroup
+  static_assert(!SWIGLU || NT % 2 == 0, "SwiGLU pairs each gate tile with its up tile");
+  static_assert(!QH || (SWIGLU && TO == 2), "the quantised output takes 32 columns of h per workgroup");
   int tile[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    const int ot = min((int)blockIdx.x * TO + (SWIGLU ? 0 : t), a.out_tiles - 1);
-    tile[t] = (SWIGLU && t == 1) ? a.up_tile0 + ot : ot;
+    const int ot = min((int)blockIdx.x * TO + (SWIGLU ? t % TO : t), a.out_tiles - 1);
+    tile[t] = (SWIGLU && t >= TO) ? a.up_tile0 + ot : ot;
   }
   // A row r of block b = token 16 b + r: rows past N start out of range
   uint32_t xrow[TB], srow[TB];
@@ -215,25 +228,62 @@ __global__ __launch_bounds__(512) void k_mxgemv(MxArgs a) {
     for (int b = 0; b < TB; ++b)
       *reinterpret_cast<f32x4*>(red + ((size_t)((wave * NT + t) * TB + b) * 64 + lane) * 4) = acc[t][b];
   __syncthreads();
+  float* hb = red + (size_t)W * NT * TB * 256;   // QH: h [16 TB tokens][16 TO columns]
   for (int o = threadIdx.x; o < TO * TB * 256; o += blockDim.x) {
     const int t = o / (TB * 256), rem = o - t * TB * 256;
     const int b = rem >> 8, tl = (rem >> 4) & 15, row = rem & 15;
     const int tok = 16 * b + tl;
     const int ot = (int)blockIdx.x * TO + t;
     const int col = ot * 16 + row;
-    if (tok >= a.N || ot >= a.out_tiles || col >= a.M) continue;
+    if (!QH && (tok >= a.N || ot >= a.out_tiles || col >= a.M)) continue;
     const int idx = b * 256 + ((tl >> 2) * 16 + row) * 4 + (tl & 3);
     float v = 0.f;
     for (int w = 0; w < W; ++w) v += red[(size_t)(w * NT + t) * TB * 256 + idx];
     const size_t at = (size_t)tok * a.M + col;
     if constexpr (SWIGLU) {
       float u = 0.f;
-      for (int w = 0; w < W; ++w) u += red[(size_t)(w * NT + 1) * TB * 256 + idx];
+      for (int w = 0; w < W; ++w) u += red[(size_t)(w * NT + TO + t) * TB * 256 + idx];
       v = v / (1.0f + expf(-v)) * u;
     } else {
       if (a.res) v += a.res[at];
     }
-    a.y[at] = v;
+    if constexpr (QH) {
+      hb[tok * (16 * TO) + t * 16 + row] = v;
+      if (a.y && tok < a.N) a.y[at] = v;
+    } else {
+      a.y[at] = v;
+    }
+  }
+  if constexpr (QH) {
+    __syncthreads();
+    // eight lanes per (token, 32-column block), four values each: the block's
+    // amax over the bf16 magnitudes as integers, X = floor(log2 amax) - 8 in
+    // [-127, 127], codes of bf16(h) * 2^-X (qgemv_act_quant's steps). The
+    // trip count is a multiple of 64, so the eight lanes run together.
+    for (int q = threadIdx.x; q < TB * 16 * 8; q += blockDim.x) {
+      const int tok = q >> 3, sub = q & 7;
+      const float* hv = hb + tok * 32 + sub * 4;
+      uint32_t bits[4], m = 0u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        bits[i] = bf16_rne_bits(hv[i]);
+        m = max(m, bits[i] & 0x7FFFu);
+      }
+      m = max(m, (uint32_t)__shfl_xor((int)m, 1, 8));
+      m = max(m, (uint32_t)__shfl_xor((int)m, 2, 8));
+      m = max(m, (uint32_t)__shfl_xor((int)m, 4, 8));
+      int X = (int)(m >> 7) - 127 - 8;
+      X = m == 0 ? -127 : max(-127, min(127, X));
+      const float sc = __uint_as_float((uint32_t)(127 - X) << 23);   // 2^-X
+      uint32_t c = 0u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) c |= e4m3_rne_sat(__uint_as_float(bits[i] << 16) * sc) << (8 * i);
+      const int col0 = (int)blockIdx.x * 32 + sub * 4;
+      if (tok < a.N && col0 < a.M) {
+        *reinterpret_cast<uint32_t*>(a.hq + (size_t)tok * a.M + col0) = c;
+        if (sub == 0) a.hs[(size_t)tok * (a.M / 32) + (col0 >> 5)] = (uint8_t)(X + 127);
+      }
+    }
   }
 }
 
@@ -327,20 +377,21 @@ MxShape mx_shape_pairs(int fmt, int64_t pairs, int64_t KS, int N) {
   return s;
 }
 
-template <int FMT, int NT, bool SWIGLU, int TB>
+template <int FMT, int NT, bool SWIGLU, int TB, bool QH>
 hipError_t launch_mx_tb(const MxArgs& a, const MxShape& s, hipStream_t stream) {
-  const int TO = SWIGLU ? 1 : NT;
+  const int TO = SWIGLU ? NT / 2 : NT;
   const dim3 grid((unsigned)((a.out_tiles + TO - 1) / TO));
   const dim3 block((unsigned)(64 * s.waves));
-  const size_t lds = (size_t)s.waves * NT * TB * 256 * sizeof(float);
-  hipLaunchKernelGGL((k_mxgemv<FMT, NT, SWIGLU, TB>), grid, block, lds, stream, a);
+  const size_t lds = ((size_t)s.waves * NT * TB * 256 + (QH ? (size_t)TB * 16 * 16 * TO : 0)) * sizeof(float);
+  hipLaunchKernelGGL((k_mxgemv<FMT, NT, SWIGLU, TB, QH>), grid, block, lds, stream, a);
   return hipGetLastError();
 }
 
 // one or two blocks of 16 tokens
-template <int FMT, int NT, bool SWIGLU = false>
+template <int FMT, int NT, bool SWIGLU = false, bool QH = false>
 hipError_t launch_mx(const MxArgs& a, const MxShape& s, hipStream_t stream) {
-  return a.N > 16 ? launch_mx_tb<FMT, NT, SWIGLU, 2>(a, s, stream) : launch_mx_tb<FMT, NT, SWIGLU, 1>(a, s, stream);
+  return a.N > 16 ? launch_mx_tb<FMT, NT, SWIGLU, 2, QH>(a, s, stream)
+                  : launch_mx_tb<FMT, NT, SWIGLU, 1, QH>(a, s, stream);
 }
 
 }  // namespace
@@ -376,14 +427,18 @@ extern "C" int qgemv_act_quant(const void* x, int N, int64_t K, uint8_t* codes, 
 namespace {
 
 // Mout output columns; Mpacked packed rows (SwiGLU: 2 Mout, gate rows first)
+// hq, hs (SwiGLU only): MXFP8 codes and scales of bf16(h) instead of y
 int run_mx(int fmt, const void* wq, const void* ws, const uint8_t* xq, const uint8_t* xs, const float* residual,
-           float* y, int64_t Mout, int64_t Mpacked, int64_t K, int N, bool swiglu, hipStream_t stream) {
+           float* y, int64_t Mout, int64_t Mpacked, int64_t K, int N, bool swiglu, hipStream_t stream,
+           uint8_t* hq = nullptr, uint8_t* hs = nullptr) {
+  const bool qh = hq != nullptr;
   if (fmt != MXFP8 && fmt != MXFP4) return QGEMV_EFORMAT;
-  if (!wq || !ws || !xq || !xs || !y) return QGEMV_EINVAL;
+  if (!wq || !ws || !xq || !xs || (!y && !qh) || (qh && (!hs || !swiglu))) return QGEMV_EINVAL;
   if (Mout < 1 || K < 32 || Mpacked > (1 << 24)) return QGEMV_EINVAL;
   if (K % 32) return QGEMV_EALIGN;
   if (N < 1 || N > 32) return QGEMV_EUNSUPPORTED;
-  if (!al16(wq) || !al16(ws) || !al16(xq) || !al4(y) || (residual && !al4(residual))) return QGEMV_EALIGN;
+  if (!al16(wq) || !al16(ws) || !al16(xq) || !al4(y) || (residual && !al4(residual)) || !al4(hq)) return QGEMV_EALIGN;
+  if (qh && Mout % 32) return QGEMV_EALIGN;
   Geom g;
   if (!geom(fmt, Mpacked, K, &g)) return QGEMV_EINVAL;
   // k-steps past a wave's range are loaded with an out-of-range lane offset
@@ -409,11 +464,23 @@ int run_mx(int fmt, const void* wq, const void* ws, const uint8_t* xq, const uin
   a.N = N;
   a.out_tiles = (int)((Mout + 15) / 16);
   a.up_tile0 = swiglu ? (int)(Mout / 16) : 0;
+  a.hq = hq;
+  a.hs = hs;
   MxShape s = mx_shape(fmt, a.out_tiles, g.KS, N);
   if (swiglu) s = mx_shape_pairs(fmt, a.out_tiles, g.KS, N);
+  // the quantised SwiGLU's workgroups own two gate/up pairs: half the
+  // k-steps per wave keeps a wave's bytes those of the plain launch (measured
+  // faster for MXFP8 at every N and for MXFP4 from 8 tokens; MXFP4 at one
+  // token keeps the plain split)
+  if (qh && (fmt == MXFP8 || N >= 8)) {
+    const int64_t kpw = std::max<int64_t>((g.KS + 7) / 8, s.kpw / 2);
+    s.kpw = (int)kpw;
+    s.waves = (int)((g.KS + kpw - 1) / kpw);
+  }
   a.ks_per_wave = s.kpw;
   hipError_t e;
-  if (swiglu) e = fmt == MXFP8 ? launch_mx<MXFP8, 2, true>(a, s, stream) : launch_mx<MXFP4, 2, true>(a, s, stream);
+  if (qh) e = fmt == MXFP8 ? launch_mx<MXFP8, 4, true, true>(a, s, stream) : launch_mx<MXFP4, 4, true, true>(a, s, stream);
+  else if (swiglu) e = fmt == MXFP8 ? launch_mx<MXFP8, 2, true>(a, s, stream) : launch_mx<MXFP4, 2, true>(a, s, stream);
   else if (fmt == MXFP8) e = s.nt == 1 ? launch_mx<MXFP8, 1>(a, s, stream) : launch_mx<MXFP8, 2>(a, s, stream);
   else e = s.nt == 1 ? launch_mx<MXFP4, 1>(a, s, stream) : launch_mx<MXFP4, 2>(a, s, stream);
   return e == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
@@ -431,4 +498,13 @@ extern "C" int qgemv_mx_swiglu(int fmt, const void* wq, const void* ws, const ui
   if (I < 1) return QGEMV_EINVAL;
   if (I % 16) return QGEMV_EALIGN;
   return run_mx(fmt, wq, ws, xq, xs, nullptr, h, I, 2 * I, K, N, true, stream);
+}
+
+extern "C" int qgemv_mx_swiglu_quant(int fmt, const void* wq, const void* ws, const uint8_t* xq, const uint8_t* xs,
+                                     float* h, uint8_t* hq, uint8_t* hs, int64_t I, int64_t K, int N,
+                                     hipStream_t stream) {
+  if (!hq || !hs || I < 1) return QGEMV_EINVAL;
+  if (I % 32) return QGEMV_EALIGN;
+  if ((uint64_t)N * (uint64_t)I >= (1ull << 31)) return QGEMV_EUNSUPPORTED;
+  return run_mx(fmt, wq, ws, xq, xs, nullptr, h, I, 2 * I, K, N, true, stream, hq, hs);
 }

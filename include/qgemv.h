@@ -377,6 +377,19 @@ int qgemv_mx(int fmt, const void* wq, const void* ws, const uint8_t* xq, const u
 int qgemv_mx_swiglu(int fmt, const void* wq, const void* ws, const uint8_t* xq, const uint8_t* xs, float* h,
                     int64_t I, int64_t K, int N, hipStream_t stream);
 
+/* qgemv_mx_swiglu with h handed on already quantised for the next MX
+ * projection (NInfer article, section 2: SwiGLU fused into the matmul;
+ * Decapybara page, kernel list: the dynamic 32-element MXFP8 activation
+ * quantiser): writes the E4M3 codes hq [N][I] and E8M0 scales hs [N][I/32]
+ * that qgemv_act_quant gives for bf16(h) (h rounded to bf16, nearest even),
+ * in one launch instead of two. h [N][I] fp32 may be NULL; if given it also
+ * receives the h that was quantised (within qgemv_mx_swiglu's tolerance of
+ * the exact SwiGLU; its K split differs, so its bits may differ from
+ * qgemv_mx_swiglu's). I % 32 == 0 (QGEMV_EALIGN); hq 4-byte aligned; all
+ * device; other arguments as qgemv_mx_swiglu. */
+int qgemv_mx_swiglu_quant(int fmt, const void* wq, const void* ws, const uint8_t* xq, const uint8_t* xs, float* h,
+                          uint8_t* hq, uint8_t* hs, int64_t I, int64_t K, int N, hipStream_t stream);
+
 /* Measurement aid: stream-read `bytes` (multiple of 16) from `buf` with
  * 128-bit non-temporal loads, folding them into sink[0] (a device uint32).
  * Gives the achievable read bandwidth that the GEMV kernels approach. */

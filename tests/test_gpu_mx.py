@@ -3,6 +3,9 @@ MXFP8 / MXFP4) against the oracle, through the C ABI.
 
   * act_quant: codes and E8M0 scales bit for bit (one correct result);
   * dequant dump: fp32 bits equal;
+  * qgemv_mx_swiglu_quant: codes and scales bit for bit against the oracle's
+    quantiser of bf16(h), for the h the call also returns (that h against
+    the oracle's SwiGLU at tolerance);
   * qgemv_mx: y against the oracle's GEMV of the dequantised MXFP8
     activations (quantised by the oracle, whose codes the device's equal
     bit for bit) and the dequantised weights, tolerance gemv_tolerance
@@ -188,6 +191,66 @@ def test_mx_swiglu_full_size_sampled_rows():
         Wg, Wu = rows(rt), rows(RT + rt)
         href, Th = G.swiglu_from(G.gemv(x, Wg), G.gemv(x, Wu), G.gemv_tolerance(x, Wg), G.gemv_tolerance(x, Wu))
         check_tol(hg[:, rt * 16:(rt + 1) * 16], href, Th, f"tile {rt}")
+
+
+def _swiglu_quant_case(fmt, wq, ws, xb, I, K, N, rows=None):
+    """qgemv_mx_swiglu_quant's codes and scales, checked bit for bit against
+    the oracle's MXFP8 quantiser applied to bf16 of the h the call returns
+    (and against the device's act_quant of it), and that h against the
+    oracle's SwiGLU (all rows, or the row tiles listed)."""
+    xq, xs = _device_quant(xb, N, K)
+    h = torch.full((N, I), float("nan"), dtype=torch.float32, device="cuda")
+    hq = torch.full((N, I), 0xAA, dtype=torch.uint8, device="cuda")
+    hs = torch.full((N, I // 32), 0xAA, dtype=torch.uint8, device="cuda")
+    qg().qgemv_mx_swiglu_quant(fmt, dev(wq, torch), dev(ws, torch), xq, xs, hq, hs, I, K, N, h=h)
+    torch.cuda.synchronize()
+    hg = h.cpu().numpy()
+    hb = synthetic.bf16_bits(hg)
+    codes, e = Q.mx_act_quant(hb)
+    got_c, got_e = hq.cpu().numpy(), hs.cpu().numpy()
+    assert np.array_equal(got_e, e), np.argwhere(got_e != e)[:5]
+    assert np.array_equal(got_c, codes), np.argwhere(got_c != codes)[:5]
+    dq, ds = _device_quant(hb, N, I)
+    assert np.array_equal(dq.cpu().numpy(), got_c) and np.array_equal(ds.cpu().numpy(), got_e)
+    # without h the codes are the same
+    hq2 = torch.zeros((N, I), dtype=torch.uint8, device="cuda")
+    hs2 = torch.zeros((N, I // 32), dtype=torch.uint8, device="cuda")
+    qg().qgemv_mx_swiglu_quant(fmt, dev(wq, torch), dev(ws, torch), xq, xs, hq2, hs2, I, K, N)
+    torch.cuda.synchronize()
+    assert np.array_equal(hq2.cpu().numpy(), got_c) and np.array_equal(hs2.cpu().numpy(), got_e)
+    x = G.mx_activations(xb)
+    q = L.unpack(fmt, 2 * I, K, wq, ws)
+    RT = I // 16
+    for rt in (range(RT) if rows is None else rows):
+        def tile(t):
+            sl = slice(t * 16, (t + 1) * 16)
+            return D.dequant(Q.Quantized(fmt, 16, K, q.codes[sl], e=q.e[sl]))
+        Wg, Wu = tile(rt), tile(RT + rt)
+        href, Th = G.swiglu_from(G.gemv(x, Wg), G.gemv(x, Wu), G.gemv_tolerance(x, Wg), G.gemv_tolerance(x, Wu))
+        check_tol(hg[:, rt * 16:(rt + 1) * 16], href, Th, f"h tile {rt}")
+    return hb
+
+
+@pytest.mark.parametrize("fmt", MX)
+@pytest.mark.parametrize("I,K,N", [(32, 128, 1), (64, 512, 1), (96, 160, 3), (256, 2048, 8), (128, 1024, 16),
+                                   (160, 640, 29), (64, 256, 32)])
+def test_mx_swiglu_quant_bit_exact(fmt, I, K, N):
+    log("mx swiglu quant", fmt, I, K, N)
+    wq, ws, xb = _mx_case(fmt, 2 * I, K, N, seed=3 * I + N)
+    _swiglu_quant_case(fmt, wq, ws, xb, I, K, N)
+
+
+@pytest.mark.parametrize("fmt,N", [("mxfp4", 1), ("mxfp8", 8)])
+def test_mx_swiglu_quant_full_size(fmt, N):
+    I, K = 17408, 5120
+    log("mx swiglu quant full", fmt, I, K, N)
+    rng = synthetic.rng_for(0, 36, I, K)
+    wq, ws = qg().pack(fmt, synthetic.weights(rng, 2 * I, K))
+    xb = synthetic.activations(rng, N, K, 0.01)
+    RT = I // 16
+    rows = sorted({0, 1, RT // 2, RT - 1, *np.random.default_rng(6).integers(0, RT, 3).tolist()})
+    hb = _swiglu_quant_case(fmt, wq, ws, xb, I, K, N, rows=rows)
+    assert np.count_nonzero(hb & 0x7FFF) > 0.99 * hb.size   # a live h, not zeros
 
 
 @pytest.mark.parametrize("fmt,M,K,N", [("mxfp8", 17408, 5120, 1), ("mxfp4", 17408, 5120, 8),

@@ -253,6 +253,13 @@ def test_mx_validation_codes():
     sw = lambda **kw: L.qgemv_mx_swiglu(kw.get("fmt", 5), FAKE, FAKE, FAKE, FAKE, FAKE, kw.get("I", 64),
                                          kw.get("K", 128), kw.get("N", 1), None)
     assert sw(fmt=3) == -2 and sw(I=0) == -1 and sw(I=24) == -3 and sw(N=33) == -7 and sw(K=40) == -3
+    def swq(**kw):
+        a = dict(fmt=5, hq=FAKE, hs=FAKE, I=64, K=128, N=1)
+        a.update(kw)
+        return L.qgemv_mx_swiglu_quant(a["fmt"], FAKE, FAKE, FAKE, FAKE, a.get("h"), a["hq"], a["hs"], a["I"], a["K"],
+                                       a["N"], None)
+    assert swq(fmt=3) == -2 and swq(I=0) == -1 and swq(I=48) == -3 and swq(N=33) == -7 and swq(K=40) == -3
+    assert swq(hq=None) == -1 and swq(hs=None) == -1 and swq(hq=FAKE + 2) == -3 and swq(h=FAKE + 2) == -3
     # MX weights are rejected by the bf16-activation entry points
     assert _gemv(fmt=5) == -2 and _gemv(fmt=6) == -2
     aq = lambda **kw: L.qgemv_act_quant(kw.get("x", FAKE), kw.get("N", 1), kw.get("K", 64), kw.get("c", FAKE),
